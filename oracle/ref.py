@@ -1,0 +1,172 @@
+"""ctypes binding of the fp64 CPU oracle (oracle/paro_ref.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg call this; the product package never imports it.  Argument
+marshalling only -- every number is computed by the C oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libparo_ref.so")
+SRC_PATH = os.path.join(HERE, "paro_ref.c")
+
+F16, BF16, F32, F64 = 0, 1, 2, 3
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PAIRS, ERR_CHECK_FAILED, ERR_NOMEM = range(7)
+
+
+def build(out_path: str = LIB_PATH, src_path: str = SRC_PATH, extra=()) -> str:
+    """Compile the oracle with gcc (plain C99 + OpenMP)."""
+    cmd = ["gcc", "-std=gnu99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-I", os.path.join(ROOT, "include"), src_path, "-o", out_path, "-lm", *extra]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+class RefLayer(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int64), ("out_features", ctypes.c_int64),
+                ("group_size", ctypes.c_int32), ("krot", ctypes.c_int32),
+                ("pairs", ctypes.c_void_p), ("theta", ctypes.c_void_p),
+                ("channel_scales", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
+                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p)]
+
+
+_lib = None
+_lib_path = None
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib, _lib_path
+    path = path or os.environ.get("PARO_REF_LIB") or LIB_PATH
+    if _lib is not None and _lib_path == path:
+        return _lib
+    if path == LIB_PATH and (not os.path.exists(path) or
+                             os.path.getmtime(path) < max(os.path.getmtime(SRC_PATH), os.path.getmtime(
+                                 os.path.join(ROOT, "include", "paro_ref.h")))):
+        build(path)
+    lib = ctypes.CDLL(path)
+    P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.paro_ref_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.paro_ref_f16_to_double.restype = D
+    lib.paro_ref_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.paro_ref_bf16_to_double.restype = D
+    lib.paro_ref_round_f16.argtypes = [D]
+    lib.paro_ref_round_f16.restype = ctypes.c_uint16
+    lib.paro_ref_round_bf16.argtypes = [D]
+    lib.paro_ref_round_bf16.restype = ctypes.c_uint16
+    lib.paro_ref_round_array.argtypes = [P, I64, I32, P]
+    lib.paro_ref_check_pairs.argtypes = [P]
+    lib.paro_ref_scale_rotate.argtypes = [P, P, I32, I64, P, I32]
+    lib.paro_ref_unpack.argtypes = [P, P, P]
+    lib.paro_ref_dequant.argtypes = [P, P, I32]
+    lib.paro_ref_linear.argtypes = [P, P, I32, I64, P, I32]
+    lib.paro_linear_ref_check.argtypes = [P, P, I32, I64, P, I32, P, D, I32, P, P]
+    lib.paro_ref_threads.argtypes = [I32]
+    for name in ("paro_ref_round_array", "paro_ref_check_pairs", "paro_ref_scale_rotate",
+                 "paro_ref_unpack", "paro_ref_dequant", "paro_ref_linear",
+                 "paro_linear_ref_check", "paro_ref_threads"):
+        getattr(lib, name).restype = I32
+    _lib, _lib_path = lib, path
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def ref_layer(layer):
+    """RefLayer struct for a synth.Layer-like object (arrays stay owned by it)."""
+    for name in ("pairs", "theta", "channel_scales", "qweight", "qzeros", "scales", "bias"):
+        a = getattr(layer, name)
+        if a is not None and not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{name} must be C-contiguous")
+    return RefLayer(layer.in_features, layer.out_features, layer.group_size, layer.krot,
+                    _ptr(layer.pairs), _ptr(layer.theta), _ptr(layer.channel_scales),
+                    _ptr(layer.qweight), _ptr(layer.qzeros), _ptr(layer.scales),
+                    _ptr(layer.bias))
+
+
+def _group(layer):
+    return layer.in_features if layer.group_size == -1 else layer.group_size
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise RuntimeError(f"{what} failed with oracle status {rc}")
+
+
+def threads(n_threads: int = 0) -> int:
+    return load().paro_ref_threads(n_threads)
+
+
+def f16_to_double(h) -> float:
+    return load().paro_ref_f16_to_double(int(h))
+
+
+def bf16_to_double(h) -> float:
+    return load().paro_ref_bf16_to_double(int(h))
+
+
+def round_array(v, dt: int) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _check(load().paro_ref_round_array(_ptr(v), v.size, dt, _ptr(out)), "round_array")
+    return out
+
+
+def check_pairs(layer) -> int:
+    return load().paro_ref_check_pairs(ctypes.byref(ref_layer(layer)))
+
+
+def scale_rotate(layer, x, x_dt: int, n_threads: int = 0) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    tokens = x.shape[0]
+    out = np.empty((tokens, layer.in_features), dtype=np.float64)
+    _check(load().paro_ref_scale_rotate(ctypes.byref(ref_layer(layer)), _ptr(x), x_dt,
+                                        tokens, _ptr(out), n_threads), "scale_rotate")
+    return out
+
+
+def unpack(layer):
+    I, O = layer.in_features, layer.out_features
+    q = np.empty((I, O), dtype=np.uint8)
+    z = np.empty((I // _group(layer), O), dtype=np.uint8)
+    _check(load().paro_ref_unpack(ctypes.byref(ref_layer(layer)), _ptr(q), _ptr(z)), "unpack")
+    return q, z
+
+
+def dequant(layer, n_threads: int = 0) -> np.ndarray:
+    w = np.empty((layer.in_features, layer.out_features), dtype=np.float64)
+    _check(load().paro_ref_dequant(ctypes.byref(ref_layer(layer)), _ptr(w), n_threads), "dequant")
+    return w
+
+
+def linear(layer, x, x_dt: int, n_threads: int = 0) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    y = np.empty((x.shape[0], layer.out_features), dtype=np.float64)
+    _check(load().paro_ref_linear(ctypes.byref(ref_layer(layer)), _ptr(x), x_dt, x.shape[0],
+                                  _ptr(y), n_threads), "linear")
+    return y
+
+
+def paro_linear_ref_check(layer, x, x_dt: int, y=None, y_dt: int = F32,
+                          rel_tol: float = 5e-3, n_threads: int = 0, want_ref: bool = False):
+    """Run the oracle's check.  Returns (status, max_abs_err, max_abs_ref, y_ref|None)."""
+    x = np.ascontiguousarray(x)
+    tokens = x.shape[0]
+    yref = np.empty((tokens, layer.out_features), dtype=np.float64) if want_ref else None
+    if y is not None:
+        y = np.ascontiguousarray(y)
+    err, ref = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    rc = load().paro_linear_ref_check(ctypes.byref(ref_layer(layer)), _ptr(x), x_dt, tokens,
+                                      _ptr(y), y_dt, _ptr(yref), rel_tol, n_threads,
+                                      ctypes.byref(err), ctypes.byref(ref))
+    return rc, err.value, ref.value, yref

@@ -1,0 +1,58 @@
+"""Planted mistakes in the oracle must fail its pins (CPU only).
+
+Each case copies oracle/paro_ref.c, plants one plausible mistake (a dropped
+term, a wrong sign, index, operand or order), compiles the copy with gcc and
+runs the pin suite (tests/test_oracle_pins.py) against it in a subprocess.
+The suite must fail for every mutant: that is what makes the pins a check of
+the oracle rather than of themselves.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import ref
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "b_prime_sign": ("row[j] = -a * s + b * c;", "row[j] = a * s + b * c;"),
+    "a_prime_sign": ("row[i] = a * c + b * s;", "row[i] = a * c - b * s;"),
+    "aliased_update": ("row[j] = -a * s + b * c;", "row[j] = -row[i] * s + b * c;"),
+    "theta_group_offset": ("g * (G / 2) + p;", "p;"),
+    "pair_members_swapped": (
+        "const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];\n"
+        "          const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];",
+        "const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];\n"
+        "          const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];"),
+    "stage_order_reversed": ("for (int t = 0; t < L->krot; ++t) {\n      for (int64_t g = 0; g < ngroups",
+                             "for (int t = L->krot - 1; t >= 0; --t) {\n      for (int64_t g = 0; g < ngroups"),
+    "channel_scale_divides": ("* (double)L->channel_scales[k];", "/ (double)L->channel_scales[k];"),
+    "awq_order_sequential": ("{0, 4, 1, 5, 2, 6, 3, 7}", "{0, 1, 2, 3, 4, 5, 6, 7}"),
+    "zero_not_subtracted": ("(double)(q - z) * s;", "(double)(q) * s;"),
+    "bias_dropped": ("y_out[m * O + n0 + n] = acc[n] + b;", "y_out[m * O + n0 + n] = acc[n];"),
+    "group_index_transposed": ("const int64_t g = k / G;", "const int64_t g = k % (I / G);"),
+    "f16_exponent_bias": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "rounding_ties_away": ("return rint(a / quantum) * quantum;", "return round(a / quantum) * quantum;"),
+    "bf16_fraction_bits": ("ldexp((double)(128 + f), e - 134)", "ldexp((double)(128 + f), e - 133)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    find, repl = MUTANTS[name]
+    with open(ref.SRC_PATH) as f:
+        src = f.read()
+    assert src.count(find) == 1, f"mutation anchor for {name} not unique/present"
+    mutant_src = tmp_path / "paro_ref_mutant.c"
+    mutant_src.write_text(src.replace(find, repl))
+    lib = tmp_path / "libparo_ref_mutant.so"
+    ref.build(str(lib), str(mutant_src))
+    env = dict(os.environ, PARO_REF_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(HERE, "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, timeout=600)
+    # exit code 1 = some pin failed (not a crash or a collection error)
+    assert r.returncode == 1, f"mutant {name}: pytest exit {r.returncode}:\n{r.stdout[-2000:]}"

@@ -1,0 +1,433 @@
+"""Pins for the fp64 CPU oracle (oracle/paro_ref.c), CPU only.
+
+The oracle is checked against things other than itself:
+  * hand-worked values derived from the pages' formulas (tests/golden/*.json,
+    each with its citation and derivation),
+  * closed forms and invariants the pages state (inverse = reversed stages
+    with negated angles, orthogonality, X_r W_r^T = X W^T, the equivalent
+    weight, the identity state),
+  * brute force (dense Givens matrices multiplied out; numpy's fp16 cast;
+    exhaustive decode of all 2^16 bit patterns),
+  * an independent vectorised numpy implementation fed with the generator's
+    raw codes (not the packed words the oracle reads).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _angle(expr):
+    return float(eval(expr, {"pi": math.pi, "sqrt": math.sqrt}))
+
+
+def tiny_layer(I, G, krot, pairs, theta, cs, O=8):
+    """A layer whose weights are irrelevant (rotation-only checks)."""
+    ng = I // (I if G == -1 else G)
+    return synth.Layer(
+        I, O, G, krot,
+        np.ascontiguousarray(np.asarray(pairs, dtype=np.int16).reshape(krot, I)),
+        np.ascontiguousarray(np.asarray(theta, dtype=np.float32).reshape(krot, I // 2)),
+        np.ascontiguousarray(np.asarray(cs, dtype=np.float32).reshape(I)),
+        np.zeros((I, O // 8), np.int32), np.zeros((ng, O // 8), np.int32),
+        np.zeros((ng, O), np.uint16), None)
+
+
+def dense_rotation(layer):
+    """Brute force: R = R_0 R_1 ... R_{krot-1}, each R_t an explicit matrix of
+    disjoint Givens blocks acting on row vectors (x' = x R_t)."""
+    I, krot = layer.in_features, layer.krot
+    G = I if layer.group_size == -1 else layer.group_size
+    R = np.eye(I)
+    for t in range(krot):
+        Rt = np.eye(I)
+        for g in range(I // G):
+            for p in range(G // 2):
+                i = g * G + int(layer.pairs[t, g * G + 2 * p])
+                j = g * G + int(layer.pairs[t, g * G + 2 * p + 1])
+                th = float(layer.theta[t, g * (G // 2) + p])
+                c, s = math.cos(th), math.sin(th)
+                Rt[i, i], Rt[j, j] = c, c
+                Rt[j, i], Rt[i, j] = s, -s
+        R = R @ Rt
+    return R
+
+
+def random_layer(I, O, G=128, krot=8, seed=0, **kw):
+    return synth.make_layer(100 + seed, 0, I, O, G, krot, **kw)
+
+
+def x_to_f64(x, dt):
+    if dt == synth.F16:
+        return x.view(np.float16).astype(np.float64)
+    if dt == synth.BF16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def numpy_linear(layer, x, dt):
+    """Independent vectorised implementation from the generator's raw codes."""
+    I, O, krot = layer.in_features, layer.out_features, layer.krot
+    G = I if layer.group_size == -1 else layer.group_size
+    ng = I // G
+    xs = x_to_f64(x, dt) * layer.channel_scales.astype(np.float64)[None, :]
+    base = (np.arange(ng) * G)[:, None]
+    for t in range(krot):
+        pr = layer.pairs[t].astype(np.int64).reshape(ng, G // 2, 2)
+        ia, ib = (base + pr[:, :, 0]).ravel(), (base + pr[:, :, 1]).ravel()
+        th = layer.theta[t].astype(np.float64)
+        c, s = np.cos(th), np.sin(th)
+        a, b = xs[:, ia].copy(), xs[:, ib].copy()
+        xs[:, ia] = a * c + b * s
+        xs[:, ib] = -a * s + b * c
+    sc = layer.scales.view(np.float16).astype(np.float64)
+    zrep = np.repeat(layer.z.astype(np.float64), G, axis=0)
+    srep = np.repeat(sc, G, axis=0)
+    w = (layer.q.astype(np.float64) - zrep) * srep
+    y = xs @ w
+    if layer.bias is not None:
+        y = y + layer.bias.view(np.float16).astype(np.float64)[None, :]
+    return y
+
+
+# --------------------------------------------------------------------------
+# Worked examples (tests/golden)
+# --------------------------------------------------------------------------
+
+def test_golden_rotation_g4_krot2():
+    fx = golden("rotation_g4_krot2.json")
+    theta = [[_angle(e) for e in row] for row in fx["theta_expr"]]
+    L = tiny_layer(fx["in_features"], fx["group_size"], fx["krot"], fx["pairs"], theta,
+                   fx["channel_scales"])
+    x = np.asarray([fx["x"]], dtype=np.float64)
+    xr = ref.scale_rotate(L, x, ref.F64)[0]
+    np.testing.assert_allclose(xr, fx["x_r"], atol=fx["tol_abs"], rtol=0)
+    assert abs(float(xr @ xr) - fx["norm2"]) < 1e-5
+    # the first stage alone
+    L1 = tiny_layer(4, 4, 1, fx["pairs"][0], theta[0], fx["channel_scales"])
+    np.testing.assert_allclose(ref.scale_rotate(L1, x, ref.F64)[0], fx["after_stage0"], atol=1e-6)
+
+
+def test_golden_rotation_two_groups():
+    fx = golden("rotation_two_groups.json")
+    theta = [[_angle(e) for e in row] for row in fx["theta_expr"]]
+    L = tiny_layer(fx["in_features"], fx["group_size"], fx["krot"], fx["pairs"], theta,
+                   fx["channel_scales"])
+    xr = ref.scale_rotate(L, np.asarray([fx["x"]], np.float64), ref.F64)[0]
+    np.testing.assert_allclose(xr, fx["x_r"], atol=fx["tol_abs"], rtol=0)
+
+
+def test_golden_single_pair():
+    fx = golden("single_pair.json")
+    theta = [[_angle(e) for e in row] for row in fx["theta_expr"]]
+    L = tiny_layer(2, 2, 1, fx["pairs"], theta, fx["channel_scales"])
+    for case in fx["cases"]:
+        xr = ref.scale_rotate(L, np.asarray([case["x"]], np.float64), ref.F64)[0]
+        np.testing.assert_allclose(xr, case["x_r"], atol=fx["tol_abs"], rtol=0)
+
+
+def test_golden_awq_words():
+    fx = golden("awq_words.json")
+    for case in fx["cases"]:
+        word = np.array([int(case["word_hex"], 16)], dtype=np.uint32).view(np.int32)
+        # the generator's packer produces the worked word ...
+        assert synth.awq_pack(np.array([case["columns"]], np.uint8))[0, 0] == word[0]
+        # ... and the oracle unpacks it to the columns
+        L = synth.Layer(2, 8, 2, 1, np.array([[0, 1]], np.int16), np.zeros((1, 1), np.float32),
+                        np.ones(2, np.float32), np.array([[word[0]], [0]], np.int32),
+                        np.array([[word[0]]], np.int32), np.zeros((1, 8), np.uint16), None)
+        q, z = ref.unpack(L)
+        assert list(q[0]) == case["columns"]
+        assert list(q[1]) == [0] * 8
+        assert list(z[0]) == case["columns"]
+
+
+def test_golden_dequant_tie():
+    fx = golden("dequant_tie.json")
+    qc = np.zeros((2, 8), np.uint8)
+    zc = np.zeros((1, 8), np.uint8)
+    qc[0, 5], zc[0, 5] = fx["q"], fx["z"]
+    sc = np.zeros((1, 8), np.uint16)
+    sc[0, 5] = int(fx["scale_bits_hex"], 16)
+    L = synth.Layer(2, 8, 2, 1, np.array([[0, 1]], np.int16), np.zeros((1, 1), np.float32),
+                    np.ones(2, np.float32), synth.awq_pack(qc), synth.awq_pack(zc), sc, None)
+    assert ref.f16_to_double(int(fx["scale_bits_hex"], 16)) == fx["scale_value"]
+    w = ref.dequant(L)
+    assert w[0, 5] == fx["w_exact"]
+    assert np.float32(w[0, 5]) == np.float32(fx["w_exact"])  # exact in fp32 too
+    assert ref.round_array([w[0, 5]], ref.F16)[0] == int(fx["w_f16_bits_hex"], 16)
+    assert ref.round_array([w[0, 5]], ref.BF16)[0] == int(fx["w_bf16_bits_hex"], 16)
+    # row 1 shares the group: (0 - 8) * s; every other column has scale 0
+    assert w[1, 5] == -8 * fx["scale_value"]
+    assert np.count_nonzero(w) == 2
+
+
+# --------------------------------------------------------------------------
+# Number formats: exhaustive decode, rounding vs library routines
+# --------------------------------------------------------------------------
+
+def test_f16_decode_exhaustive():
+    lib = ref.load()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([lib.paro_ref_f16_to_double(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_bf16_decode_exhaustive():
+    lib = ref.load()
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        want = (bits << 16).view(np.float32).astype(np.float64)
+    got = np.array([lib.paro_ref_bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def _rounding_probe_values(rng):
+    v = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e6, -1e6, 2.0 ** -24,
+         2.0 ** -25, 2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+         1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -11 + 2.0 ** -40]
+    v += list(rng.standard_normal(20000) * 10.0 ** rng.uniform(-9, 5, 20000))
+    # exact ties at several binades: k + 0.5 ulp
+    for e in range(-24, 16):
+        for k in range(0, 2048, 37):
+            v.append((1024 + k + 0.5) * 2.0 ** (e - 10))
+    return np.array(v, dtype=np.float64)
+
+
+def test_round_f16_matches_numpy():
+    rng = np.random.default_rng(1)
+    v = _rounding_probe_values(rng)
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    got = ref.round_array(v, ref.F16)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(2)
+    v32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.uniform(-30, 30, 20000).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.3895314e38, 3.4e38, 1e-39, -1e-40],
+                 dtype=np.float32),
+        # exact ties between bf16 neighbours (fp32 values with bit 15 set, low bits clear)
+        ((rng.integers(0x00800000, 0x7F000000, 5000, dtype=np.uint64).astype(np.uint32) & 0xFFFF0000) | 0x8000).view(np.float32),
+    ]).astype(np.float32)
+    want = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = ref.round_array(v32.astype(np.float64), ref.BF16)
+    assert np.array_equal(got, want)
+    # a double just above a tie rounds up (a fp32 pre-rounding would lose this)
+    assert ref.round_array([1.0 + 2.0 ** -8 + 2.0 ** -40], ref.BF16)[0] == 0x3F81
+    assert ref.round_array([1.0 + 2.0 ** -8], ref.BF16)[0] == 0x3F80
+
+
+# --------------------------------------------------------------------------
+# Rotation invariants and brute force
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,krot,I", [(2, 1, 8), (4, 2, 8), (8, 3, 16), (16, 2, 32), (128, 8, 256),
+                                      (-1, 3, 64)])
+def test_staged_equals_dense_bruteforce(G, krot, I):
+    L = random_layer(I, 8, G, krot, seed=G + krot)
+    x = np.random.default_rng(abs(G)).standard_normal((5, I))
+    want = (x * L.channel_scales.astype(np.float64)) @ dense_rotation(L)
+    got = ref.scale_rotate(L, x, ref.F64)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def _inverse_layer(L):
+    """The inverse per the pages: reverse the stage order and negate the angles."""
+    return synth.Layer(L.in_features, L.out_features, L.group_size, L.krot,
+                       np.ascontiguousarray(L.pairs[::-1]),
+                       np.ascontiguousarray(-L.theta[::-1]),
+                       np.ones(L.in_features, np.float32), L.qweight, L.qzeros, L.scales, None)
+
+
+@pytest.mark.parametrize("G,krot", [(128, 8), (16, 3), (-1, 2)])
+def test_inverse_restores_input(G, krot):
+    L = random_layer(256, 8, G, krot, seed=3)
+    x = np.random.default_rng(3).standard_normal((7, 256))
+    xr = ref.scale_rotate(L, x, ref.F64)
+    back = ref.scale_rotate(_inverse_layer(L), xr, ref.F64)
+    want = x * L.channel_scales.astype(np.float64)
+    np.testing.assert_allclose(back, want, rtol=0, atol=1e-13 * np.abs(want).max())
+
+
+def test_orthogonality_and_norm():
+    L = random_layer(256, 8, 128, 8, seed=4, identity=False)
+    Lu = synth.Layer(256, 8, 128, 8, L.pairs, L.theta, np.ones(256, np.float32),
+                     L.qweight, L.qzeros, L.scales, None)
+    R = ref.scale_rotate(Lu, np.eye(256), ref.F64)  # rows of R
+    np.testing.assert_allclose(R @ R.T, np.eye(256), rtol=0, atol=1e-13)
+    # block diagonal: nothing crosses a group boundary
+    assert np.abs(R[:128, 128:]).max() == 0.0 and np.abs(R[128:, :128]).max() == 0.0
+    x = np.random.default_rng(4).standard_normal((9, 256))
+    xr = ref.scale_rotate(Lu, x, ref.F64)
+    np.testing.assert_allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+
+
+def test_group_locality():
+    L = random_layer(384, 8, 128, 4, seed=5)
+    x = np.random.default_rng(5).standard_normal((3, 384))
+    base = ref.scale_rotate(L, x, ref.F64)
+    th = L.theta.copy()
+    th[2, 64:128] += 0.3  # angles of group 1 at stage 2
+    L2 = synth.Layer(384, 8, 128, 4, L.pairs, th, L.channel_scales, L.qweight, L.qzeros,
+                     L.scales, None)
+    out = ref.scale_rotate(L2, x, ref.F64)
+    diff = np.abs(out - base).max(axis=0)
+    assert diff[:128].max() == 0.0 and diff[256:].max() == 0.0
+    assert diff[128:256].max() > 1e-3
+
+
+def test_stage_order_matters():
+    L = random_layer(128, 8, 128, 2, seed=6)
+    x = np.random.default_rng(6).standard_normal((2, 128))
+    swapped = synth.Layer(128, 8, 128, 2, np.ascontiguousarray(L.pairs[::-1]),
+                          np.ascontiguousarray(L.theta[::-1]), L.channel_scales, L.qweight,
+                          L.qzeros, L.scales, None)
+    assert np.abs(ref.scale_rotate(L, x, ref.F64) - ref.scale_rotate(swapped, x, ref.F64)).max() > 1e-3
+
+
+def test_pairs_must_be_permutations():
+    L = random_layer(256, 8, 128, 2, seed=7)
+    assert ref.check_pairs(L) == ref.OK
+    bad = L.pairs.copy()
+    bad[1, 130] = bad[1, 131]  # duplicate inside group 1 of stage 1
+    Lb = synth.Layer(256, 8, 128, 2, bad, L.theta, L.channel_scales, L.qweight, L.qzeros,
+                     L.scales, None)
+    assert ref.check_pairs(Lb) == ref.ERR_PAIRS
+    with pytest.raises(RuntimeError):
+        ref.scale_rotate(Lb, np.zeros((1, 256)), ref.F64)
+    out_of_range = L.pairs.copy()
+    out_of_range[0, 0] = 128
+    Lo = synth.Layer(256, 8, 128, 2, out_of_range, L.theta, L.channel_scales, L.qweight,
+                     L.qzeros, L.scales, None)
+    assert ref.check_pairs(Lo) == ref.ERR_PAIRS
+
+
+# --------------------------------------------------------------------------
+# Transform identities of the pages
+# --------------------------------------------------------------------------
+
+def test_transform_equivalence_without_quantization():
+    """X_r W_r^T = X W^T with X_r = X D^-1 R, W_r = W D R (stored cs = D^-1)."""
+    I, O = 256, 48
+    L = random_layer(I, O, 128, 8, seed=8)
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((6, I))
+    W = rng.standard_normal((O, I))
+    D = np.diag(1.0 / L.channel_scales.astype(np.float64))
+    Xr = ref.scale_rotate(L, X, ref.F64)
+    Wr = W @ D @ dense_rotation(L)
+    lhs, rhs = Xr @ Wr.T, X @ W.T
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12 * np.abs(rhs).max())
+
+
+def test_equivalent_weight_identity():
+    """Y = X (Q(W_r) R^T D^-1)^T + b, the equivalent weight in input coordinates."""
+    I, O = 256, 64
+    L = random_layer(I, O, 128, 8, seed=9, keep_codes=True)
+    x = synth.make_x(109, 0, 5, I, synth.F16)
+    y = ref.linear(L, x, ref.F16)
+    sc = L.scales.view(np.float16).astype(np.float64)
+    Wdeq_t = (L.q.astype(np.float64) - np.repeat(L.z, 128, 0)) * np.repeat(sc, 128, 0)  # (I, O)
+    Qwr = Wdeq_t.T                                   # Q(W_r), (O, I)
+    Dinv = np.diag(L.channel_scales.astype(np.float64))
+    W_eq = Qwr @ dense_rotation(L).T @ Dinv          # (O, I)
+    want = x_to_f64(x, synth.F16) @ W_eq.T + L.bias.view(np.float16).astype(np.float64)
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_identity_state_is_plain_dequant_gemm():
+    I, O = 384, 40
+    L = random_layer(I, O, 128, 8, seed=10, identity=True, keep_codes=True)
+    x = synth.make_x(110, 0, 4, I, synth.BF16)
+    sc = L.scales.view(np.float16).astype(np.float64)
+    W = (L.q.astype(np.float64) - np.repeat(L.z, 128, 0)) * np.repeat(sc, 128, 0)
+    want = np.matmul(x_to_f64(x, synth.BF16), W) + L.bias.view(np.float16).astype(np.float64)
+    np.testing.assert_allclose(ref.linear(L, x, ref.BF16), want, rtol=0,
+                               atol=1e-13 * np.abs(want).max())
+
+
+def test_unpack_roundtrip_and_dequant_bruteforce():
+    I, O, G = 256, 96, 64
+    L = random_layer(I, O, G, 2, seed=11, keep_codes=True)
+    q, z = ref.unpack(L)
+    assert np.array_equal(q, L.q) and np.array_equal(z, L.z)
+    w = ref.dequant(L)
+    sc = L.scales.view(np.float16).astype(np.float64)
+    for k in range(0, I, 17):
+        for n in range(0, O, 5):
+            assert w[k, n] == (int(L.q[k, n]) - int(L.z[k // G, n])) * sc[k // G, n]
+
+
+# --------------------------------------------------------------------------
+# The whole linear against an independent numpy implementation, and the check
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("I,O,G,krot,M,dt", [(256, 256, 128, 8, 4, synth.F16),
+                                              (384, 136, 128, 8, 3, synth.BF16),
+                                              (256, 64, 32, 3, 2, synth.F32),
+                                              (128, 16, -1, 1, 1, synth.F16)])
+def test_linear_matches_numpy_mirror(I, O, G, krot, M, dt):
+    L = random_layer(I, O, G, krot, seed=12 + I, keep_codes=True)
+    x = synth.make_x(112, I, M, I, dt)
+    want = numpy_linear(L, x, dt)
+    got = ref.linear(L, x, dt)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_workload0_matches_numpy_mirror():
+    (_, L, x), = list(synth.workload_layers(0, keep_codes=True))
+    want = numpy_linear(L, x, synth.F16)
+    got = ref.linear(L, x, ref.F16)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_ref_check_status():
+    (_, L, x), = list(synth.workload_layers(0))
+    rc, err, mref, yref = ref.paro_linear_ref_check(L, x, ref.F16, want_ref=True)
+    assert rc == ref.OK and mref > 0
+    y32 = yref.astype(np.float32)
+    rc, err, _, _ = ref.paro_linear_ref_check(L, x, ref.F16, y32, ref.F32)
+    assert rc == ref.OK and err < 1e-6 * mref
+    y16 = ref.round_array(yref, ref.F16)
+    rc, err, _, _ = ref.paro_linear_ref_check(L, x, ref.F16, y16, ref.F16)
+    assert rc == ref.OK and err <= 2.0 ** -11 * mref
+    bad = y32.copy()
+    bad[1, 7] += np.float32(0.01 * mref)
+    rc, err, _, _ = ref.paro_linear_ref_check(L, x, ref.F16, bad, ref.F32)
+    assert rc == ref.ERR_CHECK_FAILED and err > 5e-3 * mref
+    nan = y32.copy()
+    nan[0, 0] = np.nan
+    rc, _, _, _ = ref.paro_linear_ref_check(L, x, ref.F16, nan, ref.F32)
+    assert rc == ref.ERR_CHECK_FAILED
+
+
+def test_zero_tokens_and_bad_shapes():
+    (_, L, x), = list(synth.workload_layers(0))
+    assert ref.paro_linear_ref_check(L, x[:0], ref.F16)[0] == ref.OK
+    bad = synth.Layer(256, 252, 128, 8, L.pairs, L.theta, L.channel_scales, L.qweight,
+                      L.qzeros, L.scales, None)
+    assert ref.paro_linear_ref_check(bad, x, ref.F16)[0] == ref.ERR_SHAPE
+    odd = synth.Layer(256, 256, 127, 8, L.pairs, L.theta, L.channel_scales, L.qweight,
+                      L.qzeros, L.scales, None)
+    assert ref.paro_linear_ref_check(odd, x, ref.F16)[0] == ref.ERR_SHAPE

@@ -1,0 +1,185 @@
+/*
+ * paro.h - C-ABI of libparo: the rotated W4A16 linear on MI355X (gfx950).
+ *
+ *   Y = (X . D^-1 . R) . Q(W_r)^T + b
+ *
+ * computed by hand-written HIP kernels.  Notation and stored tensors follow
+ * the "ParoQuant" page of the GPTQModel wiki (GPT-QModel 7.7.0):
+ *   - Concepts / Pairwise Givens rotations: within each group of G input
+ *     channels a stage splits the channels into disjoint pairs; a pair (a, b)
+ *     with angle theta becomes (a cos + b sin, -a sin + b cos); the krot
+ *     stages run in order; pair indices are local to their group.
+ *   - Concepts / Activation and weight transforms: X_r = X D^-1 R, and the
+ *     stored channel_scales are D^-1 (they multiply the activations);
+ *     Y = X_r Q(W_r)^T + b.
+ *   - Checkpoint and inference implementation / Stored tensors: qweight
+ *     (I, O/8) and qzeros (I/G, O/8) AWQ-packed int32, scales (I/G, O),
+ *     pairs int16 (krot, I), theta (krot, I/2), channel_scales (I), bias (O).
+ *   - Triton plans and tuning: the GEMM unpacks the 4-bit tile, subtracts the
+ *     zero points, multiplies by the group scales and accumulates in fp32.
+ *   - "GPTQ, GPTAQ, and RTN" wiki, quantizer: x_hat = scale * (q - zero).
+ *
+ * Readings of points the pages leave open (the same readings the CPU oracle
+ * takes, written independently there):
+ *   - pairs[t][g*G + 2p] and pairs[t][g*G + 2p + 1] are the local indices of
+ *     the first (a) and second (b) member of pair p of group g at stage t;
+ *     theta[t][g*G/2 + p] is its angle, in radians, fp32.
+ *   - AWQ word layout: bits 4s..4s+3 of qweight[k][w] hold column 8w + O(s)
+ *     with O = (0,2,4,6,1,3,5,7); qzeros uses the same layout per group.
+ *   - scales and bias are fp16 for every activation dtype; channel_scales is
+ *     fp32.
+ *
+ * Conventions for every entry point below:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch cuda memory)
+ *     owned by the caller; the library allocates nothing, keeps no pointer
+ *     after the call and performs no host synchronisation.  `layer` itself is
+ *     a host struct read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream); the
+ *     work is enqueued on it and outputs are valid once it completes.
+ *   - Return value: PARO_OK or a paro_status code.  Arguments are checked on
+ *     the host before anything is enqueued; on error nothing is launched and
+ *     paro_last_error() (thread-local) describes the failure.  Launch errors
+ *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128, O a multiple
+ *     of 8 and <= 2^21, I <= 2^24, tokens <= 2^21; x, y, x_r, w_out, qweight and scales 16-byte
+ *     aligned.  Other values give PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.
+ *   - Pair contents are NOT read on the host by the GPU entry points (they
+ *     are device memory); kernels mask every pair index into its group, so
+ *     an invalid schedule yields wrong numbers, never an out-of-bounds
+ *     access.  paro_validate_layer() checks a host copy.
+ */
+#ifndef PARO_H
+#define PARO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARO_ABI_VERSION 1
+
+typedef enum {
+  PARO_F16 = 0,  /* IEEE binary16 */
+  PARO_BF16 = 1, /* bfloat16      */
+  PARO_F32 = 2   /* IEEE binary32 */
+} paro_dtype;
+
+typedef enum {
+  PARO_OK = 0,
+  PARO_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  PARO_ERR_SHAPE = 2,       /* sizes inconsistent or out of range            */
+  PARO_ERR_DTYPE = 3,       /* dtype not allowed for this argument           */
+  PARO_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
+  PARO_ERR_UNSUPPORTED = 5, /* valid for the method, not on this GPU path    */
+  PARO_ERR_PAIRS = 6,       /* host-side pair schedule check failed          */
+  PARO_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required       */
+  PARO_ERR_HIP = 8          /* a HIP runtime call or launch failed           */
+} paro_status;
+
+/* Which kernel sequence paro_w4a16_linear_path() runs. */
+typedef enum {
+  PARO_PATH_AUTO = 0,         /* choose by shape (what paro_w4a16_linear does)   */
+  PARO_PATH_DECODE_FUSED = 1, /* one kernel: rotation in the activation-load
+                                 prologue + split-K MFMA GEMV; tokens <= 16      */
+  PARO_PATH_DECODE_SPLIT = 2, /* scale_rotate into the workspace, then the same
+                                 GEMV reading X_r; tokens <= 16                  */
+  PARO_PATH_PREFILL = 3       /* scale_rotate into the workspace, then the MFMA
+                                 GEMM with LDS-staged dequantized weight tiles   */
+} paro_path;
+
+/* One rotated W4 linear layer: sizes plus device pointers to its tensors. */
+typedef struct {
+  int64_t in_features;         /* I                                          */
+  int64_t out_features;        /* O                                          */
+  int32_t group_size;          /* G (128 on the GPU; -1 means I)             */
+  int32_t krot;                /* number of rotation stages                  */
+  const int16_t *pairs;        /* [krot][I]   local pair indices             */
+  const float *theta;          /* [krot][I/2] angles (radians)               */
+  const float *channel_scales; /* [I]         D^-1                           */
+  const int32_t *qweight;      /* [I][O/8]    AWQ-packed 4-bit codes         */
+  const int32_t *qzeros;       /* [I/G][O/8]  AWQ-packed 4-bit zero points   */
+  const uint16_t *scales;      /* [I/G][O]    fp16 group scales              */
+  const uint16_t *bias;        /* [O] fp16 or NULL                           */
+} paro_w4_layer;
+
+/*
+ * Channel scaling and pairwise rotation of activations ("ParoQuant" wiki,
+ * Concepts / Pairwise Givens rotations and Activation and weight transforms):
+ *   x_r[m][k] = ((x[m] . D^-1) . R)[k]      for m < tokens, k < I,
+ * computed in fp32 and rounded to nearest even into xr_dt.
+ *   x    : [tokens][I] x_dt in {F16, BF16}, row-major, contiguous.
+ *   x_r  : [tokens][I] xr_dt in {F16, BF16, F32}; may alias x exactly when
+ *          xr_dt == x_dt (in-place); any other overlap is not allowed.
+ * Uses layer->pairs, theta, channel_scales only.  tokens == 0 is a no-op.
+ */
+int paro_scale_rotate(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
+                      int64_t tokens, void *x_r, paro_dtype xr_dt, void *stream);
+
+/*
+ * AWQ unpack and affine dequantization of the stored weight ("ParoQuant"
+ * wiki, Stored tensors and Triton plans; "GPTQ, GPTAQ, and RTN" wiki,
+ * quantizer):
+ *   q_out[k][n] = code of column n, row k          (uint8, [I][O])
+ *   z_out[g][n] = zero point of column n, group g  (uint8, [I/G][O])
+ *   w_out[k][n] = (q[k][n] - z[k/G][n]) * s[k/G][n], computed exactly and
+ *                 rounded to nearest even into w_dt in {F16, BF16, F32}.
+ * Any of q_out, z_out, w_out may be NULL (not written); all NULL is a no-op.
+ * This materialises a dense weight for tests and for callers that want a
+ * library GEMM; the linear below never materialises it.
+ */
+int paro_w4_unpack_dequant(const paro_w4_layer *layer, uint8_t *q_out, uint8_t *z_out,
+                           void *w_out, paro_dtype w_dt, void *stream);
+
+/*
+ * The rotated W4A16 linear ("ParoQuant" wiki, Activation and weight
+ * transforms; Backend reference: ParoLinear flattens leading dims, rotates,
+ * applies the quantized projection and restores the shape):
+ *   y[m][n] = sum_k x_r[m][k] * (q[k][n] - z[k/G][n]) * s[k/G][n] + bias[n]
+ * with fp32 accumulation, bias added in fp32, one RNE rounding into y_dt.
+ *   x : [tokens][I] x_dt in {F16, BF16} (leading dims flattened by caller).
+ *   y : [tokens][O] y_dt == x_dt, or F32; must not overlap x.
+ *   workspace / workspace_bytes : device scratch of at least
+ *       paro_w4a16_linear_workspace_bytes(layer, tokens, x_dt, path) bytes,
+ *       16-byte aligned.  It MUST be zero-filled before its first use with
+ *       this library; every call that completes leaves its counter area zero
+ *       again, so one zeroed workspace serves any number of sequential calls.
+ *       Calls that overlap in time (other streams) need separate workspaces.
+ * paro_w4a16_linear picks the path by shape; _path forces one (tests and
+ * tuning).  Results of different paths agree to fp32-accumulation rounding;
+ * each path is deterministic (a repeated call gives identical bits).
+ */
+int paro_w4a16_linear(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
+                      int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                      size_t workspace_bytes, void *stream);
+int paro_w4a16_linear_path(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
+                           int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                           size_t workspace_bytes, void *stream, paro_path path);
+
+/* Bytes of workspace the linear needs for this shape and path (0 allowed). */
+size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,
+                                         paro_dtype x_dt, paro_path path);
+
+/* The path paro_w4a16_linear would take for this shape (never AUTO). */
+paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *layer, int64_t tokens);
+
+/*
+ * Host-side validation of a layer whose tensor pointers are HOST copies:
+ * shape rules (G even and dividing I, O % 8 == 0, krot >= 1) and that every
+ * pairs[t][g*G : (g+1)*G] is a permutation of 0..G-1.  Returns PARO_OK,
+ * PARO_ERR_SHAPE, PARO_ERR_NULL or PARO_ERR_PAIRS.  Reads no device memory.
+ */
+int paro_validate_layer(const paro_w4_layer *host_layer);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char *paro_last_error(void);
+
+/* PARO_ABI_VERSION of the loaded library. */
+int paro_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARO_H */

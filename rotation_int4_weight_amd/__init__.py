@@ -1,0 +1,18 @@
+"""rotation_int4_weight_amd: the rotated W4A16 linear of ParoQuant on MI355X.
+
+    Y = (X . D^-1 . R) . Q(W_r)^T + b
+
+computed by hand-written HIP kernels for gfx950 behind the C-ABI of
+include/paro.h (libparo.so).  This package is the thin ctypes binding with the
+same entry-point names; PyTorch supplies device memory and streams only.
+"""
+from ._lib import (BF16, EXPORTS, F16, F32, PATH_AUTO, PATH_DECODE_FUSED, PATH_DECODE_SPLIT,
+                   PATH_PREFILL, DeviceLayer, ParoError, load, make_workspace,
+                   paro_abi_version, paro_last_error, paro_scale_rotate,
+                   paro_validate_layer, paro_w4_unpack_dequant, paro_w4a16_linear,
+                   paro_w4a16_linear_choose_path, paro_w4a16_linear_workspace_bytes)
+
+__all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "PATH_DECODE_SPLIT",
+           "PATH_PREFILL", "DeviceLayer", "ParoError", "load", "make_workspace", "paro_abi_version",
+           "paro_last_error", "paro_scale_rotate", "paro_validate_layer", "paro_w4_unpack_dequant",
+           "paro_w4a16_linear", "paro_w4a16_linear_choose_path", "paro_w4a16_linear_workspace_bytes"]

@@ -1,0 +1,188 @@
+"""ctypes binding of libparo (include/paro.h).
+
+Argument marshalling only: every step of the rotated W4A16 linear runs in the
+HIP kernels of libparo.so.  PyTorch provides device memory and streams.  The
+library must have been built (rotation_int4_weight_amd.build); there is no
+fallback of any kind: a missing library or a failing call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libparo.so")
+
+F16, BF16, F32 = 0, 1, 2
+PATH_AUTO, PATH_DECODE_FUSED, PATH_DECODE_SPLIT, PATH_PREFILL = 0, 1, 2, 3
+STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DTYPE",
+          4: "PARO_ERR_ALIGN", 5: "PARO_ERR_UNSUPPORTED", 6: "PARO_ERR_PAIRS",
+          7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
+EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
+           "paro_w4a16_linear_path", "paro_w4a16_linear_workspace_bytes",
+           "paro_w4a16_linear_choose_path", "paro_validate_layer", "paro_last_error",
+           "paro_abi_version")
+
+
+class ParoError(RuntimeError):
+    def __init__(self, status: int, what: str, msg: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ParoLayerC(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int64), ("out_features", ctypes.c_int64),
+                ("group_size", ctypes.c_int32), ("krot", ctypes.c_int32),
+                ("pairs", ctypes.c_void_p), ("theta", ctypes.c_void_p),
+                ("channel_scales", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
+                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libparo.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m rotation_int4_weight_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.paro_scale_rotate.argtypes = [P, P, I32, I64, P, I32, P]
+    lib.paro_w4_unpack_dequant.argtypes = [P, P, P, P, I32, P]
+    lib.paro_w4a16_linear.argtypes = [P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_w4a16_linear_path.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
+    lib.paro_w4a16_linear_workspace_bytes.argtypes = [P, I64, I32, I32]
+    lib.paro_w4a16_linear_workspace_bytes.restype = SZ
+    lib.paro_w4a16_linear_choose_path.argtypes = [P, I64]
+    lib.paro_validate_layer.argtypes = [P]
+    lib.paro_last_error.argtypes = []
+    lib.paro_last_error.restype = ctypes.c_char_p
+    lib.paro_abi_version.argtypes = []
+    for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
+                 "paro_w4a16_linear_path", "paro_w4a16_linear_choose_path",
+                 "paro_validate_layer", "paro_abi_version"):
+        getattr(lib, name).restype = I32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ParoError(rc, what, load().paro_last_error().decode())
+
+
+def paro_abi_version() -> int:
+    return load().paro_abi_version()
+
+
+def paro_last_error() -> str:
+    return load().paro_last_error().decode()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    import torch
+    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}[t.dtype]
+
+
+class DeviceLayer:
+    """A layer's stored tensors in device memory plus its C descriptor.
+
+    Built from any object with the synth.Layer fields (numpy host arrays);
+    torch allocates and owns the device copies.
+    """
+
+    def __init__(self, host, device="cuda"):
+        import torch
+        self.in_features = int(host.in_features)
+        self.out_features = int(host.out_features)
+        self.group_size = int(host.group_size)
+        self.krot = int(host.krot)
+
+        def up(a, dtype):
+            return None if a is None else torch.from_numpy(a).to(device=device).view(dtype).contiguous()
+
+        self.pairs = up(host.pairs, torch.int16)
+        self.theta = up(host.theta, torch.float32)
+        self.channel_scales = up(host.channel_scales, torch.float32)
+        self.qweight = up(host.qweight, torch.int32)
+        self.qzeros = up(host.qzeros, torch.int32)
+        self.scales = up(host.scales.view("int16"), torch.float16)
+        self.bias = None if host.bias is None else up(host.bias.view("int16"), torch.float16)
+        self.c = ParoLayerC(self.in_features, self.out_features, self.group_size, self.krot,
+                            self.pairs.data_ptr(), self.theta.data_ptr(),
+                            self.channel_scales.data_ptr(), self.qweight.data_ptr(),
+                            self.qzeros.data_ptr(), self.scales.data_ptr(),
+                            None if self.bias is None else self.bias.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def paro_validate_layer(host) -> None:
+    """Host-side check of a layer's pair schedule and shape rules (numpy arrays)."""
+    import numpy as np
+    pairs = np.ascontiguousarray(host.pairs, dtype=np.int16)
+    c = ParoLayerC(int(host.in_features), int(host.out_features), int(host.group_size),
+                   int(host.krot), pairs.ctypes.data, None, None, None, None, None, None)
+    _check(load().paro_validate_layer(ctypes.byref(c)), "paro_validate_layer")
+
+
+def paro_scale_rotate(layer: DeviceLayer, x, x_r, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16 cuda tensor; x_r: (tokens, I) fp16/bf16/fp32 output."""
+    _check(load().paro_scale_rotate(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(x_r), _dt(x_r),
+                                    _stream_handle(stream)), "paro_scale_rotate")
+
+
+def paro_w4_unpack_dequant(layer: DeviceLayer, q_out=None, z_out=None, w_out=None, stream=None) -> None:
+    w_dt = _dt(w_out) if w_out is not None else F32
+    _check(load().paro_w4_unpack_dequant(layer.ref, _ptr(q_out), _ptr(z_out), _ptr(w_out), w_dt,
+                                         _stream_handle(stream)), "paro_w4_unpack_dequant")
+
+
+def paro_w4a16_linear_workspace_bytes(layer: DeviceLayer, tokens: int, x_dt: int = F16,
+                                      path: int = PATH_AUTO) -> int:
+    return int(load().paro_w4a16_linear_workspace_bytes(layer.ref, tokens, x_dt, path))
+
+
+def paro_w4a16_linear_choose_path(layer: DeviceLayer, tokens: int) -> int:
+    return int(load().paro_w4a16_linear_choose_path(layer.ref, tokens))
+
+
+def make_workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace (the contract requires zeros before first use)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def paro_w4a16_linear(layer: DeviceLayer, x, y, workspace=None, stream=None, path: int = PATH_AUTO) -> None:
+    """y = rotated W4A16 linear of x.  x: (tokens, I) fp16/bf16; y: (tokens, O) x dtype or fp32."""
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load()
+    if path == PATH_AUTO:
+        rc = lib.paro_w4a16_linear(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y), ws_ptr,
+                                   ws_bytes, _stream_handle(stream))
+    else:
+        rc = lib.paro_w4a16_linear_path(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y), ws_ptr,
+                                        ws_bytes, _stream_handle(stream), path)
+    _check(rc, "paro_w4a16_linear")

@@ -1,0 +1,132 @@
+// common.hpp - device helpers shared by the libparo kernels (gfx950 / CDNA4).
+//
+// Formats: fp16 = IEEE binary16, bf16 = upper half of binary32.  Every
+// narrowing is round-to-nearest-even (the hardware default mode).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace paro {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// dtype codes of the C-ABI (paro_dtype)
+enum : int { kF16 = 0, kBF16 = 1, kF32 = 2 };
+
+// Group width of the GPU path and its pair count.
+constexpr int kG = 128;
+constexpr int kPairs = kG / 2;
+
+// AWQ word layout: bits 4s..4s+3 of a packed word hold column 8w + awq_col(s);
+// the interleave puts the even columns 0,2,4,6 in slots 0..3 and the odd
+// columns 1,3,5,7 in slots 4..7.
+__host__ __device__ constexpr int awq_col(int slot) { return ((slot & 3) << 1) | (slot >> 2); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+template <int DT>
+__device__ __forceinline__ float act_to_f32(uint32_t bits16) {
+  if constexpr (DT == kF16) return f16_bits_to_f32(bits16);
+  else return bf16_bits_to_f32(bits16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+// Two floats -> packed pair (lo in bits 0..15), RNE.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == kF16) {
+    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+  } else {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  }
+}
+
+// Wavefront-scope ordering of LDS traffic between lanes of one wave: LDS
+// operations of a wave execute in issue order, so only the compiler needs to
+// be kept from reordering across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------
+// Pairwise Givens rotation of T token rows of one 128-channel group.
+//
+// The rows live in LDS as fp32, row r at xs[r * rs + c] (c < 128).  Lane p of
+// the calling wave owns pair p at every stage: it reads the pair's two
+// channels for all T rows, applies
+//     a' =  a cos(theta) + b sin(theta),   b' = -a sin(theta) + b cos(theta)
+// and writes them back.  Pairs of a stage are disjoint, so no lane touches
+// another's channels within a stage; stages are ordered by wave_lds_sync().
+// The pair words of up to 8 stages and their sin/cos live in registers.
+//   pairs_g : &pairs[0][g*128]   (row stride `pstride` int16 = I)
+//   theta_g : &theta[0][g*64]    (row stride `tstride` floats = I/2)
+// Pair indices are masked into the group, so a bad schedule cannot read or
+// write outside the group's 128 channels.
+// ---------------------------------------------------------------------------
+template <int MAXT>
+__device__ __forceinline__ void rotate_rows_lds(float *xs, int rs, int T,
+                                                const int16_t *__restrict__ pairs_g, int64_t pstride,
+                                                const float *__restrict__ theta_g, int64_t tstride,
+                                                int krot, int lane) {
+  constexpr int KR = 8;
+  for (int t0 = 0; t0 < krot; t0 += KR) {
+    uint32_t pw[KR];
+    float cs[KR], sn[KR];
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+      if (t0 + u < krot) {
+        pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)(t0 + u) * pstride + 2 * lane);
+        const float th = theta_g[(int64_t)(t0 + u) * tstride + lane];
+        __sincosf(th, &sn[u], &cs[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+      if (t0 + u < krot) {
+        const int a = (int)(pw[u] & (kG - 1));
+        const int b = (int)((pw[u] >> 16) & (kG - 1));
+        float va[MAXT], vb[MAXT];
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+          if (m < T) {
+            va[m] = xs[m * rs + a];
+            vb[m] = xs[m * rs + b];
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+          if (m < T) {
+            // explicit contraction: every kernel rounds the stage identically
+            const float na = __builtin_fmaf(va[m], cs[u], vb[m] * sn[u]);
+            const float nb = __builtin_fmaf(vb[m], cs[u], -(va[m] * sn[u]));
+            xs[m * rs + a] = na;
+            xs[m * rs + b] = nb;
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+  }
+}
+
+}  // namespace paro

@@ -1,0 +1,58 @@
+// launch.hpp - internal host launchers of the libparo kernels.
+//
+// The C-ABI layer (paro_abi.cpp) validates every argument before calling
+// these; they only compute grids and enqueue kernels on `st`, returning the
+// launch status.  All pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace paro {
+
+hipError_t launch_scale_rotate(const uint16_t *x, int x_dt, void *xr, int xr_dt, int64_t tokens, int64_t I,
+                               const int16_t *pairs, const float *theta, const float *cs, int krot,
+                               hipStream_t st);
+
+hipError_t launch_unpack_dequant(const int32_t *qweight, const int32_t *qzeros, const uint16_t *scales,
+                                 int64_t I, int64_t O, int64_t G, uint8_t *q_out, uint8_t *z_out,
+                                 void *w_out, int w_dt, hipStream_t st);
+
+// Everything one linear launch needs (device pointers; sizes already checked).
+struct LinearArgs {
+  int64_t I, O, tokens;
+  int krot;
+  const int16_t *pairs;
+  const float *theta;
+  const float *cs;
+  const int32_t *qweight;
+  const int32_t *qzeros;
+  const uint16_t *scales;
+  const uint16_t *bias;  // may be null
+  const void *x;         // [tokens][I] act dtype
+  int x_dt;              // kF16 / kBF16
+  void *y;               // [tokens][O]
+  int y_dt;              // x_dt or kF32
+};
+
+// Decode (tokens <= 16): split-K MFMA GEMV.  With `xr` == nullptr the
+// rotation runs fused in each workgroup's prologue; otherwise `xr` holds the
+// rotated activations ([tokens][I], x dtype) and is read directly.
+struct DecodePlan {
+  int wpl;        // packed words per lane and row (1 or 2)
+  int ntile;      // output columns per workgroup (= 128 * wpl)
+  int n_tiles;    // ceil(O / ntile)
+  int kgroups;    // 128-row groups per workgroup
+  int splits;     // workgroups along K (ceil(I/128 / kgroups))
+};
+DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused);
+// Bytes of fp32 split-K partial sums the plan needs (0 with one split).
+size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O);
+// counters: >= n_tiles zeroed uint32 (left zeroed); partials: decode_partial_bytes.
+hipError_t launch_decode(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
+                         float *partials, hipStream_t st);
+
+// Prefill: MFMA GEMM over rotated activations xr ([tokens][I], x dtype).
+hipError_t launch_prefill_gemm(const LinearArgs &a, const void *xr, hipStream_t st);
+
+}  // namespace paro

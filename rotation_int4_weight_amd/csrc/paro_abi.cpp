@@ -1,0 +1,291 @@
+// paro_abi.cpp - C-ABI of libparo: argument validation, path choice,
+// workspace layout and launch-error mapping.  Declarations and the contract
+// of every entry point are in include/paro.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "paro.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PARO_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxTokens = int64_t(1) << 21;  // keeps every grid dimension < 65536
+constexpr int kMaxKrot = 64;
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxOut = int64_t(1) << 21;
+// Every workspace starts with a fixed counter area for the split-K
+// reduction (one 32-bit counter per 128-column tile, at most kMaxOut/128),
+// so a zero-filled workspace stays valid across shapes and paths: no path
+// ever writes anything but zeros-at-exit into it.
+constexpr size_t kCounterBytes = (size_t)(kMaxOut / 128) * 4;
+
+int64_t group_of(const paro_w4_layer *L) { return L->group_size == -1 ? L->in_features : L->group_size; }
+
+// Shape rules of the method ("ParoQuant" wiki: even groups dividing I; AWQ
+// packing needs O % 8 == 0; krot >= 1).
+int check_method_shape(const paro_w4_layer *L) {
+  if (!L) return fail(PARO_ERR_NULL, "layer is NULL");
+  const int64_t I = L->in_features, O = L->out_features, G = group_of(L);
+  if (I <= 0 || O <= 0) return fail(PARO_ERR_SHAPE, "in_features=%lld out_features=%lld must be positive",
+                                    (long long)I, (long long)O);
+  if (O % 8) return fail(PARO_ERR_SHAPE, "out_features=%lld is not a multiple of 8", (long long)O);
+  if (G <= 0 || G % 2 || I % G)
+    return fail(PARO_ERR_SHAPE, "group_size=%d must be even and divide in_features=%lld", L->group_size,
+                (long long)I);
+  if (L->krot < 1) return fail(PARO_ERR_SHAPE, "krot=%d must be >= 1", L->krot);
+  return PARO_OK;
+}
+
+// What the GPU kernels support on top of the method's rules.
+int check_gpu_shape(const paro_w4_layer *L) {
+  int rc = check_method_shape(L);
+  if (rc) return rc;
+  if (group_of(L) != 128)
+    return fail(PARO_ERR_UNSUPPORTED, "group_size=%d: the GPU path supports 128 only", L->group_size);
+  if (L->krot > kMaxKrot) return fail(PARO_ERR_UNSUPPORTED, "krot=%d exceeds %d", L->krot, kMaxKrot);
+  if (L->in_features > kMaxDim || L->out_features > kMaxOut)
+    return fail(PARO_ERR_UNSUPPORTED, "in_features > %lld or out_features > %lld", (long long)kMaxDim,
+                (long long)kMaxOut);
+  return PARO_OK;
+}
+
+int check_rotation_tensors(const paro_w4_layer *L) {
+  if (!L->pairs || !L->theta || !L->channel_scales)
+    return fail(PARO_ERR_NULL, "pairs, theta and channel_scales are required");
+  if (!aligned(L->pairs, 4) || !aligned(L->theta, 4) || !aligned(L->channel_scales, 4))
+    return fail(PARO_ERR_ALIGN, "pairs, theta, channel_scales must be 4-byte aligned");
+  return PARO_OK;
+}
+
+int check_weight_tensors(const paro_w4_layer *L) {
+  if (!L->qweight || !L->qzeros || !L->scales) return fail(PARO_ERR_NULL, "qweight, qzeros, scales are required");
+  if (!aligned(L->qweight, 16) || !aligned(L->scales, 16) || !aligned(L->qzeros, 4) ||
+      (L->bias && !aligned(L->bias, 2)))
+    return fail(PARO_ERR_ALIGN, "qweight/scales must be 16-byte aligned, qzeros 4, bias 2");
+  return PARO_OK;
+}
+
+int check_tokens(int64_t tokens) {
+  if (tokens < 0) return fail(PARO_ERR_SHAPE, "tokens=%lld is negative", (long long)tokens);
+  if (tokens > kMaxTokens) return fail(PARO_ERR_UNSUPPORTED, "tokens=%lld exceeds %lld", (long long)tokens,
+                                       (long long)kMaxTokens);
+  return PARO_OK;
+}
+
+bool act_dtype(int dt) { return dt == PARO_F16 || dt == PARO_BF16; }
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(PARO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+paro_path auto_path(int64_t tokens) {
+  if (tokens <= 4) return PARO_PATH_DECODE_FUSED;
+  if (tokens <= 16) return PARO_PATH_DECODE_SPLIT;
+  return PARO_PATH_PREFILL;
+}
+
+// Workspace layout: [counters kCounterBytes][x_r (split / prefill)][partials]
+size_t xr_region(const paro_w4_layer *L, int64_t tokens, paro_path path) {
+  return path == PARO_PATH_DECODE_FUSED ? 0 : align_up((size_t)tokens * (size_t)L->in_features * 2, 256);
+}
+
+size_t workspace_for(const paro_w4_layer *L, int64_t tokens, paro_path path) {
+  const int64_t I = L->in_features, O = L->out_features;
+  size_t bytes = kCounterBytes + xr_region(L, tokens, path);
+  if (path != PARO_PATH_PREFILL)
+    bytes += paro::decode_partial_bytes(paro::plan_decode(I, O, tokens, path == PARO_PATH_DECODE_FUSED), tokens, O);
+  return bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paro_abi_version(void) { return PARO_ABI_VERSION; }
+
+const char *paro_last_error(void) { return g_last_error.c_str(); }
+
+int paro_validate_layer(const paro_w4_layer *L) {
+  int rc = check_method_shape(L);
+  if (rc) return rc;
+  if (!L->pairs) return fail(PARO_ERR_NULL, "pairs is NULL");
+  const int64_t I = L->in_features, G = group_of(L);
+  if (G > 32768) return fail(PARO_ERR_SHAPE, "group_size=%lld exceeds int16 pair indices", (long long)G);
+  std::vector<unsigned char> seen((size_t)G);
+  for (int t = 0; t < L->krot; ++t) {
+    for (int64_t g = 0; g < I / G; ++g) {
+      std::fill(seen.begin(), seen.end(), 0);
+      for (int64_t e = 0; e < G; ++e) {
+        const int v = L->pairs[(int64_t)t * I + g * G + e];
+        if (v < 0 || v >= G || seen[(size_t)v])
+          return fail(PARO_ERR_PAIRS, "pairs[%d][%lld] = %d: stage %d group %lld is not a permutation of 0..%lld",
+                      t, (long long)(g * G + e), v, t, (long long)g, (long long)(G - 1));
+        seen[(size_t)v] = 1;
+      }
+    }
+  }
+  return ok();
+}
+
+int paro_scale_rotate(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *x_r,
+                      paro_dtype xr_dt, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (!act_dtype(xr_dt) && xr_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "x_r dtype %d invalid", (int)xr_dt);
+  if (tokens == 0) return ok();
+  if (!x || !x_r) return fail(PARO_ERR_NULL, "x and x_r are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(x_r, 16)) return fail(PARO_ERR_ALIGN, "x and x_r must be 16-byte aligned");
+  const int64_t I = L->in_features;
+  const size_t xb = (size_t)tokens * I * 2, ob = (size_t)tokens * I * (xr_dt == PARO_F32 ? 4 : 2);
+  const char *xs = (const char *)x, *os = (const char *)x_r;
+  const bool overlap = xs < os + ob && os < xs + xb;
+  if (overlap && !(x == x_r && x_dt == xr_dt))
+    return fail(PARO_ERR_SHAPE, "x_r overlaps x (only exact in-place with equal dtypes is allowed)");
+  hipError_t e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, x_r, (int)xr_dt, tokens, I, L->pairs,
+                                           L->theta, L->channel_scales, L->krot, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+  return ok();
+}
+
+int paro_w4_unpack_dequant(const paro_w4_layer *L, uint8_t *q_out, uint8_t *z_out, void *w_out, paro_dtype w_dt,
+                           void *stream) {
+  int rc = check_gpu_shape(L);
+  if (rc) return rc;
+  if (w_out && !act_dtype(w_dt) && w_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "w dtype %d invalid", (int)w_dt);
+  if (!q_out && !z_out && !w_out) return ok();
+  rc = check_weight_tensors(L);
+  if (rc) return rc;
+  if ((q_out && !aligned(q_out, 8)) || (z_out && !aligned(z_out, 8)) || (w_out && !aligned(w_out, 16)))
+    return fail(PARO_ERR_ALIGN, "q_out/z_out must be 8-byte and w_out 16-byte aligned");
+  hipError_t e = paro::launch_unpack_dequant(L->qweight, L->qzeros, L->scales, L->in_features, L->out_features,
+                                             group_of(L), q_out, z_out, w_out, (int)w_dt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "unpack_dequant launch");
+  return ok();
+}
+
+paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {
+  (void)L;
+  return auto_path(tokens);
+}
+
+size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens, paro_dtype x_dt,
+                                         paro_path path) {
+  (void)x_dt;
+  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
+  if (path == PARO_PATH_AUTO) path = auto_path(tokens);
+  return workspace_for(L, tokens, path);
+}
+
+int paro_w4a16_linear_path(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                           paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream,
+                           paro_path path) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
+  if (path < PARO_PATH_AUTO || path > PARO_PATH_PREFILL) return fail(PARO_ERR_SHAPE, "unknown path %d", (int)path);
+  if (tokens == 0) return ok();
+  if (path == PARO_PATH_AUTO) path = auto_path(tokens);
+  if ((path == PARO_PATH_DECODE_FUSED || path == PARO_PATH_DECODE_SPLIT) && tokens > 16)
+    return fail(PARO_ERR_UNSUPPORTED, "decode paths take at most 16 tokens (got %lld)", (long long)tokens);
+  if (!x || !y) return fail(PARO_ERR_NULL, "x and y are required");
+  rc = check_rotation_tensors(L);
+  if (!rc) rc = check_weight_tensors(L);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(PARO_ERR_ALIGN, "x and y must be 16-byte aligned");
+  const int64_t I = L->in_features, O = L->out_features;
+  {
+    const char *xs = (const char *)x, *ys = (const char *)y;
+    const size_t xb = (size_t)tokens * I * 2, yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+    if (xs < ys + yb && ys < xs + xb) return fail(PARO_ERR_SHAPE, "y overlaps x");
+  }
+  const size_t need = workspace_for(L, tokens, path);
+  if (need > 0) {
+    if (!workspace) return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(PARO_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+
+  paro::LinearArgs a;
+  a.I = I;
+  a.O = O;
+  a.tokens = tokens;
+  a.krot = L->krot;
+  a.pairs = L->pairs;
+  a.theta = L->theta;
+  a.cs = L->channel_scales;
+  a.qweight = L->qweight;
+  a.qzeros = L->qzeros;
+  a.scales = L->scales;
+  a.bias = L->bias;
+  a.x = x;
+  a.x_dt = (int)x_dt;
+  a.y = y;
+  a.y_dt = (int)y_dt;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+
+  uint32_t *counters = (uint32_t *)workspace;
+  char *xr = (char *)workspace + kCounterBytes;
+  float *partials = (float *)(xr + xr_region(L, tokens, path));
+  if (path == PARO_PATH_DECODE_FUSED) {
+    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, true);
+    e = paro::launch_decode(a, p, nullptr, counters, partials, st);
+    if (e != hipSuccess) return hip_fail(e, "decode (fused) launch");
+    return ok();
+  }
+  // X_r into the workspace, then the contraction over it
+  e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
+                                L->channel_scales, L->krot, st);
+  if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+  if (path == PARO_PATH_DECODE_SPLIT) {
+    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, false);
+    e = paro::launch_decode(a, p, xr, counters, partials, st);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+  }
+  e = paro::launch_prefill_gemm(a, xr, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
+  return ok();
+}
+
+int paro_w4a16_linear(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                      paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream) {
+  return paro_w4a16_linear_path(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, PARO_PATH_AUTO);
+}
+
+}  // extern "C"

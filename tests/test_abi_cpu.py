@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: exported symbols, host validation, error
+codes and the argument checks every entry point performs before it enqueues
+anything.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ref
+
+paro = pytest.importorskip("rotation_int4_weight_amd")
+from rotation_int4_weight_amd import _lib  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared(header):
+    """Function names declared in a C header (return type, name, '(')."""
+    with open(os.path.join(ROOT, "include", header)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b((?:paro)_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_libparo_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared("paro.h")
+    assert "paro_w4a16_linear" in names and "paro_scale_rotate" in names
+    assert set(_lib.EXPORTS) == set(names)
+    for n in names:
+        assert getattr(lib, n) is not None
+    assert lib.paro_abi_version() == 1
+
+
+def test_oracle_exports_every_declared_symbol():
+    lib = ref.load()
+    names = declared("paro_ref.h")
+    assert "paro_linear_ref_check" in names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_oracle_and_gpu_library_share_no_code():
+    """The checker and the product are separate libraries with no shared symbol."""
+    lib_names = set(declared("paro.h"))
+    ref_names = set(declared("paro_ref.h"))
+    assert not (lib_names & ref_names)
+    with open(os.path.join(ROOT, "oracle", "paro_ref.c")) as f:
+        src = f.read()
+    assert "paro.h" not in src.replace("paro_ref.h", "")
+    for fn in os.listdir(os.path.join(ROOT, "rotation_int4_weight_amd", "csrc")):
+        with open(os.path.join(ROOT, "rotation_int4_weight_amd", "csrc", fn)) as f:
+            s = f.read()
+        assert "paro_ref" not in s and "oracle" not in s.lower()
+
+
+def test_validate_layer_codes():
+    L = synth.make_layer(400, 0, 256, 64)
+    _lib.paro_validate_layer(L)
+    bad = synth.make_layer(400, 0, 256, 64)
+    bad.pairs[3, 200] = 300
+    with pytest.raises(_lib.ParoError) as e:
+        _lib.paro_validate_layer(bad)
+    assert e.value.status == 6
+    odd = synth.make_layer(400, 0, 256, 64)
+    odd.group_size = 100
+    with pytest.raises(_lib.ParoError) as e:
+        _lib.paro_validate_layer(odd)
+    assert e.value.status == 2
+
+
+# -- argument checks of the GPU entry points (host side, nothing enqueued) --
+#
+# The descriptors below point at addresses no kernel ever sees: each case
+# fails validation before any launch.  Guard: only run where no GPU exists.
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+needs_no_gpu = pytest.mark.skipif(not _no_gpu(), reason="host-only checks; run on a machine without a GPU")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced on the host
+
+
+def fake_layer(I=256, O=64, G=128, krot=8, **over):
+    f = dict(pairs=FAKE, theta=FAKE, channel_scales=FAKE, qweight=FAKE, qzeros=FAKE, scales=FAKE,
+             bias=FAKE)
+    f.update(over)
+    return _lib.ParoLayerC(I, O, G, krot, f["pairs"], f["theta"], f["channel_scales"], f["qweight"],
+                           f["qzeros"], f["scales"], f["bias"])
+
+
+def lin(L, x=FAKE, xdt=0, tokens=4, y=FAKE * 2, ydt=0, ws=FAKE * 4, wsb=1 << 30, path=0):
+    return _lib.load().paro_w4a16_linear_path(ctypes.byref(L), x, xdt, tokens, y, ydt, ws, wsb, None, path)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("case,code", [
+    (dict(L=dict(G=64)), 5),             # only G = 128 on the GPU
+    (dict(L=dict(G=-1, I=256)), 5),      # G = I = 256
+    (dict(L=dict(O=60)), 2),             # O % 8
+    (dict(L=dict(G=100)), 2),            # G does not divide I
+    (dict(L=dict(krot=0)), 2),
+    (dict(L=dict(krot=65)), 5),
+    (dict(L=dict(pairs=0)), 1),
+    (dict(L=dict(qweight=0)), 1),
+    (dict(L=dict(qweight=FAKE + 4)), 4),
+    (dict(x=0), 1),
+    (dict(x=FAKE + 2), 4),
+    (dict(xdt=2), 3),                    # fp32 activations not accepted
+    (dict(ydt=1), 3),                    # y must be x dtype or fp32
+    (dict(tokens=-1), 2),
+    (dict(tokens=17, path=1), 5),        # decode paths take <= 16 tokens
+    (dict(tokens=17, path=2), 5),
+    (dict(ws=0, path=3), 7),
+    (dict(wsb=16, path=3), 7),
+    (dict(ws=FAKE + 8, path=3), 4),
+    (dict(y=FAKE + 64), 2),              # y overlaps x
+    (dict(path=9), 2),
+])
+def test_linear_argument_checks(case, code):
+    L = fake_layer(**{k: v for k, v in case.get("L", {}).items() if k in ("I", "O", "G", "krot")},
+                   **{k: v for k, v in case.get("L", {}).items() if k not in ("I", "O", "G", "krot")})
+    kw = {k: v for k, v in case.items() if k != "L"}
+    rc = lin(L, **kw)
+    assert rc == code, _lib.paro_last_error()
+    assert _lib.paro_last_error()
+
+
+@needs_no_gpu
+def test_zero_tokens_returns_ok_without_touching_memory():
+    assert lin(fake_layer(), tokens=0, x=0, y=0, ws=0, wsb=0) == 0
+    lib = _lib.load()
+    assert lib.paro_scale_rotate(ctypes.byref(fake_layer()), None, 0, 0, None, 0, None) == 0
+
+
+@needs_no_gpu
+def test_scale_rotate_and_dequant_argument_checks():
+    lib = _lib.load()
+    L = fake_layer()
+    assert lib.paro_scale_rotate(ctypes.byref(L), FAKE, 0, 4, FAKE * 2, 7, None) == 3
+    assert lib.paro_scale_rotate(ctypes.byref(L), FAKE, 0, 4, FAKE + 32, 0, None) == 2  # partial overlap
+    assert lib.paro_scale_rotate(ctypes.byref(L), None, 0, 4, FAKE, 0, None) == 1
+    assert lib.paro_w4_unpack_dequant(ctypes.byref(L), None, None, None, 0, None) == 0  # nothing requested
+    assert lib.paro_w4_unpack_dequant(ctypes.byref(L), FAKE + 4, None, None, 0, None) == 4
+    assert lib.paro_w4_unpack_dequant(ctypes.byref(fake_layer(scales=0)), FAKE, None, None, 0, None) == 1
+    assert lib.paro_w4_unpack_dequant(ctypes.byref(L), None, None, FAKE, 9, None) == 3
+
+
+def test_workspace_sizes_and_path_choice():
+    lib = _lib.load()
+    L = fake_layer(I=4096, O=4096)
+    pick = lambda m: lib.paro_w4a16_linear_choose_path(ctypes.byref(L), m)
+    assert pick(1) == 1 and pick(4) == 1 and pick(5) == 2 and pick(16) == 2 and pick(17) == 3
+    wsb = lambda m, p: _lib.load().paro_w4a16_linear_workspace_bytes(ctypes.byref(L), m, 0, p)
+    # prefill holds X_r (tokens * I * 2 bytes) after the fixed counter area
+    assert wsb(2048, 3) - wsb(1024, 3) == 1024 * 4096 * 2
+    assert wsb(1, 1) > 0 and wsb(16, 2) > wsb(16, 1)
+    assert wsb(0, 1) == 0

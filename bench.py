@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W4A16 linear (ParoQuant inference hot path) on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+
+One step = one pass of the whole path (channel scale, pairwise rotation, AWQ
+unpack, dequant, contraction, bias, output rounding) over one batch of seeded
+synthetic input, through libparo's C-ABI.  The default workload is the
+Llama-3-8B q_proj decode layer (4096 -> 4096, 1 token, fp16).  Every timed
+step reads a different copy of the layer's tensors (a rotation through at
+least 512 MB of distinct buffers, twice the 256 MB MALL) so the weight stream
+comes from HBM, with every input already resident in device memory.
+
+Prints ONE JSON line: metric, value (decode: weight GB/s = (qweight + qzeros +
+scales bytes) / step time; prefill: TFLOP/s = 2*M*I*O / step time), the
+roofline of the dominant kernel (its algorithmic bytes or flops per launch
+over its average launch duration, timed live with HIP events on the stream
+it runs on), and the fp64 CPU oracle timed on a bounded sample of the same
+workload as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ParoQuant linear: decode weight GB/s, prefill TFLOP/s, % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, published
+MALL_ROTATION_BYTES = 512 << 20
+PATH_NAMES = {1: "decode_fused", 2: "decode_split", 3: "prefill"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(I, O, krot, G=128, bias=True):
+    """Stored-tensor bytes of one layer: weight part and rotation part."""
+    weight = I * O // 2 + (I // G) * O // 2 + (I // G) * O * 2
+    rot = krot * I * 2 + krot * (I // 2) * 4 + I * 4 + (O * 2 if bias else 0)
+    return weight, rot
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources: counter readings are only valid for them."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rotation_int4_weight_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(str(workload))
+    if not rec or rec.get("kernel_sources") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=1, help="0..4 (synth.WORKLOADS)")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode_fused, 2 decode_split, 3 prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the rotated W4A16 linear is measured per GPU; the multi-GPU sharding is a design "
+              "note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rotation_int4_weight_amd as paro
+    import synth
+
+    paro.load()  # raises if libparo.so is missing: there is no fallback
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    spec = synth.WORKLOADS[args.workload]
+    M, act = spec["tokens"], spec["act"]
+    tdt = torch.float16 if act == synth.F16 else torch.bfloat16
+
+    # ---- one host copy per layer, replicated into distinct device buffers ----
+    layers = []
+    per_set = 0
+    for li, (lname, I, O) in enumerate(spec["layers"]):
+        host = synth.make_layer(args.workload, li, I, O)
+        x = synth.make_x(args.workload, li, M, I, act)
+        w_b, r_b = layer_bytes(I, O, host.krot)
+        per_set += w_b + r_b + M * I * 2
+        layers.append((lname, I, O, host, x))
+    nsets = max(1, -(-MALL_ROTATION_BYTES // per_set))
+    log(f"workload {args.workload} ({spec['name']}): {len(layers)} layer(s), {nsets} buffer sets "
+        f"x {per_set / 1e6:.1f} MB")
+    sets = []  # sets[s][l] = (DeviceLayer, x)
+    for s in range(nsets):
+        row = []
+        for lname, I, O, host, x in layers:
+            D = paro.DeviceLayer(host, device=dev)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
+            row.append((D, xd))
+        sets.append(row)
+    path = args.path or paro.paro_w4a16_linear_choose_path(sets[0][0][0], M)
+    ys = [torch.empty((M, O), dtype=tdt, device=dev) for _, I, O, _, _ in layers]
+    ws_bytes = max(paro.paro_w4a16_linear_workspace_bytes(sets[0][l][0], M, act, path)
+                   for l in range(len(layers)))
+    ws = paro.make_workspace(ws_bytes, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        row = sets[i % nsets]
+        for l, (D, xd) in enumerate(row):
+            paro.paro_w4a16_linear(D, xd, ys[l], ws, stream=stream, path=path)
+
+    # ---- whole-path timing ----
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    weight_bytes = sum(layer_bytes(I, O, 8)[0] for _, I, O, _, _ in layers)
+    flops = sum(2.0 * M * I * O for _, I, O, _, _ in layers)
+    alg_bytes = sum(sum(layer_bytes(I, O, h.krot)) + M * I * 2 + M * O * 2 for _, I, O, h, _ in layers)
+    decode = path in (1, 2)
+    if decode:
+        value, unit = weight_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+
+    # ---- dominant kernel, timed live on its own stream ----
+    # decode_fused: the step is that one kernel.  split / prefill: the
+    # contraction kernel, run alone over pre-rotated activations.
+    kern = None
+    if not args.no_kernel_timing:
+        n_launch = max(args.steps, 20)
+        if path == 1:
+            launch = step
+            per_launch_bytes, per_launch_flops = alg_bytes, flops
+            launches_per_call = len(layers)
+        else:
+            xrs = []
+            for row in sets:
+                xr_row = []
+                for D, xd in row:
+                    xr = torch.empty_like(xd)
+                    paro.paro_scale_rotate(D, xd, xr, stream=stream)
+                    xr_row.append(xr)
+                xrs.append(xr_row)
+
+            def launch(i):
+                row = sets[i % nsets]
+                for l, (D, _) in enumerate(row):
+                    paro.paro_w4a16_linear_prerotated(D, xrs[i % nsets][l], ys[l], ws, stream=stream, path=path)
+            per_launch_bytes, per_launch_flops = alg_bytes, flops
+            launches_per_call = len(layers)
+        for i in range(min(args.warmup, 20)):
+            launch(i)
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for i in range(n_launch):
+            launch(i)
+        k1.record(stream)
+        torch.cuda.synchronize()
+        us = k0.elapsed_time(k1) * 1e3 / (n_launch * launches_per_call)
+        kern = {"name": {1: "decode_kernel<fused>", 2: "decode_kernel", 3: "prefill_gemm_kernel"}[path],
+                "avg_us": us, "launches": n_launch * launches_per_call,
+                "bytes_per_launch": per_launch_bytes / launches_per_call,
+                "flops_per_launch": per_launch_flops / launches_per_call}
+
+    khash = kernel_source_hash()
+    roofline = None
+    if kern:
+        if decode:
+            ach = kern["bytes_per_launch"] / (kern["avg_us"] * 1e-6) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4)}
+        else:
+            ach = kern["flops_per_launch"] / (kern["avg_us"] * 1e-6) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+        roofline["traffic"] = load_traffic(args.workload, khash)
+        roofline["kernel"] = kern["name"]
+        roofline["avg_launch_us"] = round(kern["avg_us"], 3)
+
+    # ---- CPU baseline: the oracle as it stands, on a bounded sample ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        lname, I, O, host, x = layers[0]
+        rows = M if decode else min(M, 32)
+        xs = np.ascontiguousarray(x[:rows])
+        n, t_start = 0, time.perf_counter()
+        while True:
+            ref.linear(host, xs, act)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        per_call = el / n
+        if decode:
+            w_b = layer_bytes(I, O, host.krot)[0]
+            cval, cunit = w_b / per_call / 1e9, "GB/s"
+            sample = f"{n} full oracle calls on layer '{lname}' ({rows} token(s)), {el:.1f} s"
+        else:
+            cval, cunit = 2.0 * rows * I * O / per_call / 1e12, "TFLOP/s"
+            sample = f"{n} oracle call(s) on {rows} of {M} token rows of layer '{lname}', {el:.1f} s"
+        cpu = {"value": cval, "unit": cunit, "cores": ref.threads(0), "kind": "oracle", "sample": sample}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if act == synth.F16 else "bf16", "data": "synthetic",
+        "config": {"workload": spec["name"], "layers": [[n, I, O] for n, I, O, _, _ in layers], "tokens": M,
+                   "group_size": 128, "krot": 8, "path": PATH_NAMES[path], "buffer_sets": nsets,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernel_sources": khash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

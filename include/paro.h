@@ -40,9 +40,10 @@
  *     the host before anything is enqueued; on error nothing is launched and
  *     paro_last_error() (thread-local) describes the failure.  Launch errors
  *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
- *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128, O a multiple
- *     of 8 and <= 2^21, I <= 2^24, tokens <= 2^21; x, y, x_r, w_out, qweight and scales 16-byte
- *     aligned.  Other values give PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.
+ *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^24,
+ *     O a multiple of 8 and <= 2^21, tokens <= 2^21; x, y, x_r, w_out,
+ *     qweight and scales 16-byte aligned.  Other values give
+ *     PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.
  *   - Pair contents are NOT read on the host by the GPU entry points (they
  *     are device memory); kernels mask every pair index into its group, so
  *     an invalid schedule yields wrong numbers, never an out-of-bounds
@@ -156,6 +157,20 @@ int paro_w4a16_linear(const paro_w4_layer *layer, const void *x, paro_dtype x_dt
 int paro_w4a16_linear_path(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
                            int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
                            size_t workspace_bytes, void *stream, paro_path path);
+
+/*
+ * The quantized projection alone, over activations that are already scaled
+ * and rotated (x_r, e.g. from paro_scale_rotate with xr_dt == x_dt):
+ *   y[m][n] = sum_k x_r[m][k] * (q[k][n] - z[k/G][n]) * s[k/G][n] + bias[n].
+ * It runs exactly the contraction kernel of the DECODE_SPLIT path (tokens <=
+ * 16) or of the PREFILL path, so timing it isolates that kernel.  path must be
+ * PARO_PATH_AUTO, _DECODE_SPLIT or _PREFILL; layer->pairs/theta/
+ * channel_scales are not used.  Workspace as for paro_w4a16_linear (the
+ * same size suffices).
+ */
+int paro_w4a16_linear_prerotated(const paro_w4_layer *layer, const void *x_r, paro_dtype x_dt,
+                                 int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                                 size_t workspace_bytes, void *stream, paro_path path);
 
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,

@@ -19,7 +19,8 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           4: "PARO_ERR_ALIGN", 5: "PARO_ERR_UNSUPPORTED", 6: "PARO_ERR_PAIRS",
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
-           "paro_w4a16_linear_path", "paro_w4a16_linear_workspace_bytes",
+           "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+           "paro_w4a16_linear_workspace_bytes",
            "paro_w4a16_linear_choose_path", "paro_validate_layer", "paro_last_error",
            "paro_abi_version")
 
@@ -56,6 +57,7 @@ def load(path: str | None = None):
     lib.paro_w4_unpack_dequant.argtypes = [P, P, P, P, I32, P]
     lib.paro_w4a16_linear.argtypes = [P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_linear_path.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
+    lib.paro_w4a16_linear_prerotated.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
     lib.paro_w4a16_linear_workspace_bytes.argtypes = [P, I64, I32, I32]
     lib.paro_w4a16_linear_workspace_bytes.restype = SZ
     lib.paro_w4a16_linear_choose_path.argtypes = [P, I64]
@@ -64,7 +66,8 @@ def load(path: str | None = None):
     lib.paro_last_error.restype = ctypes.c_char_p
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
-                 "paro_w4a16_linear_path", "paro_w4a16_linear_choose_path",
+                 "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+                 "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
         getattr(lib, name).restype = I32
     if path == LIB_PATH:
@@ -186,3 +189,13 @@ def paro_w4a16_linear(layer: DeviceLayer, x, y, workspace=None, stream=None, pat
         rc = lib.paro_w4a16_linear_path(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y), ws_ptr,
                                         ws_bytes, _stream_handle(stream), path)
     _check(rc, "paro_w4a16_linear")
+
+
+def paro_w4a16_linear_prerotated(layer: DeviceLayer, x_r, y, workspace=None, stream=None,
+                                 path: int = PATH_AUTO) -> None:
+    """The quantized projection alone over already rotated activations x_r."""
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_w4a16_linear_prerotated(layer.ref, _ptr(x_r), _dt(x_r), x_r.shape[0], _ptr(y), _dt(y),
+                                               ws_ptr, ws_bytes, _stream_handle(stream), path),
+           "paro_w4a16_linear_prerotated")

@@ -66,66 +66,94 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Workgroups of a launch are handed to the 8 XCDs round-robin by id.  This
+// maps launch id b to a logical index so that each XCD receives a contiguous
+// run of logical indices (a bijection on [0, total); ids past the last full
+// round keep their own index).  Only data placement in the XCDs' L2 caches
+// depends on it, never correctness.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_local_order(int b, int total) {
+  const int q = total / kXcds;
+  if (b >= q * kXcds) return b;
+  return (b % kXcds) * q + b / kXcds;
+}
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------
-// Pairwise Givens rotation of T token rows of one 128-channel group.
+// Pairwise Givens rotation of NR token rows of one 128-channel group.
 //
 // The rows live in LDS as fp32, row r at xs[r * rs + c] (c < 128).  Lane p of
 // the calling wave owns pair p at every stage: it reads the pair's two
-// channels for all T rows, applies
+// channels for all NR rows, applies
 //     a' =  a cos(theta) + b sin(theta),   b' = -a sin(theta) + b cos(theta)
 // and writes them back.  Pairs of a stage are disjoint, so no lane touches
 // another's channels within a stage; stages are ordered by wave_lds_sync().
-// The pair words of up to 8 stages and their sin/cos live in registers.
+// NR is a compile-time row count (callers pad with zero rows), so the row
+// loops are branch-free and every load of a stage is issued before its first
+// use.
 //   pairs_g : &pairs[0][g*128]   (row stride `pstride` int16 = I)
 //   theta_g : &theta[0][g*64]    (row stride `tstride` floats = I/2)
 // Pair indices are masked into the group, so a bad schedule cannot read or
 // write outside the group's 128 channels.
+//
+// The pair words and angles of the first kStageRegs stages can be loaded
+// early (RotParams::load), long before the rows are rotated, so that their
+// latency hides behind other memory traffic; later stages, if any, are
+// fetched as they are applied.
 // ---------------------------------------------------------------------------
-template <int MAXT>
-__device__ __forceinline__ void rotate_rows_lds(float *xs, int rs, int T,
+constexpr int kStageRegs = 8;
+
+struct RotParams {
+  uint32_t pw[kStageRegs];
+  float th[kStageRegs];
+  __device__ __forceinline__ void load(const int16_t *__restrict__ pairs_g, int64_t pstride,
+                                       const float *__restrict__ theta_g, int64_t tstride, int krot,
+                                       int lane) {
+#pragma unroll
+    for (int u = 0; u < kStageRegs; ++u) {
+      const int t = u < krot ? u : 0;  // stages past krot are never applied
+      pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * pstride + 2 * lane);
+      th[u] = theta_g[(int64_t)t * tstride + lane];
+    }
+  }
+};
+
+template <int NR>
+__device__ __forceinline__ void rotate_stage(float *xs, int rs, uint32_t pw, float cs, float sn) {
+  const int a = (int)(pw & (kG - 1));
+  const int b = (int)((pw >> 16) & (kG - 1));
+  float va[NR], vb[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    va[m] = xs[m * rs + a];
+    vb[m] = xs[m * rs + b];
+  }
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    // explicit contraction: every kernel rounds the stage identically
+    xs[m * rs + a] = __builtin_fmaf(va[m], cs, vb[m] * sn);
+    xs[m * rs + b] = __builtin_fmaf(vb[m], cs, -(va[m] * sn));
+  }
+  wave_lds_sync();
+}
+
+template <int NR>
+__device__ __forceinline__ void rotate_rows_lds(float *xs, int rs, const RotParams &rp,
                                                 const int16_t *__restrict__ pairs_g, int64_t pstride,
                                                 const float *__restrict__ theta_g, int64_t tstride,
                                                 int krot, int lane) {
-  constexpr int KR = 8;
-  for (int t0 = 0; t0 < krot; t0 += KR) {
-    uint32_t pw[KR];
-    float cs[KR], sn[KR];
+  float cs[kStageRegs], sn[kStageRegs];
 #pragma unroll
-    for (int u = 0; u < KR; ++u) {
-      if (t0 + u < krot) {
-        pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)(t0 + u) * pstride + 2 * lane);
-        const float th = theta_g[(int64_t)(t0 + u) * tstride + lane];
-        __sincosf(th, &sn[u], &cs[u]);
-      }
-    }
+  for (int u = 0; u < kStageRegs; ++u) __sincosf(rp.th[u], &sn[u], &cs[u]);
 #pragma unroll
-    for (int u = 0; u < KR; ++u) {
-      if (t0 + u < krot) {
-        const int a = (int)(pw[u] & (kG - 1));
-        const int b = (int)((pw[u] >> 16) & (kG - 1));
-        float va[MAXT], vb[MAXT];
-#pragma unroll
-        for (int m = 0; m < MAXT; ++m) {
-          if (m < T) {
-            va[m] = xs[m * rs + a];
-            vb[m] = xs[m * rs + b];
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MAXT; ++m) {
-          if (m < T) {
-            // explicit contraction: every kernel rounds the stage identically
-            const float na = __builtin_fmaf(va[m], cs[u], vb[m] * sn[u]);
-            const float nb = __builtin_fmaf(vb[m], cs[u], -(va[m] * sn[u]));
-            xs[m * rs + a] = na;
-            xs[m * rs + b] = nb;
-          }
-        }
-        wave_lds_sync();
-      }
-    }
+  for (int u = 0; u < kStageRegs; ++u)
+    if (u < krot) rotate_stage<NR>(xs, rs, rp.pw[u], cs[u], sn[u]);
+  for (int t = kStageRegs; t < krot; ++t) {
+    const uint32_t pw = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * pstride + 2 * lane);
+    float c, s;
+    __sincosf(theta_g[(int64_t)t * tstride + lane], &s, &c);
+    rotate_stage<NR>(xs, rs, pw, c, s);
   }
 }
 

@@ -7,30 +7,43 @@
 // Triton plans and tuning: unpack, subtract zero points, multiply by group
 // scales, fp32 accumulation.)
 //
-// Work split.  A workgroup (4 waves) owns a tile of 128*WPL output columns
-// and a range of `kgroups` 128-row groups; wave w takes groups w, w+4, ... of
-// that range.  For one group a lane loads, for each of the group's four
-// 32-row k-steps, the 8 rows of its 8-row block (lane>>4) of its WPL packed
-// words (lane&15): a 16-lane row segment is contiguous in memory.  Each packed
-// word turns into eight MFMA B fragments (one per nibble slot = one output
-// column each), so no transpose is needed: v_perm_b32 gathers the bytes of a
-// row pair and an OR with an exponent-bias constant turns a nibble into a
-// half-precision number (fp16: 0x6400|q = 1024+q, 0x6400|(q<<4) = 1024+16q;
-// bf16: 0x4300|q = 128+q).  The offset and the zero point are removed once per
-// group, with the row sums of the rounded activations that one extra MFMA
-// against a fragment of ones produces in the same output layout:
+// Work split.  A k-step is 32 rows of the weight.  A workgroup (NW waves)
+// owns a tile of 128*WPL output columns and NW*KSW consecutive k-steps; wave
+// w takes KSW consecutive k-steps of them.  For one k-step a lane loads the 8 rows of
+// its 8-row block (lane>>4) of its WPL consecutive packed words (lane&15), so
+// the 16 lanes of a block read 64*WPL contiguous bytes of each row (256 B
+// with WPL = 4).  A wave issues the loads of all its k-steps before it
+// computes, in the order it consumes them, so the MFMAs of a k-step start as
+// soon as its own loads have landed.  Each packed word turns into eight MFMA
+// B fragments (one per nibble slot = one output column each), so no
+// transpose is needed: v_perm_b32 gathers the bytes of a row pair and an OR
+// with an exponent-bias constant turns a nibble into a half-precision number
+// (fp16: 0x6400|q = 1024+q, 0x6400|(q<<4) = 1024+16q; bf16: 0x4300|q =
+// 128+q).  The offset and the zero point are removed with the row sums of the
+// rounded activations, which one extra MFMA against a fragment of ones
+// produces in the output layout:
 //   sum_k x (off + c*q) = off*xsum + c*sum_k x q
-//   =>  sum_k x (q - z) = (acc - (off + c*z) * xsum) / c.
-// v_mfma_f32_16x16x32_{f16,bf16}: lane l holds A row l&15 and B column l&15 of
-// its 8-element k block; the 16x16 fp32 result has row 4*(l>>4)+r, column
-// l&15 in register r.
+//   =>  sum_k x (q - z) = (acc - (off + c*z) * xsum) / c,
+// folded into the running sum with the group scale once per group (or per
+// k-step when a wave owns a single k-step; the fold is linear, so both are the
+// same sum).  v_mfma_f32_16x16x32_{f16,bf16}: lane l holds A row l&15 and B
+// column l&15 of its 8-element k block; the 16x16 fp32 result has row
+// 4*(l>>4)+r, column l&15 in register r.
 //
-// Reduction.  The four waves' partial tiles are summed in LDS in wave order.
-// With one K split the workgroup adds the bias and stores y.  Otherwise it
-// stores its fp32 partial to the workspace, and the last workgroup of the
-// column tile to arrive (device-scope counter) sums all partials in split
-// order, adds the bias and stores y; it then resets the counter.  The result
-// is therefore independent of arrival order (bitwise deterministic).
+// Workgroups are numbered tile-fastest (all column tiles of split 0, then of
+// split 1, ...) and that order is dealt out to the XCDs in contiguous runs
+// (xcd_local_order), so the tiles sharing the same weight rows run on one XCD
+// at the same time and their row segments merge in its L2 into long DRAM
+// bursts.
+//
+// Reduction.  The NW waves' tiles are summed in LDS in wave order.  With
+// one K split the workgroup adds the bias and stores y.  Otherwise it stores
+// its fp32 partial with device-scope atomic stores (coherent across the XCDs'
+// L2 caches without whole-cache write-backs), waits for them, and bumps a
+// device-scope counter; the last workgroup of the column tile to arrive
+// loads every split's partial (all loads in flight together), sums them in
+// split order, adds the bias, stores y and resets the counter.  The result is
+// independent of arrival order (bitwise deterministic).
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -39,6 +52,7 @@
 namespace paro {
 
 constexpr int kDecodeRS = kG + 4;  // fused-rotation LDS row stride (floats)
+constexpr int kCounterStride = 32; // uint32 per split-K counter: one 128-byte line each
 
 template <int DT>
 struct MfmaTypes;
@@ -108,138 +122,209 @@ __device__ __forceinline__ constexpr float slot_mult(int s) {
   return (DT == kF16 && (s & 1)) ? 16.0f : 1.0f;
 }
 
-template <int DT, int WPL, bool FUSED, int FR>
-__global__ void __launch_bounds__(256)
-decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int kgroups, int splits,
-              float *__restrict__ partial, uint32_t *__restrict__ counters) {
+// Output of one element (bias already added in fp32; one rounding into the
+// output dtype).
+__device__ __forceinline__ void store_out(const LinearArgs &a, int64_t row, int64_t n, float out) {
+  if (a.y_dt == kF32) reinterpret_cast<float *>(a.y)[row * a.O + n] = out;
+  else if (a.y_dt == kF16) reinterpret_cast<uint16_t *>(a.y)[row * a.O + n] = f32_to_f16_bits(out);
+  else reinterpret_cast<uint16_t *>(a.y)[row * a.O + n] = f32_to_bf16_bits(out);
+}
+
+// Load WPL consecutive packed words of one row (one vector load when WPL > 1).
+template <int WPL>
+__device__ __forceinline__ void load_words(const int32_t *__restrict__ p, uint32_t out[WPL]) {
+  if constexpr (WPL == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (WPL == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = (uint32_t)p[0];
+  }
+}
+
+// MT: token rows carried per wave (1, 2, 4, 8 or 16; M <= MT, rows >= M are
+// zero).  FR = min(MT, 4) accumulator registers can hold real rows.
+template <int DT, int WPL, int KSW, int NW, bool FUSED, int MT>
+__global__ void __launch_bounds__(64 * NW)
+decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *__restrict__ partial,
+              uint32_t *__restrict__ counters) {
+  constexpr int FR = MT < 4 ? MT : 4;
+  constexpr int NT = 8 * WPL;                 // MFMA column tiles per wave
+  constexpr int NG = KSW < 4 ? 1 : KSW / 4;   // groups a wave touches (its k-steps are aligned)
+  // k-steps of loads kept in flight (16-wave groups have half the registers)
+  constexpr int PD = KSW < (NW >= 16 ? 2 : 4) ? KSW : (NW >= 16 ? 2 : 4);
+  constexpr int NTH = 64 * NW;
+  constexpr int NTILE = 128 * WPL;
+  constexpr int EPT = (MT * NTILE + NTH - 1) / NTH;  // output elements per thread
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int s_last;
   const int lane = lane_id(), wave = wave_id();
   const int cl = lane & 15, kb = lane >> 4;
-  const int ntile = 128 * WPL;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int n_tiles = (int)((a.O + NTILE - 1) / NTILE);
+  const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * splits);
+  const int tile = lwg % n_tiles, split = lwg / n_tiles;
   const int64_t I = a.I, O = a.O, W = O / 8;
   const int M = (int)a.tokens;
-  const int64_t ngroups = I / kG;
-  const int64_t g_begin = (int64_t)split * kgroups;
-  const int64_t g_end = (g_begin + kgroups < ngroups) ? g_begin + kgroups : ngroups;
-  const int64_t word_base = (int64_t)tile * 16 * WPL + cl * WPL;  // this lane's first word
+  const int64_t nks = I / 32;
+  const int64_t ks0 = ((int64_t)split * NW + wave) * KSW;  // first k-step of this wave
+  const int nk = (int)((ks0 >= nks) ? 0 : ((nks - ks0) < KSW ? (nks - ks0) : KSW));
   const uint16_t *__restrict__ x = reinterpret_cast<const uint16_t *>(a.x);
+  const int64_t n0 = (int64_t)tile * NTILE;
+  const int nel = M * NTILE;
 
-  f32x4 tot[WPL * 8];
+  // ---- small early loads: this thread's bias values ----
+  float bias_v[EPT];
 #pragma unroll
-  for (int j = 0; j < WPL * 8; ++j) tot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + j * NTH;
+    const int64_t n = n0 + (e % NTILE);
+    bias_v[j] = (a.bias && e < nel && n < O) ? f16_bits_to_f32(a.bias[n]) : 0.0f;
+  }
 
-  float *xs = smem + wave * (16 * kDecodeRS);  // fused rotation rows of this wave
+  // Columns past O (last tile only) read an in-bounds word and are zeroed;
+  // their outputs are never stored.  WPL words never straddle O (O % 16 == 0
+  // for WPL == 2, O % 32 == 0 for WPL == 4).
+  const int64_t wbase = (int64_t)tile * 16 * WPL + cl * WPL;
+  const bool wok = wbase < W;
+  const int64_t wcl = wok ? wbase : W - WPL;
 
-  for (int64_t g = g_begin + wave; g < g_end; g += 4) {
-    // ---- issue the group's weight loads first (they dominate latency) ----
-    uint32_t qv[4][8][WPL];
+  float tot[NT][FR];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int64_t k = g * kG + ks * 32 + kb * 8 + r;
-        const int32_t *row = a.qweight + k * W;
-#pragma unroll
-        for (int w = 0; w < WPL; ++w) {
-          const int64_t wi = word_base + w;
-          qv[ks][r][w] = (wi < W) ? (uint32_t)row[wi] : 0u;
-        }
-      }
-    }
-    u32x4 sv[WPL];
-    uint32_t zv[WPL];
-#pragma unroll
-    for (int w = 0; w < WPL; ++w) {
-      const int64_t wi = word_base + w;
-      if (wi < W) {
-        sv[w] = *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * wi);
-        zv[w] = (uint32_t)a.qzeros[g * W + wi];
-      } else {
-        sv[w] = u32x4{0u, 0u, 0u, 0u};
-        zv[w] = 0u;
-      }
-    }
+    for (int i = 0; i < FR; ++i) tot[j][i] = 0.0f;
 
-    // ---- A fragments: rotated activations of this group, rounded to DT ----
-    u32x4 af[4];
-    if constexpr (FUSED) {
+  if (nk > 0) {
+    const int64_t g_first = ks0 / 4;
+    float *xs = smem + wave * (MT * kDecodeRS);  // fused rotation rows of this wave
+    // ---- fused: the first group's rotation inputs, before the weight stream ----
+    RotParams rp;
+    float xin[MT][2];
+    float cs0 = 0.f, cs1 = 0.f;
+    auto load_rot_inputs = [&](int64_t g) {
       const int64_t c0 = g * kG + 2 * lane;
-      const float s0 = a.cs[c0], s1 = a.cs[c0 + 1];
-      for (int m = 0; m < M; ++m) {
-        const uint32_t wv = *reinterpret_cast<const uint32_t *>(x + (int64_t)m * I + c0);
-        xs[m * kDecodeRS + 2 * lane] = act_to_f32<DT>(wv & 0xffffu) * s0;
-        xs[m * kDecodeRS + 2 * lane + 1] = act_to_f32<DT>(wv >> 16) * s1;
-      }
-      wave_lds_sync();
-      rotate_rows_lds<16>(xs, kDecodeRS, M, a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot, lane);
+      rp.load(a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot, lane);
+      cs0 = a.cs[c0];
+      cs1 = a.cs[c0 + 1];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (cl < M) {
-          const float *src = xs + cl * kDecodeRS + ks * 32 + kb * 8;
-          const float4 lo = *reinterpret_cast<const float4 *>(src);
-          const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-          af[ks] = u32x4{pack2<DT>(lo.x, lo.y), pack2<DT>(lo.z, lo.w), pack2<DT>(hi.x, hi.y),
-                         pack2<DT>(hi.z, hi.w)};
-        } else {
-          af[ks] = u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int m = 0; m < MT; ++m) {
+        const uint32_t wv = *reinterpret_cast<const uint32_t *>(x + (int64_t)(m < M ? m : 0) * I + c0);
+        xin[m][0] = act_to_f32<DT>(wv & 0xffffu);
+        xin[m][1] = act_to_f32<DT>(wv >> 16);
       }
-      wave_lds_sync();  // the next group's rotation rewrites xs
-    } else {
+    };
+    if constexpr (FUSED) load_rot_inputs(g_first);
+
+    // ---- A fragments (non-fused), group scales / zeros, then the weights of
+    //      the first PD k-steps, in the order they are consumed ----
+    u32x4 af[KSW];
+    const int arow = cl < M ? cl : 0;
+    auto load_a = [&](int k) {  // non-fused: rotated activations from the workspace
+      const int64_t ks = ks0 + (k < nk ? k : 0);
+      af[k] = *reinterpret_cast<const u32x4 *>(xr + (int64_t)arow * I + ks * 32 + kb * 8);
+      if (cl >= M) af[k] = u32x4{0u, 0u, 0u, 0u};
+    };
+    if constexpr (!FUSED) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        af[ks] = (cl < M) ? *reinterpret_cast<const u32x4 *>(xr + (int64_t)cl * I + g * kG + ks * 32 + kb * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int k = 0; k < PD; ++k) load_a(k);
     }
-
-    // ---- row sums of the rounded activations (same layout as the output) ----
-    const u32x4 ones = {MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes,
-                        MfmaTypes<DT>::kOnes};
-    f32x4 xsum = {0.f, 0.f, 0.f, 0.f};
+    u32x4 sv[NG][WPL];
+    uint32_t zv[NG][WPL];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xsum = mfma16<DT>(af[ks], ones, xsum);
-
-    // ---- the group's products ----
-    f32x4 acc[WPL * 8];
-#pragma unroll
-    for (int j = 0; j < WPL * 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int gi = 0; gi < NG; ++gi) {
+      const int64_t g0 = g_first + gi;
+      const int64_t g = g0 < I / kG ? g0 : I / kG - 1;
 #pragma unroll
       for (int w = 0; w < WPL; ++w) {
-        uint32_t rw[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rw[r] = qv[ks][r][w];
-        u32x4 bf[8];
-        build_b_frags<DT>(rw, bf);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) acc[w * 8 + s] = mfma16<DT>(af[ks], bf[s], acc[w * 8 + s]);
+        sv[gi][w] = wok ? *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * (wcl + w)) : u32x4{0u, 0u, 0u, 0u};
+        zv[gi][w] = (uint32_t)a.qzeros[g * W + wcl + w];
       }
     }
+    uint32_t qv[KSW][8][WPL];
+    auto load_ks = [&](int k) {
+      const int64_t ks = ks0 + (k < nk ? k : 0);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) load_words<WPL>(a.qweight + (ks * 32 + kb * 8 + r) * W + wcl, qv[k][r]);
+    };
+#pragma unroll
+    for (int k = 0; k < PD; ++k) load_ks(k);
 
-    // ---- fold: tot += s/c * (acc - (off + c*z) * xsum) ----
+    const u32x4 ones = {MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes,
+                        MfmaTypes<DT>::kOnes};
+    f32x4 acc[NT];
+    f32x4 xsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < WPL; ++w) {
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int col = awq_col(s);
-        const uint32_t sb = (sv[w][col >> 1] >> (16 * (col & 1))) & 0xffffu;
-        const float c = slot_mult<DT>(s);
-        const float sc = f16_bits_to_f32(sb) * (1.0f / c);
-        const float zz = MfmaTypes<DT>::kOff + c * (float)((zv[w] >> (4 * s)) & 0xfu);
+    for (int k = 0; k < KSW; ++k) {
+      if (k < nk) {
+        const int64_t ks = ks0 + k;
+        const int64_t g = ks / 4;
+        const int gi = (int)(g - g_first);
+        if constexpr (FUSED) {
+          if (k == 0 || (ks % 4) == 0) {  // entering a group: rotate it into LDS
+            if (k != 0) load_rot_inputs(g);
+            wave_lds_sync();
 #pragma unroll
-        for (int i = 0; i < FR; ++i) tot[w * 8 + s][i] += sc * (acc[w * 8 + s][i] - zz * xsum[i]);
+            for (int m = 0; m < MT; ++m) {
+              xs[m * kDecodeRS + 2 * lane] = m < M ? xin[m][0] * cs0 : 0.0f;
+              xs[m * kDecodeRS + 2 * lane + 1] = m < M ? xin[m][1] * cs1 : 0.0f;
+            }
+            wave_lds_sync();
+            rotate_rows_lds<MT>(xs, kDecodeRS, rp, a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot,
+                                lane);
+          }
+          const float *src = xs + (cl < MT ? cl : 0) * kDecodeRS + (ks % 4) * 32 + kb * 8;
+          const float4 lo = *reinterpret_cast<const float4 *>(src);
+          const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+          af[k] = u32x4{pack2<DT>(lo.x, lo.y), pack2<DT>(lo.z, lo.w), pack2<DT>(hi.x, hi.y),
+                        pack2<DT>(hi.z, hi.w)};
+          if (cl >= M) af[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if (k + PD < KSW) {  // keep PD k-steps in flight
+          if constexpr (!FUSED) load_a(k + PD);
+          load_ks(k + PD);
+        }
+        xsum = mfma16<DT>(af[k], ones, xsum);
+#pragma unroll
+        for (int w = 0; w < WPL; ++w) {
+          uint32_t rw[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) rw[r] = qv[k][r][w];
+          u32x4 bf[8];
+          build_b_frags<DT>(rw, bf);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc[w * 8 + s] = mfma16<DT>(af[k], bf[s], acc[w * 8 + s]);
+        }
+        // fold at the end of a group or of this wave's k-steps:
+        //   tot += s/c * (acc - (off + c*z) * xsum)
+        if ((ks % 4) == 3 || k == nk - 1) {
+#pragma unroll
+          for (int w = 0; w < WPL; ++w) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const int col = awq_col(s);
+              const uint32_t sb = (sv[gi][w][col >> 1] >> (16 * (col & 1))) & 0xffffu;
+              const float c = slot_mult<DT>(s);
+              const float sc = f16_bits_to_f32(sb) * (1.0f / c);
+              const float zz = MfmaTypes<DT>::kOff + c * (float)((zv[gi][w] >> (4 * s)) & 0xfu);
+#pragma unroll
+              for (int i = 0; i < FR; ++i) tot[w * 8 + s][i] += sc * (acc[w * 8 + s][i] - zz * xsum[i]);
+              acc[w * 8 + s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+          xsum = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
   }
 
-  // ---- reduce the four waves' tiles in LDS (wave order) ----
-  const int rows = (FR < 4) ? FR : 16;  // rows held in registers across the wave
-  __syncthreads();  // every wave is done with its rotation rows
-  float *red = smem;  // [4][rows][ntile]
+  // ---- reduce the NW waves' tiles in LDS (wave order) ----
+  __syncthreads();   // every wave is done with its rotation rows
+  float *red = smem; // [NW][MT][NTILE]
 #pragma unroll
   for (int w = 0; w < WPL; ++w) {
 #pragma unroll
@@ -248,54 +333,85 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int kgroups, int sp
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
         const int row = 4 * kb + i;
-        if (row < rows) red[(wave * rows + row) * ntile + col] = tot[w * 8 + s][i];
+        if (row < MT) red[(wave * MT + row) * NTILE + col] = tot[w * 8 + s][i];
       }
     }
   }
   __syncthreads();
 
-  const int64_t n0 = (int64_t)tile * ntile;
-  const int nel = M * ntile;
-  const bool direct = (splits == 1);
-  for (int e = threadIdx.x; e < nel; e += 256) {
-    const int row = e / ntile, col = e - row * ntile;
-    const float v = ((red[(0 * rows + row) * ntile + col] + red[(1 * rows + row) * ntile + col]) +
-                     red[(2 * rows + row) * ntile + col]) +
-                    red[(3 * rows + row) * ntile + col];
-    const int64_t n = n0 + col;
-    if (n >= O) continue;
-    if (direct) {
-      const float out = v + (a.bias ? f16_bits_to_f32(a.bias[n]) : 0.0f);
-      if (a.y_dt == kF32) reinterpret_cast<float *>(a.y)[(int64_t)row * O + n] = out;
-      else if (a.y_dt == kF16) reinterpret_cast<uint16_t *>(a.y)[(int64_t)row * O + n] = f32_to_f16_bits(out);
-      else reinterpret_cast<uint16_t *>(a.y)[(int64_t)row * O + n] = f32_to_bf16_bits(out);
-    } else {
-      partial[((int64_t)split * M + row) * O + n] = v;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + j * NTH;
+    v[j] = 0.0f;
+    if (e < nel) {
+      v[j] = red[e];  // wave 0: [row][col] = e
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v[j] += red[w * MT * NTILE + e];
     }
   }
-  if (direct) return;
+  auto store_elems = [&](const float *val) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = threadIdx.x + j * NTH;
+      const int row = e / NTILE;
+      const int64_t n = n0 + (e - row * NTILE);
+      if (e < nel && n < O) store_out(a, row, n, val[j] + bias_v[j]);
+    }
+  };
+  if (splits == 1) {
+    store_elems(v);
+    return;
+  }
 
-  __threadfence();  // release this workgroup's partial (device scope)
+  // ---- split-K handoff (see the header) ----
+  const int64_t sstride = (int64_t)M * O;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + j * NTH;
+    const int row = e / NTILE;
+    const int64_t n = n0 + (e - row * NTILE);
+    if (e < nel && n < O)
+      __hip_atomic_store(&partial[split * sstride + (int64_t)row * O + n], v[j], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
+  uint32_t *cnt = counters + (int64_t)tile * kCounterStride;
   if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&counters[tile], 1u);
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == (uint32_t)(splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire every other workgroup's partial
-  for (int e = threadIdx.x; e < nel; e += 256) {
-    const int row = e / ntile, col = e - row * ntile;
-    const int64_t n = n0 + col;
-    if (n >= O) continue;
-    float v = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) v += __builtin_nontemporal_load(&partial[((int64_t)sp * M + row) * O + n]);
-    const float out = v + (a.bias ? f16_bits_to_f32(a.bias[n]) : 0.0f);
-    if (a.y_dt == kF32) reinterpret_cast<float *>(a.y)[(int64_t)row * O + n] = out;
-    else if (a.y_dt == kF16) reinterpret_cast<uint16_t *>(a.y)[(int64_t)row * O + n] = f32_to_f16_bits(out);
-    else reinterpret_cast<uint16_t *>(a.y)[(int64_t)row * O + n] = f32_to_bf16_bits(out);
+  // Gather every split's partial, all loads of a batch in flight together,
+  // summing in split order.
+  constexpr int SB = EPT >= 32 ? 1 : 32 / EPT;  // splits per batch
+  float sum[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) sum[j] = 0.0f;
+  for (int sp = 0; sp < splits; sp += SB) {
+    float t[EPT][SB];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = threadIdx.x + j * NTH;
+      const int row = e / NTILE;
+      const int64_t n = n0 + (e - row * NTILE);
+      const bool ok = e < nel && n < O;
+      const float *pp = partial + (int64_t)row * O + (ok ? n : 0);
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        t[j][u] = (ok && sp + u < splits)
+                      ? __hip_atomic_load(pp + (sp + u) * sstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+#pragma unroll
+      for (int u = 0; u < SB; ++u) sum[j] += t[j][u];
   }
-  if (threadIdx.x == 0) atomicExch(&counters[tile], 0u);
+  store_elems(sum);
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static int env_int(const char *name, int dflt) {
@@ -306,23 +422,33 @@ static int env_int(const char *name, int dflt) {
 DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused) {
   (void)fused;
   DecodePlan p;
-  p.wpl = 1;
+  const int64_t nks = I / 32;
+  if (tokens <= 4) {
+    // Few rows: the per-k-step fold is nearly free (one register row), so a
+    // wave owns one k-step of 128-byte row segments; eight waves per
+    // workgroup keep the K splits (whose partials the last workgroup gathers)
+    // at nks / 8 while filling the chip.
+    p.wpl = (O % 16 == 0) ? 2 : 1;
+    p.ksw = 1;
+    p.nw = 8;
+  } else {
+    // Up to 16 rows: the partial sums cost splits * tokens * O * 8 bytes, so
+    // an eight-wave workgroup covers up to 2048 rows (eight k-steps per wave,
+    // folded once per group) of a 128-column tile.
+    p.wpl = 1;
+    p.nw = 8;
+    p.ksw = 8;
+    while (p.ksw > 1 && (int64_t)p.nw * (p.ksw / 2) >= nks) p.ksw /= 2;
+  }
+  const int fw = env_int("PARO_DECODE_WPL", 0);
+  if (fw == 1 || (fw == 2 && O % 16 == 0) || (fw == 4 && O % 32 == 0)) p.wpl = fw;
+  const int fk = env_int("PARO_DECODE_KSW", 0);
+  if (fk == 1 || fk == 2 || fk == 4 || fk == 8) p.ksw = fk;
+  const int fn = env_int("PARO_DECODE_NW", 0);
+  if (fn == 4 || fn == 8 || fn == 16) p.nw = fn;
   p.ntile = 128 * p.wpl;
   p.n_tiles = (int)((O + p.ntile - 1) / p.ntile);
-  const int64_t ngroups = I / kG;
-  // Largest multiple of 4 groups per workgroup that still fills the chip
-  // with one full wave of workgroups; fewer K splits mean less partial-sum
-  // traffic (tokens * O * 4 bytes written and read per extra split).
-  int kg = 4;
-  for (int cand = 4; cand <= 4 * ((ngroups + 3) / 4); cand *= 2) {
-    const int64_t wgs = (int64_t)p.n_tiles * ((ngroups + cand - 1) / cand);
-    if (wgs >= 240) kg = cand;
-  }
-  const int forced = env_int("PARO_DECODE_KGROUPS", 0);
-  if (forced > 0) kg = forced;
-  (void)tokens;
-  p.kgroups = kg;
-  p.splits = (int)((ngroups + kg - 1) / kg);
+  p.splits = (int)((nks + p.nw * p.ksw - 1) / (p.nw * p.ksw));
   return p;
 }
 
@@ -331,41 +457,63 @@ size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O) {
   return (size_t)p.splits * (size_t)tokens * (size_t)O * 4;
 }
 
-template <int DT, int WPL, bool FUSED>
+template <int DT, int WPL, int KSW, int NW, bool FUSED>
 static hipError_t launch_decode_t(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
                                   float *partial, hipStream_t st) {
-  dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits);
+  dim3 grid((unsigned)(p.n_tiles * p.splits));
   const int M = (int)a.tokens;
-  const int rows = (M <= 1) ? 1 : (M <= 2) ? 2 : 16;
-  size_t red_bytes = (size_t)4 * rows * p.ntile * 4;
-  size_t rot_bytes = FUSED ? (size_t)4 * 16 * kDecodeRS * 4 : 0;
+  const int mt = (M <= 1) ? 1 : (M <= 2) ? 2 : (M <= 4) ? 4 : (M <= 8) ? 8 : 16;
+  size_t red_bytes = (size_t)NW * mt * p.ntile * 4;
+  size_t rot_bytes = FUSED ? (size_t)NW * mt * kDecodeRS * 4 : 0;
   size_t shmem = red_bytes > rot_bytes ? red_bytes : rot_bytes;
   const uint16_t *xrp = reinterpret_cast<const uint16_t *>(xr);
-  if (M <= 1)
-    hipLaunchKernelGGL((decode_kernel<DT, WPL, FUSED, 1>), grid, dim3(256), shmem, st, a, xrp, p.kgroups,
-                       p.splits, partial, counters);
-  else if (M <= 2)
-    hipLaunchKernelGGL((decode_kernel<DT, WPL, FUSED, 2>), grid, dim3(256), shmem, st, a, xrp, p.kgroups,
-                       p.splits, partial, counters);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT, WPL, FUSED, 4>), grid, dim3(256), shmem, st, a, xrp, p.kgroups,
-                       p.splits, partial, counters);
+#define PARO_DECODE_LAUNCH(MT)                                                                                \
+  hipLaunchKernelGGL((decode_kernel<DT, WPL, KSW, NW, FUSED, MT>), grid, dim3(64 * NW), shmem, st, a, xrp, p.splits, \
+                     partial, counters)
+  switch (mt) {
+    case 1: PARO_DECODE_LAUNCH(1); break;
+    case 2: PARO_DECODE_LAUNCH(2); break;
+    case 4: PARO_DECODE_LAUNCH(4); break;
+    case 8: PARO_DECODE_LAUNCH(8); break;
+    default: PARO_DECODE_LAUNCH(16); break;
+  }
+#undef PARO_DECODE_LAUNCH
   return hipGetLastError();
+}
+
+template <int DT, bool FUSED>
+static hipError_t launch_decode_dt(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
+                                   float *partials, hipStream_t st) {
+  // every (wpl, ksw, nw) the planner produces is instantiated; other
+  // combinations (tuning overrides only) are rejected
+#define PARO_DECODE_CFG(WPL, KSW, NW) \
+  if (p.wpl == WPL && p.ksw == KSW && p.nw == NW) return launch_decode_t<DT, WPL, KSW, NW, FUSED>(a, p, xr, counters, partials, st)
+  PARO_DECODE_CFG(2, 1, 8);
+  PARO_DECODE_CFG(1, 1, 8);
+  PARO_DECODE_CFG(4, 1, 8);
+  PARO_DECODE_CFG(2, 2, 4);
+  PARO_DECODE_CFG(1, 8, 16);
+  PARO_DECODE_CFG(1, 8, 8);
+  PARO_DECODE_CFG(1, 4, 8);
+  PARO_DECODE_CFG(1, 2, 8);
+  PARO_DECODE_CFG(2, 4, 8);
+  PARO_DECODE_CFG(1, 4, 16);
+  PARO_DECODE_CFG(1, 2, 16);
+  PARO_DECODE_CFG(1, 1, 16);
+  PARO_DECODE_CFG(1, 8, 4);
+  PARO_DECODE_CFG(1, 4, 4);
+#undef PARO_DECODE_CFG
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
                          float *partials, hipStream_t st) {
   const bool fused = (xr == nullptr);
-#define PARO_DECODE_CASE(DT, WPL)                                                   \
-  return fused ? launch_decode_t<DT, WPL, true>(a, p, xr, counters, partials, st) \
-               : launch_decode_t<DT, WPL, false>(a, p, xr, counters, partials, st)
-  if (a.x_dt == kF16) {
-    if (p.wpl == 2) PARO_DECODE_CASE(kF16, 2);
-    PARO_DECODE_CASE(kF16, 1);
-  }
-  if (p.wpl == 2) PARO_DECODE_CASE(kBF16, 2);
-  PARO_DECODE_CASE(kBF16, 1);
-#undef PARO_DECODE_CASE
+  if (a.x_dt == kF16)
+    return fused ? launch_decode_dt<kF16, true>(a, p, xr, counters, partials, st)
+                 : launch_decode_dt<kF16, false>(a, p, xr, counters, partials, st);
+  return fused ? launch_decode_dt<kBF16, true>(a, p, xr, counters, partials, st)
+               : launch_decode_dt<kBF16, false>(a, p, xr, counters, partials, st);
 }
 
 }  // namespace paro

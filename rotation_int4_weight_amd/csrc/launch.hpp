@@ -39,11 +39,12 @@ struct LinearArgs {
 // rotation runs fused in each workgroup's prologue; otherwise `xr` holds the
 // rotated activations ([tokens][I], x dtype) and is read directly.
 struct DecodePlan {
-  int wpl;        // packed words per lane and row (1 or 2)
+  int wpl;        // packed words per lane and row (1, 2 or 4)
+  int ksw;        // 32-row k-steps per wave (a workgroup covers nw * ksw)
+  int nw;         // waves per workgroup (4 or 8)
   int ntile;      // output columns per workgroup (= 128 * wpl)
   int n_tiles;    // ceil(O / ntile)
-  int kgroups;    // 128-row groups per workgroup
-  int splits;     // workgroups along K (ceil(I/128 / kgroups))
+  int splits;     // workgroups along K (ceil(I/32 / (nw * ksw)))
 };
 DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused);
 // Bytes of fp32 split-K partial sums the plan needs (0 with one split).

@@ -40,10 +40,10 @@ constexpr int kMaxKrot = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxOut = int64_t(1) << 21;
 // Every workspace starts with a fixed counter area for the split-K
-// reduction (one 32-bit counter per 128-column tile, at most kMaxOut/128),
-// so a zero-filled workspace stays valid across shapes and paths: no path
-// ever writes anything but zeros-at-exit into it.
-constexpr size_t kCounterBytes = (size_t)(kMaxOut / 128) * 4;
+// reduction (one 32-bit counter on its own 128-byte line per 128-column tile,
+// at most kMaxOut/128 tiles), so a zero-filled workspace stays valid across
+// shapes and paths: no path ever writes anything but zeros-at-exit into it.
+constexpr size_t kCounterBytes = (size_t)(kMaxOut / 128) * 128;
 
 int64_t group_of(const paro_w4_layer *L) { return L->group_size == -1 ? L->in_features : L->group_size; }
 
@@ -208,21 +208,31 @@ size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens,
   return workspace_for(L, tokens, path);
 }
 
-int paro_w4a16_linear_path(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
-                           paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream,
-                           paro_path path) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the linear entry points.  prerotated: x already holds X_r.
+int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream, paro_path path,
+                bool prerotated) {
   int rc = check_gpu_shape(L);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
   if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
   if (path < PARO_PATH_AUTO || path > PARO_PATH_PREFILL) return fail(PARO_ERR_SHAPE, "unknown path %d", (int)path);
+  if (prerotated && path == PARO_PATH_DECODE_FUSED)
+    return fail(PARO_ERR_SHAPE, "the fused decode path rotates itself; use AUTO, DECODE_SPLIT or PREFILL");
   if (tokens == 0) return ok();
-  if (path == PARO_PATH_AUTO) path = auto_path(tokens);
+  if (path == PARO_PATH_AUTO) {
+    path = auto_path(tokens);
+    if (prerotated && path == PARO_PATH_DECODE_FUSED) path = PARO_PATH_DECODE_SPLIT;
+  }
   if ((path == PARO_PATH_DECODE_FUSED || path == PARO_PATH_DECODE_SPLIT) && tokens > 16)
     return fail(PARO_ERR_UNSUPPORTED, "decode paths take at most 16 tokens (got %lld)", (long long)tokens);
   if (!x || !y) return fail(PARO_ERR_NULL, "x and y are required");
-  rc = check_rotation_tensors(L);
+  rc = prerotated ? PARO_OK : check_rotation_tensors(L);
   if (!rc) rc = check_weight_tensors(L);
   if (rc) return rc;
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(PARO_ERR_ALIGN, "x and y must be 16-byte aligned");
@@ -268,19 +278,38 @@ int paro_w4a16_linear_path(const paro_w4_layer *L, const void *x, paro_dtype x_d
     if (e != hipSuccess) return hip_fail(e, "decode (fused) launch");
     return ok();
   }
-  // X_r into the workspace, then the contraction over it
-  e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
-                                L->channel_scales, L->krot, st);
-  if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+  const void *xin = x;
+  if (!prerotated) {  // X_r into the workspace, then the contraction over it
+    e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
+                                  L->channel_scales, L->krot, st);
+    if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+    xin = xr;
+  }
   if (path == PARO_PATH_DECODE_SPLIT) {
     const paro::DecodePlan p = paro::plan_decode(I, O, tokens, false);
-    e = paro::launch_decode(a, p, xr, counters, partials, st);
+    e = paro::launch_decode(a, p, xin, counters, partials, st);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
   }
-  e = paro::launch_prefill_gemm(a, xr, st);
+  e = paro::launch_prefill_gemm(a, xin, st);
   if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paro_w4a16_linear_path(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                           paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream,
+                           paro_path path) {
+  return linear_impl(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, path, false);
+}
+
+int paro_w4a16_linear_prerotated(const paro_w4_layer *L, const void *x_r, paro_dtype x_dt, int64_t tokens,
+                                 void *y, paro_dtype y_dt, void *workspace, size_t workspace_bytes,
+                                 void *stream, paro_path path) {
+  return linear_impl(L, x_r, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, path, true);
 }
 
 int paro_w4a16_linear(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,

@@ -5,48 +5,51 @@
 // Pairwise Givens rotations: krot ordered stages of disjoint pair rotations,
 // local to each 128-channel group.
 //
-// One workgroup = 4 waves on one group g and up to 4*TW token rows; each wave
-// stages TW rows x 128 channels of the group in LDS (fp32), applies every
+// One workgroup = 4 waves on one group g and up to 4*RW token rows; each wave
+// stages RW rows x 128 channels of the group in LDS (fp32), applies every
 // stage with the pair/angle of lane p held in registers, and writes the rows
 // back out coalesced (lane p owns channels 2p and 2p+1 on load and store).
+// RW is 16 for many tokens (the pair/angle loads and sin/cos are amortised
+// over more rows) and 1..4 for few tokens (more waves, shorter chains of
+// dependent LDS stages).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace paro {
 
-constexpr int kRotTW = 16;       // token rows per wave
 constexpr int kRotRS = kG + 4;   // LDS row stride (floats), staggers banks across rows
 
-template <int XDT, int ODT>
+template <int XDT, int ODT, int RW>
 __global__ void __launch_bounds__(256)
 scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64_t tokens, int64_t I,
                     const int16_t *__restrict__ pairs, const float *__restrict__ theta,
                     const float *__restrict__ cscale, int krot) {
-  __shared__ float lds[4][kRotTW * kRotRS];
+  __shared__ float lds[4][RW * kRotRS];
   const int lane = lane_id(), wave = wave_id();
   const int64_t g = blockIdx.x;
-  const int64_t m0 = ((int64_t)blockIdx.y * 4 + wave) * kRotTW;
+  const int64_t m0 = ((int64_t)blockIdx.y * 4 + wave) * RW;
   if (m0 >= tokens) return;  // whole wave idle (no block-level barrier below)
-  const int T = (int)((tokens - m0) < kRotTW ? (tokens - m0) : kRotTW);
+  const int T = (int)((tokens - m0) < RW ? (tokens - m0) : RW);
   float *xs = lds[wave];
   const int64_t c0 = g * kG + 2 * lane;
 
-  // load + channel scale (x . D^-1)
+  RotParams rp;
+  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  // load + channel scale (x . D^-1); rows past the last token are zero
   const float s0 = cscale[c0], s1 = cscale[c0 + 1];
 #pragma unroll
-  for (int m = 0; m < kRotTW; ++m) {
-    if (m < T) {
-      const uint32_t w = *reinterpret_cast<const uint32_t *>(x + (m0 + m) * I + c0);
-      xs[m * kRotRS + 2 * lane] = act_to_f32<XDT>(w & 0xffffu) * s0;
-      xs[m * kRotRS + 2 * lane + 1] = act_to_f32<XDT>(w >> 16) * s1;
-    }
+  for (int m = 0; m < RW; ++m) {
+    const int mm = m < T ? m : 0;
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(x + (m0 + mm) * I + c0);
+    xs[m * kRotRS + 2 * lane] = m < T ? act_to_f32<XDT>(w & 0xffffu) * s0 : 0.0f;
+    xs[m * kRotRS + 2 * lane + 1] = m < T ? act_to_f32<XDT>(w >> 16) * s1 : 0.0f;
   }
   wave_lds_sync();
 
-  rotate_rows_lds<kRotTW>(xs, kRotRS, T, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  rotate_rows_lds<RW>(xs, kRotRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
 
 #pragma unroll
-  for (int m = 0; m < kRotTW; ++m) {
+  for (int m = 0; m < RW; ++m) {
     if (m < T) {
       const float a = xs[m * kRotRS + 2 * lane], b = xs[m * kRotRS + 2 * lane + 1];
       const int64_t o = (m0 + m) * I + c0;
@@ -59,14 +62,22 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
   }
 }
 
+template <int XDT, int ODT, int RW>
+static hipError_t launch_rot_rw(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
+                                const float *theta, const float *cs, int krot, hipStream_t st) {
+  const int64_t per_block = 4 * RW;
+  dim3 grid((unsigned)(I / kG), (unsigned)((tokens + per_block - 1) / per_block));
+  hipLaunchKernelGGL((scale_rotate_kernel<XDT, ODT, RW>), grid, dim3(256), 0, st, x, xr, tokens, I, pairs,
+                     theta, cs, krot);
+  return hipGetLastError();
+}
+
 template <int XDT, int ODT>
 static hipError_t launch_rot(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
                              const float *theta, const float *cs, int krot, hipStream_t st) {
-  const int64_t per_block = 4 * kRotTW;
-  dim3 grid((unsigned)(I / kG), (unsigned)((tokens + per_block - 1) / per_block));
-  hipLaunchKernelGGL((scale_rotate_kernel<XDT, ODT>), grid, dim3(256), 0, st, x, xr, tokens, I, pairs,
-                     theta, cs, krot);
-  return hipGetLastError();
+  if (tokens <= 4) return launch_rot_rw<XDT, ODT, 1>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  if (tokens <= 64) return launch_rot_rw<XDT, ODT, 4>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  return launch_rot_rw<XDT, ODT, 16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
 }
 
 hipError_t launch_scale_rotate(const uint16_t *x, int x_dt, void *xr, int xr_dt, int64_t tokens, int64_t I,

@@ -165,3 +165,15 @@ def test_workspace_sizes_and_path_choice():
     assert wsb(2048, 3) - wsb(1024, 3) == 1024 * 4096 * 2
     assert wsb(1, 1) > 0 and wsb(16, 2) > wsb(16, 1)
     assert wsb(0, 1) == 0
+
+
+@needs_no_gpu
+def test_prerotated_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(pairs=0, theta=0, channel_scales=0)  # rotation tensors are not needed
+    call = lambda path, tokens=4, ws=FAKE * 4: lib.paro_w4a16_linear_prerotated(
+        ctypes.byref(L), FAKE, 0, tokens, FAKE * 2, 0, ws, 1 << 30, None, path)
+    assert call(1) == 2                        # fused path rotates itself
+    assert call(2, tokens=17) == 5
+    assert call(3, ws=0) == 7
+    assert call(0, tokens=0) == 0

@@ -274,3 +274,48 @@ def test_one_workspace_serves_many_shapes_and_paths():
         rc, err, mref, _ = ref.paro_linear_ref_check(L, x, synth.F16, to_host_bits(y), synth.F32, LIN_TOL)
         say(f"  shared ws I={L.in_features} O={L.out_features} M={x.shape[0]} {path}: {err / mref:.3e}")
         assert rc == ref.OK
+
+
+@pytest.mark.parametrize("cfg,path", [(1, "split"), (2, "split"), (3, "prefill")])
+def test_prerotated_projection_matches_linear(cfg, path):
+    """paro_scale_rotate + the projection alone == the linear, bit for bit."""
+    lname, L, x, dt = workload(cfg)
+    say(f"prerotated cfg{cfg} {lname} path={path}")
+    D = paro.DeviceLayer(L)
+    xd = x_to_device(x, dt)
+    M, O = x.shape[0], L.out_features
+    full = to_host_bits(run_linear(D, xd, O, synth.F32, PATHS[path]))
+    xr = torch.empty_like(xd)
+    paro.paro_scale_rotate(D, xd, xr)
+    y = torch.empty((M, O), dtype=torch.float32, device="cuda")
+    ws = paro.make_workspace(paro.paro_w4a16_linear_workspace_bytes(D, M, dt, PATHS[path]))
+    paro.paro_w4a16_linear_prerotated(D, xr, y, ws, path=PATHS[path])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(y).view(np.uint32), full.view(np.uint32))
+
+
+@pytest.mark.parametrize("I,O,M,path", [(4096, 4096, 1, "fused"), (4096, 2048, 16, "split"),
+                                        (2048, 1024, 3, "fused")])
+def test_split_k_handoff_alternating_inputs(I, O, M, path):
+    """Two inputs alternate on one workspace for many calls: every output must
+    equal its first (oracle-checked) result bit for bit, so no call ever sees
+    another call's partial sums or a counter left non-zero."""
+    L = synth.make_layer(330, M, I, O)
+    xa = synth.make_x(330, M, M, I, synth.F16)
+    xb = synth.make_x(331, M, M, I, synth.F16)
+    D = paro.DeviceLayer(L)
+    ws = paro.make_workspace(paro.paro_w4a16_linear_workspace_bytes(D, M, 0, PATHS[path]))
+    say(f"handoff stress I={I} O={O} M={M} path={path}")
+    outs = []
+    for x in (xa, xb):
+        xd = x_to_device(x, synth.F16)
+        y = run_linear(D, xd, O, synth.F32, PATHS[path], ws=ws)
+        rc, err, mref, _ = ref.paro_linear_ref_check(L, x, synth.F16, to_host_bits(y), synth.F32, LIN_TOL)
+        assert rc == ref.OK
+        outs.append((xd, y.clone()))
+    ys = [torch.empty((M, O), dtype=torch.float32, device="cuda") for _ in range(200)]
+    for i, yi in enumerate(ys):
+        paro.paro_w4a16_linear(D, outs[i % 2][0], yi, ws, path=PATHS[path])
+    torch.cuda.synchronize()
+    for i, yi in enumerate(ys):
+        assert torch.equal(yi.view(torch.int32), outs[i % 2][1].view(torch.int32)), f"call {i} differs"

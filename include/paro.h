@@ -40,7 +40,7 @@
  *     the host before anything is enqueued; on error nothing is launched and
  *     paro_last_error() (thread-local) describes the failure.  Launch errors
  *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
- *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^24,
+ *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^22,
  *     O a multiple of 8 and <= 2^21, tokens <= 2^21; x, y, x_r, w_out,
  *     qweight and scales 16-byte aligned.  Other values give
  *     PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.

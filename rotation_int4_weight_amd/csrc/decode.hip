@@ -490,6 +490,7 @@ static hipError_t launch_decode_dt(const LinearArgs &a, const DecodePlan &p, con
   if (p.wpl == WPL && p.ksw == KSW && p.nw == NW) return launch_decode_t<DT, WPL, KSW, NW, FUSED>(a, p, xr, counters, partials, st)
   PARO_DECODE_CFG(2, 1, 8);
   PARO_DECODE_CFG(1, 1, 8);
+  PARO_DECODE_CFG(2, 1, 16);
   PARO_DECODE_CFG(4, 1, 8);
   PARO_DECODE_CFG(2, 2, 4);
   PARO_DECODE_CFG(1, 8, 16);

@@ -37,7 +37,9 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kMaxTokens = int64_t(1) << 21;  // keeps every grid dimension < 65536
 constexpr int kMaxKrot = 64;
-constexpr int64_t kMaxDim = int64_t(1) << 24;
+// The prefill GEMM addresses a 256-row activation tile with 32-bit buffer
+// offsets (256 * I * 2 bytes < 2^32).
+constexpr int64_t kMaxDim = int64_t(1) << 22;
 constexpr int64_t kMaxOut = int64_t(1) << 21;
 // Every workspace starts with a fixed counter area for the split-K
 // reduction (one 32-bit counter on its own 128-byte line per 128-column tile,

@@ -110,6 +110,7 @@ def lin(L, x=FAKE, xdt=0, tokens=4, y=FAKE * 2, ydt=0, ws=FAKE * 4, wsb=1 << 30,
     (dict(L=dict(G=100)), 2),            # G does not divide I
     (dict(L=dict(krot=0)), 2),
     (dict(L=dict(krot=65)), 5),
+    (dict(L=dict(I=(1 << 22) + 128)), 5),  # 32-bit tile offsets of the prefill GEMM
     (dict(L=dict(pairs=0)), 1),
     (dict(L=dict(qweight=0)), 1),
     (dict(L=dict(qweight=FAKE + 4)), 4),

@@ -86,8 +86,9 @@ typedef enum {
                                  prologue + split-K MFMA GEMV; tokens <= 16      */
   PARO_PATH_DECODE_SPLIT = 2, /* scale_rotate into the workspace, then the same
                                  GEMV reading X_r; tokens <= 16                  */
-  PARO_PATH_PREFILL = 3       /* scale_rotate into the workspace, then the MFMA
-                                 GEMM with LDS-staged dequantized weight tiles   */
+  PARO_PATH_PREFILL = 3       /* scale_rotate into the workspace (in the GEMM's
+                                 16-row tiled layout), then the MFMA GEMM with
+                                 LDS-staged dequantized weight tiles            */
 } paro_path;
 
 /* One rotated W4 linear layer: sizes plus device pointers to its tensors. */
@@ -163,7 +164,9 @@ int paro_w4a16_linear_path(const paro_w4_layer *layer, const void *x, paro_dtype
  * and rotated (x_r, e.g. from paro_scale_rotate with xr_dt == x_dt):
  *   y[m][n] = sum_k x_r[m][k] * (q[k][n] - z[k/G][n]) * s[k/G][n] + bias[n].
  * It runs exactly the contraction kernel of the DECODE_SPLIT path (tokens <=
- * 16) or of the PREFILL path, so timing it isolates that kernel.  path must be
+ * 16) or of the PREFILL path, so timing it isolates that kernel; for PREFILL
+ * x_r is first copied into the GEMM's tiled layout in the workspace (a
+ * separate copy kernel, one read and one write of x_r).  path must be
  * PARO_PATH_AUTO, _DECODE_SPLIT or _PREFILL; layer->pairs/theta/
  * channel_scales are not used.  Workspace as for paro_w4a16_linear (the
  * same size suffices).

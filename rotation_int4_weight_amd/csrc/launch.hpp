@@ -53,7 +53,24 @@ size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O);
 hipError_t launch_decode(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
                          float *partials, hipStream_t st);
 
-// Prefill: MFMA GEMM over rotated activations xr ([tokens][I], x dtype).
-hipError_t launch_prefill_gemm(const LinearArgs &a, const void *xr, hipStream_t st);
+// Fragment-major tiled layout of rotated activations for the prefill GEMM
+// (x dtype).  Rows are padded to a multiple of 16 with zeros.  Each 16-row x
+// 32-column block is 1 KB, contiguous, in the order one
+// v_mfma_f32_16x16x32 A operand is held across the 64 lanes:
+//   element (m, k) at half index
+//     ((m/16) * (I/32) + k/32) * 512 + (((k%32)/8) * 16 + m%16) * 8 + k%8
+// so one 16-byte load per lane fetches a whole fragment from 8 full cache
+// lines.  Size: tiled_rows(tokens) * I * 2 bytes.
+inline int64_t tiled_rows(int64_t tokens) { return (tokens + 15) / 16 * 16; }
+
+// X_r = X D^-1 R written in the tiled layout (pad rows zero).
+hipError_t launch_scale_rotate_tiled(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
+                                     const int16_t *pairs, const float *theta, const float *cs, int krot,
+                                     hipStream_t st);
+// Row-major [tokens][I] (2-byte elements) -> tiled layout (pad rows zero).
+hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64_t I, hipStream_t st);
+
+// Prefill: MFMA GEMM over rotated activations in the tiled layout.
+hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStream_t st);
 
 }  // namespace paro

@@ -115,8 +115,12 @@ paro_path auto_path(int64_t tokens) {
 }
 
 // Workspace layout: [counters kCounterBytes][x_r (split / prefill)][partials]
+// X_r in the workspace: row-major for the split decode path, the GEMM's
+// 16-row tiled layout (rows padded to a multiple of 16) for prefill.
 size_t xr_region(const paro_w4_layer *L, int64_t tokens, paro_path path) {
-  return path == PARO_PATH_DECODE_FUSED ? 0 : align_up((size_t)tokens * (size_t)L->in_features * 2, 256);
+  if (path == PARO_PATH_DECODE_FUSED) return 0;
+  const int64_t rows = path == PARO_PATH_PREFILL ? paro::tiled_rows(tokens) : tokens;
+  return align_up((size_t)rows * (size_t)L->in_features * 2, 256);
 }
 
 size_t workspace_for(const paro_w4_layer *L, int64_t tokens, paro_path path) {
@@ -280,20 +284,29 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     if (e != hipSuccess) return hip_fail(e, "decode (fused) launch");
     return ok();
   }
-  const void *xin = x;
-  if (!prerotated) {  // X_r into the workspace, then the contraction over it
-    e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
-                                  L->channel_scales, L->krot, st);
-    if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
-    xin = xr;
-  }
-  if (path == PARO_PATH_DECODE_SPLIT) {
+  if (path == PARO_PATH_DECODE_SPLIT) {  // row-major X_r into the workspace, then the split-K GEMV over it
+    const void *xin = x;
+    if (!prerotated) {
+      e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
+                                    L->channel_scales, L->krot, st);
+      if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+      xin = xr;
+    }
     const paro::DecodePlan p = paro::plan_decode(I, O, tokens, false);
     e = paro::launch_decode(a, p, xin, counters, partials, st);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
   }
-  e = paro::launch_prefill_gemm(a, xin, st);
+  // prefill: X_r in the tiled layout (rotated straight into it, or re-tiled
+  // from the caller's row-major X_r), then the GEMM
+  uint16_t *xt = (uint16_t *)xr;
+  if (prerotated)
+    e = paro::launch_retile((const uint16_t *)x, xt, tokens, I, st);
+  else
+    e = paro::launch_scale_rotate_tiled((const uint16_t *)x, (int)x_dt, xt, tokens, I, L->pairs, L->theta,
+                                        L->channel_scales, L->krot, st);
+  if (e != hipSuccess) return hip_fail(e, prerotated ? "retile launch" : "scale_rotate launch");
+  e = paro::launch_prefill_gemm(a, xt, st);
   if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
   return ok();
 }

@@ -7,50 +7,81 @@
 // Triton plans and tuning: unpack the 4-bit tile, subtract zero points,
 // multiply by group scales, accumulate in fp32.)
 //
-// Tiling: a workgroup (4 waves, one per SIMD) computes a BM=256 x BN=128 tile
-// of y; wave w owns rows 64w..64w+63 (4 MFMA row tiles) and all 128 columns
-// (8 column tiles): 32 v_mfma_f32_16x16x32 per 32-deep k step.
-//   * A (rotated activations, [tokens][I]) is read straight into MFMA
-//     fragments (lane l: row l&15, 8 consecutive k of block l>>4) with buffer
-//     loads two k steps ahead.  The buffer descriptor's base moves along k in
-//     scalar registers, and its record count ends at the last token, so rows
-//     past the end read as zeros without any per-lane test.  The k loop is
-//     unrolled by a whole 128-row group, so every prefetch buffer is consumed
-//     in place (no register copies of load targets).
-//   * B: each k step the workgroup turns its 32 x 128 packed tile (512 words:
-//     each thread one word of two adjacent rows) into compute-dtype weights in
-//     a double-buffered LDS tile [column][k].  fp16: a byte permute and an OR
-//     with 0x6400 make 1024+q exactly, then one packed add of -(1024+z) and one
-//     packed multiply by s give (q-z)*s rounded once, two weights per
+// A workgroup computes a BM=256 x BN=128 tile of y with 8 waves in two
+// roles, one of each per SIMD:
+//   * consumer waves 0..3 own rows 64c..64c+63 and all 128 columns (4 x 8
+//     MFMA tiles, 32 v_mfma_f32_16x16x32 per 32-deep k step) and issue
+//     nothing but their MFMAs, the LDS reads of the next step's B fragments
+//     (in two halves, each hidden behind the other half's MFMAs) and the
+//     loads of A two steps ahead;
+//   * producer waves 4..7 load the packed weight words four steps before
+//     they are needed, decode each group's scales and zero points and
+//     dequantize the tile two steps ahead into a ring of four LDS tiles.
+// On gfx950 a SIMD hides only about one VALU instruction per 16-cycle MFMA
+// from the same wave but about two from a second wave, so the split keeps
+// the matrix pipe fed while the dequantization runs beside it.  Both roles
+// meet at one barrier per k step.
+//
+// Operand layouts are chosen for whole-cache-line loads (the texture/L1 path
+// bounds this kernel otherwise):
+//   * A comes in the fragment-major tiled layout (launch.hpp): one 16-byte
+//     load per lane fetches a complete 16 x 32 MFMA fragment, 1 KB over 8
+//     full cache lines.  The buffer descriptor's base moves along k in
+//     scalar registers and its record count ends at the last row tile, so
+//     tiles past the end read as zeros.
+//   * B: a producer thread loads word t&15 of rows 2(t>>4), +1 (a wave's load
+//     covers four rows of 64 contiguous bytes) and writes its 8 columns x 2
+//     rows into the LDS tile [column][k].  fp16: a byte permute and an OR
+//     with 0x6400 make 1024+q exactly, then one packed add of -(1024+z) and
+//     one packed multiply by s give (q-z)*s rounded once, two weights per
 //     instruction.  bf16 (no packed bf16 arithmetic): byte-to-float converts,
 //     an fma q*s + (-z*s) that is exact in fp32, and a paired round to bf16.
-//     Zero points and scales are decoded once per group.  Waves read B
-//     fragments as two 8-byte LDS loads; the column stride of 36 halves keeps
-//     those reads free of bank conflicts.
+//     Within each column the four 8-row blocks of k are XOR-permuted by
+//     (column/16)&3, which spreads the 4-byte stores over all banks and
+//     leaves each fragment read (8 consecutive k, two 8-byte loads)
+//     contiguous.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace paro {
 
 constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
 constexpr int kStepsPerGroup = kG / kBK;
 constexpr int kBStride = kBK + 4;  // halves per LDS column (72 bytes)
+constexpr int kTiles = 4;           // LDS ring of expanded weight tiles
 // Buffer descriptor word 3 for raw (untyped) buffers on the gfx9 family.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// c += A * B on one 16x16 tile (v_mfma_f32_16x16x32_{f16,bf16}), with c tied
+// to one AGPR quadruple.  Written as asm because the builtin lets the
+// register allocator pick a destination other than c, and it then shuffles
+// accumulators between loop iterations with v_accvgpr moves that each wait
+// for the MFMA just issued.  The compiler does not see these as MFMAs, so
+// the wait states before the accumulators are read back are inserted by hand
+// (mfma_drain); operands come straight from buffer and LDS loads, which need
+// none.
 template <int DT>
-__device__ __forceinline__ f32x4 mfma_tile(u32x4 a, u32x4 b, f32x4 c) {
+__device__ __forceinline__ void mfma_acc(const u32x4 &a, const u32x4 &b, f32x4 &c) {
   if constexpr (DT == kF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
-                                                  0, 0, 0);
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   c, 0, 0, 0);
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 64 wait states: more than any MFMA needs before a VALU reads its result.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferWord3);
 }
+
+// Physical k-pair index of k-pair rp (k = 2rp, 2rp+1) in column col: the
+// four 8-row blocks are XOR-permuted by (col/16)&3.
+__device__ __forceinline__ int swz_pair(int col, int rp) { return rp ^ (4 * ((col >> 4) & 3)); }
 
 // Per-group constants of one expansion thread, for the 8 nibble slots of its
 // word (slot s = column 8w + awq_col(s)).  fp16: packed pairs -(1024+z) and
@@ -85,7 +116,7 @@ struct GroupConsts<kBF16> {
 };
 
 // Dequantize one packed word of rows 2rp (ra) and 2rp+1 (rb) into the LDS
-// tile: slot s goes to column 8w + awq_col(s), k = 2rp, 2rp+1 as one u32.
+// tile: slot s goes to column 8w + awq_col(s), k-pair rp (swizzled) as one u32.
 template <int DT>
 __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, const GroupConsts<DT> &gc,
                                                    uint16_t *bl, int w, int rp) {
@@ -106,9 +137,9 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
     }
   } else {
     // bytes of lo_* hold slots 0,2,4,6 and of hi_* slots 1,3,5,7.  The empty
-    // asm hides the masks from the optimizer, which would otherwise merge
-    // them into per-nibble bit-field extracts instead of using the
-    // byte-to-float converts (v_cvt_f32_ubyte0..3).
+    // asm keeps the optimizer from merging the masks into per-nibble
+    // bit-field extracts instead of using the byte-to-float converts
+    // (v_cvt_f32_ubyte0..3).
     uint32_t lo_a = ra & 0x0f0f0f0fu, hi_a = (ra >> 4) & 0x0f0f0f0fu;
     uint32_t lo_b = rb & 0x0f0f0f0fu, hi_b = (rb >> 4) & 0x0f0f0f0fu;
     asm volatile("" : "+v"(lo_a), "+v"(hi_a), "+v"(lo_b), "+v"(hi_b));
@@ -121,120 +152,191 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
       v[s] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));  // one paired RNE
     }
   }
+  const int prp = swz_pair(8 * w, rp);  // the word's 8 columns share one 16-column block
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    *reinterpret_cast<uint32_t *>(bl + (8 * w + awq_col(s)) * kBStride + 2 * rp) = v[s];
+    *reinterpret_cast<uint32_t *>(bl + (8 * w + awq_col(s)) * kBStride + 2 * prp) = v[s];
 }
 
 template <int DT>
-__global__ void __launch_bounds__(256)
-prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xr) {
-  __shared__ __attribute__((aligned(16))) uint16_t bl[2][kBN * kBStride];
+__global__ void __launch_bounds__(kThreads)
+prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
+  __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
   const int lane = lane_id(), wave = wave_id();
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
   // XCD-local order: consecutive logical tiles (the N tiles of one M block)
-  // share an XCD and its L2.
+  // share an XCD and its L2.  The tile indices are uniform; readfirstlane
+  // moves them (computed with VALU division) to scalar registers so that the
+  // buffer descriptors derived from them stay scalar too.
   const int n_tiles = (int)((O + kBN - 1) / kBN), m_tiles = (int)((M + kBM - 1) / kBM);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
-  const int64_t n0 = (int64_t)(lwg % n_tiles) * kBN;
-  const int64_t mb = (int64_t)(lwg / n_tiles) * kBM;
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * kBN;
+  const int64_t mb = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * kBM;
   const int nsteps = (int)(I / kBK), ngroups = (int)(I / kG);
 
-  // expansion role: word dw of the tile's 16, rows 2*drp and 2*drp+1 of a step
-  const int drp = threadIdx.x & 15, dw = threadIdx.x >> 4;
-  const int64_t dword = n0 / 8 + dw;
-  const uint32_t dwc = (uint32_t)(dword < W ? dword : W - 1);  // tail tile: any in-bounds word
-  const uint32_t w_off = (uint32_t)((2 * drp) * W + dwc) * 4u;
-  const uint32_t w_step_bytes = (uint32_t)(kBK * W * 4);
+  // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
+  // the (16-row padded) tiled buffer; later ones read as zeros.
+  const int64_t rtiles = (M + 15) / 16 - mb / 16;
+  const int tiles = (int)(rtiles < kBM / 16 ? rtiles : kBM / 16);
+  const uint32_t tile_bytes = (uint32_t)nsteps * 1024u;  // one row tile over all of k
+  const uint32_t a_bytes = (uint32_t)tiles * tile_bytes;
+  const char *a_base = reinterpret_cast<const char *>(xt + (mb / 16) * (I / 32) * 512);
+  auto a_rsrc = [&](int step) {
+    const int st = step < nsteps ? step : nsteps - 1;  // past the end: any in-bounds step, unused
+    const uint32_t kb = (uint32_t)st * 1024u;
+    return raw_rsrc(a_base + kb, a_bytes - kb);
+  };
 
-  // fragment role: row fr of a row tile, k block fk
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  // A rows of this workgroup: [mb, mb + rows); the descriptor covers exactly
-  // those rows, so fragment rows at or past `rows` load zeros.
-  const int64_t rows = (M - mb) < kBM ? (M - mb) : kBM;
-  const uint32_t a_bytes = (uint32_t)(rows * I * 2);
+  if (wave >= 4) {
+    // ------------------------------ producer ------------------------------
+    const int tp = threadIdx.x - 256;
+    const int dw = tp & 15, drp = tp >> 4;  // word dw of the tile's 16, rows 2drp, 2drp+1 of a step
+    const int64_t dword = n0 / 8 + dw;
+    const uint32_t dwc = (uint32_t)(dword < W ? dword : W - 1);  // tail tile: any in-bounds word
+    const uint32_t w_off = (uint32_t)((2 * drp) * W + dwc) * 4u;
+    const uint32_t w_step_bytes = (uint32_t)(kBK * W * 4);
+
+    struct Words {
+      uint32_t ra, rb;
+    };
+    auto load_words = [&](int step, Words &wd) {
+      const int st = step < nsteps ? step : nsteps - 1;
+      const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.qweight + (int64_t)st * kBK * W, w_step_bytes);
+      wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
+      wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
+    };
+    struct GroupRaw {
+      u32x4 sw;
+      uint32_t zw;
+    };
+    auto load_group = [&](int g, GroupRaw &gr) {
+      const int gg = g < ngroups ? g : ngroups - 1;
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.scales + (int64_t)gg * O, (uint32_t)(O * 2));
+      gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
+      const __amdgpu_buffer_rsrc_t rz = raw_rsrc(a.qzeros + (int64_t)gg * W, (uint32_t)(W * 4));
+      gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
+    };
+
+    GroupConsts<DT> gc;
+    GroupRaw graw[2];
+    Words wd[4];
+    load_group(0, graw[0]);
+    load_group(1, graw[1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_words(k, wd[k]);
+    gc.decode(graw[0].sw, graw[0].zw);
+    expand_pair_to_lds<DT>(wd[0].ra, wd[0].rb, gc, bl[0], dw, drp);
+    expand_pair_to_lds<DT>(wd[1].ra, wd[1].rb, gc, bl[1], dw, drp);
+    load_words(4, wd[0]);
+    load_words(5, wd[1]);
+    __syncthreads();
+
+    // Step s: expand step s+2 (words slot (s+2)&3) into tile (s+2)&3, whose
+    // last readers finished two barriers ago; refill that slot with step
+    // s+6.
+    // Group g+1's scales/zeros (fetched during group g-1) are decoded at step
+    // 4g+2, just before the expansion of step 4g+4; group g+2's are fetched
+    // at step 4g.  Past the end everything runs on clamped, in-bounds
+    // addresses into tiles no consumer reads.
+    auto pstep = [&](int step, int ph, const GroupRaw &gnext) {
+      if (ph == 2) gc.decode(gnext.sw, gnext.zw);
+      Words &w = wd[(step + 2) & 3];
+      expand_pair_to_lds<DT>(w.ra, w.rb, gc, bl[(step + 2) & 3], dw, drp);
+      load_words(step + 6, w);
+      __syncthreads();
+    };
+    for (int g = 0; g < ngroups; g += 2) {
+      // two groups per iteration: every ring slot index is a constant
+      const int s0 = g * kStepsPerGroup;
+      load_group(g + 2, graw[0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pstep(s0 + k, k, graw[1]);
+      if (g + 1 < ngroups) {
+        load_group(g + 3, graw[1]);
+#pragma unroll
+        for (int k = 4; k < 8; ++k) pstep(s0 + k, k - 4, graw[0]);
+      }
+    }
+    return;
+  }
+
+  // ------------------------------ consumer ------------------------------
+  const int fr = lane & 15, fk = (lane >> 4) * 8;  // lane row / k block of each 16 x 32 fragment
   uint32_t a_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (uint32_t)(((wave * 64 + i * 16 + fr) * I + fk) * 2);
-  const char *a_base = reinterpret_cast<const char *>(xr + mb * I);
+  for (int i = 0; i < 4; ++i) a_off[i] = (uint32_t)(wave * 4 + i) * tile_bytes + (uint32_t)lane * 16u;
+  auto load_a = [&](int step, u32x4 af[4]) {
+    const __amdgpu_buffer_rsrc_t r = a_rsrc(step);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
+  };
+  // B fragments of column tiles j0..j0+3 of one k step: column 16j + fr, k
+  // block fk (physical block (fk/8) ^ (j&3)), two 8-byte LDS reads each.
+  // Only the four lane offsets for j&3 live in registers; the tile and j>=4
+  // are constant offsets folded into the LDS instructions.
+  uint32_t fcol[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) fcol[jj] = (uint32_t)((jj * 16 + fr) * kBStride + 8 * ((fk >> 3) ^ jj));
+  auto read_frags = [&](int tile, int j0, u32x4 bf[8]) {
+    const uint16_t *bt = &bl[0][0] + tile * (kBN * kBStride);
+#pragma unroll
+    for (int j = j0; j < j0 + 4; ++j) {
+      const uint16_t *col = bt + fcol[j & 3] + (j >> 2) * 64 * kBStride;
+      const u32x2 lo = *reinterpret_cast<const u32x2 *>(col);
+      const u32x2 hi = *reinterpret_cast<const u32x2 *>(col + 4);
+      bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
 
   f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto load_a = [&](int step, u32x4 af[4]) {
-    const int st = step < nsteps ? step : nsteps - 1;  // past the end: any in-bounds step, unused
-    const uint32_t kb = (uint32_t)st * (kBK * 2);
-    const __amdgpu_buffer_rsrc_t r = raw_rsrc(a_base + kb, a_bytes - kb);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
-  };
-  struct Words {
-    uint32_t ra, rb;
-  };
-  auto load_words = [&](int step, Words &wd) {
-    const int st = step < nsteps ? step : nsteps - 1;
-    const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.qweight + (int64_t)st * kBK * W, w_step_bytes);
-    wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
-    wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
-  };
-  struct GroupRaw {
-    u32x4 sw;
-    uint32_t zw;
-  };
-  auto load_group = [&](int g, GroupRaw &gr) {
-    const int gg = g < ngroups ? g : ngroups - 1;
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.scales + (int64_t)gg * O, (uint32_t)(O * 2));
-    gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
-    const __amdgpu_buffer_rsrc_t rz = raw_rsrc(a.qzeros + (int64_t)gg * W, (uint32_t)(W * 4));
-    gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
-  };
-
-  GroupConsts<DT> gc;
-  GroupRaw graw;
-  Words wd[2];
-  u32x4 ab[2][4];
-  load_group(0, graw);
-  load_words(0, wd[0]);
-  load_words(1, wd[1]);
+  u32x4 ab[2][4], bf[8];
   load_a(0, ab[0]);
   load_a(1, ab[1]);
-  gc.decode(graw.sw, graw.zw);
-  expand_pair_to_lds<DT>(wd[0].ra, wd[0].rb, gc, bl[0], dw, drp);
-  load_words(2, wd[0]);
   __syncthreads();
+  // When both waves of a SIMD are ready, issue the consumer's MFMAs first;
+  // the producer's VALU work fills the cycles in between.
+  __builtin_amdgcn_s_setprio(2);
+  read_frags(0, 0, bf);
+  read_frags(0, 4, bf);
 
-  // Step s: MFMAs on A[s&1] and LDS tile s&1; refill A[s&1] <- s+2; expand
-  // the words of step s+1 into the other tile; refill those words <- s+3;
-  // barrier.  The group's next scales/zeros are fetched at its first step
-  // and decoded just before the first expansion that needs them.
-  auto do_step = [&](int step, u32x4(&A)[4], Words &wnext, const uint16_t *bcur, uint16_t *bnext, bool last_of_group) {
+  // Step s: MFMAs of column tiles 0..3 on A slot s&1; refill fragments 0..3
+  // with those of step s+1 (tile (s+1)&3, expanded during step s-1) while
+  // tiles 4..7 compute; refill fragments 4..7, which arrive during the next
+  // step's first 16 MFMAs; refill the A slot with step s+2; barrier.  The
+  // scheduling barriers keep each refill after the MFMAs that read the old
+  // fragments (an MFMA reads its sources when issued).
+  auto cstep = [&](int step, u32x4(&A)[4]) {
+    const int next = (step + 1) & 3;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(bcur + (j * 16 + fr) * kBStride + fk);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(bcur + (j * 16 + fr) * kBStride + fk + 4);
-      const u32x4 bfrag = {lo[0], lo[1], hi[0], hi[1]};
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_tile<DT>(A[i], bfrag, acc[i][j]);
-    }
+      for (int i = 0; i < 4; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(next, 0, bf);
+#pragma unroll
+    for (int j = 4; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(next, 4, bf);
     load_a(step + 2, A);
-    if (step + 1 < nsteps) {
-      if (last_of_group) gc.decode(graw.sw, graw.zw);
-      expand_pair_to_lds<DT>(wnext.ra, wnext.rb, gc, bnext, dw, drp);
-    }
-    load_words(step + 3, wnext);
-    __syncthreads();
+    // Barrier without waiting for this wave's own LDS reads: the tile they
+    // read is rewritten only three barriers later.  The memory clobber keeps
+    // the compiler from moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
   };
-  for (int g = 0; g < ngroups; ++g) {
-    const int s0 = g * kStepsPerGroup;
-    load_group(g + 1, graw);
-    do_step(s0 + 0, ab[0], wd[1], bl[0], bl[1], false);
-    do_step(s0 + 1, ab[1], wd[0], bl[1], bl[0], false);
-    do_step(s0 + 2, ab[0], wd[1], bl[0], bl[1], false);
-    do_step(s0 + 3, ab[1], wd[0], bl[1], bl[0], true);
+  // (unrolled by two only: the A slots need constant indices, nothing else
+  // does, and a longer unroll makes the register allocator rotate buffers)
+  for (int step = 0; step < nsteps; step += 2) {
+    cstep(step, ab[0]);
+    cstep(step + 1, ab[1]);
   }
+  __builtin_amdgcn_s_setprio(0);
+  mfma_drain();
 
   // epilogue: bias in fp32, one rounding to the output dtype
   const int64_t m0 = mb + wave * 64;
@@ -258,13 +360,12 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xr) {
   }
 }
 
-hipError_t launch_prefill_gemm(const LinearArgs &a, const void *xr, hipStream_t st) {
+hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
   dim3 grid((unsigned)(((a.O + kBN - 1) / kBN) * ((a.tokens + kBM - 1) / kBM)));
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(xr);
   if (a.x_dt == kF16)
-    hipLaunchKernelGGL((prefill_gemm_kernel<kF16>), grid, dim3(256), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kF16>), grid, dim3(kThreads), 0, st, a, x);
   else
-    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16>), grid, dim3(256), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16>), grid, dim3(kThreads), 0, st, a, x);
   return hipGetLastError();
 }
 

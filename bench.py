@@ -35,6 +35,7 @@ METRIC = "ParoQuant linear: decode weight GB/s, prefill TFLOP/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, published
 MALL_ROTATION_BYTES = 512 << 20
+MAX_BUFFER_SETS = 256
 PATH_NAMES = {1: "decode_fused", 2: "decode_split", 3: "prefill"}
 
 
@@ -49,27 +50,35 @@ def layer_bytes(I, O, krot, G=128, bias=True):
     return weight, rot
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources: counter readings are only valid for them."""
+# Sources of the dominant kernel of each path (counter readings are valid
+# only for the code they were taken on).
+KERNEL_FILES = {1: ("decode.hip", "common.hpp"), 2: ("decode.hip", "common.hpp"),
+                3: ("prefill.hip", "common.hpp")}
+
+
+def kernel_source_hash(path):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rotation_int4_weight_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in KERNEL_FILES[path]:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(workload, kernel_hash):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings (scaled by the readings of a
+    plain copy of known size), or None when they were taken on other code."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    rec = data.get(str(workload))
+    rec = data.get("workloads", {}).get(str(workload))
     if not rec or rec.get("kernel_sources") != kernel_hash:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    cal = data["calibration"]
+    return round((rec["fetch_kib"] * cal["fetch_factor"] + rec["write_kib"] * cal["write_factor"]) * 1024)
 
 
 def main():
@@ -82,6 +91,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark: copy BYTES between two device buffers --steps times "
+                         "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -93,6 +105,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calib_copy:
+        src = torch.ones(args.calib_copy // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": src.numel() * 4, "dispatches": args.steps}), flush=True)
+        return
 
     import rotation_int4_weight_amd as paro
     import synth
@@ -113,7 +134,7 @@ def main():
         w_b, r_b = layer_bytes(I, O, host.krot)
         per_set += w_b + r_b + M * I * 2
         layers.append((lname, I, O, host, x))
-    nsets = max(1, -(-MALL_ROTATION_BYTES // per_set))
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // per_set)))
     log(f"workload {args.workload} ({spec['name']}): {len(layers)} layer(s), {nsets} buffer sets "
         f"x {per_set / 1e6:.1f} MB")
     sets = []  # sets[s][l] = (DeviceLayer, x)
@@ -159,8 +180,9 @@ def main():
         value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
 
     # ---- dominant kernel, timed live on its own stream ----
-    # decode_fused: the step is that one kernel.  split / prefill: the
-    # contraction kernel, run alone over pre-rotated activations.
+    # decode_fused: the step is that one kernel.  decode_split: the GEMV run
+    # alone over pre-rotated activations.  prefill: the GEMM run alone over
+    # X_r already in its tiled layout.
     kern = None
     if not args.no_kernel_timing:
         n_launch = max(args.steps, 20)
@@ -168,7 +190,7 @@ def main():
             launch = step
             per_launch_bytes, per_launch_flops = alg_bytes, flops
             launches_per_call = len(layers)
-        else:
+        elif path == 2:
             xrs = []
             for row in sets:
                 xr_row = []
@@ -182,6 +204,22 @@ def main():
                 row = sets[i % nsets]
                 for l, (D, _) in enumerate(row):
                     paro.paro_w4a16_linear_prerotated(D, xrs[i % nsets][l], ys[l], ws, stream=stream, path=path)
+            per_launch_bytes, per_launch_flops = alg_bytes, flops
+            launches_per_call = len(layers)
+        else:  # prefill: the GEMM kernel alone, over X_r already in its tiled layout
+            xts = []
+            for row in sets:
+                xt_row = []
+                for D, xd in row:
+                    xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device=dev)
+                    paro.paro_scale_rotate_tiled(D, xd, xt, stream=stream)
+                    xt_row.append(xt)
+                xts.append(xt_row)
+
+            def launch(i):
+                row = sets[i % nsets]
+                for l, (D, _) in enumerate(row):
+                    paro.paro_w4a16_linear_tiled(D, xts[i % nsets][l], act, M, ys[l], stream=stream)
             per_launch_bytes, per_launch_flops = alg_bytes, flops
             launches_per_call = len(layers)
         for i in range(min(args.warmup, 20)):
@@ -199,7 +237,7 @@ def main():
                 "bytes_per_launch": per_launch_bytes / launches_per_call,
                 "flops_per_launch": per_launch_flops / launches_per_call}
 
-    khash = kernel_source_hash()
+    khash = kernel_source_hash(path)
     roofline = None
     if kern:
         if decode:

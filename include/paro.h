@@ -175,6 +175,36 @@ int paro_w4a16_linear_prerotated(const paro_w4_layer *layer, const void *x_r, pa
                                  int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
                                  size_t workspace_bytes, void *stream, paro_path path);
 
+/*
+ * Tiled X_r: the operand layout of the PREFILL contraction.  Rows are padded
+ * to a multiple of 16 (pad rows are zero) and every 16-row x 32-column block
+ * is 1 KB, contiguous, in the order the 64 lanes of one 16x16x32 MFMA hold
+ * an A operand.  Element (m, k), m < rows, k < I, is at element index
+ *     ((m/16) * (I/32) + k/32) * 512 + (((k%32)/8) * 16 + m%16) * 8 + k%8
+ * (2-byte elements of the activation dtype).  paro_tiled_bytes() gives the
+ * buffer size: ceil(tokens/16) * 16 * I * 2 bytes.
+ */
+size_t paro_tiled_bytes(const paro_w4_layer *layer, int64_t tokens);
+
+/*
+ * paro_scale_rotate with the result written in the tiled layout above
+ * (x_t, x dtype, 16-byte aligned, paro_tiled_bytes(layer, tokens) bytes;
+ * must not overlap x).  It is the first kernel of the PREFILL path.
+ */
+int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
+                            int64_t tokens, void *x_t, void *stream);
+
+/*
+ * The PREFILL contraction alone over X_r in the tiled layout (for example
+ * from paro_scale_rotate_tiled): y as in paro_w4a16_linear.  Needs no
+ * workspace; layer->pairs/theta/channel_scales are not used.  Together the
+ * two calls compute exactly what paro_w4a16_linear_path(..., PREFILL)
+ * computes, and a rotated x_t can be reused by several projections that
+ * share the same rotation.
+ */
+int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dtype x_dt,
+                            int64_t tokens, void *y, paro_dtype y_dt, void *stream);
+
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,
                                          paro_dtype x_dt, paro_path path);

@@ -20,6 +20,7 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+           "paro_tiled_bytes", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
            "paro_w4a16_linear_workspace_bytes",
            "paro_w4a16_linear_choose_path", "paro_validate_layer", "paro_last_error",
            "paro_abi_version")
@@ -58,6 +59,10 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear.argtypes = [P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_linear_path.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
     lib.paro_w4a16_linear_prerotated.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
+    lib.paro_tiled_bytes.argtypes = [P, I64]
+    lib.paro_tiled_bytes.restype = SZ
+    lib.paro_scale_rotate_tiled.argtypes = [P, P, I32, I64, P, P]
+    lib.paro_w4a16_linear_tiled.argtypes = [P, P, I32, I64, P, I32, P]
     lib.paro_w4a16_linear_workspace_bytes.argtypes = [P, I64, I32, I32]
     lib.paro_w4a16_linear_workspace_bytes.restype = SZ
     lib.paro_w4a16_linear_choose_path.argtypes = [P, I64]
@@ -67,6 +72,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+                 "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
         getattr(lib, name).restype = I32
@@ -199,3 +205,20 @@ def paro_w4a16_linear_prerotated(layer: DeviceLayer, x_r, y, workspace=None, str
     _check(load().paro_w4a16_linear_prerotated(layer.ref, _ptr(x_r), _dt(x_r), x_r.shape[0], _ptr(y), _dt(y),
                                                ws_ptr, ws_bytes, _stream_handle(stream), path),
            "paro_w4a16_linear_prerotated")
+
+
+def paro_tiled_bytes(layer: DeviceLayer, tokens: int) -> int:
+    """Bytes of an X_r buffer in the prefill GEMM's tiled layout."""
+    return int(load().paro_tiled_bytes(layer.ref, tokens))
+
+
+def paro_scale_rotate_tiled(layer: DeviceLayer, x, x_t, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16; x_t: device buffer of paro_tiled_bytes() bytes (any dtype view)."""
+    _check(load().paro_scale_rotate_tiled(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(x_t),
+                                          _stream_handle(stream)), "paro_scale_rotate_tiled")
+
+
+def paro_w4a16_linear_tiled(layer: DeviceLayer, x_t, x_dt: int, tokens: int, y, stream=None) -> None:
+    """The prefill contraction over X_r in the tiled layout; y: (tokens, O) x dtype or fp32."""
+    _check(load().paro_w4a16_linear_tiled(layer.ref, _ptr(x_t), x_dt, tokens, _ptr(y), _dt(y),
+                                          _stream_handle(stream)), "paro_w4a16_linear_tiled")

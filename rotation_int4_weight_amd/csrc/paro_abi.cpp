@@ -108,6 +108,27 @@ int hip_fail(hipError_t e, const char *what) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+paro::LinearArgs linear_args(const paro_w4_layer *L, int64_t tokens, const void *x, paro_dtype x_dt, void *y,
+                             paro_dtype y_dt) {
+  paro::LinearArgs a;
+  a.I = L->in_features;
+  a.O = L->out_features;
+  a.tokens = tokens;
+  a.krot = L->krot;
+  a.pairs = L->pairs;
+  a.theta = L->theta;
+  a.cs = L->channel_scales;
+  a.qweight = L->qweight;
+  a.qzeros = L->qzeros;
+  a.scales = L->scales;
+  a.bias = L->bias;
+  a.x = x;
+  a.x_dt = (int)x_dt;
+  a.y = y;
+  a.y_dt = (int)y_dt;
+  return a;
+}
+
 paro_path auto_path(int64_t tokens) {
   if (tokens <= 4) return PARO_PATH_DECODE_FUSED;
   if (tokens <= 16) return PARO_PATH_DECODE_SPLIT;
@@ -185,6 +206,54 @@ int paro_scale_rotate(const paro_w4_layer *L, const void *x, paro_dtype x_dt, in
   return ok();
 }
 
+size_t paro_tiled_bytes(const paro_w4_layer *L, int64_t tokens) {
+  if (!L || tokens <= 0 || L->in_features <= 0) return 0;
+  return (size_t)paro::tiled_rows(tokens) * (size_t)L->in_features * 2;
+}
+
+int paro_scale_rotate_tiled(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *x_t,
+                            void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (tokens == 0) return ok();
+  if (!x || !x_t) return fail(PARO_ERR_NULL, "x and x_t are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(x_t, 16)) return fail(PARO_ERR_ALIGN, "x and x_t must be 16-byte aligned");
+  const int64_t I = L->in_features;
+  const size_t xb = (size_t)tokens * I * 2, tb = paro_tiled_bytes(L, tokens);
+  const char *xs = (const char *)x, *ts = (const char *)x_t;
+  if (xs < ts + tb && ts < xs + xb) return fail(PARO_ERR_SHAPE, "x_t overlaps x");
+  hipError_t e = paro::launch_scale_rotate_tiled((const uint16_t *)x, (int)x_dt, (uint16_t *)x_t, tokens, I,
+                                                 L->pairs, L->theta, L->channel_scales, L->krot, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scale_rotate_tiled launch");
+  return ok();
+}
+
+int paro_w4a16_linear_tiled(const paro_w4_layer *L, const void *x_t, paro_dtype x_dt, int64_t tokens, void *y,
+                            paro_dtype y_dt, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
+  if (tokens == 0) return ok();
+  if (!x_t || !y) return fail(PARO_ERR_NULL, "x_t and y are required");
+  rc = check_weight_tensors(L);
+  if (rc) return rc;
+  if (!aligned(x_t, 16) || !aligned(y, 16)) return fail(PARO_ERR_ALIGN, "x_t and y must be 16-byte aligned");
+  const int64_t O = L->out_features;
+  const size_t tb = paro_tiled_bytes(L, tokens), yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+  const char *ts = (const char *)x_t, *ys = (const char *)y;
+  if (ts < ys + yb && ys < ts + tb) return fail(PARO_ERR_SHAPE, "y overlaps x_t");
+  paro::LinearArgs a = linear_args(L, tokens, x_t, x_dt, y, y_dt);
+  hipError_t e = paro::launch_prefill_gemm(a, (const uint16_t *)x_t, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
+  return ok();
+}
+
 int paro_w4_unpack_dequant(const paro_w4_layer *L, uint8_t *q_out, uint8_t *z_out, void *w_out, paro_dtype w_dt,
                            void *stream) {
   int rc = check_gpu_shape(L);
@@ -256,22 +325,7 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
 
-  paro::LinearArgs a;
-  a.I = I;
-  a.O = O;
-  a.tokens = tokens;
-  a.krot = L->krot;
-  a.pairs = L->pairs;
-  a.theta = L->theta;
-  a.cs = L->channel_scales;
-  a.qweight = L->qweight;
-  a.qzeros = L->qzeros;
-  a.scales = L->scales;
-  a.bias = L->bias;
-  a.x = x;
-  a.x_dt = (int)x_dt;
-  a.y = y;
-  a.y_dt = (int)y_dt;
+  paro::LinearArgs a = linear_args(L, tokens, x, x_dt, y, y_dt);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
 

@@ -178,3 +178,29 @@ def test_prerotated_argument_checks():
     assert call(2, tokens=17) == 5
     assert call(3, ws=0) == 7
     assert call(0, tokens=0) == 0
+
+
+@needs_no_gpu
+def test_tiled_entry_point_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(I=256, O=64)
+    assert lib.paro_tiled_bytes(ctypes.byref(L), 1) == 16 * 256 * 2
+    assert lib.paro_tiled_bytes(ctypes.byref(L), 33) == 48 * 256 * 2
+    assert lib.paro_tiled_bytes(ctypes.byref(L), 0) == 0
+    rot = lambda x=FAKE, dt=0, tokens=4, xt=FAKE * 2, L=L: lib.paro_scale_rotate_tiled(
+        ctypes.byref(L), x, dt, tokens, xt, None)
+    assert rot(dt=2) == 3                      # fp32 activations not accepted
+    assert rot(x=0) == 1
+    assert rot(xt=FAKE * 2 + 8) == 4
+    assert rot(xt=FAKE + 64) == 2              # overlaps x
+    assert rot(tokens=0, x=0, xt=0) == 0
+    assert rot(L=fake_layer(pairs=0)) == 1
+    lin = lambda xt=FAKE, dt=0, tokens=4, y=FAKE * 4, ydt=0, L=L: lib.paro_w4a16_linear_tiled(
+        ctypes.byref(L), xt, dt, tokens, y, ydt, None)
+    assert lin(ydt=1) == 3                     # y must be x dtype or fp32
+    assert lin(y=0) == 1
+    assert lin(y=FAKE + 64) == 2               # overlaps the tiled x
+    assert lin(L=fake_layer(qweight=0)) == 1
+    assert lin(L=fake_layer(G=64)) == 5
+    assert lin(tokens=0, xt=0, y=0) == 0
+    assert lin(L=fake_layer(pairs=0, theta=0, channel_scales=0)) != 1  # rotation tensors unused

@@ -294,6 +294,64 @@ def test_prerotated_projection_matches_linear(cfg, path):
     assert np.array_equal(to_host_bits(y).view(np.uint32), full.view(np.uint32))
 
 
+def untile(bits, M, I):
+    """Tiled X_r (layout of include/paro.h) -> row-major [rows][I], rows padded to 16.
+
+    Element (m, k) sits at ((m/16)*(I/32) + k/32)*512 + (((k%32)/8)*16 + m%16)*8 + k%8,
+    i.e. the flat buffer is an array [m/16][k/32][(k%32)/8][m%16][k%8].
+    """
+    rows = (M + 15) // 16 * 16
+    a = np.asarray(bits).reshape(rows // 16, I // 32, 4, 16, 8)
+    return a.transpose(0, 3, 1, 2, 4).reshape(rows, I)
+
+
+@pytest.mark.parametrize("I,M,krot,dt", [(128, 1, 1, synth.F16), (4096, 17, 8, synth.F16),
+                                         (384, 65, 9, synth.BF16), (1024, 48, 8, synth.BF16)])
+def test_scale_rotate_tiled(I, M, krot, dt):
+    """The tiled rotation holds the same bits as paro_scale_rotate, zero pad rows,
+    and meets the oracle's rotated-activation gate."""
+    L = synth.make_layer(205, krot, I, 8, krot=krot)
+    x = synth.make_x(205, krot, M, I, dt)
+    say(f"scale_rotate_tiled I={I} M={M} krot={krot} dt={dt}")
+    D = paro.DeviceLayer(L)
+    xd = x_to_device(x, dt)
+    nbytes = paro.paro_tiled_bytes(D, M)
+    assert nbytes == (M + 15) // 16 * 16 * I * 2
+    xt = torch.full((nbytes // 2,), -1, dtype=torch.int16, device="cuda")  # poison
+    paro.paro_scale_rotate_tiled(D, xd, xt)
+    rm = torch.empty_like(xd)
+    paro.paro_scale_rotate(D, xd, rm)
+    torch.cuda.synchronize()
+    t = untile(xt.cpu().numpy().view(np.uint16), M, I)
+    assert np.array_equal(t[:M], to_host_bits(rm))
+    assert not t[M:].any()
+    xr_ref = ref.scale_rotate(L, np.ascontiguousarray(x), dt)
+    err = np.abs(bits_to_f64(t[:M], dt) - xr_ref).max(axis=1) / np.abs(xr_ref).max(axis=1)
+    assert float(err.max()) <= ROT_TOL + U[dt]
+
+
+@pytest.mark.parametrize("cfg,extra", [(0, None), (3, None), ("edge", (1024, 200, 40, synth.F16))])
+def test_linear_tiled_matches_prefill_path(cfg, extra):
+    """paro_scale_rotate_tiled + paro_w4a16_linear_tiled == the PREFILL path, bit for bit."""
+    if cfg == "edge":
+        I, O, M, dt = extra
+        L = synth.make_layer(206, 0, I, O)
+        x = synth.make_x(206, 0, M, I, dt)
+    else:
+        _, L, x, dt = workload(cfg)
+    M, I, O = x.shape[0], L.in_features, L.out_features
+    say(f"linear_tiled cfg={cfg} I={I} O={O} M={M}")
+    D = paro.DeviceLayer(L)
+    xd = x_to_device(x, dt)
+    full = to_host_bits(run_linear(D, xd, O, synth.F32, PATHS["prefill"]))
+    xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_scale_rotate_tiled(D, xd, xt)
+    y = torch.empty((M, O), dtype=torch.float32, device="cuda")
+    paro.paro_w4a16_linear_tiled(D, xt, dt, M, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(y).view(np.uint32), full.view(np.uint32))
+
+
 @pytest.mark.parametrize("I,O,M,path", [(4096, 4096, 1, "fused"), (4096, 2048, 16, "split"),
                                         (2048, 1024, 3, "fused")])
 def test_split_k_handoff_alternating_inputs(I, O, M, path):

@@ -42,7 +42,8 @@
  *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
  *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^22,
  *     O a multiple of 8 and <= 2^21, tokens <= 2^21; x, y, x_r, w_out,
- *     qweight and scales 16-byte aligned.  Other values give
+ *     qweight and scales 16-byte aligned, bias 8-byte aligned, qzeros,
+ *     pairs, theta and channel_scales 4-byte aligned.  Other values give
  *     PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.
  *   - Pair contents are NOT read on the host by the GPU entry points (they
  *     are device memory); kernels mask every pair index into its group, so

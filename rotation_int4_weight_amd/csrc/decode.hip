@@ -36,14 +36,16 @@
 // at the same time and their row segments merge in its L2 into long DRAM
 // bursts.
 //
-// Reduction.  The NW waves' tiles are summed in LDS in wave order.  With
-// one K split the workgroup adds the bias and stores y.  Otherwise it stores
-// its fp32 partial with device-scope atomic stores (coherent across the XCDs'
-// L2 caches without whole-cache write-backs), waits for them, and bumps a
+// Reduction.  The NW waves' tiles are summed in LDS in wave order, each
+// thread taking quads of 4 consecutive outputs.  With one K split the
+// workgroup adds the bias and stores y.  Otherwise it stores its fp32 partial
+// with 16-byte device-coherent stores (SC1: coherent across the XCDs' L2
+// caches without whole-cache write-backs), waits for them, and bumps a
 // device-scope counter; the last workgroup of the column tile to arrive
-// loads every split's partial (all loads in flight together), sums them in
-// split order, adds the bias, stores y and resets the counter.  The result is
-// independent of arrival order (bitwise deterministic).
+// loads every split's quads with 16-byte device-coherent loads, all in flight
+// together, sums them in split order, adds the bias, stores y and resets the
+// counter.  The result is independent of arrival order (bitwise
+// deterministic).
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -53,6 +55,9 @@ namespace paro {
 
 constexpr int kDecodeRS = kG + 4;  // fused-rotation LDS row stride (floats)
 constexpr int kCounterStride = 32; // uint32 per split-K counter: one 128-byte line each
+// Cache policy of the raw buffer loads/stores that exchange split-K partials:
+// SC1, the device-scope coherent form (the one relaxed device-scope atomics use).
+constexpr int kDeviceCoherent = 16;
 
 template <int DT>
 struct MfmaTypes;
@@ -122,14 +127,6 @@ __device__ __forceinline__ constexpr float slot_mult(int s) {
   return (DT == kF16 && (s & 1)) ? 16.0f : 1.0f;
 }
 
-// Output of one element (bias already added in fp32; one rounding into the
-// output dtype).
-__device__ __forceinline__ void store_out(const LinearArgs &a, int64_t row, int64_t n, float out) {
-  if (a.y_dt == kF32) reinterpret_cast<float *>(a.y)[row * a.O + n] = out;
-  else if (a.y_dt == kF16) reinterpret_cast<uint16_t *>(a.y)[row * a.O + n] = f32_to_f16_bits(out);
-  else reinterpret_cast<uint16_t *>(a.y)[row * a.O + n] = f32_to_bf16_bits(out);
-}
-
 // Load WPL consecutive packed words of one row (one vector load when WPL > 1).
 template <int WPL>
 __device__ __forceinline__ void load_words(const int32_t *__restrict__ p, uint32_t out[WPL]) {
@@ -157,7 +154,8 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   constexpr int PD = KSW < (NW >= 16 ? 2 : 4) ? KSW : (NW >= 16 ? 2 : 4);
   constexpr int NTH = 64 * NW;
   constexpr int NTILE = 128 * WPL;
-  constexpr int EPT = (MT * NTILE + NTH - 1) / NTH;  // output elements per thread
+  constexpr int QUADS = MT * NTILE / 4;                 // 4-column output quads of the tile
+  constexpr int QPT = (QUADS + NTH - 1) / NTH;          // quads per thread
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int s_last;
   const int lane = lane_id(), wave = wave_id();
@@ -172,15 +170,24 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   const int nk = (int)((ks0 >= nks) ? 0 : ((nks - ks0) < KSW ? (nks - ks0) : KSW));
   const uint16_t *__restrict__ x = reinterpret_cast<const uint16_t *>(a.x);
   const int64_t n0 = (int64_t)tile * NTILE;
-  const int nel = M * NTILE;
 
   // ---- small early loads: this thread's bias values ----
-  float bias_v[EPT];
+  // Quad q holds outputs 4q..4q+3 of the tile ([row][col], NTILE columns per
+  // row); a quad is entirely inside or entirely past O (O % 8 == 0).
+  // Branch-free: every load reads a valid address (a stand-in tensor when
+  // there is no bias, a clamped column past O) and the value is selected
+  // afterwards.  A conditional load would make the compiler wait for it at
+  // the join, i.e. one full memory round trip before the weight stream.
+  float bias_v[QPT][4];
+  const uint16_t *bias_src = a.bias ? a.bias : a.scales;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + j * NTH;
-    const int64_t n = n0 + (e % NTILE);
-    bias_v[j] = (a.bias && e < nel && n < O) ? f16_bits_to_f32(a.bias[n]) : 0.0f;
+  for (int j = 0; j < QPT; ++j) {
+    const int q = threadIdx.x + j * NTH;
+    const int64_t n = n0 + (4 * q) % NTILE;
+    const bool use = a.bias && q < M * NTILE / 4 && n < O;
+    const u32x2 b = *reinterpret_cast<const u32x2 *>(bias_src + (n < O ? n : O - 4));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bias_v[j][c] = use ? f16_bits_to_f32((b[c >> 1] >> (16 * (c & 1))) & 0xffffu) : 0.0f;
   }
 
   // Columns past O (last tile only) read an in-bounds word and are zeroed;
@@ -238,7 +245,8 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
       const int64_t g = g0 < I / kG ? g0 : I / kG - 1;
 #pragma unroll
       for (int w = 0; w < WPL; ++w) {
-        sv[gi][w] = wok ? *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * (wcl + w)) : u32x4{0u, 0u, 0u, 0u};
+        sv[gi][w] = *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * (wcl + w));  // wcl is in bounds
+        if (!wok) sv[gi][w] = u32x4{0u, 0u, 0u, 0u};
         zv[gi][w] = (uint32_t)a.qzeros[g * W + wcl + w];
       }
     }
@@ -339,41 +347,63 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   }
   __syncthreads();
 
-  float v[EPT];
+  // quads of this thread: sum over the waves in wave order
+  const int nq = M * NTILE / 4;  // quads holding real rows
+  f32x4 v[QPT];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + j * NTH;
-    v[j] = 0.0f;
-    if (e < nel) {
-      v[j] = red[e];  // wave 0: [row][col] = e
+  for (int j = 0; j < QPT; ++j) {
+    const int q = threadIdx.x + j * NTH;
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (q < nq) {
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v[j] += red[w * MT * NTILE + e];
+      for (int w = 0; w < NW; ++w) v[j] += *reinterpret_cast<const f32x4 *>(red + w * MT * NTILE + 4 * q);
     }
   }
-  auto store_elems = [&](const float *val) {
+  auto quad_out = [&](int j, int &row, int64_t &n) {
+    const int q = threadIdx.x + j * NTH;
+    row = (4 * q) / NTILE;
+    n = n0 + (4 * q - row * NTILE);
+    return q < nq && n < O;
+  };
+  auto store_quads = [&](const f32x4 *val) {
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int e = threadIdx.x + j * NTH;
-      const int row = e / NTILE;
-      const int64_t n = n0 + (e - row * NTILE);
-      if (e < nel && n < O) store_out(a, row, n, val[j] + bias_v[j]);
+    for (int j = 0; j < QPT; ++j) {
+      int row;
+      int64_t n;
+      if (quad_out(j, row, n)) {
+        const float o0 = val[j][0] + bias_v[j][0], o1 = val[j][1] + bias_v[j][1];
+        const float o2 = val[j][2] + bias_v[j][2], o3 = val[j][3] + bias_v[j][3];
+        if (a.y_dt == kF32) {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * O + n) = f32x4{o0, o1, o2, o3};
+        } else {
+          u32x2 h;
+          if (a.y_dt == kF16) h = u32x2{pack2<kF16>(o0, o1), pack2<kF16>(o2, o3)};
+          else h = u32x2{pack2<kBF16>(o0, o1), pack2<kBF16>(o2, o3)};
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.y) + row * O + n) = h;
+        }
+      }
     }
   };
   if (splits == 1) {
-    store_elems(v);
+    store_quads(v);
     return;
   }
 
   // ---- split-K handoff (see the header) ----
-  const int64_t sstride = (int64_t)M * O;
+  // partial: [tile][split][M][NTILE] fp32.  One raw buffer per tile: its
+  // splits * M * NTILE * 4 bytes (at most 2^14 * 16 * 512 * 4 = 2^29) keep
+  // every offset in 32 bits.
+  const uint32_t sstride = (uint32_t)(M * NTILE);  // floats per split
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      partial + (int64_t)tile * splits * sstride, (short)0, (int)((uint32_t)splits * sstride * 4u), 0x00020000);
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + j * NTH;
-    const int row = e / NTILE;
-    const int64_t n = n0 + (e - row * NTILE);
-    if (e < nel && n < O)
-      __hip_atomic_store(&partial[split * sstride + (int64_t)row * O + n], v[j], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+  for (int j = 0; j < QPT; ++j) {
+    int row;
+    int64_t n;
+    if (quad_out(j, row, n))
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[j]), prs,
+                                             ((uint32_t)split * sstride + 4u * (uint32_t)(threadIdx.x + j * NTH)) * 4u,
+                                             0, kDeviceCoherent);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
@@ -384,33 +414,33 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   }
   __syncthreads();
   if (!s_last) return;
-  // Gather every split's partial, all loads of a batch in flight together,
+  // Gather every split's quads, all loads of a batch in flight together (the
+  // addresses of splits past the last are clamped and their values dropped),
   // summing in split order.
-  constexpr int SB = EPT >= 32 ? 1 : 32 / EPT;  // splits per batch
-  float sum[EPT];
+  constexpr int SB = QPT >= 16 ? 1 : 16 / QPT;  // splits per batch
+  f32x4 sum[QPT];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) sum[j] = 0.0f;
+  for (int j = 0; j < QPT; ++j) sum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < splits; sp += SB) {
-    float t[EPT][SB];
+    f32x4 t[QPT][SB];
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int e = threadIdx.x + j * NTH;
-      const int row = e / NTILE;
-      const int64_t n = n0 + (e - row * NTILE);
-      const bool ok = e < nel && n < O;
-      const float *pp = partial + (int64_t)row * O + (ok ? n : 0);
+    for (int j = 0; j < QPT; ++j) {
+      const uint32_t q = (uint32_t)(threadIdx.x + j * NTH);
+      const uint32_t off = 16u * (q < (uint32_t)nq ? q : 0u);
 #pragma unroll
-      for (int u = 0; u < SB; ++u)
-        t[j][u] = (ok && sp + u < splits)
-                      ? __hip_atomic_load(pp + (sp + u) * sstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : 0.0f;
+      for (int u = 0; u < SB; ++u) {
+        const uint32_t spc = (uint32_t)(sp + u < splits ? sp + u : splits - 1);
+        t[j][u] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off + spc * sstride * 4u, 0, kDeviceCoherent));
+      }
     }
 #pragma unroll
-    for (int j = 0; j < EPT; ++j)
+    for (int j = 0; j < QPT; ++j)
 #pragma unroll
-      for (int u = 0; u < SB; ++u) sum[j] += t[j][u];
+      for (int u = 0; u < SB; ++u)
+        if (sp + u < splits) sum[j] += t[j][u];
   }
-  store_elems(sum);
+  store_quads(sum);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -433,18 +463,21 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused) {
     p.nw = 8;
   } else {
     // Up to 16 rows: the partial sums cost splits * tokens * O * 8 bytes, so
-    // an eight-wave workgroup covers up to 2048 rows (eight k-steps per wave,
-    // folded once per group) of a 128-column tile.
-    p.wpl = 1;
+    // an eight-wave workgroup covers long K ranges (several k-steps per wave,
+    // folded once per group).  256-column tiles with four k-steps per wave
+    // measured fastest on 4096 -> 14336 at 16 tokens (one 128-byte segment
+    // per weight row and lane group, four splits).
+    p.wpl = (O % 16 == 0) ? 2 : 1;
     p.nw = 8;
-    p.ksw = 8;
+    p.ksw = p.wpl == 2 ? 4 : 8;
     while (p.ksw > 1 && (int64_t)p.nw * (p.ksw / 2) >= nks) p.ksw /= 2;
   }
-  const int fw = env_int("PARO_DECODE_WPL", 0);
+  // Tuning overrides, read once per process: PARO_DECODE_WPL / _KSW / _NW.
+  static const int fw = env_int("PARO_DECODE_WPL", 0);
+  static const int fk = env_int("PARO_DECODE_KSW", 0);
+  static const int fn = env_int("PARO_DECODE_NW", 0);
   if (fw == 1 || (fw == 2 && O % 16 == 0) || (fw == 4 && O % 32 == 0)) p.wpl = fw;
-  const int fk = env_int("PARO_DECODE_KSW", 0);
   if (fk == 1 || fk == 2 || fk == 4 || fk == 8) p.ksw = fk;
-  const int fn = env_int("PARO_DECODE_NW", 0);
   if (fn == 4 || fn == 8 || fn == 16) p.nw = fn;
   p.ntile = 128 * p.wpl;
   p.n_tiles = (int)((O + p.ntile - 1) / p.ntile);
@@ -453,8 +486,10 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused) {
 }
 
 size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O) {
+  (void)O;
   if (p.splits <= 1) return 0;
-  return (size_t)p.splits * (size_t)tokens * (size_t)O * 4;
+  // [tile][split][tokens][ntile] fp32
+  return (size_t)p.n_tiles * (size_t)p.splits * (size_t)tokens * (size_t)p.ntile * 4;
 }
 
 template <int DT, int WPL, int KSW, int NW, bool FUSED>
@@ -498,6 +533,7 @@ static hipError_t launch_decode_dt(const LinearArgs &a, const DecodePlan &p, con
   PARO_DECODE_CFG(1, 4, 8);
   PARO_DECODE_CFG(1, 2, 8);
   PARO_DECODE_CFG(2, 4, 8);
+  PARO_DECODE_CFG(2, 2, 8);
   PARO_DECODE_CFG(1, 4, 16);
   PARO_DECODE_CFG(1, 2, 16);
   PARO_DECODE_CFG(1, 1, 16);

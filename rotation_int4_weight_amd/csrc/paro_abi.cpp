@@ -88,8 +88,8 @@ int check_rotation_tensors(const paro_w4_layer *L) {
 int check_weight_tensors(const paro_w4_layer *L) {
   if (!L->qweight || !L->qzeros || !L->scales) return fail(PARO_ERR_NULL, "qweight, qzeros, scales are required");
   if (!aligned(L->qweight, 16) || !aligned(L->scales, 16) || !aligned(L->qzeros, 4) ||
-      (L->bias && !aligned(L->bias, 2)))
-    return fail(PARO_ERR_ALIGN, "qweight/scales must be 16-byte aligned, qzeros 4, bias 2");
+      (L->bias && !aligned(L->bias, 8)))
+    return fail(PARO_ERR_ALIGN, "qweight/scales must be 16-byte aligned, qzeros 4, bias 8");
   return PARO_OK;
 }
 

@@ -114,6 +114,7 @@ def lin(L, x=FAKE, xdt=0, tokens=4, y=FAKE * 2, ydt=0, ws=FAKE * 4, wsb=1 << 30,
     (dict(L=dict(pairs=0)), 1),
     (dict(L=dict(qweight=0)), 1),
     (dict(L=dict(qweight=FAKE + 4)), 4),
+    (dict(L=dict(bias=FAKE + 4)), 4),    # bias is read 8 bytes at a time
     (dict(x=0), 1),
     (dict(x=FAKE + 2), 4),
     (dict(xdt=2), 3),                    # fp32 activations not accepted

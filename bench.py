@@ -211,9 +211,12 @@ def main():
             for row in sets:
                 xt_row = []
                 for D, xd in row:
+                    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
+                    paro.paro_rotation_matrix(D, act, hl, stream=stream)
                     xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device=dev)
-                    paro.paro_scale_rotate_tiled(D, xd, xt, stream=stream)
+                    paro.paro_scale_rotate_tiled(D, hl, xd, xt, stream=stream)
                     xt_row.append(xt)
+                    del hl
                 xts.append(xt_row)
 
             def launch(i):

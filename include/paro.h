@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARO_ABI_VERSION 1
+#define PARO_ABI_VERSION 2
 
 typedef enum {
   PARO_F16 = 0,  /* IEEE binary16 */
@@ -188,12 +188,32 @@ int paro_w4a16_linear_prerotated(const paro_w4_layer *layer, const void *x_r, pa
 size_t paro_tiled_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /*
- * paro_scale_rotate with the result written in the tiled layout above
- * (x_t, x dtype, 16-byte aligned, paro_tiled_bytes(layer, tokens) bytes;
- * must not overlap x).  It is the first kernel of the PREFILL path.
+ * Dense form of the scaled rotation, per 128-channel group g ("ParoQuant"
+ * wiki, Concepts / Pairwise Givens rotations: the stages compose to one
+ * orthogonal map per group; Activation and weight transforms: D^-1 then R):
+ *   R'_g[i][j] = ((e_i . diag(cs_g)) . R_g)[j],   i, j < 128,
+ * i.e. the scaled unit rows pushed through the krot stages in fp32, stored
+ * as two matrices in x_dt, H = rne(R') and L = rne(R' - H), whose sum holds
+ * R' to about 2^-16 relative (BF16; 2^-22 for F16).
+ *   hl : paro_rotation_matrix_bytes(layer) = I * 512 bytes, 16-byte aligned,
+ *        caller-owned; layout [g][H, L][128 output channels in the order the
+ *        matrix cores consume them][128 input channels].  Its contents are
+ *        for paro_scale_rotate_tiled only.
+ * Uses layer->pairs, theta, channel_scales; depends on the layer and x_dt,
+ * not on the tokens, so one build serves every later call with that layer.
  */
-int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
-                            int64_t tokens, void *x_t, void *stream);
+size_t paro_rotation_matrix_bytes(const paro_w4_layer *layer);
+int paro_rotation_matrix(const paro_w4_layer *layer, paro_dtype x_dt, void *hl, void *stream);
+
+/*
+ * paro_scale_rotate with the result written in the tiled layout above, as
+ * x_t = rne(x . H + x . L) with fp32 accumulation on the matrix cores
+ * (hl from paro_rotation_matrix for this layer and x_dt; x_t: x dtype,
+ * 16-byte aligned, paro_tiled_bytes(layer, tokens) bytes; must not overlap
+ * x or hl).  The two calls are the rotation of the PREFILL path.
+ */
+int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *hl, const void *x,
+                            paro_dtype x_dt, int64_t tokens, void *x_t, void *stream);
 
 /*
  * The PREFILL contraction alone over X_r in the tiled layout (for example

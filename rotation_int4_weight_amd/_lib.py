@@ -20,7 +20,8 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-           "paro_tiled_bytes", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
+           "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
+           "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
            "paro_w4a16_linear_workspace_bytes",
            "paro_w4a16_linear_choose_path", "paro_validate_layer", "paro_last_error",
            "paro_abi_version")
@@ -61,7 +62,10 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear_prerotated.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
-    lib.paro_scale_rotate_tiled.argtypes = [P, P, I32, I64, P, P]
+    lib.paro_rotation_matrix_bytes.argtypes = [P]
+    lib.paro_rotation_matrix_bytes.restype = SZ
+    lib.paro_rotation_matrix.argtypes = [P, I32, P, P]
+    lib.paro_scale_rotate_tiled.argtypes = [P, P, P, I32, I64, P, P]
     lib.paro_w4a16_linear_tiled.argtypes = [P, P, I32, I64, P, I32, P]
     lib.paro_w4a16_linear_workspace_bytes.argtypes = [P, I64, I32, I32]
     lib.paro_w4a16_linear_workspace_bytes.restype = SZ
@@ -72,7 +76,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-                 "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
+                 "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
         getattr(lib, name).restype = I32
@@ -212,9 +216,21 @@ def paro_tiled_bytes(layer: DeviceLayer, tokens: int) -> int:
     return int(load().paro_tiled_bytes(layer.ref, tokens))
 
 
-def paro_scale_rotate_tiled(layer: DeviceLayer, x, x_t, stream=None) -> None:
-    """x: (tokens, I) fp16/bf16; x_t: device buffer of paro_tiled_bytes() bytes (any dtype view)."""
-    _check(load().paro_scale_rotate_tiled(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(x_t),
+def paro_rotation_matrix_bytes(layer: DeviceLayer) -> int:
+    """Bytes of the dense rotation (H and L) that paro_rotation_matrix writes."""
+    return int(load().paro_rotation_matrix_bytes(layer.ref))
+
+
+def paro_rotation_matrix(layer: DeviceLayer, x_dt: int, hl, stream=None) -> None:
+    """Build H + L = diag(cs) . R per group into hl (device buffer of paro_rotation_matrix_bytes())."""
+    _check(load().paro_rotation_matrix(layer.ref, x_dt, _ptr(hl), _stream_handle(stream)),
+           "paro_rotation_matrix")
+
+
+def paro_scale_rotate_tiled(layer: DeviceLayer, hl, x, x_t, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16; hl: from paro_rotation_matrix for x's dtype;
+    x_t: device buffer of paro_tiled_bytes() bytes (any dtype view)."""
+    _check(load().paro_scale_rotate_tiled(layer.ref, _ptr(hl), _ptr(x), _dt(x), x.shape[0], _ptr(x_t),
                                           _stream_handle(stream)), "paro_scale_rotate_tiled")
 
 

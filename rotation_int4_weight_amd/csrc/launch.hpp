@@ -61,12 +61,17 @@ hipError_t launch_decode(const LinearArgs &a, const DecodePlan &p, const void *x
 //     ((m/16) * (I/32) + k/32) * 512 + (((k%32)/8) * 16 + m%16) * 8 + k%8
 // so one 16-byte load per lane fetches a whole fragment from 8 full cache
 // lines.  Size: tiled_rows(tokens) * I * 2 bytes.
-inline int64_t tiled_rows(int64_t tokens) { return (tokens + 15) / 16 * 16; }
+__host__ __device__ inline int64_t tiled_rows(int64_t tokens) { return (tokens + 15) / 16 * 16; }
 
-// X_r = X D^-1 R written in the tiled layout (pad rows zero).
-hipError_t launch_scale_rotate_tiled(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
-                                     const int16_t *pairs, const float *theta, const float *cs, int krot,
-                                     hipStream_t st);
+// Dense form of the rotation: R'_g = diag(cs_g) . R_g per 128-channel group,
+// stored as H + L in the activation dtype (rot_mat_bytes(I) bytes), and
+// X_r = X . (H + L) on the matrix cores, written in the tiled layout (pad
+// rows zero).
+size_t rot_mat_bytes(int64_t I);
+hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
+                            int krot, uint16_t *hl, hipStream_t st);
+hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
+                            const uint16_t *hl, hipStream_t st);
 // Row-major [tokens][I] (2-byte elements) -> tiled layout (pad rows zero).
 hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64_t I, hipStream_t st);
 

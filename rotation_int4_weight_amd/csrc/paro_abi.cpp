@@ -135,7 +135,7 @@ paro_path auto_path(int64_t tokens) {
   return PARO_PATH_PREFILL;
 }
 
-// Workspace layout: [counters kCounterBytes][x_r (split / prefill)][partials]
+// Workspace layout: [counters kCounterBytes][x_r (split / prefill)][partials (decode) | H, L (prefill)]
 // X_r in the workspace: row-major for the split decode path, the GEMM's
 // 16-row tiled layout (rows padded to a multiple of 16) for prefill.
 size_t xr_region(const paro_w4_layer *L, int64_t tokens, paro_path path) {
@@ -149,6 +149,8 @@ size_t workspace_for(const paro_w4_layer *L, int64_t tokens, paro_path path) {
   size_t bytes = kCounterBytes + xr_region(L, tokens, path);
   if (path != PARO_PATH_PREFILL)
     bytes += paro::decode_partial_bytes(paro::plan_decode(I, O, tokens, path == PARO_PATH_DECODE_FUSED), tokens, O);
+  else
+    bytes += paro::rot_mat_bytes(I);
   return bytes;
 }
 
@@ -211,23 +213,42 @@ size_t paro_tiled_bytes(const paro_w4_layer *L, int64_t tokens) {
   return (size_t)paro::tiled_rows(tokens) * (size_t)L->in_features * 2;
 }
 
-int paro_scale_rotate_tiled(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *x_t,
-                            void *stream) {
+size_t paro_rotation_matrix_bytes(const paro_w4_layer *L) {
+  if (!L || L->in_features <= 0) return 0;
+  return paro::rot_mat_bytes(L->in_features);
+}
+
+int paro_rotation_matrix(const paro_w4_layer *L, paro_dtype x_dt, void *hl, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (!hl) return fail(PARO_ERR_NULL, "hl is required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  if (!aligned(hl, 16)) return fail(PARO_ERR_ALIGN, "hl must be 16-byte aligned");
+  hipError_t e = paro::launch_rot_build((int)x_dt, L->in_features, L->pairs, L->theta, L->channel_scales, L->krot,
+                                        (uint16_t *)hl, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+  return ok();
+}
+
+int paro_scale_rotate_tiled(const paro_w4_layer *L, const void *hl, const void *x, paro_dtype x_dt, int64_t tokens,
+                            void *x_t, void *stream) {
   int rc = check_gpu_shape(L);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
   if (tokens == 0) return ok();
-  if (!x || !x_t) return fail(PARO_ERR_NULL, "x and x_t are required");
-  rc = check_rotation_tensors(L);
-  if (rc) return rc;
-  if (!aligned(x, 16) || !aligned(x_t, 16)) return fail(PARO_ERR_ALIGN, "x and x_t must be 16-byte aligned");
+  if (!hl || !x || !x_t) return fail(PARO_ERR_NULL, "hl, x and x_t are required");
+  if (!aligned(hl, 16) || !aligned(x, 16) || !aligned(x_t, 16))
+    return fail(PARO_ERR_ALIGN, "hl, x and x_t must be 16-byte aligned");
   const int64_t I = L->in_features;
-  const size_t xb = (size_t)tokens * I * 2, tb = paro_tiled_bytes(L, tokens);
-  const char *xs = (const char *)x, *ts = (const char *)x_t;
+  const size_t xb = (size_t)tokens * I * 2, tb = paro_tiled_bytes(L, tokens), hb = paro::rot_mat_bytes(I);
+  const char *xs = (const char *)x, *ts = (const char *)x_t, *hs = (const char *)hl;
   if (xs < ts + tb && ts < xs + xb) return fail(PARO_ERR_SHAPE, "x_t overlaps x");
-  hipError_t e = paro::launch_scale_rotate_tiled((const uint16_t *)x, (int)x_dt, (uint16_t *)x_t, tokens, I,
-                                                 L->pairs, L->theta, L->channel_scales, L->krot, (hipStream_t)stream);
+  if (hs < ts + tb && ts < hs + hb) return fail(PARO_ERR_SHAPE, "x_t overlaps hl");
+  hipError_t e = paro::launch_rot_apply((const uint16_t *)x, (int)x_dt, (uint16_t *)x_t, tokens, I,
+                                        (const uint16_t *)hl, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scale_rotate_tiled launch");
   return ok();
 }
@@ -351,15 +372,20 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
   }
-  // prefill: X_r in the tiled layout (rotated straight into it, or re-tiled
-  // from the caller's row-major X_r), then the GEMM
+  // prefill: X_r in the tiled layout (the dense rotation built into the
+  // workspace and applied on the matrix cores, or the caller's row-major X_r
+  // re-tiled), then the GEMM
   uint16_t *xt = (uint16_t *)xr;
-  if (prerotated)
+  if (prerotated) {
     e = paro::launch_retile((const uint16_t *)x, xt, tokens, I, st);
-  else
-    e = paro::launch_scale_rotate_tiled((const uint16_t *)x, (int)x_dt, xt, tokens, I, L->pairs, L->theta,
-                                        L->channel_scales, L->krot, st);
-  if (e != hipSuccess) return hip_fail(e, prerotated ? "retile launch" : "scale_rotate launch");
+    if (e != hipSuccess) return hip_fail(e, "retile launch");
+  } else {
+    uint16_t *hl = (uint16_t *)((char *)xr + xr_region(L, tokens, path));
+    e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot, hl, st);
+    if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+    e = paro::launch_rot_apply((const uint16_t *)x, (int)x_dt, xt, tokens, I, hl, st);
+    if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+  }
   e = paro::launch_prefill_gemm(a, xt, st);
   if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
   return ok();

@@ -42,6 +42,7 @@
 //     contiguous.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace paro {
 
@@ -50,34 +51,6 @@ constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer wa
 constexpr int kStepsPerGroup = kG / kBK;
 constexpr int kBStride = kBK + 4;  // halves per LDS column (72 bytes)
 constexpr int kTiles = 4;           // LDS ring of expanded weight tiles
-// Buffer descriptor word 3 for raw (untyped) buffers on the gfx9 family.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-// c += A * B on one 16x16 tile (v_mfma_f32_16x16x32_{f16,bf16}), with c tied
-// to one AGPR quadruple.  Written as asm because the builtin lets the
-// register allocator pick a destination other than c, and it then shuffles
-// accumulators between loop iterations with v_accvgpr moves that each wait
-// for the MFMA just issued.  The compiler does not see these as MFMAs, so
-// the wait states before the accumulators are read back are inserted by hand
-// (mfma_drain); operands come straight from buffer and LDS loads, which need
-// none.
-template <int DT>
-__device__ __forceinline__ void mfma_acc(const u32x4 &a, const u32x4 &b, f32x4 &c) {
-  if constexpr (DT == kF16)
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  else
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-// 64 wait states: more than any MFMA needs before a VALU reads its result.
-__device__ __forceinline__ void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferWord3);
-}
 
 // Physical k-pair index of k-pair rp (k = 2rp, 2rp+1) in column col: the
 // four 8-row blocks are XOR-permuted by (col/16)&3.

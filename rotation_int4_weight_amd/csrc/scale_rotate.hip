@@ -14,6 +14,7 @@
 // dependent LDS stages).
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace paro {
 
@@ -62,61 +63,217 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
   }
 }
 
-// Same transform, output in the fragment-major tiled layout (launch.hpp):
-// each wave holds one complete 16-row tile of group g (rows past the last
-// token are zero) and writes its four 32-column blocks as 1 KB contiguous
-// stores, lane L taking row L&15 and columns 8(L>>4)..+7 of each block.
+// ---------------------------------------------------------------------------
+// Tiled output for the prefill GEMM, on the matrix cores.
+//
+// The rotation of one 128-channel group is a fixed linear map, so
+//     x_r[m][g*128 + j] = sum_i x[m][g*128 + i] * R'_g[i][j],
+//     R'_g = diag(cs_g) . R_g      (R_g: the krot stages applied in order)
+// (composition of linear maps: the staged result is this product exactly in
+// real arithmetic).
+// rot_build_kernel pushes the 128 scaled identity rows of every group through
+// the stages (the same staged code as above, fp32) and stores R'_g as two
+// matrices in the activation dtype, R' = H + L with H = rne(R') and
+// L = rne(R' - H): their sum represents R' to about 2^-16 relative (bf16;
+// 2^-22 for fp16), far inside the rotated-activation tolerance.
+// rot_apply_kernel then computes x.H + x.L with v_mfma_f32_16x16x32 in fp32
+// (x is exact in its own dtype), rounds once to the activation dtype and
+// writes the tiled layout.  At 2048 tokens the build is 1/16 of the staged
+// work and the rest runs on the matrix cores instead of as LDS gathers.
+// ---------------------------------------------------------------------------
+
+// hl: [group][2 (H, L)][128 (output channel, MFMA order)][128 (input channel i)],
+// x dtype.  The apply kernel computes the transpose, x_r^T = R'^T . x^T, with
+// H_T / L_T as the A operand: A row 4q+r (q, r < 4) of the 16-row tile 2b+h
+// (b < 4, h < 2) is output channel 32b + 8q + 4h + r.  The accumulators of
+// tiles 2b and 2b+1 then give each lane, for its token l%16, the channels
+// 32b + 8(l/16) .. +7 in order: one 16-byte piece of the tiled layout.
+constexpr int64_t kRotMatHalves = 2 * kG * kG;  // per group
+
+__device__ __forceinline__ int mfma_row_of_channel(int j) {
+  return (j & ~31) | (((j >> 2) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3);
+}
+
 template <int XDT>
 __global__ void __launch_bounds__(256)
-scale_rotate_tiled_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int64_t tokens, int64_t I,
-                          const int16_t *__restrict__ pairs, const float *__restrict__ theta,
-                          const float *__restrict__ cscale, int krot) {
+rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__restrict__ theta,
+                 const float *__restrict__ cscale, int krot, uint16_t *__restrict__ hl) {
   constexpr int RW = 16;
   __shared__ float lds[4][RW * kRotRS];
   const int lane = lane_id(), wave = wave_id();
   const int64_t g = blockIdx.x;
-  const int64_t m0 = ((int64_t)blockIdx.y * 4 + wave) * RW;
-  if (m0 >= tokens) return;  // whole tile past the padded end (no block-level barrier below)
-  const int T = (int)((tokens - m0) < RW ? (tokens - m0) : RW);
+  const int i0 = blockIdx.y * 64 + wave * RW;  // identity rows i0 .. i0+15 of this wave
   float *xs = lds[wave];
-  const int64_t c0 = g * kG + 2 * lane;
 
   RotParams rp;
   rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
-  const float s0 = cscale[c0], s1 = cscale[c0 + 1];
+  const float cs_i = cscale[g * kG + i0 + (lane & 15)];  // lanes 0..15: the scales of this wave's rows
 #pragma unroll
   for (int m = 0; m < RW; ++m) {
-    const int mm = m < T ? m : 0;
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(x + (m0 + mm) * I + c0);
-    xs[m * kRotRS + 2 * lane] = m < T ? act_to_f32<XDT>(w & 0xffffu) * s0 : 0.0f;
-    xs[m * kRotRS + 2 * lane + 1] = m < T ? act_to_f32<XDT>(w >> 16) * s1 : 0.0f;
+    const float c = __shfl(cs_i, m);
+    xs[m * kRotRS + 2 * lane] = (2 * lane == i0 + m) ? c : 0.0f;
+    xs[m * kRotRS + 2 * lane + 1] = (2 * lane + 1 == i0 + m) ? c : 0.0f;
   }
   wave_lds_sync();
 
   rotate_rows_lds<RW>(xs, kRotRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
 
-  const int r = lane & 15, kb = lane >> 4;
-  uint16_t *blk = xt + ((m0 / 16) * (I / 32) + g * (kG / 32)) * 512 + lane * 8;
+  // xs[m][j] = R'[i0 + m][j]; lane p handles output channels j = 2p, 2p+1:
+  // H_T[row(j)][i0 .. i0+15] and L_T[row(j)][i0 .. i0+15], 32 contiguous bytes each.
+  uint16_t *hg = hl + g * kRotMatHalves;
 #pragma unroll
-  for (int q = 0; q < kG / 32; ++q) {
-    const float *src = xs + r * kRotRS + 32 * q + 8 * kb;
-    u32x4 v;
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = 2 * lane + jj;
+    const int row = mfma_row_of_channel(j);
+    u32x4 h[2], l[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = pack2<XDT>(src[2 * e], src[2 * e + 1]);
-    *reinterpret_cast<u32x4 *>(blk + q * 512) = v;
+    for (int m = 0; m < RW; m += 2) {
+      const float v0 = xs[m * kRotRS + j], v1 = xs[(m + 1) * kRotRS + j];
+      const uint32_t hb = pack2<XDT>(v0, v1);
+      const float r0 = v0 - act_to_f32<XDT>(hb & 0xffffu), r1 = v1 - act_to_f32<XDT>(hb >> 16);  // exact
+      h[m >> 3][(m >> 1) & 3] = hb;
+      l[m >> 3][(m >> 1) & 3] = pack2<XDT>(r0, r1);
+    }
+    u32x4 *dh = reinterpret_cast<u32x4 *>(hg + (int64_t)row * kG + i0);
+    u32x4 *dl = reinterpret_cast<u32x4 *>(hg + (int64_t)(kG + row) * kG + i0);
+    dh[0] = h[0];
+    dh[1] = h[1];
+    dl[0] = l[0];
+    dl[1] = l[1];
   }
 }
 
-hipError_t launch_scale_rotate_tiled(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
-                                     const int16_t *pairs, const float *theta, const float *cs, int krot,
-                                     hipStream_t st) {
-  dim3 grid((unsigned)(I / kG), (unsigned)((tokens + 63) / 64));
+// One workgroup: group g = blockIdx.x, token rows [512*blockIdx.y, +512); each
+// wave takes batches of 4 row tiles (64 rows) and prefetches the next batch's
+// x fragments as the current ones retire.  LDS holds H_T and L_T of the group
+// (row stride 136 halves: the 16-byte fragment reads of 16 lanes spread over
+// the banks).
+constexpr int kHS = kG + 8;
+constexpr int kApplyRows = 512;
+constexpr int kApplyTiles = 4;  // row tiles per wave and batch
+
+template <int XDT>
+__global__ void __launch_bounds__(256, 2)
+rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int64_t tokens, int64_t I,
+                 const uint16_t *__restrict__ hl) {
+  __shared__ __attribute__((aligned(16))) uint16_t hlds[2 * kG * kHS];
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int64_t g = blockIdx.x;
+  const int64_t mt_end = tiled_rows(tokens) / 16;  // row tiles of the tiled buffer
+  const int64_t mt_first = (int64_t)blockIdx.y * (kApplyRows / 16);
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const uint32_t lane_off = (uint32_t)((fr * I + fk) * 2);
+
+  // x fragments (B operand: token l%16, input channels 8(l/16)..+7 of k-step
+  // ks) of the batch starting at row tile mt0; raw buffer over its 64 rows, so
+  // rows past the last token read as zeros.
+  auto load_x = [&](int64_t mt0, u32x4 (&xf)[kApplyTiles][4]) {
+    const int64_t row0 = mt0 * 16;
+    const int64_t rows = tokens - row0 < 64 ? tokens - row0 : 64;
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + row0 * I + g * kG, rows > 0 ? (uint32_t)(rows * I * 2) : 0u);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < kApplyTiles; ++t)
+        xf[t][ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, lane_off, (int)((t * 16 * I + ks * 32) * 2), 0);
+  };
+
+  int64_t mt0 = mt_first + wave * kApplyTiles;
+  u32x4 xf[kApplyTiles][4];
+  if (mt0 < mt_end) load_x(mt0, xf);
+
+  // H_T, L_T of the group into LDS: 256 rows x 16 chunks of 16 bytes (16 per
+  // thread, in two halves so that the x fragments in flight stay in registers)
+  const uint16_t *hg = hl + g * kRotMatHalves;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = threadIdx.x + 256 * (8 * half + u);  // chunk: matrix row c/16 (of 256), part c%16
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(hg + (int64_t)c * 8);
+      *reinterpret_cast<u32x4 *>(hlds + (c >> 4) * kHS + (c & 15) * 8) = v;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  constexpr int kStride = 4 * kApplyTiles;  // row tiles per batch of the workgroup
+  for (; mt0 < mt_end && mt0 < mt_first + kApplyRows / 16; mt0 += kStride) {
+    const int64_t next = mt0 + kStride;
+    const bool more = next < mt_end && next < mt_first + kApplyRows / 16;
+    f32x4 acc[kApplyTiles][8];
+#pragma unroll
+    for (int t = 0; t < kApplyTiles; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_fence(acc[t][ct]);
+      }
+    asm volatile("s_nop 7");  // accumulator writes -> first MFMA
+    // 64 steps (k-step ks, channel tile ct, H or L): one 16-byte LDS read of
+    // the A fragment, issued two steps ahead, and 4 MFMAs (one per row tile)
+    auto read_a = [&](int step) {
+      const int ks = step >> 4, ct = (step >> 1) & 7, hlm = step & 1;
+      return *reinterpret_cast<const u32x4 *>(hlds + (hlm * kG + ct * 16 + fr) * kHS + ks * 32 + fk);
+    };
+    u32x4 ar[3];
+    ar[0] = read_a(0);
+    ar[1] = read_a(1);
+#pragma unroll
+    for (int step = 0; step < 64; ++step) {
+      const int ks = step >> 4, ct = (step >> 1) & 7;
+      if (step + 2 < 64) ar[(step + 2) % 3] = read_a(step + 2);
+#pragma unroll
+      for (int t = 0; t < kApplyTiles; ++t) mfma_acc<XDT>(ar[step % 3], xf[t][ks], acc[t][ct]);
+      if ((step & 15) == 15 && more) {  // k-step ks consumed: fetch the next batch's fragments
+        const int64_t row0 = next * 16;
+        const int64_t rows = tokens - row0 < 64 ? tokens - row0 : 64;
+        const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + row0 * I + g * kG, (uint32_t)(rows * I * 2));
+#pragma unroll
+        for (int t = 0; t < kApplyTiles; ++t)
+          xf[t][ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, lane_off, (int)((t * 16 * I + ks * 32) * 2), 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_drain();
+#pragma unroll
+    for (int t = 0; t < kApplyTiles; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc_fence(acc[t][ct]);
+    // lane l, tile t, 32-channel block b: token l%16, channels 32b + 8(l/16) .. +7
+#pragma unroll
+    for (int t = 0; t < kApplyTiles; ++t) {
+      if (mt0 + t >= mt_end) break;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 lo = acc[t][2 * b], hi = acc[t][2 * b + 1];
+        const u32x4 v{pack2<XDT>(lo[0], lo[1]), pack2<XDT>(lo[2], lo[3]), pack2<XDT>(hi[0], hi[1]),
+                      pack2<XDT>(hi[2], hi[3])};
+        *reinterpret_cast<u32x4 *>(xt + ((mt0 + t) * (I / 32) + g * 4 + b) * 512 + lane * 8) = v;
+      }
+    }
+  }
+}
+
+size_t rot_mat_bytes(int64_t I) { return (size_t)(I / kG) * (size_t)kRotMatHalves * 2; }
+
+hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
+                            int krot, uint16_t *hl, hipStream_t st) {
+  const dim3 grid((unsigned)(I / kG), 2);
   if (x_dt == kF16)
-    hipLaunchKernelGGL((scale_rotate_tiled_kernel<kF16>), grid, dim3(256), 0, st, x, xt, tokens, I, pairs, theta,
-                       cs, krot);
+    hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(256), 0, st, I, pairs, theta, cs, krot, hl);
   else
-    hipLaunchKernelGGL((scale_rotate_tiled_kernel<kBF16>), grid, dim3(256), 0, st, x, xt, tokens, I, pairs, theta,
-                       cs, krot);
+    hipLaunchKernelGGL((rot_build_kernel<kBF16>), grid, dim3(256), 0, st, I, pairs, theta, cs, krot, hl);
+  return hipGetLastError();
+}
+
+hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
+                            const uint16_t *hl, hipStream_t st) {
+  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + kApplyRows - 1) / kApplyRows));
+  if (x_dt == kF16)
+    hipLaunchKernelGGL((rot_apply_kernel<kF16>), grid, dim3(256), 0, st, x, xt, tokens, I, hl);
+  else
+    hipLaunchKernelGGL((rot_apply_kernel<kBF16>), grid, dim3(256), 0, st, x, xt, tokens, I, hl);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ def test_libparo_exports_every_declared_symbol():
     assert set(_lib.EXPORTS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.paro_abi_version() == 1
+    assert lib.paro_abi_version() == 2
 
 
 def test_oracle_exports_every_declared_symbol():
@@ -188,14 +188,26 @@ def test_tiled_entry_point_argument_checks():
     assert lib.paro_tiled_bytes(ctypes.byref(L), 1) == 16 * 256 * 2
     assert lib.paro_tiled_bytes(ctypes.byref(L), 33) == 48 * 256 * 2
     assert lib.paro_tiled_bytes(ctypes.byref(L), 0) == 0
-    rot = lambda x=FAKE, dt=0, tokens=4, xt=FAKE * 2, L=L: lib.paro_scale_rotate_tiled(
-        ctypes.byref(L), x, dt, tokens, xt, None)
+    assert lib.paro_rotation_matrix_bytes(ctypes.byref(L)) == 256 * 512
+    mat = lambda dt=0, hl=FAKE * 8, L=L: lib.paro_rotation_matrix(ctypes.byref(L), dt, hl, None)
+    assert mat(dt=2) == 3
+    assert mat(hl=0) == 1
+    assert mat(hl=FAKE * 8 + 4) == 4
+    assert mat(L=fake_layer(pairs=0)) == 1
+    assert mat(L=fake_layer(theta=0)) == 1
+    assert mat(L=fake_layer(G=64)) == 5
+    rot = lambda x=FAKE, dt=0, tokens=4, xt=FAKE * 2, hl=FAKE * 8, L=L: lib.paro_scale_rotate_tiled(
+        ctypes.byref(L), hl, x, dt, tokens, xt, None)
     assert rot(dt=2) == 3                      # fp32 activations not accepted
     assert rot(x=0) == 1
+    assert rot(hl=0) == 1
     assert rot(xt=FAKE * 2 + 8) == 4
+    assert rot(hl=FAKE * 8 + 8) == 4
     assert rot(xt=FAKE + 64) == 2              # overlaps x
-    assert rot(tokens=0, x=0, xt=0) == 0
-    assert rot(L=fake_layer(pairs=0)) == 1
+    assert rot(hl=FAKE * 2 + 4096) == 2        # x_t overlaps hl
+    assert rot(tokens=0, x=0, xt=0, hl=0) == 0
+    assert rot(tokens=-1) == 2
+    assert rot(L=fake_layer(G=64)) == 5
     lin = lambda xt=FAKE, dt=0, tokens=4, y=FAKE * 4, ydt=0, L=L: lib.paro_w4a16_linear_tiled(
         ctypes.byref(L), xt, dt, tokens, y, ydt, None)
     assert lin(ydt=1) == 3                     # y must be x dtype or fp32

@@ -278,15 +278,25 @@ def test_one_workspace_serves_many_shapes_and_paths():
 
 @pytest.mark.parametrize("cfg,path", [(1, "split"), (2, "split"), (3, "prefill")])
 def test_prerotated_projection_matches_linear(cfg, path):
-    """paro_scale_rotate + the projection alone == the linear, bit for bit."""
+    """The projection alone over the linear's own X_r == the linear, bit for bit
+    (X_r from paro_scale_rotate for the split path, from the dense tiled
+    rotation for PREFILL)."""
     lname, L, x, dt = workload(cfg)
     say(f"prerotated cfg{cfg} {lname} path={path}")
     D = paro.DeviceLayer(L)
     xd = x_to_device(x, dt)
     M, O = x.shape[0], L.out_features
     full = to_host_bits(run_linear(D, xd, O, synth.F32, PATHS[path]))
-    xr = torch.empty_like(xd)
-    paro.paro_scale_rotate(D, xd, xr)
+    if path == "prefill":  # the PREFILL linear rotates with the dense matrix: take its X_r
+        hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+        paro.paro_rotation_matrix(D, dt, hl)
+        xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device="cuda")
+        paro.paro_scale_rotate_tiled(D, hl, xd, xt)
+        rows = untile(xt.cpu().numpy().view(np.uint16), M, L.in_features)[:M]
+        xr = x_to_device(np.ascontiguousarray(rows), dt)
+    else:
+        xr = torch.empty_like(xd)
+        paro.paro_scale_rotate(D, xd, xr)
     y = torch.empty((M, O), dtype=torch.float32, device="cuda")
     ws = paro.make_workspace(paro.paro_w4a16_linear_workspace_bytes(D, M, dt, PATHS[path]))
     paro.paro_w4a16_linear_prerotated(D, xr, y, ws, path=PATHS[path])
@@ -305,11 +315,65 @@ def untile(bits, M, I):
     return a.transpose(0, 3, 1, 2, 4).reshape(rows, I)
 
 
+def mfma_row_of_channel(j):
+    """Row of output channel j (< 128) in the H / L matrices: the matrix cores
+    take row 4q+r of 16-row tile 2b+h as channel 32b + 8q + 4h + r."""
+    j = np.asarray(j)
+    return (j & ~31) | (((j >> 2) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3)
+
+
+def within_one_ulp(a, b, dt):
+    """Elementwise: a and b (values of dtype dt) are equal or adjacent."""
+    mant, tiny = (10, 2.0 ** -14) if dt == synth.F16 else (7, 2.0 ** -126)
+    mag = np.maximum(np.maximum(np.abs(a), np.abs(b)), tiny)
+    return np.abs(a - b) <= 2.0 ** (np.floor(np.log2(mag)) - mant)
+
+
+ONE_BITS = {synth.F16: 0x3C00, synth.BF16: 0x3F80}
+
+
+@pytest.mark.parametrize("I,krot,dt", [(128, 1, synth.F16), (256, 8, synth.BF16), (512, 9, synth.F16),
+                                       (384, 40, synth.BF16)])
+def test_rotation_matrix_is_the_scaled_rotation(I, krot, dt):
+    """H + L == diag(cs) . R per group: the oracle's scaling and rotation of
+    the unit rows (x = identity, exact in either dtype) gives R' row by row."""
+    L = synth.make_layer(207, krot, I, 8, krot=krot)
+    say(f"rotation_matrix I={I} krot={krot} dt={dt}")
+    D = paro.DeviceLayer(L)
+    nbytes = paro.paro_rotation_matrix_bytes(D)
+    assert nbytes == I * 512
+    hl = torch.full((nbytes // 2,), -1, dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
+    torch.cuda.synchronize()
+    eye = np.zeros((I, I), dtype=np.uint16)
+    eye[np.arange(I), np.arange(I)] = ONE_BITS[dt]
+    r_ref = ref.scale_rotate(L, eye, dt)  # r_ref[i][k] = R'[i][k] (block diagonal)
+    m = bits_to_f64(hl.cpu().numpy().view(np.uint16), dt).reshape(I // 128, 2, 128, 128)
+    rows = mfma_row_of_channel(np.arange(128))
+    tol = 4e-6 if dt == synth.F16 else 4e-5
+    for g in range(I // 128):
+        blk = r_ref[g * 128:(g + 1) * 128, g * 128:(g + 1) * 128]
+        rec = (m[g, 0] + m[g, 1])[rows, :].T  # rec[i][j] = H_T[row(j)][i] + L_T[row(j)][i]
+        assert np.abs(rec - blk).max() <= tol * np.abs(blk).max(), g
+        h = m[g, 0][rows, :].T
+        # H is R' rounded to the dtype: within one unit in the last place, or,
+        # for entries near zero, within the fp32 error of the staged build
+        # (about krot * 2^-24 of the block's scale)
+        fp32_err = krot * 2.0 ** -23 * np.abs(blk).max()
+        assert (within_one_ulp(h, blk, dt) | (np.abs(h - blk) <= fp32_err)).all()
+    off = r_ref.copy()
+    for g in range(I // 128):
+        off[g * 128:(g + 1) * 128, g * 128:(g + 1) * 128] = 0
+    assert not off.any()  # the oracle's rotation never mixes groups
+
+
 @pytest.mark.parametrize("I,M,krot,dt", [(128, 1, 1, synth.F16), (4096, 17, 8, synth.F16),
-                                         (384, 65, 9, synth.BF16), (1024, 48, 8, synth.BF16)])
+                                         (384, 65, 9, synth.BF16), (1024, 48, 8, synth.BF16),
+                                         (256, 600, 8, synth.F16), (128, 1040, 3, synth.BF16)])
 def test_scale_rotate_tiled(I, M, krot, dt):
-    """The tiled rotation holds the same bits as paro_scale_rotate, zero pad rows,
-    and meets the oracle's rotated-activation gate."""
+    """The tiled rotation (dense H + L on the matrix cores) meets the oracle's
+    rotated-activation gate, is within one unit in the last place of the
+    staged row-major rotation, and leaves the pad rows zero."""
     L = synth.make_layer(205, krot, I, 8, krot=krot)
     x = synth.make_x(205, krot, M, I, dt)
     say(f"scale_rotate_tiled I={I} M={M} krot={krot} dt={dt}")
@@ -317,22 +381,32 @@ def test_scale_rotate_tiled(I, M, krot, dt):
     xd = x_to_device(x, dt)
     nbytes = paro.paro_tiled_bytes(D, M)
     assert nbytes == (M + 15) // 16 * 16 * I * 2
+    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
     xt = torch.full((nbytes // 2,), -1, dtype=torch.int16, device="cuda")  # poison
-    paro.paro_scale_rotate_tiled(D, xd, xt)
+    paro.paro_scale_rotate_tiled(D, hl, xd, xt)
     rm = torch.empty_like(xd)
     paro.paro_scale_rotate(D, xd, rm)
     torch.cuda.synchronize()
     t = untile(xt.cpu().numpy().view(np.uint16), M, I)
-    assert np.array_equal(t[:M], to_host_bits(rm))
     assert not t[M:].any()
+    tv, rv = bits_to_f64(t[:M], dt), bits_to_f64(to_host_bits(rm), dt)
+    # the dense and the staged rotation differ only in fp32 rounding: one unit
+    # in the last place, except near zero (cancellation), where both sit
+    # within 2^-12 of the row's scale of the exact value
+    ulp1 = within_one_ulp(tv, rv, dt)
+    near = np.abs(tv - rv) <= 2.0 ** -12 * np.abs(rv).max(axis=1, keepdims=True)
+    assert (ulp1 | near).all()
+    assert ulp1.mean() >= 0.999
     xr_ref = ref.scale_rotate(L, np.ascontiguousarray(x), dt)
-    err = np.abs(bits_to_f64(t[:M], dt) - xr_ref).max(axis=1) / np.abs(xr_ref).max(axis=1)
+    err = np.abs(tv - xr_ref).max(axis=1) / np.abs(xr_ref).max(axis=1)
     assert float(err.max()) <= ROT_TOL + U[dt]
 
 
 @pytest.mark.parametrize("cfg,extra", [(0, None), (3, None), ("edge", (1024, 200, 40, synth.F16))])
 def test_linear_tiled_matches_prefill_path(cfg, extra):
-    """paro_scale_rotate_tiled + paro_w4a16_linear_tiled == the PREFILL path, bit for bit."""
+    """paro_rotation_matrix + paro_scale_rotate_tiled + paro_w4a16_linear_tiled
+    == the PREFILL path, bit for bit."""
     if cfg == "edge":
         I, O, M, dt = extra
         L = synth.make_layer(206, 0, I, O)
@@ -344,8 +418,10 @@ def test_linear_tiled_matches_prefill_path(cfg, extra):
     D = paro.DeviceLayer(L)
     xd = x_to_device(x, dt)
     full = to_host_bits(run_linear(D, xd, O, synth.F32, PATHS["prefill"]))
+    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
     xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device="cuda")
-    paro.paro_scale_rotate_tiled(D, xd, xt)
+    paro.paro_scale_rotate_tiled(D, hl, xd, xt)
     y = torch.empty((M, O), dtype=torch.float32, device="cuda")
     paro.paro_w4a16_linear_tiled(D, xt, dt, M, y)
     torch.cuda.synchronize()

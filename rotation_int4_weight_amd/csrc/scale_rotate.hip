@@ -71,9 +71,10 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
 //     R'_g = diag(cs_g) . R_g      (R_g: the krot stages applied in order)
 // (composition of linear maps: the staged result is this product exactly in
 // real arithmetic).
-// rot_build_kernel pushes the 128 scaled identity rows of every group through
-// the stages (the same staged code as above, fp32) and stores R'_g as two
-// matrices in the activation dtype, R' = H + L with H = rne(R') and
+// rot_build_kernel forms R'_g^T = R_g^T . diag(cs_g) row by row: unit row e_j
+// through the transposed stages (each a Givens rotation by -theta) in reverse
+// order, then times cs (the same staged code as above, fp32).  It stores R'_g
+// as two matrices in the activation dtype, R' = H + L with H = rne(R') and
 // L = rne(R' - H): their sum represents R' to about 2^-16 relative (bf16;
 // 2^-22 for fp16), far inside the rotated-activation tolerance.
 // rot_apply_kernel then computes x.H + x.L with v_mfma_f32_16x16x32 in fp32
@@ -90,56 +91,68 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
 // 32b + 8(l/16) .. +7 in order: one 16-byte piece of the tiled layout.
 constexpr int64_t kRotMatHalves = 2 * kG * kG;  // per group
 
-__device__ __forceinline__ int mfma_row_of_channel(int j) {
-  return (j & ~31) | (((j >> 2) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3);
+__device__ __forceinline__ int channel_of_mfma_row(int r) {
+  return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
+// One wave: group g = blockIdx.x, rows r0 = 16 * blockIdx.y .. r0+15 of H_T and
+// L_T (output channels j = channel_of_mfma_row(r)).  Each row is written as
+// one coalesced 256-byte store per matrix.
 template <int XDT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__restrict__ theta,
                  const float *__restrict__ cscale, int krot, uint16_t *__restrict__ hl) {
   constexpr int RW = 16;
-  __shared__ float lds[4][RW * kRotRS];
-  const int lane = lane_id(), wave = wave_id();
+  __shared__ float xs[RW * kRotRS];
+  const int lane = lane_id();
   const int64_t g = blockIdx.x;
-  const int i0 = blockIdx.y * 64 + wave * RW;  // identity rows i0 .. i0+15 of this wave
-  float *xs = lds[wave];
+  const int r0 = blockIdx.y * RW;
+  const int16_t *pairs_g = pairs + g * kG;
+  const float *theta_g = theta + g * kPairs;
 
-  RotParams rp;
-  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
-  const float cs_i = cscale[g * kG + i0 + (lane & 15)];  // lanes 0..15: the scales of this wave's rows
+  // parameters of the last kStageRegs stages (applied first), issued up front
+  uint32_t pw[kStageRegs];
+  float th[kStageRegs];
+#pragma unroll
+  for (int u = 0; u < kStageRegs; ++u) {
+    const int t = krot - 1 - u >= 0 ? krot - 1 - u : 0;
+    pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    th[u] = theta_g[(int64_t)t * (I / 2) + lane];
+  }
+  const float2 cs2 = *reinterpret_cast<const float2 *>(cscale + g * kG + 2 * lane);
+
 #pragma unroll
   for (int m = 0; m < RW; ++m) {
-    const float c = __shfl(cs_i, m);
-    xs[m * kRotRS + 2 * lane] = (2 * lane == i0 + m) ? c : 0.0f;
-    xs[m * kRotRS + 2 * lane + 1] = (2 * lane + 1 == i0 + m) ? c : 0.0f;
+    const int j = channel_of_mfma_row(r0 + m);
+    xs[m * kRotRS + 2 * lane] = 2 * lane == j ? 1.0f : 0.0f;
+    xs[m * kRotRS + 2 * lane + 1] = 2 * lane + 1 == j ? 1.0f : 0.0f;
   }
   wave_lds_sync();
 
-  rotate_rows_lds<RW>(xs, kRotRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
-
-  // xs[m][j] = R'[i0 + m][j]; lane p handles output channels j = 2p, 2p+1:
-  // H_T[row(j)][i0 .. i0+15] and L_T[row(j)][i0 .. i0+15], 32 contiguous bytes each.
-  uint16_t *hg = hl + g * kRotMatHalves;
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = 2 * lane + jj;
-    const int row = mfma_row_of_channel(j);
-    u32x4 h[2], l[2];
-#pragma unroll
-    for (int m = 0; m < RW; m += 2) {
-      const float v0 = xs[m * kRotRS + j], v1 = xs[(m + 1) * kRotRS + j];
-      const uint32_t hb = pack2<XDT>(v0, v1);
-      const float r0 = v0 - act_to_f32<XDT>(hb & 0xffffu), r1 = v1 - act_to_f32<XDT>(hb >> 16);  // exact
-      h[m >> 3][(m >> 1) & 3] = hb;
-      l[m >> 3][(m >> 1) & 3] = pack2<XDT>(r0, r1);
+  for (int u = 0; u < kStageRegs; ++u) {
+    if (u < krot) {
+      float c, sn;
+      __sincosf(th[u], &sn, &c);
+      rotate_stage<RW>(xs, kRotRS, pw[u], c, -sn);
     }
-    u32x4 *dh = reinterpret_cast<u32x4 *>(hg + (int64_t)row * kG + i0);
-    u32x4 *dl = reinterpret_cast<u32x4 *>(hg + (int64_t)(kG + row) * kG + i0);
-    dh[0] = h[0];
-    dh[1] = h[1];
-    dl[0] = l[0];
-    dl[1] = l[1];
+  }
+  for (int t = krot - 1 - kStageRegs; t >= 0; --t) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    float c, sn;
+    __sincosf(theta_g[(int64_t)t * (I / 2) + lane], &sn, &c);
+    rotate_stage<RW>(xs, kRotRS, w, c, -sn);
+  }
+
+  // xs[m][i] * cs[i] = R'[i][j_m]: lane p holds input channels 2p, 2p+1
+  uint32_t *hrow = reinterpret_cast<uint32_t *>(hl + g * kRotMatHalves + (int64_t)r0 * kG) + lane;
+#pragma unroll
+  for (int m = 0; m < RW; ++m) {
+    const float v0 = xs[m * kRotRS + 2 * lane] * cs2.x, v1 = xs[m * kRotRS + 2 * lane + 1] * cs2.y;
+    const uint32_t hb = pack2<XDT>(v0, v1);
+    const float e0 = v0 - act_to_f32<XDT>(hb & 0xffffu), e1 = v1 - act_to_f32<XDT>(hb >> 16);  // exact
+    hrow[m * (kG / 2)] = hb;
+    hrow[(kG + m) * (kG / 2)] = pack2<XDT>(e0, e1);
   }
 }
 
@@ -240,7 +253,10 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
     for (int t = 0; t < kApplyTiles; ++t)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc_fence(acc[t][ct]);
-    // lane l, tile t, 32-channel block b: token l%16, channels 32b + 8(l/16) .. +7
+    // lane l, tile t, 32-channel block b: token l%16, channels 32b + 8(l/16) .. +7.
+    // Streaming (non-temporal) stores: X_r is not read again by this kernel,
+    // and keeping it out of the caches leaves them to the x stream (measured
+    // a third faster than ordinary stores).
 #pragma unroll
     for (int t = 0; t < kApplyTiles; ++t) {
       if (mt0 + t >= mt_end) break;
@@ -249,7 +265,7 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
         const f32x4 lo = acc[t][2 * b], hi = acc[t][2 * b + 1];
         const u32x4 v{pack2<XDT>(lo[0], lo[1]), pack2<XDT>(lo[2], lo[3]), pack2<XDT>(hi[0], hi[1]),
                       pack2<XDT>(hi[2], hi[3])};
-        *reinterpret_cast<u32x4 *>(xt + ((mt0 + t) * (I / 32) + g * 4 + b) * 512 + lane * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(xt + ((mt0 + t) * (I / 32) + g * 4 + b) * 512 + lane * 8));
       }
     }
   }
@@ -259,11 +275,11 @@ size_t rot_mat_bytes(int64_t I) { return (size_t)(I / kG) * (size_t)kRotMatHalve
 
 hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
                             int krot, uint16_t *hl, hipStream_t st) {
-  const dim3 grid((unsigned)(I / kG), 2);
+  const dim3 grid((unsigned)(I / kG), kG / 16);
   if (x_dt == kF16)
-    hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(256), 0, st, I, pairs, theta, cs, krot, hl);
+    hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, hl);
   else
-    hipLaunchKernelGGL((rot_build_kernel<kBF16>), grid, dim3(256), 0, st, I, pairs, theta, cs, krot, hl);
+    hipLaunchKernelGGL((rot_build_kernel<kBF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, hl);
   return hipGetLastError();
 }
 

@@ -12,15 +12,17 @@
 //   * consumer waves 0..3 own rows 64c..64c+63 and all 128 columns (4 x 8
 //     MFMA tiles, 32 v_mfma_f32_16x16x32 per 32-deep k step) and issue
 //     nothing but their MFMAs, the LDS reads of the next step's B fragments
-//     (in two halves, each hidden behind the other half's MFMAs) and the
-//     loads of A two steps ahead;
-//   * producer waves 4..7 load the packed weight words four steps before
+//     (each issued after the last MFMA that reads its register, with seven
+//     column tiles of MFMAs to arrive in) and the loads of A four steps
+//     ahead;
+//   * producer waves 4..7 load the packed weight words eight steps before
 //     they are needed, decode each group's scales and zero points and
-//     dequantize the tile two steps ahead into a ring of four LDS tiles.
+//     dequantize each tile four steps ahead into a ring of eight LDS tiles.
 // On gfx950 a SIMD hides only about one VALU instruction per 16-cycle MFMA
 // from the same wave but about two from a second wave, so the split keeps
 // the matrix pipe fed while the dequantization runs beside it.  Both roles
-// meet at one barrier per k step.
+// meet at one barrier per super-step of two k steps (64 MFMAs per consumer
+// wave between barriers).
 //
 // Operand layouts are chosen for whole-cache-line loads (the texture/L1 path
 // bounds this kernel otherwise):
@@ -50,7 +52,10 @@ constexpr int kBM = 256, kBN = 128, kBK = 32;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
 constexpr int kStepsPerGroup = kG / kBK;
 constexpr int kBStride = kBK + 4;  // halves per LDS column (72 bytes)
-constexpr int kTiles = 4;           // LDS ring of expanded weight tiles
+constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k steps)
+constexpr int kWordRing = 8;        // packed weight words in flight per producer thread (steps)
+constexpr int kASlots = 4;          // A fragments in flight per consumer wave (steps)
+static_assert(kTiles == 8 && kWordRing == 8, "the producer's ring slot arithmetic assumes rings of 8");
 
 // Physical k-pair index of k-pair rp (k = 2rp, 2rp+1) in column col: the
 // four 8-row blocks are XOR-permuted by (col/16)&3.
@@ -192,42 +197,56 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 
     GroupConsts<DT> gc;
     GroupRaw graw[2];
-    Words wd[4];
+    Words wd[kWordRing];
     load_group(0, graw[0]);
     load_group(1, graw[1]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) load_words(k, wd[k]);
+    for (int k = 0; k < kWordRing; ++k) load_words(k, wd[k]);
     gc.decode(graw[0].sw, graw[0].zw);
-    expand_pair_to_lds<DT>(wd[0].ra, wd[0].rb, gc, bl[0], dw, drp);
-    expand_pair_to_lds<DT>(wd[1].ra, wd[1].rb, gc, bl[1], dw, drp);
-    load_words(4, wd[0]);
-    load_words(5, wd[1]);
+    load_group(2, graw[0]);
+    // tiles 0..3 before the first barrier: the consumers' first super-step
+    // computes steps 0, 1 and reads the fragments of steps 2 and 3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, bl[k], dw, drp);
+      load_words(k + kWordRing, wd[k]);
+      __builtin_amdgcn_sched_barrier(0);  // one expansion's temporaries live at a time
+    }
     __syncthreads();
 
-    // Step s: expand step s+2 (words slot (s+2)&3) into tile (s+2)&3, whose
-    // last readers finished two barriers ago; refill that slot with step
-    // s+6.
-    // Group g+1's scales/zeros (fetched during group g-1) are decoded at step
-    // 4g+2, just before the expansion of step 4g+4; group g+2's are fetched
-    // at step 4g.  Past the end everything runs on clamped, in-bounds
-    // addresses into tiles no consumer reads.
-    auto pstep = [&](int step, int ph, const GroupRaw &gnext) {
-      if (ph == 2) gc.decode(gnext.sw, gnext.zw);
-      Words &w = wd[(step + 2) & 3];
-      expand_pair_to_lds<DT>(w.ra, w.rb, gc, bl[(step + 2) & 3], dw, drp);
-      load_words(step + 6, w);
+    // Super-step S (the consumers' steps 2S, 2S+1): expand steps 2S+4 and
+    // 2S+5 into tiles (2S+4)%8, (2S+5)%8.  Their first reader runs in
+    // super-step S+1, after the barrier that ends S; their slots' previous
+    // tiles (2S-4, 2S-3) were last read in super-step S-2.  Each word slot is
+    // refilled kWordRing steps ahead.  A group spans two super-steps: its
+    // scales and zeros are decoded at the start of its first one and were
+    // fetched two groups earlier.  Past the end everything runs on clamped,
+    // in-bounds addresses into tiles no consumer uses.
+    // kk: position of S in a four-super-step iteration whose first S is a
+    // multiple of 4, so that the ring slots (2kk+4+u) % 8 are constants.
+    auto psuper = [&](int S, int kk, bool new_group, GroupRaw &graw_slot, int g_refill) {
+      if (new_group) {
+        gc.decode(graw_slot.sw, graw_slot.zw);
+        load_group(g_refill, graw_slot);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int slot = (2 * kk + 4 + u) % kTiles;  // == (2S+4+u) % 8
+        Words &w = wd[slot];
+        expand_pair_to_lds<DT>(w.ra, w.rb, gc, bl[slot], dw, drp);
+        load_words(2 * S + 4 + u + kWordRing, w);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __syncthreads();
     };
     for (int g = 0; g < ngroups; g += 2) {
-      // two groups per iteration: every ring slot index is a constant
-      const int s0 = g * kStepsPerGroup;
-      load_group(g + 2, graw[0]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pstep(s0 + k, k, graw[1]);
+      // two groups (four super-steps) per iteration
+      const int S0 = 2 * g;
+      psuper(S0, 0, true, graw[1], g + 3);      // decodes group g+1
+      psuper(S0 + 1, 1, false, graw[1], 0);
       if (g + 1 < ngroups) {
-        load_group(g + 3, graw[1]);
-#pragma unroll
-        for (int k = 4; k < 8; ++k) pstep(s0 + k, k - 4, graw[0]);
+        psuper(S0 + 2, 2, true, graw[0], g + 4);  // decodes group g+2
+        psuper(S0 + 3, 3, false, graw[0], 0);
       }
     }
     return;
@@ -243,22 +262,18 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
   };
-  // B fragments of column tiles j0..j0+3 of one k step: column 16j + fr, k
+  // B fragment of column tile j of one k step: column 16j + fr, k
   // block fk (physical block (fk/8) ^ (j&3)), two 8-byte LDS reads each.
   // Only the four lane offsets for j&3 live in registers; the tile and j>=4
   // are constant offsets folded into the LDS instructions.
   uint32_t fcol[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) fcol[jj] = (uint32_t)((jj * 16 + fr) * kBStride + 8 * ((fk >> 3) ^ jj));
-  auto read_frags = [&](int tile, int j0, u32x4 bf[8]) {
-    const uint16_t *bt = &bl[0][0] + tile * (kBN * kBStride);
-#pragma unroll
-    for (int j = j0; j < j0 + 4; ++j) {
-      const uint16_t *col = bt + fcol[j & 3] + (j >> 2) * 64 * kBStride;
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(col);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(col + 4);
-      bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
+  auto read_frag = [&](int tile, int j, u32x4 &b) {
+    const uint16_t *col = &bl[0][0] + tile * (kBN * kBStride) + fcol[j & 3] + (j >> 2) * 64 * kBStride;
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(col);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(col + 4);
+    b = u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
   f32x4 acc[4][8];
@@ -266,50 +281,53 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ab[2][4], bf[8];
-  load_a(0, ab[0]);
-  load_a(1, ab[1]);
+  u32x4 ab[kASlots][4], bf[8];
+#pragma unroll
+  for (int k = 0; k < kASlots; ++k) load_a(k, ab[k]);
   __syncthreads();
   // When both waves of a SIMD are ready, issue the consumer's MFMAs first;
   // the producer's VALU work fills the cycles in between.
   __builtin_amdgcn_s_setprio(2);
-  read_frags(0, 0, bf);
-  read_frags(0, 4, bf);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) read_frag(0, j, bf[j]);
 
-  // Step s: MFMAs of column tiles 0..3 on A slot s&1; refill fragments 0..3
-  // with those of step s+1 (tile (s+1)&3, expanded during step s-1) while
-  // tiles 4..7 compute; refill fragments 4..7, which arrive during the next
-  // step's first 16 MFMAs; refill the A slot with step s+2; barrier.  The
-  // scheduling barriers keep each refill after the MFMAs that read the old
-  // fragments (an MFMA reads its sources when issued).
-  auto cstep = [&](int step, u32x4(&A)[4]) {
-    const int next = (step + 1) & 3;
+  // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
+  // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at
+  // least one barrier earlier), which has the other seven tiles' MFMAs to
+  // arrive in; then the refill of the A slot with step s+4, and a barrier
+  // after odd steps.  The scheduling barriers keep each refill after the
+  // MFMAs that read the old fragment (an MFMA reads its sources when issued).
+  auto cstep = [&](int step, u32x4(&A)[4], bool barrier) {
+    const int next = (step + 1) % kTiles;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(next, 0, bf);
-#pragma unroll
-    for (int j = 4; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(next, 4, bf);
-    load_a(step + 2, A);
-    // Barrier without waiting for this wave's own LDS reads: the tile they
-    // read is rewritten only three barriers later.  The memory clobber keeps
-    // the compiler from moving LDS accesses across it.
-    asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      read_frag(next, j, bf[j]);
+    }
+    load_a(step + kASlots, A);
+    // One barrier per super-step of two k steps, without waiting for this
+    // wave's own LDS reads: the tiles they read are rewritten only two
+    // barriers later.  The memory clobber keeps the compiler from moving LDS
+    // accesses across it.
+    if (barrier) asm volatile("s_barrier" ::: "memory");
   };
-  // (unrolled by two only: the A slots need constant indices, nothing else
-  // does, and a longer unroll makes the register allocator rotate buffers)
-  for (int step = 0; step < nsteps; step += 2) {
-    cstep(step, ab[0]);
-    cstep(step + 1, ab[1]);
-  }
+  // (unrolled by kASlots: the A slots need constant indices; nsteps is a
+  // positive multiple of 4.  A do-while has no zero-trip path, whose join
+  // would let the compiler copy accumulators out before the drain below.)
+  int step = 0;
+  do {
+#pragma unroll
+    for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], (k & 1) != 0);
+    step += kASlots;
+  } while (step < nsteps);
   __builtin_amdgcn_s_setprio(0);
   mfma_drain();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
 
   // epilogue: bias in fp32, one rounding to the output dtype
   const int64_t m0 = mb + wave * 64;

@@ -55,6 +55,7 @@ constexpr int kBStride = kBK + 4;  // halves per LDS column (72 bytes)
 constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k steps)
 constexpr int kWordRing = 8;        // packed weight words in flight per producer thread (steps)
 constexpr int kASlots = 4;          // A fragments in flight per consumer wave (steps)
+constexpr int kStageRS = kBN + 4;   // epilogue staging row stride (floats): the four row groups of a store hit distinct banks
 static_assert(kTiles == 8 && kWordRing == 8, "the producer's ring slot arithmetic assumes rings of 8");
 
 // Physical k-pair index of k-pair rp (k = 2rp, 2rp+1) in column col: the
@@ -140,6 +141,7 @@ template <int DT>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
+  __shared__ __attribute__((aligned(16))) float stage[4][32 * kStageRS];  // epilogue, one per consumer wave
   const int lane = lane_id(), wave = wave_id();
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
   // XCD-local order: consecutive logical tiles (the N tiles of one M block)
@@ -329,25 +331,48 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
 
-  // epilogue: bias in fp32, one rounding to the output dtype
+  // Epilogue.  Each consumer wave stages its 64 x 128 fp32 tile through its
+  // own LDS region, 32 rows at a time; a lane then holds 4 consecutive columns
+  // of one row: bias added in fp32, one rounding, one 8-byte store (16 bytes
+  // for fp32 output), so every row's 128 columns leave as whole cache lines.
+  float *stg = stage[wave];
   const int64_t m0 = mb + wave * 64;
+  const int sc = (lane & 31) * 4, srow = lane >> 5;  // quad column, row parity of this lane
+  const int64_t n = n0 + sc;
+  const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
+  f32x4 bias4{0.f, 0.f, 0.f, 0.f};
+  if (a.bias && n_ok) {
+    const u32x2 bb = *reinterpret_cast<const u32x2 *>(a.bias + n);
+    bias4 = f32x4{f16_bits_to_f32(bb[0] & 0xffffu), f16_bits_to_f32(bb[0] >> 16), f16_bits_to_f32(bb[1] & 0xffffu),
+                  f16_bits_to_f32(bb[1] >> 16)};
+  }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t n = n0 + j * 16 + fr;
-    if (n >= O) continue;
-    const float bias = a.bias ? f16_bits_to_f32(a.bias[n]) : 0.0f;
+  for (int p = 0; p < 2; ++p) {
+    // D of tile (i, j): row 16i + 4(lane/16) + r, column 16j + lane%16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + i * 16 + (lane >> 4) * 4 + r;
-        if (row >= M) continue;
-        const float v = acc[i][j][r] + bias;
-        if (a.y_dt == kF32) reinterpret_cast<float *>(a.y)[row * O + n] = v;
-        else if (a.y_dt == kF16) reinterpret_cast<uint16_t *>(a.y)[row * O + n] = f32_to_f16_bits(v);
-        else reinterpret_cast<uint16_t *>(a.y)[row * O + n] = f32_to_bf16_bits(v);
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          stg[(16 * ii + (lane >> 4) * 4 + r) * kStageRS + 16 * j + fr] = acc[2 * p + ii][j][r];
+    wave_lds_sync();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int lr = 2 * rr + srow;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + lr * kStageRS + sc) + bias4;
+      const int64_t row = m0 + 32 * p + lr;
+      if (row < M && n_ok) {
+        if (a.y_dt == kF32) {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * O + n) = v;
+        } else {
+          const u32x2 o = a.y_dt == kF16 ? u32x2{pack2<kF16>(v[0], v[1]), pack2<kF16>(v[2], v[3])}
+                                         : u32x2{pack2<kBF16>(v[0], v[1]), pack2<kBF16>(v[2], v[3])};
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.y) + row * O + n) = o;
+        }
       }
     }
+    wave_lds_sync();  // this pass's reads are done before the next pass's writes
   }
 }
 

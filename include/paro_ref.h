@@ -106,6 +106,36 @@ int paro_ref_unpack(const paro_ref_layer *layer, uint8_t *q_out, uint8_t *z_out)
 /* W_deq as double [I][O]. */
 int paro_ref_dequant(const paro_ref_layer *layer, double *w_out, int n_threads);
 
+/*
+ * Offline side of the method (the step before the stored tensors exist):
+ *
+ * W_r = W . D . R row by row ("ParoQuant" wiki, Concepts / Activation and
+ * weight transforms; W is (out_features, in_features) = [O][I], the stored
+ * channel_scales are D^-1, so they divide W's input channels).  Uses the
+ * layer's I, O, G, krot, pairs, theta, channel_scales; w_r is double [O][I].
+ */
+int paro_ref_transform_weight(const paro_ref_layer *layer, const void *w, int w_dt, double *w_r,
+                              int n_threads);
+/*
+ * Group round-to-nearest quantization of w_r (double [O][I]), per output row
+ * n and group g of G input channels ("GPTQ, GPTAQ, and RTN" wiki, quantizer:
+ * q = clamp(round(x / scale) + zero, 0, maxq), x_hat = scale (q - zero),
+ * the observed range includes zero, symmetric ranges are +-max|x| with the
+ * midpoint zero, affine zeros are round(-xmin / scale), all-zero ranges get a
+ * finite sentinel range; "ParoQuant" wiki: four-bit codes, scales bounded to
+ * [1e-5, 1e5], symmetric codes -8..7 exported with zero point 8).  maxq = 15,
+ * rounding half to even, all decisions in double precision.
+ *   q_out     : uint8 [I][O] codes 0..15 (the layout paro_ref_unpack returns)
+ *   z_out     : uint8 [I/G][O] zero points
+ *   s_out     : fp16 bits [I/G][O], the scale rounded to nearest even
+ *   scale_out : double [I/G][O] unrounded scales, or NULL
+ */
+int paro_ref_quantize(int64_t O, int64_t I, int32_t group_size, const double *w_r, int sym,
+                      uint8_t *q_out, uint8_t *z_out, uint16_t *s_out, double *scale_out);
+/* AWQ pack of q [I][O] and z [I/G][O] into qweight [I][O/8] and qzeros
+ * [I/G][O/8], the inverse of paro_ref_unpack (O % 8 == 0). */
+int paro_ref_pack(int64_t I, int64_t O, int32_t group_size, const uint8_t *q, const uint8_t *z,
+                  int32_t *qweight, int32_t *qzeros);
 /* Y as double [tokens][O]. */
 int paro_ref_linear(const paro_ref_layer *layer, const void *x, int x_dt,
                     int64_t tokens, double *y_out, int n_threads);

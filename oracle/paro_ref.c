@@ -190,6 +190,43 @@ int paro_ref_check_pairs(const paro_ref_layer *L) {
 /* Channel scaling and the pairwise rotation.                                */
 /* ------------------------------------------------------------------------ */
 
+/* cos/sin of every angle, once (libm, double precision); NULL if out of memory */
+static double *angle_table(const paro_ref_layer *L) {
+  const int64_t I = L->in_features;
+  const int64_t nang = (int64_t)L->krot * (I / 2);
+  double *cs_tab = (double *)malloc(sizeof(double) * 2 * (size_t)(nang > 0 ? nang : 1));
+  if (!cs_tab) return NULL;
+  for (int64_t e = 0; e < nang; ++e) {
+    const double th = (double)L->theta[e];
+    cs_tab[2 * e] = cos(th);
+    cs_tab[2 * e + 1] = sin(th);
+  }
+  return cs_tab;
+}
+
+/* Rotation of one row in place: [P1] Concepts / Pairwise Givens rotations.
+ * Stages run in order t = 0..krot-1; within a stage each group's channels form
+ * disjoint pairs with group-local indices, so pairs are independent.  For a
+ * pair (a, b) with angle theta:
+ *     a' =  a cos(theta) + b sin(theta)
+ *     b' = -a sin(theta) + b cos(theta)                                      */
+static void rotate_row(const paro_ref_layer *L, const double *cs_tab, double *row) {
+  const int64_t I = L->in_features, G = group_of(L), ngroups = I / G;
+  for (int t = 0; t < L->krot; ++t) {
+    for (int64_t g = 0; g < ngroups; ++g) {
+      for (int64_t p = 0; p < G / 2; ++p) {
+        const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];
+        const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];
+        const int64_t ang = (int64_t)t * (I / 2) + g * (G / 2) + p;
+        const double c = cs_tab[2 * ang], s = cs_tab[2 * ang + 1];
+        const double a = row[i], b = row[j];
+        row[i] = a * c + b * s;
+        row[j] = -a * s + b * c;
+      }
+    }
+  }
+}
+
 int paro_ref_scale_rotate(const paro_ref_layer *L, const void *x, int x_dt,
                           int64_t tokens, double *x_r, int n_threads) {
   int rc = check_shape(L);
@@ -200,17 +237,9 @@ int paro_ref_scale_rotate(const paro_ref_layer *L, const void *x, int x_dt,
   if (!x || !x_r || !L->theta || !L->channel_scales) return PARO_REF_ERR_NULL;
   rc = paro_ref_check_pairs(L);
   if (rc) return rc;
-  const int64_t I = L->in_features, G = group_of(L), ngroups = I / G;
-
-  /* cos/sin of every angle, once (libm, double precision) */
-  const int64_t nang = (int64_t)L->krot * (I / 2);
-  double *cs_tab = (double *)malloc(sizeof(double) * 2 * (size_t)nang);
+  const int64_t I = L->in_features;
+  double *cs_tab = angle_table(L);
   if (!cs_tab) return PARO_REF_ERR_NOMEM;
-  for (int64_t e = 0; e < nang; ++e) {
-    const double th = (double)L->theta[e];
-    cs_tab[2 * e] = cos(th);
-    cs_tab[2 * e + 1] = sin(th);
-  }
 
 #pragma omp parallel for schedule(static) num_threads(paro_ref_threads(n_threads))
   for (int64_t m = 0; m < tokens; ++m) {
@@ -220,26 +249,8 @@ int paro_ref_scale_rotate(const paro_ref_layer *L, const void *x, int x_dt,
      * so they multiply the activations. */
     for (int64_t k = 0; k < I; ++k)
       row[k] = load_elem(x, x_dt, m * I + k) * (double)L->channel_scales[k];
-
-    /* Step 2, rotation: [P1] Concepts / Pairwise Givens rotations.  Stages
-     * run in order t = 0..krot-1; within a stage each group's channels form
-     * disjoint pairs with group-local indices, so pairs are independent.
-     * For a pair (a, b) with angle theta:
-     *     a' =  a cos(theta) + b sin(theta)
-     *     b' = -a sin(theta) + b cos(theta)                                */
-    for (int t = 0; t < L->krot; ++t) {
-      for (int64_t g = 0; g < ngroups; ++g) {
-        for (int64_t p = 0; p < G / 2; ++p) {
-          const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];
-          const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];
-          const int64_t ang = (int64_t)t * (I / 2) + g * (G / 2) + p;
-          const double c = cs_tab[2 * ang], s = cs_tab[2 * ang + 1];
-          const double a = row[i], b = row[j];
-          row[i] = a * c + b * s;
-          row[j] = -a * s + b * c;
-        }
-      }
-    }
+    /* Step 2, the staged rotation */
+    rotate_row(L, cs_tab, row);
   }
   free(cs_tab);
   return PARO_REF_OK;
@@ -297,6 +308,107 @@ int paro_ref_dequant(const paro_ref_layer *L, double *w_out, int n_threads) {
       w_out[k * O + n] = (double)(q - z) * s;
     }
   }
+  return PARO_REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Offline transform, group quantization and AWQ packing of a dense weight.  */
+/* ------------------------------------------------------------------------ */
+
+int paro_ref_transform_weight(const paro_ref_layer *L, const void *w, int w_dt, double *w_r, int n_threads) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (w_dt < PARO_REF_F16 || w_dt > PARO_REF_F64) return PARO_REF_ERR_DTYPE;
+  if (!w || !w_r || !L->theta || !L->channel_scales) return PARO_REF_ERR_NULL;
+  rc = paro_ref_check_pairs(L);
+  if (rc) return rc;
+  const int64_t I = L->in_features, O = L->out_features;
+  double *cs_tab = angle_table(L);
+  if (!cs_tab) return PARO_REF_ERR_NOMEM;
+
+#pragma omp parallel for schedule(static) num_threads(paro_ref_threads(n_threads))
+  for (int64_t n = 0; n < O; ++n) {
+    double *row = w_r + n * I;
+    /* [P1] Concepts / Activation and weight transforms: W_r = W D R for W in
+     * (out_features, in_features) order.  The stored channel_scales are D^-1,
+     * so they divide the weight's input channels (the activations are
+     * multiplied by them; the product X_r W_r^T is X W^T). */
+    for (int64_t k = 0; k < I; ++k) row[k] = load_elem(w, w_dt, n * I + k) / (double)L->channel_scales[k];
+    rotate_row(L, cs_tab, row);
+  }
+  free(cs_tab);
+  return PARO_REF_OK;
+}
+
+int paro_ref_quantize(int64_t O, int64_t I, int32_t group_size, const double *w_r, int sym,
+                      uint8_t *q_out, uint8_t *z_out, uint16_t *s_out, double *scale_out) {
+  if (O <= 0 || I <= 0) return PARO_REF_ERR_SHAPE;
+  const int64_t G = group_size == -1 ? I : group_size;
+  if (G <= 0 || I % G != 0) return PARO_REF_ERR_SHAPE;
+  if (!w_r || !q_out || !z_out || !s_out) return PARO_REF_ERR_NULL;
+  const double maxq = 15.0;  /* four bits */
+  for (int64_t n = 0; n < O; ++n) {
+    for (int64_t g = 0; g < I / G; ++g) {
+      const double *x = w_r + n * I + g * G;
+      /* [P4] quantizer parameter selection: the observed range includes zero */
+      double xmin = 0.0, xmax = 0.0;
+      for (int64_t e = 0; e < G; ++e) {
+        if (x[e] < xmin) xmin = x[e];
+        if (x[e] > xmax) xmax = x[e];
+      }
+      /* symmetric: the range is widened to +-max|x| where it reaches below zero */
+      if (sym) {
+        if (-xmin > xmax) xmax = -xmin;
+        if (xmin < 0.0) xmin = -xmax;
+      }
+      /* all-zero range: finite sentinel range */
+      if (xmin == 0.0 && xmax == 0.0) {
+        xmin = -1.0;
+        xmax = 1.0;
+      }
+      double scale = (xmax - xmin) / maxq;
+      /* [P1] quantizer scales are bounded to [1e-5, 1e5] */
+      if (scale < 1e-5) scale = 1e-5;
+      if (scale > 1e5) scale = 1e5;
+      /* midpoint zero for symmetric, rounded -xmin/scale for affine (ties to even) */
+      double zero = sym ? (maxq + 1.0) / 2.0 : rint(-xmin / scale);
+      if (zero < 0.0) zero = 0.0;
+      if (zero > maxq) zero = maxq;
+      z_out[g * O + n] = (uint8_t)zero;
+      s_out[g * O + n] = paro_ref_round_f16(scale);
+      if (scale_out) scale_out[g * O + n] = scale;
+      /* [P4] q = clamp(round(x / scale) + zero, 0, maxq), round half to even */
+      for (int64_t e = 0; e < G; ++e) {
+        double q = rint(x[e] / scale) + zero;
+        if (q < 0.0) q = 0.0;
+        if (q > maxq) q = maxq;
+        q_out[(g * G + e) * O + n] = (uint8_t)q;
+      }
+    }
+  }
+  return PARO_REF_OK;
+}
+
+int paro_ref_pack(int64_t I, int64_t O, int32_t group_size, const uint8_t *q, const uint8_t *z,
+                  int32_t *qweight, int32_t *qzeros) {
+  if (O <= 0 || I <= 0 || O % 8 != 0) return PARO_REF_ERR_SHAPE;
+  const int64_t G = group_size == -1 ? I : group_size;
+  if (G <= 0 || I % G != 0) return PARO_REF_ERR_SHAPE;
+  if (!q || !z || !qweight || !qzeros) return PARO_REF_ERR_NULL;
+  /* [P1] Stored tensors: AWQ layout, 8 columns per int32 word; column 8w+j
+   * goes to bits 4*SLOT_OF_COL[j] (the order paro_ref_unpack reads). */
+  for (int64_t k = 0; k < I; ++k)
+    for (int64_t w = 0; w < O / 8; ++w) {
+      uint32_t word = 0;
+      for (int j = 0; j < 8; ++j) word |= (uint32_t)(q[k * O + 8 * w + j] & 0xfu) << (4 * SLOT_OF_COL[j]);
+      qweight[k * (O / 8) + w] = (int32_t)word;
+    }
+  for (int64_t g = 0; g < I / G; ++g)
+    for (int64_t w = 0; w < O / 8; ++w) {
+      uint32_t word = 0;
+      for (int j = 0; j < 8; ++j) word |= (uint32_t)(z[g * O + 8 * w + j] & 0xfu) << (4 * SLOT_OF_COL[j]);
+      qzeros[g * (O / 8) + w] = (int32_t)word;
+    }
   return PARO_REF_OK;
 }
 

@@ -70,9 +70,13 @@ def load(path: str | None = None):
     lib.paro_ref_linear.argtypes = [P, P, I32, I64, P, I32]
     lib.paro_linear_ref_check.argtypes = [P, P, I32, I64, P, I32, P, D, I32, P, P]
     lib.paro_ref_threads.argtypes = [I32]
+    lib.paro_ref_transform_weight.argtypes = [P, P, I32, P, I32]
+    lib.paro_ref_quantize.argtypes = [I64, I64, ctypes.c_int32, P, I32, P, P, P, P]
+    lib.paro_ref_pack.argtypes = [I64, I64, ctypes.c_int32, P, P, P, P]
     for name in ("paro_ref_round_array", "paro_ref_check_pairs", "paro_ref_scale_rotate",
                  "paro_ref_unpack", "paro_ref_dequant", "paro_ref_linear",
-                 "paro_linear_ref_check", "paro_ref_threads"):
+                 "paro_linear_ref_check", "paro_ref_threads", "paro_ref_transform_weight",
+                 "paro_ref_quantize", "paro_ref_pack"):
         getattr(lib, name).restype = I32
     _lib, _lib_path = lib, path
     return lib
@@ -170,3 +174,41 @@ def paro_linear_ref_check(layer, x, x_dt: int, y=None, y_dt: int = F32,
                                       _ptr(y), y_dt, _ptr(yref), rel_tol, n_threads,
                                       ctypes.byref(err), ctypes.byref(ref))
     return rc, err.value, ref.value, yref
+
+
+def transform_weight(layer, w, w_dt: int, n_threads: int = 0) -> np.ndarray:
+    """W_r = W . D . R as double [O][I] (w: [O][I] bits of w_dt, or float64 for F64)."""
+    O, I = layer.out_features, layer.in_features
+    w = np.ascontiguousarray(w)
+    assert w.shape == (O, I)
+    out = np.empty((O, I), dtype=np.float64)
+    L = ref_layer(layer)
+    _check(load().paro_ref_transform_weight(ctypes.byref(L), _ptr(w), w_dt, _ptr(out), n_threads),
+           "paro_ref_transform_weight")
+    return out
+
+
+def quantize(w_r, group_size: int, sym: bool):
+    """Group RTN of w_r [O][I]: (q [I][O] uint8, z [I/G][O] uint8, s16 [I/G][O] uint16, scale [I/G][O])."""
+    w_r = np.ascontiguousarray(w_r, dtype=np.float64)
+    O, I = w_r.shape
+    G = I if group_size == -1 else group_size
+    q = np.empty((I, O), dtype=np.uint8)
+    z = np.empty((I // G, O), dtype=np.uint8)
+    s16 = np.empty((I // G, O), dtype=np.uint16)
+    scale = np.empty((I // G, O), dtype=np.float64)
+    _check(load().paro_ref_quantize(O, I, group_size, _ptr(w_r), int(bool(sym)), _ptr(q), _ptr(z), _ptr(s16),
+                                    _ptr(scale)), "paro_ref_quantize")
+    return q, z, s16, scale
+
+
+def pack(q, z, group_size: int):
+    """AWQ pack of q [I][O], z [I/G][O] -> (qweight int32 [I][O/8], qzeros int32 [I/G][O/8])."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    I, O = q.shape
+    G = I if group_size == -1 else group_size
+    qw = np.empty((I, O // 8), dtype=np.int32)
+    qz = np.empty((I // G, O // 8), dtype=np.int32)
+    _check(load().paro_ref_pack(I, O, group_size, _ptr(q), _ptr(z), _ptr(qw), _ptr(qz)), "paro_ref_pack")
+    return qw, qz

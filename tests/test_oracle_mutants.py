@@ -23,11 +23,11 @@ MUTANTS = {
     "theta_group_offset": ("g * (G / 2) + p;", "p;"),
     "pair_members_swapped": (
         "const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];\n"
-        "          const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];",
+        "        const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];",
         "const int64_t i = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p + 1];\n"
-        "          const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];"),
-    "stage_order_reversed": ("for (int t = 0; t < L->krot; ++t) {\n      for (int64_t g = 0; g < ngroups",
-                             "for (int t = L->krot - 1; t >= 0; --t) {\n      for (int64_t g = 0; g < ngroups"),
+        "        const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];"),
+    "stage_order_reversed": ("for (int t = 0; t < L->krot; ++t) {\n    for (int64_t g = 0; g < ngroups",
+                             "for (int t = L->krot - 1; t >= 0; --t) {\n    for (int64_t g = 0; g < ngroups"),
     "channel_scale_divides": ("* (double)L->channel_scales[k];", "/ (double)L->channel_scales[k];"),
     "awq_order_sequential": ("{0, 4, 1, 5, 2, 6, 3, 7}", "{0, 1, 2, 3, 4, 5, 6, 7}"),
     "zero_not_subtracted": ("(double)(q - z) * s;", "(double)(q) * s;"),
@@ -37,6 +37,17 @@ MUTANTS = {
     "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "rounding_ties_away": ("return rint(a / quantum) * quantum;", "return round(a / quantum) * quantum;"),
     "bf16_fraction_bits": ("ldexp((double)(128 + f), e - 134)", "ldexp((double)(128 + f), e - 133)"),
+    "quant_zero_outside_range": ("double xmin = 0.0, xmax = 0.0;", "double xmin = x[0], xmax = x[0];"),
+    "quant_ties_away": ("double q = rint(x[e] / scale) + zero;", "double q = round(x[e] / scale) + zero;"),
+    "quant_sym_zero": ("(maxq + 1.0) / 2.0", "maxq / 2.0"),
+    "quant_steps_16": ("double scale = (xmax - xmin) / maxq;", "double scale = (xmax - xmin) / (maxq + 1.0);"),
+    "quant_affine_zero_sign": ("rint(-xmin / scale)", "rint(xmin / scale)"),
+    "quant_sym_one_sided": ("if (xmin < 0.0) xmin = -xmax;", ""),
+    "quant_no_sentinel": ("xmin = -1.0;\n        xmax = 1.0;", "xmin = 0.0;\n        xmax = 0.0;"),
+    "quant_no_lower_bound": ("if (scale < 1e-5) scale = 1e-5;", ""),
+    "transform_multiplies": ("/ (double)L->channel_scales[k];", "* (double)L->channel_scales[k];"),
+    "pack_sequential_slots": ("<< (4 * SLOT_OF_COL[j]);\n      qweight", "<< (4 * j);\n      qweight"),
+    "pack_zeros_sequential": ("<< (4 * SLOT_OF_COL[j]);\n      qzeros", "<< (4 * j);\n      qzeros"),
 }
 
 
@@ -47,6 +58,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
         src = f.read()
     assert src.count(find) == 1, f"mutation anchor for {name} not unique/present"
     mutant_src = tmp_path / "paro_ref_mutant.c"
+    assert find in src, f"mutant {name}: its target text is not in the oracle"
     mutant_src.write_text(src.replace(find, repl))
     lib = tmp_path / "libparo_ref_mutant.so"
     ref.build(str(lib), str(mutant_src))

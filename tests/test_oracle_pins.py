@@ -431,3 +431,126 @@ def test_zero_tokens_and_bad_shapes():
     odd = synth.Layer(256, 256, 127, 8, L.pairs, L.theta, L.channel_scales, L.qweight,
                       L.qzeros, L.scales, None)
     assert ref.paro_linear_ref_check(odd, x, ref.F16)[0] == ref.ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# Offline transform, group quantization and AWQ packing
+# ---------------------------------------------------------------------------
+
+def _frac(expr):
+    return float(eval(expr, {}))
+
+
+def test_golden_quantize_worked_examples():
+    fx = golden("quantize_worked.json")
+    for c in fx["cases"]:
+        x = np.asarray([c["x"]], dtype=np.float64)
+        q, z, s16, scale = ref.quantize(x, 4, c["sym"])
+        assert q[:, 0].tolist() == c["q"], c
+        assert int(z[0, 0]) == c["zero"], c
+        assert scale[0, 0] == pytest.approx(_frac(c["scale"]), rel=1e-15), c
+        assert int(s16[0, 0]) == int(np.float16(_frac(c["scale"])).view(np.uint16)), c
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_quantize_is_round_to_nearest_on_its_grid(sym):
+    """Every value lies within half a step of its dequantized code (the range
+    fit makes clamping cost at most that half step), and grid points map to
+    themselves."""
+    rng = np.random.default_rng(11)
+    O, I, G = 24, 256, 128
+    w = rng.normal(0, 0.03, size=(O, I)) * rng.uniform(0.2, 3.0, size=(O, 1))
+    q, z, _, scale = ref.quantize(w, G, sym)
+    for g in range(I // G):
+        s = scale[g][None, :]                                    # [1][O]
+        xh = s * (q[g * G:(g + 1) * G].astype(np.float64) - z[g][None, :])
+        err = np.abs(xh - w[:, g * G:(g + 1) * G].T)
+        assert (err <= 0.5 * s * (1 + 1e-12)).all()
+    # re-quantizing the dequantized grid points reproduces the codes when the
+    # range is unchanged (affine: the extremes are grid points only where hit)
+    if sym:
+        xh_full = np.concatenate([(scale[g][None, :] * (q[g * G:(g + 1) * G].astype(np.float64) - z[g][None, :])).T
+                                  for g in range(I // G)], axis=1)
+        q2, z2, _, s2 = ref.quantize(xh_full, G, sym)
+        same = np.isclose(s2, scale, rtol=1e-12)
+        for g in range(I // G):
+            cols = same[g]
+            assert (q2[g * G:(g + 1) * G, cols] == q[g * G:(g + 1) * G, cols]).all()
+
+
+def test_pack_is_the_inverse_of_unpack():
+    rng = np.random.default_rng(12)
+    I, O, G = 256, 48, 128
+    q = rng.integers(0, 16, size=(I, O)).astype(np.uint8)
+    z = rng.integers(0, 16, size=(I // G, O)).astype(np.uint8)
+    qw, qz = ref.pack(q, z, G)
+    L = synth.Layer(I, O, G, 1, np.zeros((1, I), np.int16), np.zeros((1, I // 2), np.float32),
+                    np.ones(I, np.float32), qw, qz, np.zeros((I // G, O), np.uint16), None)
+    q2, z2 = ref.unpack(L)
+    assert np.array_equal(q2, q) and np.array_equal(z2, z)
+    fx = golden("awq_words.json")
+    for c in fx["cases"]:
+        qq = np.zeros((128, 8), np.uint8)
+        qq[0] = c["columns"]
+        w, _ = ref.pack(qq, np.zeros((1, 8), np.uint8), 128)
+        assert int(w[0, 0]) & 0xFFFFFFFF == int(c["word_hex"], 16)
+
+
+def test_transform_weight_identity_and_channel_division():
+    rng = np.random.default_rng(13)
+    I, O, G, krot = 256, 16, 128, 3
+    w = rng.normal(size=(O, I))
+    pairs = np.stack([np.concatenate([rng.permutation(G) for _ in range(I // G)]) for _ in range(krot)])
+    cs = rng.uniform(0.5, 2.0, size=I)
+    L = tiny_layer(I, G, krot, pairs, np.zeros((krot, I // 2)), np.ones(I), O=O)
+    assert np.array_equal(ref.transform_weight(L, w, ref.F64), w)     # identity state
+    L = tiny_layer(I, G, krot, pairs, np.zeros((krot, I // 2)), cs, O=O)
+    np.testing.assert_allclose(ref.transform_weight(L, w, ref.F64), w / cs.astype(np.float32), rtol=1e-15)
+
+
+def test_transform_weight_keeps_the_product():
+    """X_r W_r^T = X W^T: the activations are multiplied by the stored scales,
+    the weight divided, both rotated by the same orthogonal R."""
+    rng = np.random.default_rng(14)
+    I, O, G, krot, M = 256, 24, 64, 5, 7
+    pairs = np.stack([np.concatenate([rng.permutation(G) for _ in range(I // G)]) for _ in range(krot)])
+    theta = rng.uniform(-np.pi / 4, np.pi / 4, size=(krot, I // 2))
+    cs = rng.uniform(0.5, 2.0, size=I)
+    L = tiny_layer(I, G, krot, pairs, theta, cs, O=O)
+    x = rng.normal(size=(M, I))
+    w = rng.normal(size=(O, I))
+    xr = ref.scale_rotate(L, x, ref.F64)
+    wr = ref.transform_weight(L, w, ref.F64)
+    lhs, rhs = xr @ wr.T, x @ w.T
+    assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(rhs).max()
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_quantized_layer_reproduces_dense_linear_within_rounding(sym):
+    """Transform, quantize and pack a dense weight, then run the oracle linear:
+    |Y - (X W^T + b)| <= sum_k |x_r[k]| * scale_k / 2 (each weight is off by at
+    most half a step, the rotation is exact up to fp64)."""
+    rng = np.random.default_rng(15 + sym)
+    I, O, G, krot, M = 256, 32, 128, 4, 5
+    pairs = np.stack([np.concatenate([rng.permutation(G) for _ in range(I // G)]) for _ in range(krot)])
+    theta = rng.uniform(-np.pi / 4, np.pi / 4, size=(krot, I // 2)).astype(np.float32)
+    cs = rng.uniform(0.5, 2.0, size=I).astype(np.float32)
+    w = rng.normal(0, 0.02, size=(O, I))
+    L0 = tiny_layer(I, G, krot, pairs, theta, cs, O=O)
+    wr = ref.transform_weight(L0, w, ref.F64)
+    q, z, s16, scale = ref.quantize(wr, G, sym)
+    qw, qz = ref.pack(q, z, G)
+    # the layer stores fp16 scales; re-quantize against them so codes and
+    # stored scales are consistent (a step of the fp16 scale differs from the
+    # exact one by at most 2^-11 relative)
+    s_eff = np.asarray([[ref.f16_to_double(h) for h in row] for row in s16])
+    bias = synth.f16_bits(rng.normal(0, 0.01, size=O))
+    L = synth.Layer(I, O, G, krot, L0.pairs, L0.theta, L0.channel_scales, qw, qz, s16, bias)
+    x = rng.normal(size=(M, I))
+    y = ref.linear(L, x, ref.F64)
+    b = np.asarray([ref.f16_to_double(h) for h in bias])
+    xr = ref.scale_rotate(L, x, ref.F64)
+    step = np.repeat(np.maximum(s_eff, scale), G, axis=0)               # [I][O]
+    extra = np.repeat(np.abs(s_eff - scale), G, axis=0) * 15            # scale rounding
+    bound = np.abs(xr) @ (0.5 * step + extra)
+    assert (np.abs(y - (x @ w.T + b)) <= bound * (1 + 1e-9) + 1e-12).all()

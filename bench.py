@@ -81,6 +81,79 @@ def load_traffic(workload, kernel_hash):
     return round((rec["fetch_kib"] * cal["fetch_factor"] + rec["write_kib"] * cal["write_factor"]) * 1024)
 
 
+QUANT_METRIC = "ParoQuant offline transform + quantize + pack: dense weight GB/s, % of HBM roofline"
+KERNEL_FILES["quantize"] = ("quantize.hip", "common.hpp")
+
+
+def bench_quantize(args, paro, synth, np, torch, dev):
+    """Time paro_w4_quantize_pack on the workload's first layer shape (weight
+    in the workload's activation dtype, symmetric codes as the public
+    configuration uses), rotating through >= 512 MB of distinct weights."""
+    spec = synth.WORKLOADS[args.workload]
+    lname, I, O = spec["layers"][0]
+    dt = spec["act"]
+    tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
+    host = synth.make_layer(args.workload, 0, I, O)
+    w = synth.make_w(args.workload, 0, O, I, dt)
+    w_bytes = O * I * 2
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // w_bytes)))
+    log(f"quantize: workload {args.workload} layer {lname} ({O} x {I}), {nsets} weight copies")
+    D = paro.DeviceLayer(host, device=dev)
+    wds = [torch.from_numpy(w.view(np.int16)).to(dev).view(tdt) for _ in range(nsets)]
+    qw = torch.empty((I, O // 8), dtype=torch.int32, device=dev)
+    qz = torch.empty((I // 128, O // 8), dtype=torch.int32, device=dev)
+    sc = torch.empty((I // 128, O), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    step = lambda i: paro.paro_w4_quantize_pack(D, wds[i % nsets], True, qw, qz, sc, stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    weight_b, rot_b = layer_bytes(I, O, host.krot, bias=False)
+    alg = w_bytes + weight_b + rot_b           # W read once; codes, zeros, scales written; rotation read
+    value = w_bytes / (us * 1e-6) / 1e9
+    ach = alg / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        rows = 64
+        sub = synth.Layer(I, rows, 128, host.krot, host.pairs, host.theta, host.channel_scales,
+                          np.zeros((I, rows // 8), np.int32), np.zeros((I // 128, rows // 8), np.int32),
+                          np.zeros((I // 128, rows), np.uint16), None)
+        n, t_start = 0, time.perf_counter()
+        while True:
+            wr = ref.transform_weight(sub, np.ascontiguousarray(w[:rows]), dt)
+            q, z, s16, _ = ref.quantize(wr, 128, True)
+            ref.pack(q, z, 128)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = {"value": rows * I * 2 / (el / n) / 1e9, "unit": "GB/s", "cores": ref.threads(0), "kind": "oracle",
+               "sample": f"{n} oracle transform+quantize+pack call(s) on {rows} of {O} output rows of "
+                         f"'{lname}', {el:.1f} s"}
+    out = {
+        "metric": QUANT_METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{lname}-weight-{O}x{I}-{'f16' if dt == synth.F16 else 'bf16'}-sym",
+                   "group_size": 128, "krot": host.krot, "weight_copies": nsets, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"quantize-{args.workload}", kernel_source_hash("quantize")),
+                     "kernel": "quantize_pack_kernel",
+                     "avg_launch_us": round(us, 3)},
+        "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("quantize"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +164,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
+    ap.add_argument("--op", choices=("linear", "quantize"), default="linear",
+                    help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
+                         "qzeros, scales) transform of the workload's first layer")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark: copy BYTES between two device buffers --steps times "
                          "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -121,6 +197,9 @@ def main():
     paro.load()  # raises if libparo.so is missing: there is no fallback
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.op == "quantize":
+        bench_quantize(args, paro, synth, np, torch, dev)
+        return
     spec = synth.WORKLOADS[args.workload]
     M, act = spec["tokens"], spec["act"]
     tdt = torch.float16 if act == synth.F16 else torch.bfloat16

@@ -226,6 +226,31 @@ int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *hl, const vo
 int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dtype x_dt,
                             int64_t tokens, void *y, paro_dtype y_dt, void *stream);
 
+/*
+ * The offline step before the stored tensors exist: transform a dense weight
+ * into the rotated domain, quantize it group-wise to four bits and pack it
+ * ("ParoQuant" wiki, Concepts / Activation and weight transforms: W_r = W D R,
+ * with the stored channel_scales = D^-1 dividing W's input channels;
+ * Straight-through estimation: four-bit codes, symmetric codes -8..7 exported
+ * with zero point 8, quantizer scales bounded to [1e-5, 1e5]; "GPTQ, GPTAQ,
+ * and RTN" wiki, quantizer: q = clamp(round(x / scale) + zero, 0, 15), range
+ * including zero, symmetric midpoint zero, affine zero = round(-xmin/scale),
+ * finite sentinel range for all-zero groups; Stored tensors: AWQ layout).
+ * Per output row n and group g of 128 input channels, all decisions in fp32
+ * with correctly rounded division, rounding half to even.
+ *   w        : [O][I] w_dt in {F16, BF16, F32}, row-major (out_features
+ *              first), 4-byte aligned (8 for F32).
+ *   symmetric: nonzero = symmetric (zero point 8), 0 = affine.
+ *   qweight  : [I][O/8] int32 AWQ words, qzeros [I/128][O/8] int32, scales
+ *              [I/128][O] fp16 bits; caller-owned device memory that must not
+ *              overlap w or each other.
+ * Uses layer->in_features, out_features, group_size (128), krot, pairs, theta,
+ * channel_scales; layer->qweight/qzeros/scales/bias are ignored.  The outputs
+ * plus the layer's rotation tensors form a layer for paro_w4a16_linear.
+ */
+int paro_w4_quantize_pack(const paro_w4_layer *layer, const void *w, paro_dtype w_dt, int symmetric,
+                          int32_t *qweight, int32_t *qzeros, uint16_t *scales, void *stream);
+
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,
                                          paro_dtype x_dt, paro_path path);

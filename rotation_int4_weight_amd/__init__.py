@@ -12,11 +12,13 @@ from ._lib import (BF16, EXPORTS, F16, F32, PATH_AUTO, PATH_DECODE_FUSED, PATH_D
                    paro_validate_layer, paro_w4_unpack_dequant, paro_w4a16_linear,
                    paro_w4a16_linear_choose_path, paro_w4a16_linear_prerotated,
                    paro_w4a16_linear_workspace_bytes, paro_tiled_bytes, paro_rotation_matrix_bytes,
-                   paro_rotation_matrix, paro_scale_rotate_tiled, paro_w4a16_linear_tiled)
+                   paro_rotation_matrix, paro_scale_rotate_tiled, paro_w4a16_linear_tiled,
+                   paro_w4_quantize_pack)
 
 __all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "PATH_DECODE_SPLIT",
            "PATH_PREFILL", "DeviceLayer", "ParoError", "load", "make_workspace", "paro_abi_version",
            "paro_last_error", "paro_scale_rotate", "paro_validate_layer", "paro_w4_unpack_dequant",
            "paro_w4a16_linear", "paro_w4a16_linear_choose_path", "paro_w4a16_linear_prerotated",
            "paro_w4a16_linear_workspace_bytes", "paro_tiled_bytes", "paro_rotation_matrix_bytes",
-           "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled"]
+           "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
+           "paro_w4_quantize_pack"]

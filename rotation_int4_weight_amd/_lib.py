@@ -20,6 +20,7 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+           "paro_w4_quantize_pack",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
            "paro_w4a16_linear_workspace_bytes",
@@ -62,6 +63,7 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear_prerotated.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
+    lib.paro_w4_quantize_pack.argtypes = [P, P, I32, I32, P, P, P, P]
     lib.paro_rotation_matrix_bytes.argtypes = [P]
     lib.paro_rotation_matrix_bytes.restype = SZ
     lib.paro_rotation_matrix.argtypes = [P, I32, P, P]
@@ -76,6 +78,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+                 "paro_w4_quantize_pack",
                  "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
@@ -214,6 +217,13 @@ def paro_w4a16_linear_prerotated(layer: DeviceLayer, x_r, y, workspace=None, str
 def paro_tiled_bytes(layer: DeviceLayer, tokens: int) -> int:
     """Bytes of an X_r buffer in the prefill GEMM's tiled layout."""
     return int(load().paro_tiled_bytes(layer.ref, tokens))
+
+
+def paro_w4_quantize_pack(layer: DeviceLayer, w, symmetric: bool, qweight, qzeros, scales, stream=None) -> None:
+    """w: (O, I) fp16/bf16/fp32 device tensor; qweight int32 (I, O/8), qzeros int32 (I/128, O/8),
+    scales fp16/int16 view (I/128, O)."""
+    _check(load().paro_w4_quantize_pack(layer.ref, _ptr(w), _dt(w), int(bool(symmetric)), _ptr(qweight),
+                                        _ptr(qzeros), _ptr(scales), _stream_handle(stream)), "paro_w4_quantize_pack")
 
 
 def paro_rotation_matrix_bytes(layer: DeviceLayer) -> int:

@@ -78,4 +78,11 @@ hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64
 // Prefill: MFMA GEMM over rotated activations in the tiled layout.
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStream_t st);
 
+// W_r = W D R, group quantization and AWQ packing (the offline step):
+// w [O][I] (F16, BF16 or F32); qweight [I][O/8], qzeros [I/128][O/8],
+// scales [I/128][O] fp16.
+hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, int64_t I, const int16_t *pairs,
+                                const float *theta, const float *cs, int krot, int32_t *qweight, int32_t *qzeros,
+                                uint16_t *scales, hipStream_t st);
+
 }  // namespace paro

@@ -291,6 +291,33 @@ int paro_w4_unpack_dequant(const paro_w4_layer *L, uint8_t *q_out, uint8_t *z_ou
   return ok();
 }
 
+int paro_w4_quantize_pack(const paro_w4_layer *L, const void *w, paro_dtype w_dt, int symmetric, int32_t *qweight,
+                          int32_t *qzeros, uint16_t *scales, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (rc) return rc;
+  if (!act_dtype(w_dt) && w_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "w dtype %d invalid", (int)w_dt);
+  if (!w || !qweight || !qzeros || !scales) return fail(PARO_ERR_NULL, "w, qweight, qzeros and scales are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  if (!aligned(w, w_dt == PARO_F32 ? 8 : 4) || !aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2))
+    return fail(PARO_ERR_ALIGN, "w must be 4-byte (8 for F32) and qweight/qzeros/scales 4/4/2-byte aligned");
+  const int64_t I = L->in_features, O = L->out_features;
+  const size_t wb = (size_t)I * O * (w_dt == PARO_F32 ? 4 : 2);
+  const char *ws = (const char *)w;
+  const char *outs[3] = {(const char *)qweight, (const char *)qzeros, (const char *)scales};
+  const size_t outb[3] = {(size_t)I * O / 2, (size_t)(I / 128) * O / 2, (size_t)(I / 128) * O * 2};
+  for (int i = 0; i < 3; ++i) {
+    if (ws < outs[i] + outb[i] && outs[i] < ws + wb) return fail(PARO_ERR_SHAPE, "an output overlaps w");
+    for (int j = 0; j < i; ++j)
+      if (outs[j] < outs[i] + outb[i] && outs[i] < outs[j] + outb[j])
+        return fail(PARO_ERR_SHAPE, "qweight, qzeros and scales must not overlap");
+  }
+  hipError_t e = paro::launch_quantize_pack(w, (int)w_dt, symmetric != 0, O, I, L->pairs, L->theta,
+                                            L->channel_scales, L->krot, qweight, qzeros, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
+  return ok();
+}
+
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {
   (void)L;
   return auto_path(tokens);

@@ -91,6 +91,8 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
 // 32b + 8(l/16) .. +7 in order: one 16-byte piece of the tiled layout.
 constexpr int64_t kRotMatHalves = 2 * kG * kG;  // per group
 
+constexpr int kBuildRows = 16;  // rows of H_T / L_T per one-wave workgroup
+
 __device__ __forceinline__ int channel_of_mfma_row(int r) {
   return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
@@ -102,7 +104,7 @@ template <int XDT>
 __global__ void __launch_bounds__(64)
 rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__restrict__ theta,
                  const float *__restrict__ cscale, int krot, uint16_t *__restrict__ hl) {
-  constexpr int RW = 16;
+  constexpr int RW = kBuildRows;
   __shared__ float xs[RW * kRotRS];
   const int lane = lane_id();
   const int64_t g = blockIdx.x;
@@ -275,7 +277,7 @@ size_t rot_mat_bytes(int64_t I) { return (size_t)(I / kG) * (size_t)kRotMatHalve
 
 hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
                             int krot, uint16_t *hl, hipStream_t st) {
-  const dim3 grid((unsigned)(I / kG), kG / 16);
+  const dim3 grid((unsigned)(I / kG), kG / kBuildRows);
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, hl);
   else

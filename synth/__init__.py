@@ -23,6 +23,8 @@ for Llama-3-8B-shaped layers, since no trained weights or datasets are used):
   q, z       integers 0..15, (I, O) and (I/G, O), AWQ-packed into int32.
   scales     uniform(0.005, 0.02), (I/G, O), fp16.
   bias       N(0, 0.01), (O,), fp16.
+  w          (for the offline quantizer) a dense weight (O, I): N(0, 0.02)
+             times a per-row factor uniform(0.5, 2), fp16/bf16/fp32.
 """
 from __future__ import annotations
 
@@ -35,7 +37,7 @@ import numpy as np
 AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 
 TENSOR_IDS = {"x": 0, "outliers": 1, "pairs": 2, "theta": 3, "cs": 4,
-              "q": 5, "z": 6, "scales": 7, "bias": 8}
+              "q": 5, "z": 6, "scales": 7, "bias": 8, "w": 9, "w_rows": 10}
 
 F16, BF16, F32 = 0, 1, 2  # dtype codes shared by both C-ABIs' conventions
 
@@ -150,6 +152,22 @@ def make_x(workload: int, layer: int, tokens: int, in_features: int, act: int,
     if act == F32:
         return x.astype(np.float32)
     raise ValueError("unknown activation dtype code")
+
+
+def make_w(workload: int, layer: int, out_features: int, in_features: int, dt: int,
+           base: int = 0) -> np.ndarray:
+    """A dense weight (out_features, in_features) for the offline quantizer:
+    N(0, 0.02) scaled per output row by uniform[0.5, 2], as fp16/bf16 bits
+    (uint16) or fp32."""
+    w = rng_for(workload, layer, "w", base).normal(0.0, 0.02, size=(out_features, in_features))
+    w *= rng_for(workload, layer, "w_rows", base).uniform(0.5, 2.0, size=(out_features, 1))
+    if dt == F16:
+        return f16_bits(w)
+    if dt == BF16:
+        return f32_to_bf16_bits(w.astype(np.float32))
+    if dt == F32:
+        return w.astype(np.float32)
+    raise ValueError("unknown weight dtype code")
 
 
 def workload_layers(workload: int, **kw):

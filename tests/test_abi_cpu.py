@@ -217,3 +217,24 @@ def test_tiled_entry_point_argument_checks():
     assert lin(L=fake_layer(G=64)) == 5
     assert lin(tokens=0, xt=0, y=0) == 0
     assert lin(L=fake_layer(pairs=0, theta=0, channel_scales=0)) != 1  # rotation tensors unused
+
+
+@needs_no_gpu
+def test_quantize_pack_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(I=256, O=64)
+    qz_off = 256 * 64 // 2            # qweight bytes
+    sc_off = qz_off + 2 * 64 // 2     # + qzeros bytes
+    call = lambda w=FAKE * 8, dt=0, qw=FAKE, qz=FAKE + qz_off, sc=FAKE + sc_off, L=L: lib.paro_w4_quantize_pack(
+        ctypes.byref(L), w, dt, 1, qw, qz, sc, None)
+    assert call(dt=3) == 3                        # no such dtype
+    assert call(w=0) == 1
+    assert call(qz=0) == 1
+    assert call(w=FAKE * 8 + 2) == 4              # 16-bit weights: 4-byte aligned
+    assert call(w=FAKE * 8 + 4, dt=2) == 4        # fp32 weights: 8-byte aligned
+    assert call(qw=FAKE + 2) == 4
+    assert call(sc=FAKE + sc_off + 1) == 4
+    assert call(w=FAKE) == 2                      # w overlaps qweight
+    assert call(qz=FAKE + 64) == 2                # qzeros inside qweight
+    assert call(L=fake_layer(I=256, O=64, G=64)) == 5
+    assert call(L=fake_layer(I=256, O=64, pairs=0)) == 1

@@ -107,6 +107,19 @@ int paro_ref_unpack(const paro_ref_layer *layer, uint8_t *q_out, uint8_t *z_out)
 int paro_ref_dequant(const paro_ref_layer *layer, double *w_out, int n_threads);
 
 /*
+ * Backward of the scaling and rotation for a loss L with dL/dx_r = g (double
+ * [tokens][I]), the calibration step of the method ("ParoQuant" wiki,
+ * Straight-through estimation: optimization updates weights, angles and
+ * channel scales; the pair formula of Concepts / Pairwise Givens rotations,
+ * differentiated by the chain rule):
+ *   gx     : double [tokens][I], dL/dx
+ *   gtheta : double [krot][I/2], dL/dtheta summed over the tokens
+ *   gcs    : double [I], dL/d(channel_scales) summed over the tokens
+ * The forward states are kept row by row and walked back in stage order.
+ */
+int paro_ref_scale_rotate_backward(const paro_ref_layer *layer, const void *x, int x_dt, const double *g,
+                                   int64_t tokens, double *gx, double *gtheta, double *gcs, int n_threads);
+/*
  * Offline side of the method (the step before the stored tensors exist):
  *
  * W_r = W . D . R row by row ("ParoQuant" wiki, Concepts / Activation and

@@ -71,12 +71,13 @@ def load(path: str | None = None):
     lib.paro_linear_ref_check.argtypes = [P, P, I32, I64, P, I32, P, D, I32, P, P]
     lib.paro_ref_threads.argtypes = [I32]
     lib.paro_ref_transform_weight.argtypes = [P, P, I32, P, I32]
+    lib.paro_ref_scale_rotate_backward.argtypes = [P, P, I32, P, I64, P, P, P, I32]
     lib.paro_ref_quantize.argtypes = [I64, I64, ctypes.c_int32, P, I32, P, P, P, P]
     lib.paro_ref_pack.argtypes = [I64, I64, ctypes.c_int32, P, P, P, P]
     for name in ("paro_ref_round_array", "paro_ref_check_pairs", "paro_ref_scale_rotate",
                  "paro_ref_unpack", "paro_ref_dequant", "paro_ref_linear",
                  "paro_linear_ref_check", "paro_ref_threads", "paro_ref_transform_weight",
-                 "paro_ref_quantize", "paro_ref_pack"):
+                 "paro_ref_quantize", "paro_ref_pack", "paro_ref_scale_rotate_backward"):
         getattr(lib, name).restype = I32
     _lib, _lib_path = lib, path
     return lib
@@ -212,3 +213,17 @@ def pack(q, z, group_size: int):
     qz = np.empty((I // G, O // 8), dtype=np.int32)
     _check(load().paro_ref_pack(I, O, group_size, _ptr(q), _ptr(z), _ptr(qw), _ptr(qz)), "paro_ref_pack")
     return qw, qz
+
+
+def scale_rotate_backward(layer, x, x_dt: int, g, n_threads: int = 0):
+    """(gx [M][I], gtheta [krot][I/2], gcs [I]) for dL/dx_r = g (double [M][I])."""
+    x = np.ascontiguousarray(x)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    M, I = g.shape
+    gx = np.empty((M, I), dtype=np.float64)
+    gth = np.empty((layer.krot, I // 2), dtype=np.float64)
+    gcs = np.empty(I, dtype=np.float64)
+    L = ref_layer(layer)
+    _check(load().paro_ref_scale_rotate_backward(ctypes.byref(L), _ptr(x), x_dt, _ptr(g), M, _ptr(gx), _ptr(gth),
+                                                 _ptr(gcs), n_threads), "paro_ref_scale_rotate_backward")
+    return gx, gth, gcs

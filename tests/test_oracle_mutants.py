@@ -47,6 +47,12 @@ MUTANTS = {
     "quant_no_lower_bound": ("if (scale < 1e-5) scale = 1e-5;", ""),
     "transform_multiplies": ("/ (double)L->channel_scales[k];", "* (double)L->channel_scales[k];"),
     "pack_sequential_slots": ("<< (4 * SLOT_OF_COL[j]);\n      qweight", "<< (4 * j);\n      qweight"),
+    "bwd_theta_sign": ("gth[ang] += ga * out[j] - gb * out[i];", "gth[ang] += ga * out[j] + gb * out[i];"),
+    "bwd_theta_pre_stage": ("gth[ang] += ga * out[j] - gb * out[i];",
+                            "gth[ang] += ga * states[(size_t)t * I + j] - gb * states[(size_t)t * I + i];"),
+    "bwd_grad_sign": ("grad[i] = ga * c - gb * sn;", "grad[i] = ga * c + gb * sn;"),
+    "bwd_stage_order": ("for (int t = krot - 1; t >= 0; --t) {", "for (int t = 0; t < krot; ++t) {"),
+    "bwd_cs_uses_scaled": ("gc[k] += grad[k] * xk;", "gc[k] += grad[k] * xk * (double)L->channel_scales[k];"),
     "pack_zeros_sequential": ("<< (4 * SLOT_OF_COL[j]);\n      qzeros", "<< (4 * j);\n      qzeros"),
 }
 

@@ -554,3 +554,86 @@ def test_quantized_layer_reproduces_dense_linear_within_rounding(sym):
     extra = np.repeat(np.abs(s_eff - scale), G, axis=0) * 15            # scale rounding
     bound = np.abs(xr) @ (0.5 * step + extra)
     assert (np.abs(y - (x @ w.T + b)) <= bound * (1 + 1e-9) + 1e-12).all()
+
+
+# ---------------------------------------------------------------------------
+# Backward of the scaling and rotation
+# ---------------------------------------------------------------------------
+
+def _bwd_layer(rng, I, G, krot, grid=2.0 ** -10):
+    """Angles and scales on a dyadic grid, so that +-2^-12 steps are exact in fp32."""
+    pairs = np.stack([np.concatenate([rng.permutation(G) for _ in range(I // G)]) for _ in range(krot)])
+    theta = np.round(rng.uniform(-np.pi / 4, np.pi / 4, size=(krot, I // 2)) / grid) * grid
+    cs = np.round(rng.uniform(0.5, 2.0, size=I) / grid) * grid
+    return tiny_layer(I, G, krot, pairs, theta, cs)
+
+
+def _loss(layer, x, g):
+    return float((ref.scale_rotate(layer, x, ref.F64) * g).sum())
+
+
+def test_backward_matches_central_differences():
+    rng = np.random.default_rng(21)
+    I, G, krot, M = 8, 4, 3, 3
+    L = _bwd_layer(rng, I, G, krot)
+    x = rng.normal(size=(M, I))
+    g = rng.normal(size=(M, I))
+    gx, gth, gcs = ref.scale_rotate_backward(L, x, ref.F64, g)
+    h = 2.0 ** -12
+    for t in range(krot):
+        for p in range(I // 2):
+            thp, thm = L.theta.copy(), L.theta.copy()
+            thp[t, p] += h
+            thm[t, p] -= h
+            Lp = synth.Layer(**{**L.__dict__, "theta": thp})
+            Lm = synth.Layer(**{**L.__dict__, "theta": thm})
+            num = (_loss(Lp, x, g) - _loss(Lm, x, g)) / (2 * h)
+            assert gth[t, p] == pytest.approx(num, rel=2e-5, abs=1e-7), (t, p)
+    for k in range(I):
+        csp, csm = L.channel_scales.copy(), L.channel_scales.copy()
+        csp[k] += h
+        csm[k] -= h
+        Lp = synth.Layer(**{**L.__dict__, "channel_scales": csp})
+        Lm = synth.Layer(**{**L.__dict__, "channel_scales": csm})
+        num = (_loss(Lp, x, g) - _loss(Lm, x, g)) / (2 * h)
+        assert gcs[k] == pytest.approx(num, rel=2e-5, abs=1e-7), k
+    for m in range(M):
+        for k in range(I):
+            xp, xm = x.copy(), x.copy()
+            xp[m, k] += 1e-6
+            xm[m, k] -= 1e-6
+            num = (_loss(L, xp, g) - _loss(L, xm, g)) / 2e-6
+            assert gx[m, k] == pytest.approx(num, rel=1e-6, abs=1e-9), (m, k)
+
+
+def test_backward_closed_forms_with_dense_rotation():
+    """x_r = (x * cs) R, so dL/dx = (g R^T) * cs and dL/dcs = sum_m (g R^T) * x."""
+    rng = np.random.default_rng(22)
+    I, G, krot, M = 64, 16, 5, 9
+    L = _bwd_layer(rng, I, G, krot)
+    x = rng.normal(size=(M, I))
+    g = rng.normal(size=(M, I))
+    gx, _, gcs = ref.scale_rotate_backward(L, x, ref.F64, g)
+    R = dense_rotation(L)
+    gs = g @ R.T
+    np.testing.assert_allclose(gx, gs * L.channel_scales.astype(np.float64), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gcs, (gs * x).sum(axis=0), rtol=0, atol=1e-11)
+
+
+def test_backward_theta_at_zero_angle():
+    """One stage at theta = 0 is the identity: dL/dtheta_p = sum_m (g_a x_b - g_b x_a) of the scaled rows."""
+    rng = np.random.default_rng(23)
+    I, G, M = 16, 8, 5
+    pairs = np.concatenate([rng.permutation(G) for _ in range(I // G)])[None, :]
+    cs = np.round(rng.uniform(0.5, 2.0, size=I) * 1024) / 1024
+    L = tiny_layer(I, G, 1, pairs, np.zeros((1, I // 2)), cs)
+    x = rng.normal(size=(M, I))
+    g = rng.normal(size=(M, I))
+    _, gth, _ = ref.scale_rotate_backward(L, x, ref.F64, g)
+    xs = x * cs
+    for gi in range(I // G):
+        for p in range(G // 2):
+            a = gi * G + pairs[0, gi * G + 2 * p]
+            b = gi * G + pairs[0, gi * G + 2 * p + 1]
+            want = (g[:, a] * xs[:, b] - g[:, b] * xs[:, a]).sum()
+            assert gth[0, gi * G // 2 + p] == pytest.approx(want, rel=1e-13, abs=1e-13)

@@ -154,6 +154,90 @@ def bench_quantize(args, paro, synth, np, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+BWD_METRIC = "ParoQuant rotation backward (dL/dx, dL/dtheta, dL/dcs): activation GB/s, % of HBM roofline"
+KERNEL_FILES["rotate_backward"] = ("rotate_backward.hip", "common.hpp")
+
+
+def bench_rotate_backward(args, paro, synth, np, torch, dev):
+    """Time paro_scale_rotate_backward on the workload's first layer input
+    (tokens x I; x, g = dL/dx_r and gx in the activation dtype, as autograd
+    hands them over), rotating through >= 512 MB of distinct (x, g) pairs."""
+    spec = synth.WORKLOADS[args.workload]
+    lname, I, O = spec["layers"][0]
+    M, dt = max(spec["tokens"], 64), spec["act"]
+    tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
+    host = synth.make_layer(args.workload, 0, I, O)
+    x = synth.make_x(args.workload, 0, M, I, dt)
+    g = synth.make_g(args.workload, 0, M, I, dt)
+    pair_bytes = 2 * M * I * 2
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // pair_bytes)))
+    log(f"rotate_backward: workload {args.workload} layer {lname} input ({M} x {I}), {nsets} (x, g) copies")
+    D = paro.DeviceLayer(host, device=dev)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+    xs = [up(x) for _ in range(nsets)]
+    gs = [up(g) for _ in range(nsets)]
+    gx = torch.empty((M, I), dtype=tdt, device=dev)
+    gth = torch.empty((host.krot, I // 2), dtype=torch.float32, device=dev)
+    gcs = torch.empty((I,), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(paro.paro_scale_rotate_backward_workspace_bytes(D, M), 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    step = lambda i: paro.paro_scale_rotate_backward(D, xs[i % nsets], gs[i % nsets], gx, gth, gcs, ws,
+                                                     stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    act_b = 3 * M * I * 2                           # x and g read, gx written
+    rot_b = host.krot * I * 2 + host.krot * (I // 2) * 4 + I * 4
+    alg = act_b + 2 * rot_b                         # pairs, theta, cs read; dtheta, dcs written (same sizes)
+    value = act_b / (us * 1e-6) / 1e9
+    ach = alg / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        rows = min(M, 256)
+        xh, gh = x[:rows], bits_to_f64_host(g[:rows], dt, np)
+        n, t_start = 0, time.perf_counter()
+        while True:
+            ref.scale_rotate_backward(host, xh, dt, gh)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = {"value": 3 * rows * I * 2 / (el / n) / 1e9, "unit": "GB/s", "cores": ref.threads(0),
+               "kind": "oracle",
+               "sample": f"{n} oracle backward call(s) on {rows} of {M} tokens of '{lname}' input, {el:.1f} s"}
+    wl = f"{lname}-input-backward-t{M}x{I}-{'f16' if dt == synth.F16 else 'bf16'}"
+    out = {
+        "metric": BWD_METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl, "group_size": 128, "krot": host.krot, "input_copies": nsets,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"rotate_backward-{args.workload}",
+                                             kernel_source_hash("rotate_backward")),
+                     "kernel": "rot_backward_kernel + rot_backward_reduce_kernel (one entry point)",
+                     "avg_launch_us": round(us, 3)},
+        "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("rotate_backward"),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bits_to_f64_host(bits, dt, np):
+    """fp16 / bf16 bit patterns (uint16) -> float64 (the oracle takes g in double)."""
+    if dt == 0:
+        return np.asarray(bits).view(np.float16).astype(np.float64)
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,9 +248,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
-    ap.add_argument("--op", choices=("linear", "quantize"), default="linear",
+    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward"), default="linear",
                     help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
-                         "qzeros, scales) transform of the workload's first layer")
+                         "qzeros, scales) transform of the workload's first layer; rotate_backward: the "
+                         "calibration-time backward of the scaling and rotation over that layer's input")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark: copy BYTES between two device buffers --steps times "
                          "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -199,6 +284,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.op == "quantize":
         bench_quantize(args, paro, synth, np, torch, dev)
+        return
+    if args.op == "rotate_backward":
+        bench_rotate_backward(args, paro, synth, np, torch, dev)
         return
     spec = synth.WORKLOADS[args.workload]
     M, act = spec["tokens"], spec["act"]

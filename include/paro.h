@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARO_ABI_VERSION 2
+#define PARO_ABI_VERSION 3
 
 typedef enum {
   PARO_F16 = 0,  /* IEEE binary16 */
@@ -250,6 +250,38 @@ int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dt
  */
 int paro_w4_quantize_pack(const paro_w4_layer *layer, const void *w, paro_dtype w_dt, int symmetric,
                           int32_t *qweight, int32_t *qzeros, uint16_t *scales, void *stream);
+
+/*
+ * Backward of the channel scaling and the rotation, x_r = (x * cs) . R, for
+ * the calibration step in which angles and channel scales are trained
+ * ("ParoQuant" wiki, Straight-through estimation: optimization updates
+ * angles and channel scales through the rotation; Concepts / Pairwise Givens
+ * rotations for the pair formula a' = a cos + b sin, b' = -a sin + b cos).
+ * With g = dL/dx_r, walking the stages back:
+ *   dL/dtheta(t, p) = sum over tokens of ga' b' - gb' a'
+ *   (ga, gb)        = (ga' cos - gb' sin, ga' sin + gb' cos)
+ *   dL/dx           = gs * cs,  dL/dcs = sum over tokens of gs * x
+ * (gs = gradient of the scaled rows x * cs).
+ *   x      : [tokens][I] x_dt in {F16, BF16}, the forward's input.
+ *   g      : [tokens][I] g_dt in {F32, x_dt}.
+ *   gx     : [tokens][I] gx_dt in {F32, x_dt}; written.
+ *   gtheta : [krot][I/2] fp32, gcs : [I] fp32; written (overwritten, not
+ *            accumulated); with tokens == 0 both are zero.
+ *   workspace: device memory of paro_scale_rotate_backward_workspace_bytes
+ *            bytes or more, 16-byte aligned (per-wave partial sums; the sums
+ *            are added in a fixed order, so results are deterministic).
+ * x, g and gx are 8-byte aligned; no output overlaps an input, the workspace
+ * or another output.  Caller-owned device memory; enqueued on `stream`.
+ * Uses layer->in_features, group_size (128), krot, pairs, theta,
+ * channel_scales.  Errors: PARO_ERR_NULL, _DTYPE, _ALIGN, _SHAPE,
+ * _UNSUPPORTED, _WORKSPACE, _HIP.
+ */
+int paro_scale_rotate_backward(const paro_w4_layer *layer, const void *x, paro_dtype x_dt, const void *g,
+                               paro_dtype g_dt, int64_t tokens, void *gx, paro_dtype gx_dt, float *gtheta,
+                               float *gcs, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes paro_scale_rotate_backward needs (0 if the shape is invalid). */
+size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,

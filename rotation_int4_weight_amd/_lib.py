@@ -20,7 +20,8 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-           "paro_w4_quantize_pack",
+           "paro_w4_quantize_pack", "paro_scale_rotate_backward",
+           "paro_scale_rotate_backward_workspace_bytes",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
            "paro_w4a16_linear_workspace_bytes",
@@ -64,6 +65,9 @@ def load(path: str | None = None):
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
     lib.paro_w4_quantize_pack.argtypes = [P, P, I32, I32, P, P, P, P]
+    lib.paro_scale_rotate_backward.argtypes = [P, P, I32, P, I32, I64, P, I32, P, P, P, SZ, P]
+    lib.paro_scale_rotate_backward_workspace_bytes.argtypes = [P, I64]
+    lib.paro_scale_rotate_backward_workspace_bytes.restype = SZ
     lib.paro_rotation_matrix_bytes.argtypes = [P]
     lib.paro_rotation_matrix_bytes.restype = SZ
     lib.paro_rotation_matrix.argtypes = [P, I32, P, P]
@@ -78,7 +82,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-                 "paro_w4_quantize_pack",
+                 "paro_w4_quantize_pack", "paro_scale_rotate_backward",
                  "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
@@ -224,6 +228,21 @@ def paro_w4_quantize_pack(layer: DeviceLayer, w, symmetric: bool, qweight, qzero
     scales fp16/int16 view (I/128, O)."""
     _check(load().paro_w4_quantize_pack(layer.ref, _ptr(w), _dt(w), int(bool(symmetric)), _ptr(qweight),
                                         _ptr(qzeros), _ptr(scales), _stream_handle(stream)), "paro_w4_quantize_pack")
+
+
+def paro_scale_rotate_backward_workspace_bytes(layer: DeviceLayer, tokens: int) -> int:
+    """Workspace bytes of paro_scale_rotate_backward for this many tokens."""
+    return int(load().paro_scale_rotate_backward_workspace_bytes(layer.ref, tokens))
+
+
+def paro_scale_rotate_backward(layer: DeviceLayer, x, g, gx, gtheta, gcs, workspace, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16; g = dL/dx_r: (tokens, I) fp32 or x's dtype; gx: (tokens, I) fp32 or x's
+    dtype; gtheta: fp32 (krot, I/2); gcs: fp32 (I,); workspace: device buffer of
+    paro_scale_rotate_backward_workspace_bytes() bytes."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_scale_rotate_backward(layer.ref, _ptr(x), _dt(x), _ptr(g), _dt(g), x.shape[0], _ptr(gx),
+                                             _dt(gx), _ptr(gtheta), _ptr(gcs), _ptr(workspace), ws_bytes,
+                                             _stream_handle(stream)), "paro_scale_rotate_backward")
 
 
 def paro_rotation_matrix_bytes(layer: DeviceLayer) -> int:

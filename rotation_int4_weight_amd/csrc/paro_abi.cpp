@@ -318,6 +318,59 @@ int paro_w4_quantize_pack(const paro_w4_layer *L, const void *w, paro_dtype w_dt
   return ok();
 }
 
+int paro_scale_rotate_backward(const paro_w4_layer *L, const void *x, paro_dtype x_dt, const void *g,
+                               paro_dtype g_dt, int64_t tokens, void *gx, paro_dtype gx_dt, float *gtheta,
+                               float *gcs, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (g_dt != PARO_F32 && g_dt != x_dt) return fail(PARO_ERR_DTYPE, "g dtype %d must be F32 or x's", (int)g_dt);
+  if (gx_dt != PARO_F32 && gx_dt != x_dt) return fail(PARO_ERR_DTYPE, "gx dtype %d must be F32 or x's", (int)gx_dt);
+  if (!gtheta || !gcs) return fail(PARO_ERR_NULL, "gtheta and gcs are required");
+  if (tokens > 0 && (!x || !g || !gx)) return fail(PARO_ERR_NULL, "x, g and gx are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  const int64_t I = L->in_features;
+  const size_t need = paro::rot_backward_partial_bytes(tokens, I, L->krot);
+  if (!workspace || workspace_bytes < need)
+    return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned(workspace, 16) || !aligned(gtheta, 4) || !aligned(gcs, 4) ||
+      (tokens > 0 && (!aligned(x, 8) || !aligned(g, 8) || !aligned(gx, 8))))
+    return fail(PARO_ERR_ALIGN, "x, g, gx must be 8-byte, gtheta/gcs 4-byte and workspace 16-byte aligned");
+  const size_t n = (size_t)tokens * I;
+  struct Region {
+    const void *p;
+    size_t bytes;
+  };
+  const Region in[2] = {{x, n * 2}, {g, n * (g_dt == PARO_F32 ? 4 : 2)}};
+  const Region out[4] = {{gx, n * (gx_dt == PARO_F32 ? 4 : 2)},
+                         {gtheta, (size_t)L->krot * (I / 2) * 4},
+                         {gcs, (size_t)I * 4},
+                         {workspace, need}};
+  auto overlap = [](const Region &a, const Region &b) {
+    const char *pa = (const char *)a.p, *pb = (const char *)b.p;
+    return a.bytes && b.bytes && pa < pb + b.bytes && pb < pa + a.bytes;
+  };
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(out[i], in[j])) return fail(PARO_ERR_SHAPE, "an output or the workspace overlaps x or g");
+    for (int j = 0; j < i; ++j)
+      if (overlap(out[i], out[j])) return fail(PARO_ERR_SHAPE, "gx, gtheta, gcs and the workspace must not overlap");
+  }
+  hipError_t e = paro::launch_rot_backward(x, (int)x_dt, g, (int)g_dt, tokens, I, L->pairs, L->theta,
+                                           L->channel_scales, L->krot, gx, (int)gx_dt, gtheta, gcs,
+                                           (float *)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scale_rotate_backward launch");
+  return ok();
+}
+
+size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
+  if (!L || tokens < 0 || tokens > kMaxTokens || check_gpu_shape(L)) return 0;
+  return paro::rot_backward_partial_bytes(tokens, L->in_features, L->krot);
+}
+
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {
   (void)L;
   return auto_path(tokens);

@@ -25,6 +25,8 @@ for Llama-3-8B-shaped layers, since no trained weights or datasets are used):
   bias       N(0, 0.01), (O,), fp16.
   w          (for the offline quantizer) a dense weight (O, I): N(0, 0.02)
              times a per-row factor uniform(0.5, 2), fp16/bf16/fp32.
+  g          (for the rotation backward) an upstream gradient dL/dx_r,
+             N(0, 1), (tokens, I), fp16/bf16 bits or fp32.
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ import numpy as np
 AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 
 TENSOR_IDS = {"x": 0, "outliers": 1, "pairs": 2, "theta": 3, "cs": 4,
-              "q": 5, "z": 6, "scales": 7, "bias": 8, "w": 9, "w_rows": 10}
+              "q": 5, "z": 6, "scales": 7, "bias": 8, "w": 9, "w_rows": 10, "g": 11}
 
 F16, BF16, F32 = 0, 1, 2  # dtype codes shared by both C-ABIs' conventions
 
@@ -168,6 +170,20 @@ def make_w(workload: int, layer: int, out_features: int, in_features: int, dt: i
     if dt == F32:
         return w.astype(np.float32)
     raise ValueError("unknown weight dtype code")
+
+
+def make_g(workload: int, layer: int, tokens: int, in_features: int, dt: int,
+           base: int = 0) -> np.ndarray:
+    """An upstream gradient dL/dx_r (tokens, I): N(0, 1) as fp16/bf16 bits
+    (uint16) or fp32."""
+    g = rng_for(workload, layer, "g", base).normal(0.0, 1.0, size=(tokens, in_features))
+    if dt == F16:
+        return f16_bits(g)
+    if dt == BF16:
+        return f32_to_bf16_bits(g.astype(np.float32))
+    if dt == F32:
+        return g.astype(np.float32)
+    raise ValueError("unknown gradient dtype code")
 
 
 def workload_layers(workload: int, **kw):

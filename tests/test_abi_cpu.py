@@ -32,7 +32,7 @@ def test_libparo_exports_every_declared_symbol():
     assert set(_lib.EXPORTS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.paro_abi_version() == 2
+    assert lib.paro_abi_version() == 3
 
 
 def test_oracle_exports_every_declared_symbol():
@@ -238,3 +238,38 @@ def test_quantize_pack_argument_checks():
     assert call(qz=FAKE + 64) == 2                # qzeros inside qweight
     assert call(L=fake_layer(I=256, O=64, G=64)) == 5
     assert call(L=fake_layer(I=256, O=64, pairs=0)) == 1
+
+
+@needs_no_gpu
+def test_scale_rotate_backward_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(I=256, O=64, krot=8)
+    need = lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 4)
+    assert need == 4 * (8 * 128 + 256) * 4           # one 64-row tile: 4 waves of (krot*I/2 + I) floats
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == 2 * need
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == 0
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == 0
+
+    def call(x=FAKE * 8, xdt=0, g=FAKE * 9, gdt=2, tokens=4, gx=FAKE * 10, gxdt=2, gth=FAKE * 11,
+             gcs=FAKE * 12, ws=FAKE * 13, wsb=need, L=L):
+        return lib.paro_scale_rotate_backward(ctypes.byref(L), x, xdt, g, gdt, tokens, gx, gxdt, gth, gcs, ws,
+                                              wsb, None)
+    assert call(xdt=2) == 3                           # x must be 16-bit
+    assert call(gdt=1) == 3                           # g: F32 or x's dtype
+    assert call(gxdt=1) == 3
+    assert call(gth=0) == 1
+    assert call(gcs=0, tokens=0) == 1                 # the sums are written even with no tokens
+    assert call(x=0) == 1
+    assert call(gx=0) == 1
+    assert call(ws=0) == 7
+    assert call(wsb=need - 1) == 7
+    assert call(x=FAKE * 8 + 4) == 4                  # 8-byte aligned
+    assert call(ws=FAKE * 13 + 8) == 4                # 16-byte aligned
+    assert call(gcs=FAKE * 12 + 2) == 4
+    assert call(gx=FAKE * 8 + 1024) == 2              # gx overlaps x
+    assert call(gx=FAKE * 9 + 8) == 2                 # gx overlaps g
+    assert call(ws=FAKE * 10 + 16) == 2               # workspace overlaps gx
+    assert call(gcs=FAKE * 11 + 16) == 2              # gcs overlaps gtheta
+    assert call(tokens=-1) == 2
+    assert call(L=fake_layer(G=64)) == 5
+    assert call(L=fake_layer(pairs=0)) == 1

@@ -28,7 +28,8 @@ MUTANTS = {
         "        const int64_t j = g * G + L->pairs[(int64_t)t * I + g * G + 2 * p];"),
     "stage_order_reversed": ("for (int t = 0; t < L->krot; ++t) {\n    for (int64_t g = 0; g < ngroups",
                              "for (int t = L->krot - 1; t >= 0; --t) {\n    for (int64_t g = 0; g < ngroups"),
-    "channel_scale_divides": ("* (double)L->channel_scales[k];", "/ (double)L->channel_scales[k];"),
+    "channel_scale_divides": ("row[k] = load_elem(x, x_dt, m * I + k) * (double)L->channel_scales[k];",
+                              "row[k] = load_elem(x, x_dt, m * I + k) / (double)L->channel_scales[k];"),
     "awq_order_sequential": ("{0, 4, 1, 5, 2, 6, 3, 7}", "{0, 1, 2, 3, 4, 5, 6, 7}"),
     "zero_not_subtracted": ("(double)(q - z) * s;", "(double)(q) * s;"),
     "bias_dropped": ("y_out[m * O + n0 + n] = acc[n] + b;", "y_out[m * O + n0 + n] = acc[n];"),

@@ -268,9 +268,13 @@ int paro_w4_quantize_pack(const paro_w4_layer *layer, const void *w, paro_dtype 
  *   gtheta : [krot][I/2] fp32, gcs : [I] fp32; written (overwritten, not
  *            accumulated); with tokens == 0 both are zero.
  *   workspace: device memory of paro_scale_rotate_backward_workspace_bytes
- *            bytes or more, 16-byte aligned (per-wave partial sums; the sums
- *            are added in a fixed order, so results are deterministic).
- * x, g and gx are 8-byte aligned; no output overlaps an input, the workspace
+ *            bytes or more (also needed for 0 tokens), 16-byte aligned: the
+ *            per-group Gram matrices C = g^T x of the token splits, the dense
+ *            R' = diag(cs) R and per-row partial sums of dL/dtheta.  Sums are
+ *            added in a fixed order, so results are identical call to call.
+ * Computed through C: dL/dtheta and dL/dcs from a walk over the 128 rows of
+ * C per group, dL/dx = g . R'^T on the matrix cores.
+ * x, g and gx are 16-byte aligned; no output overlaps an input, the workspace
  * or another output.  Caller-owned device memory; enqueued on `stream`.
  * Uses layer->in_features, group_size (128), krot, pairs, theta,
  * channel_scales.  Errors: PARO_ERR_NULL, _DTYPE, _ALIGN, _SHAPE,

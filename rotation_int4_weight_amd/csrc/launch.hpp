@@ -87,8 +87,8 @@ hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, in
 
 // Backward of the scaling and rotation: x [tokens][I] (F16/BF16), g = dL/dx_r
 // [tokens][I] (F32 or x's dtype) -> gx [tokens][I] (F32 or x's dtype),
-// gtheta [krot][I/2] fp32, gcs [I] fp32, through per-wave partial sums in
-// `partial` (rot_backward_partial_bytes bytes).
+// gtheta [krot][I/2] fp32, gcs [I] fp32, with `partial` as workspace
+// (rot_backward_partial_bytes bytes, 256-byte aligned regions inside).
 size_t rot_backward_partial_bytes(int64_t tokens, int64_t I, int krot);
 hipError_t launch_rot_backward(const void *x, int x_dt, const void *g, int g_dt, int64_t tokens, int64_t I,
                                const int16_t *pairs, const float *theta, const float *cs, int krot, void *gx,

@@ -337,8 +337,8 @@ int paro_scale_rotate_backward(const paro_w4_layer *L, const void *x, paro_dtype
     return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 need);
   if (!aligned(workspace, 16) || !aligned(gtheta, 4) || !aligned(gcs, 4) ||
-      (tokens > 0 && (!aligned(x, 8) || !aligned(g, 8) || !aligned(gx, 8))))
-    return fail(PARO_ERR_ALIGN, "x, g, gx must be 8-byte, gtheta/gcs 4-byte and workspace 16-byte aligned");
+      (tokens > 0 && (!aligned(x, 16) || !aligned(g, 16) || !aligned(gx, 16))))
+    return fail(PARO_ERR_ALIGN, "x, g, gx and the workspace must be 16-byte and gtheta/gcs 4-byte aligned");
   const size_t n = (size_t)tokens * I;
   struct Region {
     const void *p;
@@ -368,7 +368,7 @@ int paro_scale_rotate_backward(const paro_w4_layer *L, const void *x, paro_dtype
 
 size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
   if (!L || tokens < 0 || tokens > kMaxTokens || check_gpu_shape(L)) return 0;
-  return paro::rot_backward_partial_bytes(tokens, L->in_features, L->krot);
+  return paro::rot_backward_partial_bytes(tokens, L->in_features, L->krot);  // > 0 even for 0 tokens
 }
 
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {

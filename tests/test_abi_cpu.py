@@ -245,9 +245,10 @@ def test_scale_rotate_backward_argument_checks():
     lib = _lib.load()
     L = fake_layer(I=256, O=64, krot=8)
     need = lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 4)
-    assert need == 4 * (8 * 128 + 256) * 4           # one 64-row tile: 4 waves of (krot*I/2 + I) floats
-    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == 2 * need
-    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == 0
+    # dense R' (H and L, 2 groups), one Gram split of 2 x 128 x 128 fp32, 8 x krot x I/2 fp32 partials
+    assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 4 + 8 * 8 * 128 * 4
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == need + 2 * 128 * 128 * 4
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == need   # the walk still runs
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == 0
 
     def call(x=FAKE * 8, xdt=0, g=FAKE * 9, gdt=2, tokens=4, gx=FAKE * 10, gxdt=2, gth=FAKE * 11,
@@ -263,11 +264,12 @@ def test_scale_rotate_backward_argument_checks():
     assert call(gx=0) == 1
     assert call(ws=0) == 7
     assert call(wsb=need - 1) == 7
-    assert call(x=FAKE * 8 + 4) == 4                  # 8-byte aligned
+    assert call(x=FAKE * 8 + 4) == 4                  # 16-byte aligned
+    assert call(gx=FAKE * 10 + 8) == 4
     assert call(ws=FAKE * 13 + 8) == 4                # 16-byte aligned
     assert call(gcs=FAKE * 12 + 2) == 4
     assert call(gx=FAKE * 8 + 1024) == 2              # gx overlaps x
-    assert call(gx=FAKE * 9 + 8) == 2                 # gx overlaps g
+    assert call(gx=FAKE * 9 + 16) == 2                # gx overlaps g
     assert call(ws=FAKE * 10 + 16) == 2               # workspace overlaps gx
     assert call(gcs=FAKE * 11 + 16) == 2              # gcs overlaps gtheta
     assert call(tokens=-1) == 2

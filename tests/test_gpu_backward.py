@@ -95,7 +95,7 @@ def test_backward_zero_tokens_writes_zero_sums():
     gx = torch.empty((0, I), dtype=torch.float32, device="cuda")
     gth = torch.full((L.krot, I // 2), float("nan"), device="cuda")
     gcs = torch.full((I,), float("nan"), device="cuda")
-    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(paro.paro_scale_rotate_backward_workspace_bytes(D, 0), dtype=torch.uint8, device="cuda")
     paro.paro_scale_rotate_backward(D, x, g, gx, gth, gcs, ws)
     torch.cuda.synchronize()
     assert (gth.cpu() == 0).all() and (gcs.cpu() == 0).all()
@@ -113,7 +113,10 @@ def test_backward_identity_rotation_reduces_to_scaling():
     D = paro.DeviceLayer(L)
     gx_b, gth, gcs = gpu_backward(D, L, x, synth.F16, g, synth.F32, synth.F32)
     xv, gv, cs = bits_to_f64(x, synth.F16), g.astype(np.float64), L.channel_scales.astype(np.float64)
-    assert np.allclose(gx_b, gv * cs, rtol=2.0 ** -22, atol=0)
+    # dL/dx runs through the matrix cores with g and R' each split into a bf16
+    # high part and remainder (each to 2^-17): within 2^-15 of the row's scale
+    want_gx = gv * cs
+    assert (np.abs(gx_b - want_gx) <= 2.0 ** -15 * np.abs(want_gx).max(axis=1, keepdims=True)).all()
     assert np.abs(gcs - (gv * xv).sum(axis=0)).max() <= SUM_TOL * np.abs((gv * xv).sum(axis=0)).max()
     xs = xv * cs
     a = L.pairs[:, 0::2].astype(np.int64) + (np.arange(I // 2) // 64 * 128)[None, :]

@@ -30,8 +30,11 @@
 
 namespace paro {
 
-constexpr int kBwdTok = 64;                  // tokens per LDS tile of the Gram kernel
-constexpr int kWalkRows = 16;                // rows of C per wave in the walk
+constexpr int kBwdTok = 64;                  // token granule of the Gram splits
+// tokens per LDS tile of the Gram kernel (128-token tiles measured slower:
+// fewer splits in flight, the same transposing LDS writes per token)
+__host__ __device__ constexpr int gram_tile(int) { return kBwdTok; }
+constexpr int kWalkRows = 8;                 // rows of C per wave in the walk
 constexpr int kWalkParts = kG / kWalkRows;   // dtheta partial rows per group
 constexpr int kBwdRS = kG + 4;               // walk LDS row stride (floats)
 constexpr int kDxHS = kG + 8;                // dx LDS row stride of H / L (halves)
@@ -59,8 +62,9 @@ __device__ __forceinline__ int mfma_row_of_channel(int j) {
 // 16-byte LDS read.  Wave w owns C^T rows 32w..32w+31 (two 16-row tiles) and
 // all 128 columns: 16 accumulator tiles.
 // ---------------------------------------------------------------------------
+template <int T>
 __device__ __forceinline__ int gram_off(int ch, int tok) {
-  return ch * kBwdTok + ((((tok >> 3) ^ (ch >> 3)) & 7) << 3) + (tok & 7);
+  return ch * T + ((((tok >> 3) ^ (ch >> 3)) & (T / 8 - 1)) << 3) + (tok & 7);
 }
 
 template <int XDT, int GDT>
@@ -70,9 +74,11 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
   constexpr int MD = gram_mdt(XDT, GDT);
   constexpr int XP = (XDT == kF16 && MD == kBF16) ? 2 : 1;  // parts of x
   constexpr int GP = (GDT == kF32 || (GDT == kF16 && MD == kBF16)) ? 2 : 1;
-  constexpr int GCH = GDT == kF32 ? 8 : 4;  // 16-byte chunks of g per thread and tile
-  __shared__ __attribute__((aligned(16))) uint16_t xt[XP][kG * kBwdTok];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[GP][kG * kBwdTok];
+  constexpr int T = gram_tile(GDT);
+  constexpr int XCH = T / 16;                          // 16-byte chunks of x per thread and tile
+  constexpr int GCH = GDT == kF32 ? T / 8 : T / 16;    // and of g
+  __shared__ __attribute__((aligned(16))) uint16_t xt[XP][kG * T];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[GP][kG * T];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t g = blockIdx.x, groups = I / kG;
@@ -80,15 +86,15 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
   const int64_t m_end = tokens < m_begin + chunk ? tokens : m_begin + chunk;
   const int gsz = GDT == kF32 ? 4 : 2;
 
-  u32x4 xr[4], gr[GCH];
+  u32x4 xr[XCH], gr[GCH];
   auto load_tile = [&](int64_t m0) {
-    const int64_t rows = m_end - m0 < kBwdTok ? m_end - m0 : kBwdTok;  // > 0
+    const int64_t rows = m_end - m0 < T ? m_end - m0 : T;  // > 0
     const __amdgpu_buffer_rsrc_t rx =
         raw_rsrc(reinterpret_cast<const uint16_t *>(x) + m0 * I + g * kG, (uint32_t)(rows * I * 2));
     const __amdgpu_buffer_rsrc_t rg =
         raw_rsrc(reinterpret_cast<const char *>(gin) + (m0 * I + g * kG) * gsz, (uint32_t)(rows * I * gsz));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < XCH; ++u) {
       const int c = tid + 256 * u, row = c >> 4, cb = c & 15;
       xr[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((row * I + cb * 8) * 2), 0, 0);
     }
@@ -100,10 +106,10 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
     }
   };
 
-  auto put = [&](uint16_t *arr, int ch, int tok, uint32_t v) { arr[gram_off(ch, tok)] = (uint16_t)v; };
+  auto put = [&](uint16_t *arr, int ch, int tok, uint32_t v) { arr[gram_off<T>(ch, tok)] = (uint16_t)v; };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < XCH; ++u) {
       const int c = tid + 256 * u, tok = c >> 4, cb = c & 15;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -160,19 +166,19 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
 
   const int fr = lane & 15, fj = lane >> 4;
   auto frag = [&](const uint16_t *arr, int ch, int j) {
-    return *reinterpret_cast<const u32x4 *>(arr + ch * kBwdTok + (((j ^ (ch >> 3)) & 7) << 3));
+    return *reinterpret_cast<const u32x4 *>(arr + ch * T + (((j ^ (ch >> 3)) & (T / 8 - 1)) << 3));
   };
 
   if (m_begin < m_end) load_tile(m_begin);
-  for (int64_t m0 = m_begin; m0 < m_end; m0 += kBwdTok) {
+  for (int64_t m0 = m_begin; m0 < m_end; m0 += T) {
     __syncthreads();  // the previous tile's fragments are read
     asm volatile("s_nop 7");  // before VALU reuses registers the last asm MFMAs read
     __builtin_amdgcn_sched_barrier(0);
     store_tile();
-    if (m0 + kBwdTok < m_end) load_tile(m0 + kBwdTok);  // in flight during the products below
+    if (m0 + T < m_end) load_tile(m0 + T);  // in flight during the products below
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kBwdTok / 32; ++ks) {
+    for (int ks = 0; ks < T / 32; ++ks) {
       const int j = 4 * ks + fj;
       u32x4 a[2][XP];
 #pragma unroll
@@ -210,7 +216,7 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Walk kernel: rows i of C^T (columns of C) of one group, 16 per wave, two
+// Walk kernel: rows i of C^T (columns of C) of one group, 8 per wave, four
 // workgroups per group.  Lane p owns pair p of every stage (as in the forward
 // rotation).  Writes dL/dcs_i, the wave's dtheta partial sums and row i of
 // R' = diag(cs) R as H + L (dtype MDT) at its MFMA row for the dx product.
@@ -224,7 +230,7 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
   __shared__ float lds[4][2][RW * kBwdRS];
   const int lane = lane_id(), wave = wave_id();
   const int64_t g = blockIdx.x, groups = I / kG;
-  const int i0 = blockIdx.y * 64 + wave * RW;
+  const int i0 = blockIdx.y * (4 * RW) + wave * RW;
   float *vs = lds[wave][0], *fs = lds[wave][1];
   const int16_t *pairs_g = pairs + g * kG;
   const float *theta_g = theta + g * kPairs;
@@ -239,17 +245,33 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
     th[u] = theta_g[(int64_t)t * (I / 2) + lane];
   }
 
-  // u_i = column i of C = row i of C^T, the token splits added in order
-#pragma unroll 4
+  // u_i = column i of C = row i of C^T, the token splits added in order;
+  // four splits' loads of all rows are in flight at a time
+  float2 us[RW];
+#pragma unroll
+  for (int m = 0; m < RW; ++m) us[m] = float2{0.f, 0.f};
+  const float *crow = cpart + (g * kG + i0) * kG + 2 * lane;
+  const int64_t split_stride = groups * kG * kG;
+  for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+    float2 v[4][RW];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int m = 0; m < RW; ++m)
+        v[q][m] = sp0 + q < splits ? *reinterpret_cast<const float2 *>(crow + (sp0 + q) * split_stride + m * kG)
+                                   : float2{0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int m = 0; m < RW; ++m) {
+        us[m].x += v[q][m].x;
+        us[m].y += v[q][m].y;
+      }
+  }
+#pragma unroll
   for (int m = 0; m < RW; ++m) {
-    float2 s{0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp) {
-      const float2 v = *reinterpret_cast<const float2 *>(cpart + ((sp * groups + g) * kG + i0 + m) * kG + 2 * lane);
-      s.x += v.x;
-      s.y += v.y;
-    }
-    vs[m * kBwdRS + 2 * lane] = s.x;
-    vs[m * kBwdRS + 2 * lane + 1] = s.y;
+    vs[m * kBwdRS + 2 * lane] = us[m].x;
+    vs[m * kBwdRS + 2 * lane + 1] = us[m].y;
   }
   wave_lds_sync();
 
@@ -580,7 +602,7 @@ hipError_t launch_rot_backward(const void *x, int x_dt, const void *gin, int g_d
   if (e != hipSuccess) return e;
 
   // 2. the stage walk: dL/dcs, dtheta partials, R' for the dx product
-  const dim3 wgrid(groups, kG / 64);
+  const dim3 wgrid(groups, kG / (4 * kWalkRows));
   if (dx_mdt(g_dt) == kF16)
     hipLaunchKernelGGL((bwd_walk_kernel<kF16>), wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta, cs,
                        krot, gcs, tpart, hl);

@@ -245,8 +245,8 @@ def test_scale_rotate_backward_argument_checks():
     lib = _lib.load()
     L = fake_layer(I=256, O=64, krot=8)
     need = lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 4)
-    # dense R' (H and L, 2 groups), one Gram split of 2 x 128 x 128 fp32, 8 x krot x I/2 fp32 partials
-    assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 4 + 8 * 8 * 128 * 4
+    # dense R' (H and L, 2 groups), one Gram split of 2 x 128 x 128 fp32, 16 x krot x I/2 fp32 partials
+    assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 4 + 16 * 8 * 128 * 4
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == need + 2 * 128 * 128 * 4
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == need   # the walk still runs
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == 0

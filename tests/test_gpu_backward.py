@@ -1,15 +1,15 @@
 """GPU parity of paro_scale_rotate_backward (dL/dx, dL/dtheta, dL/dcs of the
 channel scaling and rotation) against the fp64 oracle, through the C-ABI.
 
-Tolerances, from the arithmetic: the kernel recomputes the forward and walks
-the stages back in fp32, so each dL/dx element carries a few fp32 roundings
-per stage relative to its row: |d| <= 2^-16 * row max |gx_ref| for an fp32
-gx, plus the output rounding (1.01 unit roundoffs of |gx_ref|) for a 16-bit
-gx.  dL/dtheta and dL/dcs are sums over the tokens accumulated in fp32 (16
-rows per wave, then the partials in a fixed order); with N(0, 1)-sized
-inputs the sums cancel to about sqrt(tokens) times a term while fp32
-accumulation errs by about 2^-24 * tokens times a term, so 1e-4 * max |ref|
-holds with orders of magnitude to spare at every size tested, and a dropped
+Tolerances, from the arithmetic: dL/dx is g . R'^T on the matrix cores with g
+and R' each split into a bf16 high part and remainder (each good to 2^-17)
+and fp32 accumulation: |d| <= 2^-16 * row max |gx_ref| for an fp32 gx, plus
+the output rounding (1.01 unit roundoffs of |gx_ref|) for a 16-bit gx.
+dL/dtheta and dL/dcs come from the per-group Gram matrix g^T x, accumulated
+in fp32 over the tokens and then walked through the stages in fp32; with
+N(0, 1)-sized inputs the sums cancel to about sqrt(tokens) times a term while
+fp32 accumulation errs by about 2^-24 * tokens times a term, so
+1e-4 * max |ref| holds with room to spare at every size tested, and a dropped
 or mis-signed term still breaks it.
 """
 import numpy as np

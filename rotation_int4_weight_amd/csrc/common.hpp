@@ -99,6 +99,12 @@ __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 // Pair indices are masked into the group, so a bad schedule cannot read or
 // write outside the group's 128 channels.
 //
+// Rotation groups of G = 32 or 64 channels: pairs never leave their group,
+// so a 128-channel block holds 128/G groups and is rotated as one block.  The
+// stored pair indices are local to their G-group; lane p's pair (word slots
+// 2p, 2p+1) lies in group (2p)/G of the block, so its block-local indices
+// are the stored ones plus (2p) & (128 - G).  gmask = 128 - G (0 for 128).
+//
 // The pair words and angles of the first kStageRegs stages can be loaded
 // early (RotParams::load), long before the rows are rotated, so that their
 // latency hides behind other memory traffic; later stages, if any, are
@@ -106,16 +112,25 @@ __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 // ---------------------------------------------------------------------------
 constexpr int kStageRegs = 8;
 
+__device__ __forceinline__ uint32_t block_pair_word(uint32_t w, int lane, int gmask) {
+  return w + (uint32_t)((2 * lane) & gmask) * 0x00010001u;
+}
+__device__ __forceinline__ uint32_t load_pair_word(const int16_t *__restrict__ pairs_g, int64_t pstride, int t,
+                                                   int lane, int gmask) {
+  return block_pair_word(*reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * pstride + 2 * lane), lane,
+                         gmask);
+}
+
 struct RotParams {
   uint32_t pw[kStageRegs];
   float th[kStageRegs];
   __device__ __forceinline__ void load(const int16_t *__restrict__ pairs_g, int64_t pstride,
                                        const float *__restrict__ theta_g, int64_t tstride, int krot,
-                                       int lane) {
+                                       int lane, int gmask) {
 #pragma unroll
     for (int u = 0; u < kStageRegs; ++u) {
       const int t = u < krot ? u : 0;  // stages past krot are never applied
-      pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * pstride + 2 * lane);
+      pw[u] = load_pair_word(pairs_g, pstride, t, lane, gmask);
       th[u] = theta_g[(int64_t)t * tstride + lane];
     }
   }
@@ -144,7 +159,7 @@ template <int NR>
 __device__ __forceinline__ void rotate_rows_lds(float *xs, int rs, const RotParams &rp,
                                                 const int16_t *__restrict__ pairs_g, int64_t pstride,
                                                 const float *__restrict__ theta_g, int64_t tstride,
-                                                int krot, int lane) {
+                                                int krot, int lane, int gmask) {
   float cs[kStageRegs], sn[kStageRegs];
 #pragma unroll
   for (int u = 0; u < kStageRegs; ++u) __sincosf(rp.th[u], &sn[u], &cs[u]);
@@ -152,7 +167,7 @@ __device__ __forceinline__ void rotate_rows_lds(float *xs, int rs, const RotPara
   for (int u = 0; u < kStageRegs; ++u)
     if (u < krot) rotate_stage<NR>(xs, rs, rp.pw[u], cs[u], sn[u]);
   for (int t = kStageRegs; t < krot; ++t) {
-    const uint32_t pw = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * pstride + 2 * lane);
+    const uint32_t pw = load_pair_word(pairs_g, pstride, t, lane, gmask);
     float c, s;
     __sincosf(theta_g[(int64_t)t * tstride + lane], &s, &c);
     rotate_stage<NR>(xs, rs, pw, c, s);

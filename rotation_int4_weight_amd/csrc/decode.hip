@@ -204,7 +204,10 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     for (int i = 0; i < FR; ++i) tot[j][i] = 0.0f;
 
   if (nk > 0) {
-    const int64_t g_first = ks0 / 4;
+    // 128-channel rotation blocks hold 4 k-steps; quantization groups hold
+    // G/32 = 1 << gsh (with G < 128 the plan gives each wave one k-step)
+    const int gsh = __builtin_ctz((unsigned)a.group) - 5, gmask = kG - a.group;
+    const int64_t g_first = ks0 / 4, q_first = ks0 >> gsh, nq = I / a.group;
     float *xs = smem + wave * (MT * kDecodeRS);  // fused rotation rows of this wave
     // ---- fused: the first group's rotation inputs, before the weight stream ----
     RotParams rp;
@@ -212,7 +215,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     float cs0 = 0.f, cs1 = 0.f;
     auto load_rot_inputs = [&](int64_t g) {
       const int64_t c0 = g * kG + 2 * lane;
-      rp.load(a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot, lane);
+      rp.load(a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot, lane, gmask);
       cs0 = a.cs[c0];
       cs1 = a.cs[c0 + 1];
 #pragma unroll
@@ -241,8 +244,8 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     uint32_t zv[NG][WPL];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const int64_t g0 = g_first + gi;
-      const int64_t g = g0 < I / kG ? g0 : I / kG - 1;
+      const int64_t g0 = q_first + gi;
+      const int64_t g = g0 < nq ? g0 : nq - 1;
 #pragma unroll
       for (int w = 0; w < WPL; ++w) {
         sv[gi][w] = *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * (wcl + w));  // wcl is in bounds
@@ -270,8 +273,8 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     for (int k = 0; k < KSW; ++k) {
       if (k < nk) {
         const int64_t ks = ks0 + k;
-        const int64_t g = ks / 4;
-        const int gi = (int)(g - g_first);
+        const int64_t g = ks / 4;                     // rotation block
+        const int gi = (int)((ks >> gsh) - q_first);  // quantization group of this wave
         if constexpr (FUSED) {
           if (k == 0 || (ks % 4) == 0) {  // entering a group: rotate it into LDS
             if (k != 0) load_rot_inputs(g);
@@ -283,7 +286,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
             }
             wave_lds_sync();
             rotate_rows_lds<MT>(xs, kDecodeRS, rp, a.pairs + g * kG, I, a.theta + g * kPairs, I / 2, a.krot,
-                                lane);
+                                lane, gmask);
           }
           const float *src = xs + (cl < MT ? cl : 0) * kDecodeRS + (ks % 4) * 32 + kb * 8;
           const float4 lo = *reinterpret_cast<const float4 *>(src);
@@ -309,7 +312,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
         }
         // fold at the end of a group or of this wave's k-steps:
         //   tot += s/c * (acc - (off + c*z) * xsum)
-        if ((ks % 4) == 3 || k == nk - 1) {
+        if (((ks + 1) & ((1 << gsh) - 1)) == 0 || k == nk - 1) {
 #pragma unroll
           for (int w = 0; w < WPL; ++w) {
 #pragma unroll
@@ -449,7 +452,7 @@ static int env_int(const char *name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
-DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused) {
+DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int group) {
   (void)fused;
   DecodePlan p;
   const int64_t nks = I / 32;
@@ -479,6 +482,9 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused) {
   if (fw == 1 || (fw == 2 && O % 16 == 0) || (fw == 4 && O % 32 == 0)) p.wpl = fw;
   if (fk == 1 || fk == 2 || fk == 4 || fk == 8) p.ksw = fk;
   if (fn == 4 || fn == 8 || fn == 16) p.nw = fn;
+  // groups of 32 or 64 rows: one k-step per wave (the kernel keeps one
+  // group's scales and zeros per wave and folds every k-step)
+  if (group < kG) p.ksw = 1;
   p.ntile = 128 * p.wpl;
   p.n_tiles = (int)((O + p.ntile - 1) / p.ntile);
   p.splits = (int)((nks + p.nw * p.ksw - 1) / (p.nw * p.ksw));

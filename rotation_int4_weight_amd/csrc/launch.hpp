@@ -10,8 +10,11 @@
 
 namespace paro {
 
+// `group`: the rotation / quantization group size G (32, 64 or 128); the
+// kernels rotate 128-channel blocks with the pair indices rebased into the
+// block (block_pair_word in common.hpp).
 hipError_t launch_scale_rotate(const uint16_t *x, int x_dt, void *xr, int xr_dt, int64_t tokens, int64_t I,
-                               const int16_t *pairs, const float *theta, const float *cs, int krot,
+                               const int16_t *pairs, const float *theta, const float *cs, int krot, int group,
                                hipStream_t st);
 
 hipError_t launch_unpack_dequant(const int32_t *qweight, const int32_t *qzeros, const uint16_t *scales,
@@ -22,6 +25,7 @@ hipError_t launch_unpack_dequant(const int32_t *qweight, const int32_t *qzeros, 
 struct LinearArgs {
   int64_t I, O, tokens;
   int krot;
+  int group;  // G: 32, 64 or 128 (rotation pairs and quantization groups)
   const int16_t *pairs;
   const float *theta;
   const float *cs;
@@ -46,7 +50,9 @@ struct DecodePlan {
   int n_tiles;    // ceil(O / ntile)
   int splits;     // workgroups along K (ceil(I/32 / (nw * ksw)))
 };
-DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused);
+// group < 128: one k-step per wave, so every k-step folds with its own
+// group's scale and zero point.
+DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int group = 128);
 // Bytes of fp32 split-K partial sums the plan needs (0 with one split).
 size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O);
 // counters: >= n_tiles zeroed uint32 (left zeroed); partials: decode_partial_bytes.
@@ -69,7 +75,7 @@ __host__ __device__ inline int64_t tiled_rows(int64_t tokens) { return (tokens +
 // rows zero).
 size_t rot_mat_bytes(int64_t I);
 hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
-                            int krot, uint16_t *hl, hipStream_t st);
+                            int krot, int group, uint16_t *hl, hipStream_t st);
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st);
 // Row-major [tokens][I] (2-byte elements) -> tiled layout (pad rows zero).
@@ -82,7 +88,8 @@ hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStrea
 // w [O][I] (F16, BF16 or F32); qweight [I][O/8], qzeros [I/128][O/8],
 // scales [I/128][O] fp16.
 hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, int64_t I, const int16_t *pairs,
-                                const float *theta, const float *cs, int krot, int32_t *qweight, int32_t *qzeros,
+                                const float *theta, const float *cs, int krot, int group, int32_t *qweight,
+                                int32_t *qzeros,
                                 uint16_t *scales, hipStream_t st);
 
 // Backward of the scaling and rotation: x [tokens][I] (F16/BF16), g = dL/dx_r
@@ -91,7 +98,8 @@ hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, in
 // (rot_backward_partial_bytes bytes, 256-byte aligned regions inside).
 size_t rot_backward_partial_bytes(int64_t tokens, int64_t I, int krot);
 hipError_t launch_rot_backward(const void *x, int x_dt, const void *g, int g_dt, int64_t tokens, int64_t I,
-                               const int16_t *pairs, const float *theta, const float *cs, int krot, void *gx,
+                               const int16_t *pairs, const float *theta, const float *cs, int krot, int group,
+                               void *gx,
                                int gx_dt, float *gtheta, float *gcs, float *partial, hipStream_t st);
 
 }  // namespace paro

@@ -68,8 +68,12 @@ int check_method_shape(const paro_w4_layer *L) {
 int check_gpu_shape(const paro_w4_layer *L) {
   int rc = check_method_shape(L);
   if (rc) return rc;
-  if (group_of(L) != 128)
-    return fail(PARO_ERR_UNSUPPORTED, "group_size=%d: the GPU path supports 128 only", L->group_size);
+  const int64_t G = group_of(L);
+  if (G != 32 && G != 64 && G != 128)
+    return fail(PARO_ERR_UNSUPPORTED, "group_size=%d: the GPU path supports 32, 64 and 128", L->group_size);
+  if (L->in_features % 128)
+    return fail(PARO_ERR_UNSUPPORTED, "in_features=%lld: the GPU path rotates 128-channel blocks",
+                (long long)L->in_features);
   if (L->krot > kMaxKrot) return fail(PARO_ERR_UNSUPPORTED, "krot=%d exceeds %d", L->krot, kMaxKrot);
   if (L->in_features > kMaxDim || L->out_features > kMaxOut)
     return fail(PARO_ERR_UNSUPPORTED, "in_features > %lld or out_features > %lld", (long long)kMaxDim,
@@ -115,6 +119,7 @@ paro::LinearArgs linear_args(const paro_w4_layer *L, int64_t tokens, const void 
   a.O = L->out_features;
   a.tokens = tokens;
   a.krot = L->krot;
+  a.group = (int)group_of(L);
   a.pairs = L->pairs;
   a.theta = L->theta;
   a.cs = L->channel_scales;
@@ -148,7 +153,7 @@ size_t workspace_for(const paro_w4_layer *L, int64_t tokens, paro_path path) {
   const int64_t I = L->in_features, O = L->out_features;
   size_t bytes = kCounterBytes + xr_region(L, tokens, path);
   if (path != PARO_PATH_PREFILL)
-    bytes += paro::decode_partial_bytes(paro::plan_decode(I, O, tokens, path == PARO_PATH_DECODE_FUSED), tokens, O);
+    bytes += paro::decode_partial_bytes(paro::plan_decode(I, O, tokens, path == PARO_PATH_DECODE_FUSED, (int)group_of(L)), tokens, O);
   else
     bytes += paro::rot_mat_bytes(I);
   return bytes;
@@ -203,7 +208,8 @@ int paro_scale_rotate(const paro_w4_layer *L, const void *x, paro_dtype x_dt, in
   if (overlap && !(x == x_r && x_dt == xr_dt))
     return fail(PARO_ERR_SHAPE, "x_r overlaps x (only exact in-place with equal dtypes is allowed)");
   hipError_t e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, x_r, (int)xr_dt, tokens, I, L->pairs,
-                                           L->theta, L->channel_scales, L->krot, (hipStream_t)stream);
+                                           L->theta, L->channel_scales, L->krot, (int)group_of(L),
+                                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
   return ok();
 }
@@ -227,7 +233,7 @@ int paro_rotation_matrix(const paro_w4_layer *L, paro_dtype x_dt, void *hl, void
   if (rc) return rc;
   if (!aligned(hl, 16)) return fail(PARO_ERR_ALIGN, "hl must be 16-byte aligned");
   hipError_t e = paro::launch_rot_build((int)x_dt, L->in_features, L->pairs, L->theta, L->channel_scales, L->krot,
-                                        (uint16_t *)hl, (hipStream_t)stream);
+                                        (int)group_of(L), (uint16_t *)hl, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
   return ok();
 }
@@ -313,7 +319,8 @@ int paro_w4_quantize_pack(const paro_w4_layer *L, const void *w, paro_dtype w_dt
         return fail(PARO_ERR_SHAPE, "qweight, qzeros and scales must not overlap");
   }
   hipError_t e = paro::launch_quantize_pack(w, (int)w_dt, symmetric != 0, O, I, L->pairs, L->theta,
-                                            L->channel_scales, L->krot, qweight, qzeros, scales, (hipStream_t)stream);
+                                            L->channel_scales, L->krot, (int)group_of(L), qweight, qzeros, scales,
+                                            (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
   return ok();
 }
@@ -360,7 +367,7 @@ int paro_scale_rotate_backward(const paro_w4_layer *L, const void *x, paro_dtype
       if (overlap(out[i], out[j])) return fail(PARO_ERR_SHAPE, "gx, gtheta, gcs and the workspace must not overlap");
   }
   hipError_t e = paro::launch_rot_backward(x, (int)x_dt, g, (int)g_dt, tokens, I, L->pairs, L->theta,
-                                           L->channel_scales, L->krot, gx, (int)gx_dt, gtheta, gcs,
+                                           L->channel_scales, L->krot, (int)group_of(L), gx, (int)gx_dt, gtheta, gcs,
                                            (float *)workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scale_rotate_backward launch");
   return ok();
@@ -434,7 +441,7 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
   char *xr = (char *)workspace + kCounterBytes;
   float *partials = (float *)(xr + xr_region(L, tokens, path));
   if (path == PARO_PATH_DECODE_FUSED) {
-    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, true);
+    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, true, a.group);
     e = paro::launch_decode(a, p, nullptr, counters, partials, st);
     if (e != hipSuccess) return hip_fail(e, "decode (fused) launch");
     return ok();
@@ -443,11 +450,11 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     const void *xin = x;
     if (!prerotated) {
       e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
-                                    L->channel_scales, L->krot, st);
+                                    L->channel_scales, L->krot, a.group, st);
       if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
       xin = xr;
     }
-    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, false);
+    const paro::DecodePlan p = paro::plan_decode(I, O, tokens, false, a.group);
     e = paro::launch_decode(a, p, xin, counters, partials, st);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
@@ -461,7 +468,7 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     if (e != hipSuccess) return hip_fail(e, "retile launch");
   } else {
     uint16_t *hl = (uint16_t *)((char *)xr + xr_region(L, tokens, path));
-    e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot, hl, st);
+    e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot, a.group, hl, st);
     if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
     e = paro::launch_rot_apply((const uint16_t *)x, (int)x_dt, xt, tokens, I, hl, st);
     if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");

@@ -137,7 +137,7 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
     *reinterpret_cast<uint32_t *>(bl + (8 * w + awq_col(s)) * kBStride + 2 * prp) = v[s];
 }
 
-template <int DT>
+template <int DT, int GK>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
@@ -152,7 +152,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
   const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * kBN;
   const int64_t mb = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * kBM;
-  const int nsteps = (int)(I / kBK), ngroups = (int)(I / kG);
+  // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
+  const int nsteps = (int)(I / kBK), ngroups = (int)(I / (kBK * GK));
 
   // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
   // the (16-row padded) tiled buffer; later ones read as zeros.
@@ -197,19 +198,31 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
     };
 
+    // Scales and zeros: a ring of NSLOT groups.  Group q sits in slot
+    // q % NSLOT; it is decoded just before the first k-step of the group is
+    // expanded, and the slot is refilled at once with group q + NSLOT.  Every
+    // slot index below is a compile-time constant: the step's value mod 8 is.
+    constexpr int NSLOT = GK == 1 ? 4 : 2;
     GroupConsts<DT> gc;
-    GroupRaw graw[2];
+    GroupRaw graw[NSLOT];
     Words wd[kWordRing];
-    load_group(0, graw[0]);
-    load_group(1, graw[1]);
+#pragma unroll
+    for (int q = 0; q < NSLOT; ++q) load_group(q, graw[q]);
 #pragma unroll
     for (int k = 0; k < kWordRing; ++k) load_words(k, wd[k]);
-    gc.decode(graw[0].sw, graw[0].zw);
-    load_group(2, graw[0]);
+    // step st (st % 8 == sm): enter its group if it is the group's first step
+    auto enter_group = [&](int sm, int st) {
+      if (sm % GK == 0) {
+        GroupRaw &gr = graw[(sm / GK) % NSLOT];
+        gc.decode(gr.sw, gr.zw);
+        load_group(st / GK + NSLOT, gr);
+      }
+    };
     // tiles 0..3 before the first barrier: the consumers' first super-step
     // computes steps 0, 1 and reads the fragments of steps 2 and 3
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      enter_group(k, k);
       expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, bl[k], dw, drp);
       load_words(k + kWordRing, wd[k]);
       __builtin_amdgcn_sched_barrier(0);  // one expansion's temporaries live at a time
@@ -220,20 +233,15 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     // 2S+5 into tiles (2S+4)%8, (2S+5)%8.  Their first reader runs in
     // super-step S+1, after the barrier that ends S; their slots' previous
     // tiles (2S-4, 2S-3) were last read in super-step S-2.  Each word slot is
-    // refilled kWordRing steps ahead.  A group spans two super-steps: its
-    // scales and zeros are decoded at the start of its first one and were
-    // fetched two groups earlier.  Past the end everything runs on clamped,
-    // in-bounds addresses into tiles no consumer uses.
+    // refilled kWordRing steps ahead.  Past the end everything runs on
+    // clamped, in-bounds addresses into tiles no consumer uses.
     // kk: position of S in a four-super-step iteration whose first S is a
     // multiple of 4, so that the ring slots (2kk+4+u) % 8 are constants.
-    auto psuper = [&](int S, int kk, bool new_group, GroupRaw &graw_slot, int g_refill) {
-      if (new_group) {
-        gc.decode(graw_slot.sw, graw_slot.zw);
-        load_group(g_refill, graw_slot);
-      }
+    auto psuper = [&](int S, int kk) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int slot = (2 * kk + 4 + u) % kTiles;  // == (2S+4+u) % 8
+        enter_group(slot, 2 * S + 4 + u);
         Words &w = wd[slot];
         expand_pair_to_lds<DT>(w.ra, w.rb, gc, bl[slot], dw, drp);
         load_words(2 * S + 4 + u + kWordRing, w);
@@ -241,14 +249,14 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       }
       __syncthreads();
     };
-    for (int g = 0; g < ngroups; g += 2) {
-      // two groups (four super-steps) per iteration
-      const int S0 = 2 * g;
-      psuper(S0, 0, true, graw[1], g + 3);      // decodes group g+1
-      psuper(S0 + 1, 1, false, graw[1], 0);
-      if (g + 1 < ngroups) {
-        psuper(S0 + 2, 2, true, graw[0], g + 4);  // decodes group g+2
-        psuper(S0 + 3, 3, false, graw[0], 0);
+    const int nsuper = nsteps / 2;  // a multiple of 2 (I % 128 == 0)
+    for (int S0 = 0; S0 < nsuper; S0 += 4) {
+      // four super-steps (eight k-steps) per iteration
+      psuper(S0, 0);
+      psuper(S0 + 1, 1);
+      if (S0 + 2 < nsuper) {
+        psuper(S0 + 2, 2);
+        psuper(S0 + 3, 3);
       }
     }
     return;
@@ -376,12 +384,19 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   }
 }
 
+template <int GK>
+static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
+  if (a.x_dt == kF16)
+    hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK>), grid, dim3(kThreads), 0, st, a, x);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16, GK>), grid, dim3(kThreads), 0, st, a, x);
+}
+
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
   dim3 grid((unsigned)(((a.O + kBN - 1) / kBN) * ((a.tokens + kBM - 1) / kBM)));
-  if (a.x_dt == kF16)
-    hipLaunchKernelGGL((prefill_gemm_kernel<kF16>), grid, dim3(kThreads), 0, st, a, x);
-  else
-    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16>), grid, dim3(kThreads), 0, st, a, x);
+  if (a.group == 32) launch_prefill_gk<1>(a, x, grid, st);
+  else if (a.group == 64) launch_prefill_gk<2>(a, x, grid, st);
+  else launch_prefill_gk<4>(a, x, grid, st);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 //                             transforms; W is [O][I], the stored channel
 //                             scales are D^-1, so they divide W's input
 //                             channels; R is the staged rotation)
-//   per output row n and group g of 128 input channels ("GPTQ, GPTAQ, and
+//   per output row n and group g of G input channels ("GPTQ, GPTAQ, and
 //   RTN" wiki, quantizer; "ParoQuant" wiki, Straight-through estimation):
 //     xmin = min(0, min x), xmax = max(0, max x)
 //     symmetric: xmax = max(-xmin, xmax), xmin = -xmax when xmin < 0, zero = 8
@@ -18,9 +18,10 @@
 //   scales [I/G][O] as fp16 (round to nearest even of the fp32 scale).
 // Every decision is taken in fp32 with correctly rounded division.
 //
-// A workgroup (4 waves) takes one group g and 64 output rows; a wave takes 16
-// rows, rotates them in LDS with the activation path's staged code, reduces
-// each row's range across the wave, and quantizes.  Lane p holds input
+// A workgroup (4 waves) takes one 128-channel block and 64 output rows; a
+// wave takes 16 rows, rotates them in LDS with the activation path's staged
+// code, reduces each row's range across the lanes of each G-group (G/2
+// lanes), and quantizes.  Lane p holds input
 // channels 2p, 2p+1 of all 16 rows, so it packs the qweight words of its two
 // channels (8 rows each) without any exchange.
 #include "common.hpp"
@@ -46,7 +47,7 @@ __device__ __forceinline__ float2 load_w_pair(const void *w, int64_t idx) {
 template <int WDT, bool SYM>
 __global__ void __launch_bounds__(256)
 quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int16_t *__restrict__ pairs,
-                     const float *__restrict__ theta, const float *__restrict__ cscale, int krot,
+                     const float *__restrict__ theta, const float *__restrict__ cscale, int krot, int group,
                      int32_t *__restrict__ qweight, int32_t *__restrict__ qzeros, uint16_t *__restrict__ scales) {
   constexpr int RW = 16;
   __shared__ float lds[4][RW * kQRS];
@@ -56,8 +57,9 @@ quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int
   if (n0 >= O) return;                                       // wave-uniform; no barriers below
   float *xs = lds[wave];
 
+  const int gmask = kG - group;
   RotParams rp;
-  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
   const float2 csv = *reinterpret_cast<const float2 *>(cscale + g * kG + 2 * lane);
 
   // W . D: the weight's input channels divided by the stored D^-1
@@ -69,9 +71,10 @@ quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int
     xs[m * kQRS + 2 * lane + 1] = v.y / csv.y;
   }
   wave_lds_sync();
-  rotate_rows_lds<RW>(xs, kQRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  rotate_rows_lds<RW>(xs, kQRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
 
-  // per row: range over the wave (zero included), parameters, codes
+  // per row: range over the lanes of this lane's quantization group (G/2
+  // lanes; zero included), parameters, codes
   uint32_t q0[RW], q1[RW];  // codes of channels 2p, 2p+1
   uint32_t zc[RW];
   float sc[RW];
@@ -81,8 +84,10 @@ quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int
     float lo = fminf(fminf(x0, x1), 0.0f), hi = fmaxf(fmaxf(x0, x1), 0.0f);
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      lo = fminf(lo, __shfl_xor(lo, d));
-      hi = fmaxf(hi, __shfl_xor(hi, d));
+      if (2 * d < group) {  // uniform: stays inside the G/2 lanes of the group
+        lo = fminf(lo, __shfl_xor(lo, d));
+        hi = fmaxf(hi, __shfl_xor(hi, d));
+      }
     }
     if (SYM) {
       hi = fmaxf(-lo, hi);
@@ -101,7 +106,10 @@ quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int
     sc[m] = scale;
   }
 
-  // AWQ packing: column 8w+j of a word sits at nibble slot awq_slot(j)
+  // AWQ packing: column 8w+j of a word sits at nibble slot awq_slot(j).
+  // This lane's quantization group (of I/G) and its index in that group.
+  const int64_t qg = (g * kG + 2 * lane) / group;
+  const int ql = (2 * lane) % group / 2;
   const int64_t W8 = O / 8;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -118,37 +126,38 @@ quantize_pack_kernel(const void *__restrict__ w, int64_t O, int64_t I, const int
     const int64_t k = g * kG + 2 * lane;
     qweight[k * W8 + wcol] = (int32_t)w0;
     qweight[(k + 1) * W8 + wcol] = (int32_t)w1;
-    if (lane == 0) qzeros[g * W8 + wcol] = (int32_t)wz;
+    if (ql == 0) qzeros[qg * W8 + wcol] = (int32_t)wz;  // the first lane of each group
   }
-  // scales: lane m < 16 writes row n0 + m
+  // scales: lane ql < 16 of each group writes row n0 + ql of that group
   float my_scale = sc[0];
 #pragma unroll
   for (int m = 1; m < RW; ++m)
-    if (lane == m) my_scale = sc[m];
-  if (lane < RW && n0 + lane < O) scales[g * O + n0 + lane] = f32_to_f16_bits(my_scale);
+    if (ql == m) my_scale = sc[m];
+  if (ql < RW && n0 + ql < O) scales[qg * O + n0 + ql] = f32_to_f16_bits(my_scale);
 }
 
 template <int WDT>
 static void launch_q(bool sym, dim3 grid, hipStream_t st, const void *w, int64_t O, int64_t I, const int16_t *pairs,
-                     const float *theta, const float *cs, int krot, int32_t *qw, int32_t *qz, uint16_t *sc) {
+                     const float *theta, const float *cs, int krot, int group, int32_t *qw, int32_t *qz,
+                     uint16_t *sc) {
   if (sym)
-    hipLaunchKernelGGL((quantize_pack_kernel<WDT, true>), grid, dim3(256), 0, st, w, O, I, pairs, theta, cs, krot, qw,
-                       qz, sc);
+    hipLaunchKernelGGL((quantize_pack_kernel<WDT, true>), grid, dim3(256), 0, st, w, O, I, pairs, theta, cs, krot,
+                       group, qw, qz, sc);
   else
     hipLaunchKernelGGL((quantize_pack_kernel<WDT, false>), grid, dim3(256), 0, st, w, O, I, pairs, theta, cs, krot,
-                       qw, qz, sc);
+                       group, qw, qz, sc);
 }
 
 hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, int64_t I, const int16_t *pairs,
-                                const float *theta, const float *cs, int krot, int32_t *qweight, int32_t *qzeros,
-                                uint16_t *scales, hipStream_t st) {
+                                const float *theta, const float *cs, int krot, int group, int32_t *qweight,
+                                int32_t *qzeros, uint16_t *scales, hipStream_t st) {
   const dim3 grid((unsigned)(I / kG), (unsigned)((O + 63) / 64));
   if (w_dt == kF16)
-    launch_q<kF16>(sym, grid, st, w, O, I, pairs, theta, cs, krot, qweight, qzeros, scales);
+    launch_q<kF16>(sym, grid, st, w, O, I, pairs, theta, cs, krot, group, qweight, qzeros, scales);
   else if (w_dt == kBF16)
-    launch_q<kBF16>(sym, grid, st, w, O, I, pairs, theta, cs, krot, qweight, qzeros, scales);
+    launch_q<kBF16>(sym, grid, st, w, O, I, pairs, theta, cs, krot, group, qweight, qzeros, scales);
   else
-    launch_q<kF32>(sym, grid, st, w, O, I, pairs, theta, cs, krot, qweight, qzeros, scales);
+    launch_q<kF32>(sym, grid, st, w, O, I, pairs, theta, cs, krot, group, qweight, qzeros, scales);
   return hipGetLastError();
 }
 

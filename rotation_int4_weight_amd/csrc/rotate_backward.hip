@@ -224,7 +224,7 @@ bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_
 template <int MDT>
 __global__ void __launch_bounds__(256)
 bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const int16_t *__restrict__ pairs,
-                const float *__restrict__ theta, const float *__restrict__ cscale, int krot,
+                const float *__restrict__ theta, const float *__restrict__ cscale, int krot, int gmask,
                 float *__restrict__ gcs, float *__restrict__ tpart, uint16_t *__restrict__ hl) {
   constexpr int RW = kWalkRows;
   __shared__ float lds[4][2][RW * kBwdRS];
@@ -241,7 +241,7 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
 #pragma unroll
   for (int u = 0; u < kStageRegs; ++u) {
     const int t = krot - 1 - u >= 0 ? krot - 1 - u : 0;
-    pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    pw[u] = load_pair_word(pairs_g, I, t, lane, gmask);
     th[u] = theta_g[(int64_t)t * (I / 2) + lane];
   }
 
@@ -285,7 +285,7 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
     }
   }
   for (int t = krot - 1 - kStageRegs; t >= 0; --t) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    const uint32_t w = load_pair_word(pairs_g, I, t, lane, gmask);
     float c, sn;
     __sincosf(theta_g[(int64_t)t * (I / 2) + lane], &sn, &c);
     rotate_stage<RW>(vs, kBwdRS, w, c, -sn);
@@ -313,7 +313,7 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
   // forward stages on v_i and f_i; after stage t, lane p adds
   // f_i[b] v_i[a] - f_i[a] v_i[b] over the wave's rows
   RotParams rp;
-  rp.load(pairs_g, I, theta_g, I / 2, krot, lane);
+  rp.load(pairs_g, I, theta_g, I / 2, krot, lane, gmask);
   float *prow = tpart + ((int64_t)blockIdx.y * 4 + wave) * ((int64_t)krot * (I / 2)) + g * kPairs + lane;
   for (int t = 0; t < krot; ++t) {
     uint32_t w;
@@ -328,7 +328,7 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
           tht = rp.th[u];
         }
     } else {
-      w = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+      w = load_pair_word(pairs_g, I, t, lane, gmask);
       tht = theta_g[(int64_t)t * (I / 2) + lane];
     }
     float c, s;
@@ -580,8 +580,8 @@ static void launch_dx(int gx_dt, dim3 grid, hipStream_t st, const void *g, void 
 }
 
 hipError_t launch_rot_backward(const void *x, int x_dt, const void *gin, int g_dt, int64_t tokens, int64_t I,
-                               const int16_t *pairs, const float *theta, const float *cs, int krot, void *gx,
-                               int gx_dt, float *gtheta, float *gcs, float *partial, hipStream_t st) {
+                               const int16_t *pairs, const float *theta, const float *cs, int krot, int group,
+                               void *gx, int gx_dt, float *gtheta, float *gcs, float *partial, hipStream_t st) {
   const BwdLayout L = bwd_layout(tokens, I, krot);
   char *ws = reinterpret_cast<char *>(partial);
   uint16_t *hl = reinterpret_cast<uint16_t *>(ws + L.hl_off);
@@ -605,10 +605,10 @@ hipError_t launch_rot_backward(const void *x, int x_dt, const void *gin, int g_d
   const dim3 wgrid(groups, kG / (4 * kWalkRows));
   if (dx_mdt(g_dt) == kF16)
     hipLaunchKernelGGL((bwd_walk_kernel<kF16>), wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta, cs,
-                       krot, gcs, tpart, hl);
+                       krot, kG - group, gcs, tpart, hl);
   else
     hipLaunchKernelGGL((bwd_walk_kernel<kBF16>), wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta,
-                       cs, krot, gcs, tpart, hl);
+                       cs, krot, kG - group, gcs, tpart, hl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -24,7 +24,7 @@ template <int XDT, int ODT, int RW>
 __global__ void __launch_bounds__(256)
 scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64_t tokens, int64_t I,
                     const int16_t *__restrict__ pairs, const float *__restrict__ theta,
-                    const float *__restrict__ cscale, int krot) {
+                    const float *__restrict__ cscale, int krot, int gmask) {
   __shared__ float lds[4][RW * kRotRS];
   const int lane = lane_id(), wave = wave_id();
   const int64_t g = blockIdx.x;
@@ -35,7 +35,7 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
   const int64_t c0 = g * kG + 2 * lane;
 
   RotParams rp;
-  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
   // load + channel scale (x . D^-1); rows past the last token are zero
   const float s0 = cscale[c0], s1 = cscale[c0 + 1];
 #pragma unroll
@@ -47,7 +47,7 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
   }
   wave_lds_sync();
 
-  rotate_rows_lds<RW>(xs, kRotRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane);
+  rotate_rows_lds<RW>(xs, kRotRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
 
 #pragma unroll
   for (int m = 0; m < RW; ++m) {
@@ -103,7 +103,7 @@ __device__ __forceinline__ int channel_of_mfma_row(int r) {
 template <int XDT>
 __global__ void __launch_bounds__(64)
 rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__restrict__ theta,
-                 const float *__restrict__ cscale, int krot, uint16_t *__restrict__ hl) {
+                 const float *__restrict__ cscale, int krot, int gmask, uint16_t *__restrict__ hl) {
   constexpr int RW = kBuildRows;
   __shared__ float xs[RW * kRotRS];
   const int lane = lane_id();
@@ -118,7 +118,7 @@ rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__re
 #pragma unroll
   for (int u = 0; u < kStageRegs; ++u) {
     const int t = krot - 1 - u >= 0 ? krot - 1 - u : 0;
-    pw[u] = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    pw[u] = load_pair_word(pairs_g, I, t, lane, gmask);
     th[u] = theta_g[(int64_t)t * (I / 2) + lane];
   }
   const float2 cs2 = *reinterpret_cast<const float2 *>(cscale + g * kG + 2 * lane);
@@ -140,7 +140,7 @@ rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__re
     }
   }
   for (int t = krot - 1 - kStageRegs; t >= 0; --t) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(pairs_g + (int64_t)t * I + 2 * lane);
+    const uint32_t w = load_pair_word(pairs_g, I, t, lane, gmask);
     float c, sn;
     __sincosf(theta_g[(int64_t)t * (I / 2) + lane], &sn, &c);
     rotate_stage<RW>(xs, kRotRS, w, c, -sn);
@@ -276,12 +276,13 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
 size_t rot_mat_bytes(int64_t I) { return (size_t)(I / kG) * (size_t)kRotMatHalves * 2; }
 
 hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const float *theta, const float *cs,
-                            int krot, uint16_t *hl, hipStream_t st) {
+                            int krot, int group, uint16_t *hl, hipStream_t st) {
   const dim3 grid((unsigned)(I / kG), kG / kBuildRows);
+  const int gm = kG - group;
   if (x_dt == kF16)
-    hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, hl);
+    hipLaunchKernelGGL((rot_build_kernel<kF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, gm, hl);
   else
-    hipLaunchKernelGGL((rot_build_kernel<kBF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, hl);
+    hipLaunchKernelGGL((rot_build_kernel<kBF16>), grid, dim3(64), 0, st, I, pairs, theta, cs, krot, gm, hl);
   return hipGetLastError();
 }
 
@@ -321,33 +322,34 @@ hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64
 
 template <int XDT, int ODT, int RW>
 static hipError_t launch_rot_rw(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
-                                const float *theta, const float *cs, int krot, hipStream_t st) {
+                                const float *theta, const float *cs, int krot, int gm, hipStream_t st) {
   const int64_t per_block = 4 * RW;
   dim3 grid((unsigned)(I / kG), (unsigned)((tokens + per_block - 1) / per_block));
   hipLaunchKernelGGL((scale_rotate_kernel<XDT, ODT, RW>), grid, dim3(256), 0, st, x, xr, tokens, I, pairs,
-                     theta, cs, krot);
+                     theta, cs, krot, gm);
   return hipGetLastError();
 }
 
 template <int XDT, int ODT>
 static hipError_t launch_rot(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
-                             const float *theta, const float *cs, int krot, hipStream_t st) {
-  if (tokens <= 4) return launch_rot_rw<XDT, ODT, 1>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-  if (tokens <= 64) return launch_rot_rw<XDT, ODT, 4>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-  return launch_rot_rw<XDT, ODT, 16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+                             const float *theta, const float *cs, int krot, int gm, hipStream_t st) {
+  if (tokens <= 4) return launch_rot_rw<XDT, ODT, 1>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+  if (tokens <= 64) return launch_rot_rw<XDT, ODT, 4>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+  return launch_rot_rw<XDT, ODT, 16>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
 }
 
 hipError_t launch_scale_rotate(const uint16_t *x, int x_dt, void *xr, int xr_dt, int64_t tokens, int64_t I,
                                const int16_t *pairs, const float *theta, const float *cs, int krot,
-                               hipStream_t st) {
+                               int group, hipStream_t st) {
+  const int gm = kG - group;
   if (x_dt == kF16) {
-    if (xr_dt == kF16) return launch_rot<kF16, kF16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-    if (xr_dt == kBF16) return launch_rot<kF16, kBF16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-    return launch_rot<kF16, kF32>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+    if (xr_dt == kF16) return launch_rot<kF16, kF16>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+    if (xr_dt == kBF16) return launch_rot<kF16, kBF16>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+    return launch_rot<kF16, kF32>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
   }
-  if (xr_dt == kF16) return launch_rot<kBF16, kF16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-  if (xr_dt == kBF16) return launch_rot<kBF16, kBF16>(x, xr, tokens, I, pairs, theta, cs, krot, st);
-  return launch_rot<kBF16, kF32>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  if (xr_dt == kF16) return launch_rot<kBF16, kF16>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+  if (xr_dt == kBF16) return launch_rot<kBF16, kBF16>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
+  return launch_rot<kBF16, kF32>(x, xr, tokens, I, pairs, theta, cs, krot, gm, st);
 }
 
 }  // namespace paro

@@ -104,7 +104,9 @@ def lin(L, x=FAKE, xdt=0, tokens=4, y=FAKE * 2, ydt=0, ws=FAKE * 4, wsb=1 << 30,
 
 @needs_no_gpu
 @pytest.mark.parametrize("case,code", [
-    (dict(L=dict(G=64)), 5),             # only G = 128 on the GPU
+    (dict(L=dict(G=16)), 5),             # G in {32, 64, 128} on the GPU
+    (dict(L=dict(G=256, I=512)), 5),
+    (dict(L=dict(G=64, I=320)), 5),      # 128-channel rotation blocks: I % 128 == 0
     (dict(L=dict(G=-1, I=256)), 5),      # G = I = 256
     (dict(L=dict(O=60)), 2),             # O % 8
     (dict(L=dict(G=100)), 2),            # G does not divide I
@@ -195,7 +197,7 @@ def test_tiled_entry_point_argument_checks():
     assert mat(hl=FAKE * 8 + 4) == 4
     assert mat(L=fake_layer(pairs=0)) == 1
     assert mat(L=fake_layer(theta=0)) == 1
-    assert mat(L=fake_layer(G=64)) == 5
+    assert mat(L=fake_layer(G=16)) == 5
     rot = lambda x=FAKE, dt=0, tokens=4, xt=FAKE * 2, hl=FAKE * 8, L=L: lib.paro_scale_rotate_tiled(
         ctypes.byref(L), hl, x, dt, tokens, xt, None)
     assert rot(dt=2) == 3                      # fp32 activations not accepted
@@ -207,14 +209,14 @@ def test_tiled_entry_point_argument_checks():
     assert rot(hl=FAKE * 2 + 4096) == 2        # x_t overlaps hl
     assert rot(tokens=0, x=0, xt=0, hl=0) == 0
     assert rot(tokens=-1) == 2
-    assert rot(L=fake_layer(G=64)) == 5
+    assert rot(L=fake_layer(G=16)) == 5
     lin = lambda xt=FAKE, dt=0, tokens=4, y=FAKE * 4, ydt=0, L=L: lib.paro_w4a16_linear_tiled(
         ctypes.byref(L), xt, dt, tokens, y, ydt, None)
     assert lin(ydt=1) == 3                     # y must be x dtype or fp32
     assert lin(y=0) == 1
     assert lin(y=FAKE + 64) == 2               # overlaps the tiled x
     assert lin(L=fake_layer(qweight=0)) == 1
-    assert lin(L=fake_layer(G=64)) == 5
+    assert lin(L=fake_layer(G=16)) == 5
     assert lin(tokens=0, xt=0, y=0) == 0
     assert lin(L=fake_layer(pairs=0, theta=0, channel_scales=0)) != 1  # rotation tensors unused
 
@@ -236,7 +238,7 @@ def test_quantize_pack_argument_checks():
     assert call(sc=FAKE + sc_off + 1) == 4
     assert call(w=FAKE) == 2                      # w overlaps qweight
     assert call(qz=FAKE + 64) == 2                # qzeros inside qweight
-    assert call(L=fake_layer(I=256, O=64, G=64)) == 5
+    assert call(L=fake_layer(I=256, O=64, G=16)) == 5
     assert call(L=fake_layer(I=256, O=64, pairs=0)) == 1
 
 
@@ -249,7 +251,8 @@ def test_scale_rotate_backward_argument_checks():
     assert need == 2 * 2 * 128 * 128 * 2 + 2 * 128 * 128 * 4 + 16 * 8 * 128 * 4
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == need + 2 * 128 * 128 * 4
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == need   # the walk still runs
-    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == 0
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=16)), 4) == 0
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == need
 
     def call(x=FAKE * 8, xdt=0, g=FAKE * 9, gdt=2, tokens=4, gx=FAKE * 10, gxdt=2, gth=FAKE * 11,
              gcs=FAKE * 12, ws=FAKE * 13, wsb=need, L=L):
@@ -273,5 +276,5 @@ def test_scale_rotate_backward_argument_checks():
     assert call(ws=FAKE * 10 + 16) == 2               # workspace overlaps gx
     assert call(gcs=FAKE * 11 + 16) == 2              # gcs overlaps gtheta
     assert call(tokens=-1) == 2
-    assert call(L=fake_layer(G=64)) == 5
+    assert call(L=fake_layer(G=16)) == 5
     assert call(L=fake_layer(pairs=0)) == 1

@@ -33,11 +33,11 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def gpu_quantize(D, w, dt, O, I, sym):
+def gpu_quantize(D, w, dt, O, I, sym, G=128):
     wd = x_to_device(w, dt)
     qw = torch.full((I, O // 8), -1, dtype=torch.int32, device="cuda")
-    qz = torch.full((I // 128, O // 8), -1, dtype=torch.int32, device="cuda")
-    sc = torch.full((I // 128, O), -1, dtype=torch.int16, device="cuda")
+    qz = torch.full((I // G, O // 8), -1, dtype=torch.int32, device="cuda")
+    sc = torch.full((I // G, O), -1, dtype=torch.int16, device="cuda")
     paro.paro_w4_quantize_pack(D, wd, sym, qw, qz, sc)
     torch.cuda.synchronize()
     return qw.cpu().numpy(), qz.cpu().numpy(), sc.cpu().numpy().view(np.uint16)
@@ -45,17 +45,17 @@ def gpu_quantize(D, w, dt, O, I, sym):
 
 def sub_layer(L, O):
     """The rotation of L with O output rows (weights irrelevant)."""
-    I, G = L.in_features, 128
+    I, G = L.in_features, L.group_size
     return synth.Layer(I, O, G, L.krot, L.pairs, L.theta, L.channel_scales,
                        np.zeros((I, O // 8), np.int32), np.zeros((I // G, O // 8), np.int32),
                        np.zeros((I // G, O), np.uint16), None)
 
 
-def unpack_cols(qw, qz, I, O):
-    """Oracle unpack of GPU words -> q [I][O], z [I/128][O]."""
-    L = synth.Layer(I, O, 128, 1, np.zeros((1, I), np.int16), np.zeros((1, I // 2), np.float32),
+def unpack_cols(qw, qz, I, O, G=128):
+    """Oracle unpack of GPU words -> q [I][O], z [I/G][O]."""
+    L = synth.Layer(I, O, G, 1, np.zeros((1, I), np.int16), np.zeros((1, I // 2), np.float32),
                     np.ones(I, np.float32), np.ascontiguousarray(qw), np.ascontiguousarray(qz),
-                    np.zeros((I // 128, O), np.uint16), None)
+                    np.zeros((I // G, O), np.uint16), None)
     return ref.unpack(L)
 
 
@@ -70,18 +70,17 @@ def f16_tie(scale):
 
 def compare(L, w, dt, sym, qw, qz, s16, rows):
     """Check the GPU's codes of output rows `rows` (multiple of 8 each block)."""
-    I, O = L.in_features, L.out_features
+    I, O, G = L.in_features, L.out_features, L.group_size
     sub = sub_layer(L, len(rows))
     wr = ref.transform_weight(sub, np.ascontiguousarray(w[rows]), dt)        # [R][I]
-    q_o, z_o, s_o, scale_o = ref.quantize(wr, 128, sym)                       # [I][R], [I/G][R]
-    q_g, z_g = unpack_cols(qw, qz, I, O)
+    q_o, z_o, s_o, scale_o = ref.quantize(wr, G, sym)                         # [I][R], [I/G][R]
+    q_g, z_g = unpack_cols(qw, qz, I, O, G)
     q_g, z_g, s_g = q_g[:, rows], z_g[:, rows], s16[:, rows]
     # scales: exact unless the oracle's scale is at an fp16 tie
     s_tie = f16_tie(scale_o)
     bad_s = (s_g != s_o) & ~(s_tie & (np.abs(s_g.astype(np.int64) - s_o.astype(np.int64)) == 1))
     assert not bad_s.any(), f"fp16 scales differ off ties at {np.argwhere(bad_s)[:5]}"
     # decision values of the oracle, per element: x / scale + zero
-    G = 128
     xmin = np.minimum(wr.reshape(len(rows), I // G, G).min(axis=2), 0.0).T   # [I/G][R]
     zval = -xmin / scale_o
     z_tie = (np.abs(zval - np.floor(zval) - 0.5) < TIE) if not sym else np.zeros_like(zval, bool)
@@ -94,7 +93,9 @@ def compare(L, w, dt, sym, qw, qz, s16, rows):
     diff = q_g.astype(int) - q_o.astype(int)
     bad_q = (diff != 0) & ~(tie & (np.abs(diff) == 1))
     assert not bad_q.any(), f"codes differ off ties at {np.argwhere(bad_q)[:5]}"
-    assert (diff != 0).mean() < 1e-3
+    # rare: symmetric groups put one element per group on the 7.5 tie, so the
+    # allowance scales with the number of groups (1e-3 at G = 128)
+    assert (diff != 0).mean() < 1e-3 * 128 / G
     return (diff != 0).sum()
 
 

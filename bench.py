@@ -56,6 +56,11 @@ KERNEL_FILES = {1: ("decode.hip", "common.hpp"), 2: ("decode.hip", "common.hpp")
                 3: ("prefill.hip", "common.hpp")}
 
 
+def gsuffix(args):
+    """Key suffix of a non-default group size in profiles/traffic.json."""
+    return "" if args.group == 128 else f"-g{args.group}"
+
+
 def kernel_source_hash(path):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rotation_int4_weight_amd", "csrc")
@@ -93,7 +98,7 @@ def bench_quantize(args, paro, synth, np, torch, dev):
     lname, I, O = spec["layers"][0]
     dt = spec["act"]
     tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
-    host = synth.make_layer(args.workload, 0, I, O)
+    host = synth.make_layer(args.workload, 0, I, O, group_size=args.group)
     w = synth.make_w(args.workload, 0, O, I, dt)
     w_bytes = O * I * 2
     nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // w_bytes)))
@@ -101,8 +106,8 @@ def bench_quantize(args, paro, synth, np, torch, dev):
     D = paro.DeviceLayer(host, device=dev)
     wds = [torch.from_numpy(w.view(np.int16)).to(dev).view(tdt) for _ in range(nsets)]
     qw = torch.empty((I, O // 8), dtype=torch.int32, device=dev)
-    qz = torch.empty((I // 128, O // 8), dtype=torch.int32, device=dev)
-    sc = torch.empty((I // 128, O), dtype=torch.int16, device=dev)
+    qz = torch.empty((I // args.group, O // 8), dtype=torch.int32, device=dev)
+    sc = torch.empty((I // args.group, O), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     step = lambda i: paro.paro_w4_quantize_pack(D, wds[i % nsets], True, qw, qz, sc, stream=stream)
     for i in range(args.warmup):
@@ -115,7 +120,7 @@ def bench_quantize(args, paro, synth, np, torch, dev):
     t1.record(stream)
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / args.steps
-    weight_b, rot_b = layer_bytes(I, O, host.krot, bias=False)
+    weight_b, rot_b = layer_bytes(I, O, host.krot, G=args.group, bias=False)
     alg = w_bytes + weight_b + rot_b           # W read once; codes, zeros, scales written; rotation read
     value = w_bytes / (us * 1e-6) / 1e9
     ach = alg / (us * 1e-6) / 1e9
@@ -123,14 +128,15 @@ def bench_quantize(args, paro, synth, np, torch, dev):
     if not args.no_cpu_baseline:
         from oracle import ref
         rows = 64
-        sub = synth.Layer(I, rows, 128, host.krot, host.pairs, host.theta, host.channel_scales,
-                          np.zeros((I, rows // 8), np.int32), np.zeros((I // 128, rows // 8), np.int32),
-                          np.zeros((I // 128, rows), np.uint16), None)
+        G = args.group
+        sub = synth.Layer(I, rows, G, host.krot, host.pairs, host.theta, host.channel_scales,
+                          np.zeros((I, rows // 8), np.int32), np.zeros((I // G, rows // 8), np.int32),
+                          np.zeros((I // G, rows), np.uint16), None)
         n, t_start = 0, time.perf_counter()
         while True:
             wr = ref.transform_weight(sub, np.ascontiguousarray(w[:rows]), dt)
-            q, z, s16, _ = ref.quantize(wr, 128, True)
-            ref.pack(q, z, 128)
+            q, z, s16, _ = ref.quantize(wr, G, True)
+            ref.pack(q, z, G)
             n += 1
             el = time.perf_counter() - t_start
             if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
@@ -142,11 +148,13 @@ def bench_quantize(args, paro, synth, np, torch, dev):
         "metric": QUANT_METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{lname}-weight-{O}x{I}-{'f16' if dt == synth.F16 else 'bf16'}-sym",
-                   "group_size": 128, "krot": host.krot, "weight_copies": nsets, "parallelism": "single-gpu"},
+        "config": {"workload": f"{lname}-weight-{O}x{I}-{'f16' if dt == synth.F16 else 'bf16'}-sym{gsuffix(args)}",
+                   "group_size": args.group, "krot": host.krot, "weight_copies": nsets,
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(f"quantize-{args.workload}", kernel_source_hash("quantize")),
+                     "traffic": load_traffic(f"quantize-{args.workload}{gsuffix(args)}",
+                                             kernel_source_hash("quantize")),
                      "kernel": "quantize_pack_kernel",
                      "avg_launch_us": round(us, 3)},
         "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("quantize"),
@@ -166,7 +174,7 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
     lname, I, O = spec["layers"][0]
     M, dt = max(spec["tokens"], 64), spec["act"]
     tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
-    host = synth.make_layer(args.workload, 0, I, O)
+    host = synth.make_layer(args.workload, 0, I, O, group_size=args.group)
     x = synth.make_x(args.workload, 0, M, I, dt)
     g = synth.make_g(args.workload, 0, M, I, dt)
     pair_bytes = 2 * M * I * 2
@@ -213,16 +221,16 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
         cpu = {"value": 3 * rows * I * 2 / (el / n) / 1e9, "unit": "GB/s", "cores": ref.threads(0),
                "kind": "oracle",
                "sample": f"{n} oracle backward call(s) on {rows} of {M} tokens of '{lname}' input, {el:.1f} s"}
-    wl = f"{lname}-input-backward-t{M}x{I}-{'f16' if dt == synth.F16 else 'bf16'}"
+    wl = f"{lname}-input-backward-t{M}x{I}-{'f16' if dt == synth.F16 else 'bf16'}{gsuffix(args)}"
     out = {
         "metric": BWD_METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl, "group_size": 128, "krot": host.krot, "input_copies": nsets,
+        "config": {"workload": wl, "group_size": args.group, "krot": host.krot, "input_copies": nsets,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(f"rotate_backward-{args.workload}",
+                     "traffic": load_traffic(f"rotate_backward-{args.workload}{gsuffix(args)}",
                                              kernel_source_hash("rotate_backward")),
                      "kernel": "bwd_gram + bwd_walk + bwd_dx + bwd_theta_reduce kernels (one entry point)",
                      "avg_launch_us": round(us, 3)},
@@ -245,6 +253,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=1, help="0..4 (synth.WORKLOADS)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode_fused, 2 decode_split, 3 prefill")
+    ap.add_argument("--group", type=int, default=128, choices=(32, 64, 128),
+                    help="rotation / quantization group size G of the synthetic layers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
@@ -296,9 +306,9 @@ def main():
     layers = []
     per_set = 0
     for li, (lname, I, O) in enumerate(spec["layers"]):
-        host = synth.make_layer(args.workload, li, I, O)
+        host = synth.make_layer(args.workload, li, I, O, group_size=args.group)
         x = synth.make_x(args.workload, li, M, I, act)
-        w_b, r_b = layer_bytes(I, O, host.krot)
+        w_b, r_b = layer_bytes(I, O, host.krot, G=args.group)
         per_set += w_b + r_b + M * I * 2
         layers.append((lname, I, O, host, x))
     nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // per_set)))
@@ -337,9 +347,10 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    weight_bytes = sum(layer_bytes(I, O, 8)[0] for _, I, O, _, _ in layers)
+    weight_bytes = sum(layer_bytes(I, O, 8, G=args.group)[0] for _, I, O, _, _ in layers)
     flops = sum(2.0 * M * I * O for _, I, O, _, _ in layers)
-    alg_bytes = sum(sum(layer_bytes(I, O, h.krot)) + M * I * 2 + M * O * 2 for _, I, O, h, _ in layers)
+    alg_bytes = sum(sum(layer_bytes(I, O, h.krot, G=args.group)) + M * I * 2 + M * O * 2
+                    for _, I, O, h, _ in layers)
     decode = path in (1, 2)
     if decode:
         value, unit = weight_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
@@ -418,7 +429,7 @@ def main():
             ach = kern["flops_per_launch"] / (kern["avg_us"] * 1e-6) / 1e12
             roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
-        roofline["traffic"] = load_traffic(args.workload, khash)
+        roofline["traffic"] = load_traffic(f"{args.workload}{gsuffix(args)}", khash)
         roofline["kernel"] = kern["name"]
         roofline["avg_launch_us"] = round(kern["avg_us"], 3)
 
@@ -438,7 +449,7 @@ def main():
                 break
         per_call = el / n
         if decode:
-            w_b = layer_bytes(I, O, host.krot)[0]
+            w_b = layer_bytes(I, O, host.krot, G=args.group)[0]
             cval, cunit = w_b / per_call / 1e9, "GB/s"
             sample = f"{n} full oracle calls on layer '{lname}' ({rows} token(s)), {el:.1f} s"
         else:
@@ -451,8 +462,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if act == synth.F16 else "bf16", "data": "synthetic",
-        "config": {"workload": spec["name"], "layers": [[n, I, O] for n, I, O, _, _ in layers], "tokens": M,
-                   "group_size": 128, "krot": 8, "path": PATH_NAMES[path], "buffer_sets": nsets,
+        "config": {"workload": spec["name"] + gsuffix(args), "layers": [[n, I, O] for n, I, O, _, _ in layers], "tokens": M,
+                   "group_size": args.group, "krot": 8, "path": PATH_NAMES[path], "buffer_sets": nsets,
                    "parallelism": "single-gpu"},
         "roofline": roofline, "cpu_baseline": cpu, "kernel_sources": khash,
     }

@@ -239,6 +239,79 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+MOE_METRIC = "ParoQuant MoE projection (shared rotation, stacked experts): TFLOP/s, % of MFMA roofline"
+KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp")
+
+
+def bench_moe(args, paro, synth, np, torch, dev):
+    """Time paro_w4a16_moe_linear on a mixture-of-experts workload (experts
+    stacked in one tensor, one shared rotation, seeded skewed top-k routing),
+    rotating through >= 512 MB of distinct expert weights."""
+    wl = args.workload if args.workload in synth.MOE_WORKLOADS else 5
+    spec = synth.MOE_WORKLOADS[wl]
+    lname, I, O = spec["layer"]
+    E, dt = spec["experts"], spec["act"]
+    tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
+    host = synth.make_moe_layer(wl, E, I, O, group_size=args.group)
+    offs = synth.make_routing(wl, E, spec["tokens"], spec["top_k"])
+    rows = int(offs[-1])
+    x = synth.make_x(wl, 0, rows, I, dt)
+    w_b, r_b = layer_bytes(I, O, host.krot, G=args.group)
+    set_bytes = E * w_b
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // set_bytes)))
+    log(f"moe: {spec['name']}: {E} experts of {lname} ({I} -> {O}), {rows} routed rows, loads "
+        f"{np.diff(offs).tolist()}, {nsets} weight sets")
+    Ds = [paro.DeviceLayer(host, device=dev) for _ in range(nsets)]
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
+    od = torch.from_numpy(offs).to(dev)
+    y = torch.empty((rows, O), dtype=tdt, device=dev)
+    ws = paro.make_workspace(paro.paro_w4a16_moe_linear_workspace_bytes(Ds[0], rows, dt), device=dev)
+    stream = torch.cuda.current_stream()
+    step = lambda i: paro.paro_w4a16_moe_linear(Ds[i % nsets], E, od, xd, y, ws, stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    flops = 2.0 * rows * I * O
+    value = flops / (us * 1e-6) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        e0 = int(np.argmax(np.diff(offs)))
+        n_rows = min(16, int(offs[e0 + 1] - offs[e0]))
+        sub = ref.expert_layer(host, e0)
+        xs = np.ascontiguousarray(x[offs[e0]:offs[e0] + n_rows])
+        n, t_start = 0, time.perf_counter()
+        while True:
+            ref.linear(sub, xs, dt)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = {"value": 2.0 * n_rows * I * O / (el / n) / 1e12, "unit": "TFLOP/s", "cores": ref.threads(0),
+               "kind": "oracle", "sample": f"{n} oracle call(s) on {n_rows} rows of expert {e0}, {el:.1f} s"}
+    out = {
+        "metric": MOE_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dt == synth.BF16 else "f16", "data": "synthetic",
+        "config": {"workload": spec["name"] + gsuffix(args), "experts": E, "routed_rows": rows,
+                   "top_k": spec["top_k"], "group_size": args.group, "krot": host.krot, "weight_sets": nsets,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "rot_build + rot_apply + prefill_gemm_kernel<MoE> (one entry point)",
+                     "avg_launch_us": round(us, 3)},
+        "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("moe"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bits_to_f64_host(bits, dt, np):
     """fp16 / bf16 bit patterns (uint16) -> float64 (the oracle takes g in double)."""
     if dt == 0:
@@ -258,10 +331,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
-    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward"), default="linear",
+    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward", "moe"), default="linear",
                     help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
                          "qzeros, scales) transform of the workload's first layer; rotate_backward: the "
-                         "calibration-time backward of the scaling and rotation over that layer's input")
+                         "calibration-time backward of the scaling and rotation over that layer's input; "
+                         "moe: the mixture-of-experts projection of workload 5 (synth.MOE_WORKLOADS)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark: copy BYTES between two device buffers --steps times "
                          "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -297,6 +371,9 @@ def main():
         return
     if args.op == "rotate_backward":
         bench_rotate_backward(args, paro, synth, np, torch, dev)
+        return
+    if args.op == "moe":
+        bench_moe(args, paro, synth, np, torch, dev)
         return
     spec = synth.WORKLOADS[args.workload]
     M, act = spec["tokens"], spec["act"]

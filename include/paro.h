@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARO_ABI_VERSION 3
+#define PARO_ABI_VERSION 4
 
 typedef enum {
   PARO_F16 = 0,  /* IEEE binary16 */
@@ -225,6 +225,38 @@ int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *hl, const vo
  */
 int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dtype x_dt,
                             int64_t tokens, void *y, paro_dtype y_dt, void *stream);
+
+/*
+ * Mixture-of-experts projection with one rotation shared by all experts
+ * ("ParoQuant" blog on the MLX port, technical notes: the experts' weights
+ * are stacked into one tensor and the rotations are shared between experts).
+ * The activations are scaled and rotated once for all experts, then each
+ * expert's rows go through that expert's quantized projection:
+ *   y[m] = x_r[m] . Q(W_e)^T + b_e   for offsets[e] <= m < offsets[e+1].
+ *   layer: in_features I, out_features O, group_size (32/64/128), krot and
+ *          pairs/theta/channel_scales as for paro_w4a16_linear (shared);
+ *          qweight [E][I][O/8], qzeros [E][I/G][O/8], scales [E][I/G][O] and
+ *          bias [E][O] (or NULL) stacked over the experts, expert-major.
+ *   expert_offsets: DEVICE int64 [E+1], 8-byte aligned; rows of x are grouped
+ *          by expert (the caller's routing: a token sent to k experts
+ *          appears k times).  Expected nondecreasing with offsets[0] = 0 and
+ *          offsets[E] = tokens; the kernels clamp them into [0, tokens] and
+ *          make them nondecreasing, so malformed offsets cannot cause an
+ *          out-of-bounds access, and rows outside every expert's range are
+ *          not written.
+ *   x [tokens][I] F16/BF16, y [tokens][O] x's dtype or F32, 16-byte aligned;
+ *   workspace: paro_w4a16_moe_linear_workspace_bytes bytes, 16-byte aligned.
+ * Runs on the prefill kernels (dense rotation on the matrix cores, then a
+ * grouped GEMM in which each workgroup takes one 256-row tile of one
+ * expert).  Errors as paro_w4a16_linear, plus PARO_ERR_SHAPE for
+ * num_experts outside 1..1024 and PARO_ERR_NULL / _ALIGN for the offsets.
+ */
+int paro_w4a16_moe_linear(const paro_w4_layer *layer, int num_experts, const int64_t *expert_offsets,
+                          const void *x, paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes paro_w4a16_moe_linear needs (0 for 0 tokens or an invalid layer). */
+size_t paro_w4a16_moe_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens, paro_dtype x_dt);
 
 /*
  * The offline step before the stored tensors exist: transform a dense weight

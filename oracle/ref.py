@@ -215,6 +215,30 @@ def pack(q, z, group_size: int):
     return qw, qz
 
 
+def expert_layer(layer, e: int):
+    """Expert e of a stacked mixture-of-experts layer as an ordinary layer
+    (the shared rotation and expert e's quantized weights and bias)."""
+    import dataclasses
+    return dataclasses.replace(layer, qweight=np.ascontiguousarray(layer.qweight[e]),
+                               qzeros=np.ascontiguousarray(layer.qzeros[e]),
+                               scales=np.ascontiguousarray(layer.scales[e]),
+                               bias=None if layer.bias is None else np.ascontiguousarray(layer.bias[e]))
+
+
+def moe_linear(layer, offsets, x, x_dt: int):
+    """Mixture-of-experts projection with one shared rotation ("ParoQuant" blog
+    on the MLX port, technical notes: stacked expert weights, rotations shared
+    between experts): rows offsets[e] .. offsets[e+1]-1 of x go through
+    expert e's linear, y double [rows][O].  Rows outside every range stay 0."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    y = np.zeros((x.shape[0], layer.out_features), dtype=np.float64)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y[lo:hi] = linear(expert_layer(layer, e), np.ascontiguousarray(x[lo:hi]), x_dt)
+    return y
+
+
 def scale_rotate_backward(layer, x, x_dt: int, g, n_threads: int = 0):
     """(gx [M][I], gtheta [krot][I/2], gcs [I]) for dL/dx_r = g (double [M][I])."""
     x = np.ascontiguousarray(x)

@@ -20,7 +20,8 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-           "paro_w4_quantize_pack", "paro_scale_rotate_backward",
+           "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
+           "paro_w4a16_moe_linear_workspace_bytes",
            "paro_scale_rotate_backward_workspace_bytes",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
@@ -65,6 +66,9 @@ def load(path: str | None = None):
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
     lib.paro_w4_quantize_pack.argtypes = [P, P, I32, I32, P, P, P, P]
+    lib.paro_w4a16_moe_linear.argtypes = [P, I32, P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_w4a16_moe_linear_workspace_bytes.argtypes = [P, I64, I32]
+    lib.paro_w4a16_moe_linear_workspace_bytes.restype = SZ
     lib.paro_scale_rotate_backward.argtypes = [P, P, I32, P, I32, I64, P, I32, P, P, P, SZ, P]
     lib.paro_scale_rotate_backward_workspace_bytes.argtypes = [P, I64]
     lib.paro_scale_rotate_backward_workspace_bytes.restype = SZ
@@ -82,7 +86,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
-                 "paro_w4_quantize_pack", "paro_scale_rotate_backward",
+                 "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
                  "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
@@ -228,6 +232,22 @@ def paro_w4_quantize_pack(layer: DeviceLayer, w, symmetric: bool, qweight, qzero
     scales fp16/int16 view (I/128, O)."""
     _check(load().paro_w4_quantize_pack(layer.ref, _ptr(w), _dt(w), int(bool(symmetric)), _ptr(qweight),
                                         _ptr(qzeros), _ptr(scales), _stream_handle(stream)), "paro_w4_quantize_pack")
+
+
+def paro_w4a16_moe_linear_workspace_bytes(layer: DeviceLayer, tokens: int, x_dt: int = F16) -> int:
+    """Workspace bytes of paro_w4a16_moe_linear for this many routed rows."""
+    return int(load().paro_w4a16_moe_linear_workspace_bytes(layer.ref, tokens, x_dt))
+
+
+def paro_w4a16_moe_linear(layer: DeviceLayer, num_experts: int, expert_offsets, x, y, workspace=None,
+                          stream=None) -> None:
+    """Experts stacked in `layer`'s weight tensors share its rotation.  expert_offsets: int64 device
+    tensor (E+1,); x: (rows, I) fp16/bf16 grouped by expert; y: (rows, O) x dtype or fp32."""
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_w4a16_moe_linear(layer.ref, int(num_experts), _ptr(expert_offsets), _ptr(x), _dt(x),
+                                        x.shape[0], _ptr(y), _dt(y), ws_ptr, ws_bytes, _stream_handle(stream)),
+           "paro_w4a16_moe_linear")
 
 
 def paro_scale_rotate_backward_workspace_bytes(layer: DeviceLayer, tokens: int) -> int:

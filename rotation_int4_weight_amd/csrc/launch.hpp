@@ -26,6 +26,10 @@ struct LinearArgs {
   int64_t I, O, tokens;
   int krot;
   int group;  // G: 32, 64 or 128 (rotation pairs and quantization groups)
+  // MoE (prefill only): experts > 0 stacked experts sharing the rotation,
+  // rows of expert e in [expert_offsets[e], expert_offsets[e+1]) (device)
+  int experts;
+  const int64_t *expert_offsets;
   const int16_t *pairs;
   const float *theta;
   const float *cs;
@@ -83,6 +87,8 @@ hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64
 
 // Prefill: MFMA GEMM over rotated activations in the tiled layout.
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStream_t st);
+// Upper bound on the (expert, 256-row tile) work items of a MoE call.
+int64_t moe_work_tiles(int64_t tokens, int experts);
 
 // W_r = W D R, group quantization and AWQ packing (the offline step):
 // w [O][I] (F16, BF16 or F32); qweight [I][O/8], qzeros [I/128][O/8],

@@ -131,6 +131,8 @@ paro::LinearArgs linear_args(const paro_w4_layer *L, int64_t tokens, const void 
   a.x_dt = (int)x_dt;
   a.y = y;
   a.y_dt = (int)y_dt;
+  a.experts = 0;
+  a.expert_offsets = nullptr;
   return a;
 }
 
@@ -396,9 +398,11 @@ size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens,
 namespace {
 
 // Shared body of the linear entry points.  prerotated: x already holds X_r.
+constexpr int kMaxExperts = 1024;  // each workgroup scans the expert offsets once
+
 int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
                 paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream, paro_path path,
-                bool prerotated) {
+                bool prerotated, int experts = 0, const int64_t *expert_offsets = nullptr) {
   int rc = check_gpu_shape(L);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
@@ -407,6 +411,13 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
   if (path < PARO_PATH_AUTO || path > PARO_PATH_PREFILL) return fail(PARO_ERR_SHAPE, "unknown path %d", (int)path);
   if (prerotated && path == PARO_PATH_DECODE_FUSED)
     return fail(PARO_ERR_SHAPE, "the fused decode path rotates itself; use AUTO, DECODE_SPLIT or PREFILL");
+  if (experts != 0) {
+    if (experts < 0 || experts > kMaxExperts)
+      return fail(PARO_ERR_SHAPE, "num_experts=%d must be in 1..%d", experts, kMaxExperts);
+    if (!expert_offsets) return fail(PARO_ERR_NULL, "expert_offsets is required");
+    if (!aligned(expert_offsets, 8)) return fail(PARO_ERR_ALIGN, "expert_offsets must be 8-byte aligned");
+    path = PARO_PATH_PREFILL;  // the grouped GEMM runs on the prefill kernel
+  }
   if (tokens == 0) return ok();
   if (path == PARO_PATH_AUTO) {
     path = auto_path(tokens);
@@ -434,6 +445,8 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
   }
 
   paro::LinearArgs a = linear_args(L, tokens, x, x_dt, y, y_dt);
+  a.experts = experts;
+  a.expert_offsets = expert_offsets;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
 
@@ -497,6 +510,18 @@ int paro_w4a16_linear_prerotated(const paro_w4_layer *L, const void *x_r, paro_d
 int paro_w4a16_linear(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
                       paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream) {
   return paro_w4a16_linear_path(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, PARO_PATH_AUTO);
+}
+
+int paro_w4a16_moe_linear(const paro_w4_layer *L, int num_experts, const int64_t *expert_offsets, const void *x,
+                          paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (num_experts == 0) return fail(PARO_ERR_SHAPE, "num_experts must be >= 1");
+  return linear_impl(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, PARO_PATH_PREFILL, false,
+                     num_experts, expert_offsets);
+}
+
+size_t paro_w4a16_moe_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens, paro_dtype x_dt) {
+  return paro_w4a16_linear_workspace_bytes(L, tokens, x_dt, PARO_PATH_PREFILL);
 }
 
 }  // extern "C"

@@ -137,7 +137,15 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
     *reinterpret_cast<uint32_t *>(bl + (8 * w + awq_col(s)) * kBStride + 2 * prp) = v[s];
 }
 
-template <int DT, int GK>
+// MOE: experts stacked in the weight tensors (qweight [E][I][O/8], qzeros
+// [E][I/G][O/8], scales [E][I/G][O], bias [E][O]) share one rotation; the
+// rows of expert e are [offsets[e], offsets[e+1]) of the rotated activations
+// (rotated once for all experts).  A workgroup takes one 256-row tile of one
+// expert's rows, starting at the 16-row tile that holds the expert's first
+// row: rows of neighbouring experts in its tiles are computed and dropped.
+// Offsets are clamped into [0, tokens] and made nondecreasing, so no offsets
+// can take a workgroup outside its buffers.
+template <int DT, int GK, bool MOE>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
@@ -148,16 +156,52 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // share an XCD and its L2.  The tile indices are uniform; readfirstlane
   // moves them (computed with VALU division) to scalar registers so that the
   // buffer descriptors derived from them stay scalar too.
-  const int n_tiles = (int)((O + kBN - 1) / kBN), m_tiles = (int)((M + kBM - 1) / kBM);
+  const int n_tiles = (int)((O + kBN - 1) / kBN);
+  const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + kBM - 1) / kBM);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
   const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * kBN;
-  const int64_t mb = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * kBM;
+  int64_t mb, row_lo = 0, row_hi = M;
+  const int32_t *qweight = a.qweight, *qzeros = a.qzeros;
+  const uint16_t *scales = a.scales, *bias = a.bias;
+  if constexpr (MOE) {
+    // work item (expert, 256-row tile) number lwg / n_tiles, experts in order
+    const int64_t wi = __builtin_amdgcn_readfirstlane(lwg / n_tiles);
+    int64_t cum = 0, prev = a.expert_offsets[0];
+    prev = prev < 0 ? 0 : (prev > M ? M : prev);
+    int e = -1;
+    int64_t lo = 0, hi = 0, j = 0;
+    for (int k = 0; k < a.experts; ++k) {
+      int64_t o1 = a.expert_offsets[k + 1];
+      o1 = o1 < prev ? prev : (o1 > M ? M : o1);
+      const int64_t t = o1 > prev ? (o1 - (prev & ~(int64_t)15) + kBM - 1) / kBM : 0;
+      if (wi < cum + t) {
+        e = k;
+        lo = prev;
+        hi = o1;
+        j = wi - cum;
+        break;
+      }
+      cum += t;
+      prev = o1;
+    }
+    if (e < 0) return;  // past the last tile: the whole workgroup leaves before any barrier
+    mb = (lo & ~(int64_t)15) + j * kBM;
+    row_lo = lo > mb ? lo : mb;
+    row_hi = hi < mb + kBM ? hi : mb + kBM;
+    const int64_t G = (int64_t)kBK * GK;
+    qweight += (int64_t)e * I * W;
+    qzeros += (int64_t)e * (I / G) * W;
+    scales += (int64_t)e * (I / G) * O;
+    if (bias) bias += (int64_t)e * O;
+  } else {
+    mb = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * kBM;
+  }
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
   const int nsteps = (int)(I / kBK), ngroups = (int)(I / (kBK * GK));
 
   // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
   // the (16-row padded) tiled buffer; later ones read as zeros.
-  const int64_t rtiles = (M + 15) / 16 - mb / 16;
+  const int64_t rtiles = (row_hi + 15) / 16 - mb / 16;
   const int tiles = (int)(rtiles < kBM / 16 ? rtiles : kBM / 16);
   const uint32_t tile_bytes = (uint32_t)nsteps * 1024u;  // one row tile over all of k
   const uint32_t a_bytes = (uint32_t)tiles * tile_bytes;
@@ -182,7 +226,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     };
     auto load_words = [&](int step, Words &wd) {
       const int st = step < nsteps ? step : nsteps - 1;
-      const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.qweight + (int64_t)st * kBK * W, w_step_bytes);
+      const __amdgpu_buffer_rsrc_t r = raw_rsrc(qweight + (int64_t)st * kBK * W, w_step_bytes);
       wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
       wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
     };
@@ -192,9 +236,9 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     };
     auto load_group = [&](int g, GroupRaw &gr) {
       const int gg = g < ngroups ? g : ngroups - 1;
-      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.scales + (int64_t)gg * O, (uint32_t)(O * 2));
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(scales + (int64_t)gg * O, (uint32_t)(O * 2));
       gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
-      const __amdgpu_buffer_rsrc_t rz = raw_rsrc(a.qzeros + (int64_t)gg * W, (uint32_t)(W * 4));
+      const __amdgpu_buffer_rsrc_t rz = raw_rsrc(qzeros + (int64_t)gg * W, (uint32_t)(W * 4));
       gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
     };
 
@@ -349,8 +393,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   const int64_t n = n0 + sc;
   const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
   f32x4 bias4{0.f, 0.f, 0.f, 0.f};
-  if (a.bias && n_ok) {
-    const u32x2 bb = *reinterpret_cast<const u32x2 *>(a.bias + n);
+  if (bias && n_ok) {
+    const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
     bias4 = f32x4{f16_bits_to_f32(bb[0] & 0xffffu), f16_bits_to_f32(bb[0] >> 16), f16_bits_to_f32(bb[1] & 0xffffu),
                   f16_bits_to_f32(bb[1] >> 16)};
   }
@@ -370,7 +414,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       const int lr = 2 * rr + srow;
       const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + lr * kStageRS + sc) + bias4;
       const int64_t row = m0 + 32 * p + lr;
-      if (row < M && n_ok) {
+      if (row >= row_lo && row < row_hi && n_ok) {
         if (a.y_dt == kF32) {
           *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * O + n) = v;
         } else {
@@ -384,19 +428,33 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   }
 }
 
-template <int GK>
+template <int GK, bool MOE>
 static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
   if (a.x_dt == kF16)
-    hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK>), grid, dim3(kThreads), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK, MOE>), grid, dim3(kThreads), 0, st, a, x);
   else
-    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16, GK>), grid, dim3(kThreads), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16, GK, MOE>), grid, dim3(kThreads), 0, st, a, x);
+}
+
+template <bool MOE>
+static void launch_prefill_moe(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
+  if (a.group == 32) launch_prefill_gk<1, MOE>(a, x, grid, st);
+  else if (a.group == 64) launch_prefill_gk<2, MOE>(a, x, grid, st);
+  else launch_prefill_gk<4, MOE>(a, x, grid, st);
+}
+
+int64_t moe_work_tiles(int64_t tokens, int experts) {
+  // sum over experts of ceil((rows + up to 15 rows of the first 16-row tile) / 256)
+  return (tokens + 15 * (int64_t)experts + kBM - 1) / kBM + experts;
 }
 
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
-  dim3 grid((unsigned)(((a.O + kBN - 1) / kBN) * ((a.tokens + kBM - 1) / kBM)));
-  if (a.group == 32) launch_prefill_gk<1>(a, x, grid, st);
-  else if (a.group == 64) launch_prefill_gk<2>(a, x, grid, st);
-  else launch_prefill_gk<4>(a, x, grid, st);
+  const int64_t n_tiles = (a.O + kBN - 1) / kBN;
+  if (a.experts > 0) {
+    launch_prefill_moe<true>(a, x, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
+  } else {
+    launch_prefill_moe<false>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + kBM - 1) / kBM))), st);
+  }
   return hipGetLastError();
 }
 

@@ -27,6 +27,13 @@ for Llama-3-8B-shaped layers, since no trained weights or datasets are used):
              times a per-row factor uniform(0.5, 2), fp16/bf16/fp32.
   g          (for the rotation backward) an upstream gradient dL/dx_r,
              N(0, 1), (tokens, I), fp16/bf16 bits or fp32.
+  MoE        E experts' q, z, scales, bias drawn as above with layer index
+             e, stacked expert-major; the rotation (pairs, theta, cs) is
+             expert 0's and shared.  Routing: each of T tokens is sent to
+             k experts; the expert loads are a multinomial draw of T*k rows
+             over expert probabilities from a flat Dirichlet, so loads are
+             skewed and an expert may get no rows; rows are grouped by
+             expert (offsets, E+1 int64).
 """
 from __future__ import annotations
 
@@ -39,7 +46,7 @@ import numpy as np
 AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 
 TENSOR_IDS = {"x": 0, "outliers": 1, "pairs": 2, "theta": 3, "cs": 4,
-              "q": 5, "z": 6, "scales": 7, "bias": 8, "w": 9, "w_rows": 10, "g": 11}
+              "q": 5, "z": 6, "scales": 7, "bias": 8, "w": 9, "w_rows": 10, "g": 11, "route": 12}
 
 F16, BF16, F32 = 0, 1, 2  # dtype codes shared by both C-ABIs' conventions
 
@@ -184,6 +191,34 @@ def make_g(workload: int, layer: int, tokens: int, in_features: int, dt: int,
     if dt == F32:
         return g.astype(np.float32)
     raise ValueError("unknown gradient dtype code")
+
+
+# Mixture-of-experts workloads: Mixtral-8x7B-shaped expert projections
+# (hidden 4096, expert width 14336, 8 experts, top-2 routing), synthetic.
+MOE_WORKLOADS = {
+    5: dict(name="mixtral-8x7b-w1-experts-prefill-t2048-top2-bf16", experts=8, tokens=2048, top_k=2,
+            act=BF16, layer=("w1", 4096, 14336)),
+}
+
+
+def make_moe_layer(workload: int, experts: int, in_features: int, out_features: int,
+                   group_size: int = 128, krot: int = 8, bias: bool = True, base: int = 0) -> Layer:
+    """E experts stacked in one Layer: qweight (E, I, O/8), qzeros (E, I/G, O/8),
+    scales (E, I/G, O), bias (E, O); one shared rotation (expert 0's)."""
+    parts = [make_layer(workload, e, in_features, out_features, group_size, krot, bias=bias, base=base)
+             for e in range(experts)]
+    p0 = parts[0]
+    stack = lambda name: np.ascontiguousarray(np.stack([getattr(p, name) for p in parts]))
+    return Layer(in_features, out_features, group_size, krot, p0.pairs, p0.theta, p0.channel_scales,
+                 stack("qweight"), stack("qzeros"), stack("scales"), stack("bias") if bias else None)
+
+
+def make_routing(workload: int, experts: int, tokens: int, top_k: int, base: int = 0) -> np.ndarray:
+    """Expert row offsets (E+1,) int64 for T tokens routed to top_k experts each."""
+    r = rng_for(workload, 0, "route", base)
+    p = r.dirichlet(np.ones(experts))
+    counts = r.multinomial(tokens * top_k, p)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
 
 
 def workload_layers(workload: int, **kw):

@@ -32,7 +32,7 @@ def test_libparo_exports_every_declared_symbol():
     assert set(_lib.EXPORTS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.paro_abi_version() == 3
+    assert lib.paro_abi_version() == 4
 
 
 def test_oracle_exports_every_declared_symbol():
@@ -278,3 +278,25 @@ def test_scale_rotate_backward_argument_checks():
     assert call(tokens=-1) == 2
     assert call(L=fake_layer(G=16)) == 5
     assert call(L=fake_layer(pairs=0)) == 1
+
+
+@needs_no_gpu
+def test_moe_linear_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(I=256, O=64)
+    ws = lib.paro_w4a16_moe_linear_workspace_bytes(ctypes.byref(L), 40, 1)
+    assert ws == lib.paro_w4a16_linear_workspace_bytes(ctypes.byref(L), 40, 1, 3)   # the prefill path's
+
+    def call(E=4, offs=FAKE * 16, x=FAKE, xdt=1, tokens=40, y=FAKE * 2, ydt=1, wsp=FAKE * 4, wsb=ws, L=L):
+        return lib.paro_w4a16_moe_linear(ctypes.byref(L), E, offs, x, xdt, tokens, y, ydt, wsp, wsb, None)
+    assert call(E=0) == 2
+    assert call(E=-1) == 2
+    assert call(E=1025) == 2
+    assert call(offs=0) == 1
+    assert call(offs=FAKE * 16 + 4) == 4
+    assert call(x=0) == 1
+    assert call(xdt=2) == 3
+    assert call(wsb=ws - 1) == 7
+    assert call(y=FAKE + 64) == 2                    # y overlaps x
+    assert call(L=fake_layer(G=16)) == 5
+    assert call(tokens=0, x=0, y=0) == 0             # nothing to do

@@ -637,3 +637,45 @@ def test_backward_theta_at_zero_angle():
             b = gi * G + pairs[0, gi * G + 2 * p + 1]
             want = (g[:, a] * xs[:, b] - g[:, b] * xs[:, a]).sum()
             assert gth[0, gi * G // 2 + p] == pytest.approx(want, rel=1e-13, abs=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# mixture of experts with one shared rotation (the oracle's composition)
+# ---------------------------------------------------------------------------
+
+def test_moe_with_identical_experts_is_the_plain_linear():
+    """E copies of one layer: every routing gives the plain linear on all rows."""
+    I, O, M, E = 256, 64, 37, 3
+    L = synth.make_layer(601, 0, I, O)
+    stack = lambda a: np.ascontiguousarray(np.stack([a] * E))
+    Lm = synth.Layer(I, O, 128, L.krot, L.pairs, L.theta, L.channel_scales, stack(L.qweight), stack(L.qzeros),
+                     stack(L.scales), stack(L.bias))
+    x = synth.make_x(601, 0, M, I, synth.F16)
+    want = ref.linear(L, x, synth.F16)
+    for offs in ([0, 10, 10, 37], [0, 37, 37, 37], [0, 1, 2, 37]):
+        assert np.array_equal(ref.moe_linear(Lm, offs, x, synth.F16), want)
+
+
+def test_moe_rows_depend_only_on_their_expert():
+    I, O, M, E = 256, 64, 40, 4
+    Lm = synth.make_moe_layer(602, E, I, O)
+    x = synth.make_x(602, 0, M, I, synth.BF16)
+    offs = np.array([0, 7, 7, 30, 40])
+    y = ref.moe_linear(Lm, offs, x, synth.BF16)
+    # expert 2's weights replaced: only rows 7..29 change
+    other = synth.make_layer(603, 0, I, O)
+    qw = Lm.qweight.copy(); qw[2] = other.qweight
+    sc = Lm.scales.copy(); sc[2] = other.scales
+    import dataclasses
+    y2 = ref.moe_linear(dataclasses.replace(Lm, qweight=qw, scales=sc), offs, x, synth.BF16)
+    assert np.array_equal(y2[:7], y[:7]) and np.array_equal(y2[30:], y[30:])
+    assert not np.allclose(y2[7:30], y[7:30])
+    # and each expert's rows are that expert's plain linear (empty expert 1 contributes nothing)
+    for e, (lo, hi) in enumerate(zip(offs[:-1], offs[1:])):
+        if hi > lo:
+            assert np.array_equal(y[lo:hi], ref.linear(ref.expert_layer(Lm, e), x[lo:hi], synth.BF16))
+
+
+def test_moe_routing_generator_covers_every_row():
+    offs = synth.make_routing(5, 8, 2048, 2)
+    assert offs[0] == 0 and offs[-1] == 4096 and (np.diff(offs) >= 0).all() and len(offs) == 9

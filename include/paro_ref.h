@@ -149,6 +149,21 @@ int paro_ref_quantize(int64_t O, int64_t I, int32_t group_size, const double *w_
  * [I/G][O/8], the inverse of paro_ref_unpack (O % 8 == 0). */
 int paro_ref_pack(int64_t I, int64_t O, int32_t group_size, const uint8_t *q, const uint8_t *z,
                   int32_t *qweight, int32_t *qzeros);
+/*
+ * MXFP4 (the four-bit-activation extension; "ParoQuant" blog, Bits and
+ * formats).  Blocks of 32 consecutive elements of a row share an E8M0 scale
+ * 2^(b - 127): b = floor(log2(max |v|)) - 2 + 127 clamped to 0..254 (0 for an
+ * all-zero block); elements are E2M1 codes (bit 3 sign; magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6) of v / 2^(b - 127), nearest with ties to the even code,
+ * clamped at 6, zero stored as +0.
+ *   v: double [rows][K], K % 32 == 0
+ *   codes: [rows][K/2] bytes, element 2j in the low nibble of byte j
+ *   scales: [rows][K/32] biased exponents
+ */
+int paro_ref_mxfp4_quantize(int64_t rows, int64_t K, const double *v, uint8_t *codes, uint8_t *scales);
+/* The values the codes and scales stand for, double [rows][K] (b = 255: NaN). */
+int paro_ref_mxfp4_dequant(int64_t rows, int64_t K, const uint8_t *codes, const uint8_t *scales, double *out);
+double paro_ref_e2m1_to_double(int code);
 /* Y as double [tokens][O]. */
 int paro_ref_linear(const paro_ref_layer *layer, const void *x, int x_dt,
                     int64_t tokens, double *y_out, int n_threads);

@@ -514,6 +514,82 @@ int paro_ref_pack(int64_t I, int64_t O, int32_t group_size, const uint8_t *q, co
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP4, the four-bit-activation extension ("ParoQuant" blog, Bits and       */
+/* formats: W4A4 with an MXFP4 variant).  OCP microscaling format: each block */
+/* of 32 consecutive elements along a row shares one E8M0 scale, a power of   */
+/* two 2^(b - 127) with b = 0..254; each element is E2M1 (sign, two exponent  */
+/* bits, one mantissa bit) with magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The   */
+/* block exponent is floor(log2(max |v|)) minus 2, the exponent of E2M1's     */
+/* largest value (6 = 1.5 * 2^2); elements are v / 2^exp rounded to the       */
+/* nearest E2M1 value, ties to the even code, clamped at 6.                    */
+/* ------------------------------------------------------------------------ */
+
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double paro_ref_e2m1_to_double(int code) {
+  return (code & 8 ? -1.0 : 1.0) * E2M1_MAG[code & 7];
+}
+
+/* Nearest magnitude code of a >= 0, ties to the even code (brute force). */
+static int e2m1_nearest(double a) {
+  int best = 0;
+  double bd = fabs(a - E2M1_MAG[0]);
+  for (int c = 1; c < 8; ++c) {
+    const double d = fabs(a - E2M1_MAG[c]);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+int paro_ref_mxfp4_quantize(int64_t rows, int64_t K, const double *v, uint8_t *codes, uint8_t *scales) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return PARO_REF_ERR_SHAPE;
+  if (rows > 0 && (!v || !codes || !scales)) return PARO_REF_ERR_NULL;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      const double *blk = v + r * K + 32 * b;
+      double amax = 0.0;
+      for (int e = 0; e < 32; ++e) amax = fmax(amax, fabs(blk[e]));
+      int biased = 0; /* an all-zero block: the smallest scale, all codes 0 */
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1 */
+        biased = (ex - 1) - 2 + 127;
+        if (biased < 0) biased = 0;
+        if (biased > 254) biased = 254;
+      }
+      scales[r * (K / 32) + b] = (uint8_t)biased;
+      const double X = ldexp(1.0, biased - 127);
+      for (int e = 0; e < 32; e += 2) {
+        int c[2];
+        for (int h = 0; h < 2; ++h) {
+          const double q = blk[e + h] / X;
+          const int m = e2m1_nearest(fabs(q));
+          c[h] = (q < 0.0 && m != 0) ? (m | 8) : m; /* zero is stored as +0 */
+        }
+        /* element 2j in the low nibble of byte j, 2j+1 in the high nibble */
+        codes[r * (K / 2) + 16 * b + e / 2] = (uint8_t)(c[0] | (c[1] << 4));
+      }
+    }
+  return PARO_REF_OK;
+}
+
+int paro_ref_mxfp4_dequant(int64_t rows, int64_t K, const uint8_t *codes, const uint8_t *scales, double *out) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return PARO_REF_ERR_SHAPE;
+  if (rows > 0 && (!codes || !scales || !out)) return PARO_REF_ERR_NULL;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const int byte = codes[r * (K / 2) + k / 2];
+      const int c = (k & 1) ? (byte >> 4) : (byte & 15);
+      const int biased = scales[r * (K / 32) + k / 32];
+      out[r * K + k] = biased == 255 ? NAN : paro_ref_e2m1_to_double(c) * ldexp(1.0, biased - 127);
+    }
+  return PARO_REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The linear: Y = X_r . W_deq + b.                                          */
 /* ------------------------------------------------------------------------ */
 

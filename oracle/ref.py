@@ -72,12 +72,17 @@ def load(path: str | None = None):
     lib.paro_ref_threads.argtypes = [I32]
     lib.paro_ref_transform_weight.argtypes = [P, P, I32, P, I32]
     lib.paro_ref_scale_rotate_backward.argtypes = [P, P, I32, P, I64, P, P, P, I32]
+    lib.paro_ref_mxfp4_quantize.argtypes = [I64, I64, P, P, P]
+    lib.paro_ref_mxfp4_dequant.argtypes = [I64, I64, P, P, P]
+    lib.paro_ref_e2m1_to_double.argtypes = [I32]
+    lib.paro_ref_e2m1_to_double.restype = ctypes.c_double
     lib.paro_ref_quantize.argtypes = [I64, I64, ctypes.c_int32, P, I32, P, P, P, P]
     lib.paro_ref_pack.argtypes = [I64, I64, ctypes.c_int32, P, P, P, P]
     for name in ("paro_ref_round_array", "paro_ref_check_pairs", "paro_ref_scale_rotate",
                  "paro_ref_unpack", "paro_ref_dequant", "paro_ref_linear",
                  "paro_linear_ref_check", "paro_ref_threads", "paro_ref_transform_weight",
-                 "paro_ref_quantize", "paro_ref_pack", "paro_ref_scale_rotate_backward"):
+                 "paro_ref_quantize", "paro_ref_pack", "paro_ref_scale_rotate_backward",
+                 "paro_ref_mxfp4_quantize", "paro_ref_mxfp4_dequant"):
         getattr(lib, name).restype = I32
     _lib, _lib_path = lib, path
     return lib
@@ -213,6 +218,44 @@ def pack(q, z, group_size: int):
     qz = np.empty((I // G, O // 8), dtype=np.int32)
     _check(load().paro_ref_pack(I, O, group_size, _ptr(q), _ptr(z), _ptr(qw), _ptr(qz)), "paro_ref_pack")
     return qw, qz
+
+
+def mxfp4_quantize(v):
+    """MXFP4 codes [rows][K/2] (uint8) and E8M0 scales [rows][K/32] of double v [rows][K]."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    rows, K = v.shape
+    codes = np.empty((rows, K // 2), dtype=np.uint8)
+    scales = np.empty((rows, K // 32), dtype=np.uint8)
+    _check(load().paro_ref_mxfp4_quantize(rows, K, _ptr(v), _ptr(codes), _ptr(scales)), "paro_ref_mxfp4_quantize")
+    return codes, scales
+
+
+def mxfp4_dequant(codes, scales):
+    """double [rows][K] from MXFP4 codes and scales."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((rows, K), dtype=np.float64)
+    _check(load().paro_ref_mxfp4_dequant(rows, K, _ptr(codes), _ptr(scales), _ptr(out)), "paro_ref_mxfp4_dequant")
+    return out
+
+
+def mxfp4_weight(layer, w, w_dt: int):
+    """MXFP4 codes and scales of the transformed weight W_r = W D R ([O][I] rows)."""
+    return mxfp4_quantize(transform_weight(layer, w, w_dt))
+
+
+def mxfp4_activations(layer, x, x_dt: int):
+    """MXFP4 codes and scales of the rotated activations X_r = X D^-1 R."""
+    return mxfp4_quantize(scale_rotate(layer, x, x_dt))
+
+
+def mxfp4_matmul(a_codes, a_scales, w_codes, w_scales, bias=None):
+    """Y = dequant(A) . dequant(W)^T (+ fp16 bias), double [rows][O]."""
+    y = mxfp4_dequant(a_codes, a_scales) @ mxfp4_dequant(w_codes, w_scales).T
+    if bias is not None:
+        y = y + np.asarray([f16_to_double(h) for h in bias])
+    return y
 
 
 def expert_layer(layer, e: int):

@@ -55,6 +55,10 @@ MUTANTS = {
     "bwd_stage_order": ("for (int t = krot - 1; t >= 0; --t) {", "for (int t = 0; t < krot; ++t) {"),
     "bwd_cs_uses_scaled": ("gc[k] += grad[k] * xk;", "gc[k] += grad[k] * xk * (double)L->channel_scales[k];"),
     "pack_zeros_sequential": ("<< (4 * SLOT_OF_COL[j]);\n      qzeros", "<< (4 * j);\n      qzeros"),
+    "mx_exponent_off_by_one": ("biased = (ex - 1) - 2 + 127;", "biased = (ex - 1) - 1 + 127;"),
+    "mx_ties_to_odd": ("(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
+    "mx_nibble_order": ("(uint8_t)(c[0] | (c[1] << 4));", "(uint8_t)(c[1] | (c[0] << 4));"),
+    "mx_sign_dropped": ("c[h] = (q < 0.0 && m != 0) ? (m | 8) : m;", "c[h] = m;"),
 }
 
 

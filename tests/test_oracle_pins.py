@@ -679,3 +679,79 @@ def test_moe_rows_depend_only_on_their_expert():
 def test_moe_routing_generator_covers_every_row():
     offs = synth.make_routing(5, 8, 2048, 2)
     assert offs[0] == 0 and offs[-1] == 4096 and (np.diff(offs) >= 0).all() and len(offs) == 9
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (32-element blocks, E8M0 scale, E2M1 elements)
+# ---------------------------------------------------------------------------
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def nibbles(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.stack([c & 15, c >> 4], axis=-1).reshape(c.shape[0], -1)
+
+
+def test_mxfp4_worked_block():
+    """Hand-worked: max |v| = 6 gives floor(log2 6) - 2 = 0, scale 2^0 (byte
+    127); the ties 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5 go to the even code
+    (0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0); 7.9 saturates to 6 in the next block."""
+    v = np.zeros((1, 64))
+    vals = [6.0, -3.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.3, 0.0, 4.9, -0.1, 2.9, 1.1, -6.0]
+    want = [7, 8 | 5, 0, 2, 2, 4, 4, 6, 6, 8 | 1, 0, 6, 0, 5, 2, 8 | 7]
+    v[0, :16] = vals
+    v[0, 32] = 7.9       # block 2: floor(log2 7.9) = 2, scale 1, 7.9 -> 6
+    v[0, 33] = -0.24     # -> 0, stored as +0
+    codes, scales = ref.mxfp4_quantize(v)
+    assert list(scales[0]) == [127, 127]
+    n = nibbles(codes)[0]
+    assert list(n[:16]) == want
+    assert n[32] == 7 and n[33] == 0
+    assert codes[0, 0] == (7 | (13 << 4))  # element 0 low nibble, element 1 high nibble
+
+
+def test_mxfp4_scale_exponent_and_zero_block():
+    v = np.zeros((3, 32))
+    v[0, 5] = 0.1        # floor(log2 0.1) = -4 -> exponent -6 -> byte 121; 0.1 / 2^-6 = 6.4 -> 6
+    v[1, 0] = 1000.0     # floor(log2 1000) = 9 -> exponent 7 -> byte 134; 1000 / 128 = 7.8 -> 6
+    codes, scales = ref.mxfp4_quantize(v)
+    assert scales[0, 0] == 121 and scales[1, 0] == 134 and scales[2, 0] == 0
+    back = ref.mxfp4_dequant(codes, scales)
+    assert back[0, 5] == 6 * 2.0 ** -6 and back[1, 0] == 768.0
+    assert not back[2].any() and not codes[2].any()
+
+
+def test_mxfp4_elements_are_nearest_points_brute_force():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((64, 64)) * np.exp(rng.uniform(-8, 8, size=(64, 1)))
+    codes, scales = ref.mxfp4_quantize(v)
+    back = ref.mxfp4_dequant(codes, scales)
+    n = nibbles(codes)
+    for r in range(64):
+        for b in range(2):
+            blk = v[r, 32 * b:32 * b + 32]
+            X = 2.0 ** (int(scales[r, b]) - 127)
+            amax = np.abs(blk).max()
+            assert 4 <= amax / X < 8                       # the block exponent rule
+            grid = np.array([s * m for m in E2M1_VALUES for s in (1, -1)]) * X
+            for e in range(32):
+                d = np.abs(grid - blk[e])
+                assert abs(back[r, 32 * b + e] - blk[e]) == d.min()
+                c = int(n[r, 32 * b + e])
+                if (d == d.min()).sum() > 1 and abs(blk[e]) < 6 * X:  # a tie: the even code
+                    assert c & 1 == 0
+
+
+def test_mxfp4_round_trip_of_canonical_blocks():
+    """A block whose largest magnitude code is 4 or 6 re-quantizes to itself."""
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 256, size=(16, 32), dtype=np.uint8)   # 64 elements: two blocks
+    codes[:, 0] = 7 | (6 << 4)
+    codes[:, 16] = 6 | (15 << 4)
+    scales = rng.integers(100, 150, size=(16, 2), dtype=np.uint8)
+    back = ref.mxfp4_dequant(codes, scales)
+    c2, s2 = ref.mxfp4_quantize(back)
+    # -0 (code 8) is stored as +0: compare the values they stand for
+    assert np.array_equal(s2, scales)
+    assert np.array_equal(ref.mxfp4_dequant(c2, s2), back)

@@ -312,6 +312,94 @@ def bench_moe(args, paro, synth, np, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+MX_METRIC = "ParoQuant W4A4 MXFP4 linear (rotation, activation quantization, FP4 GEMM): TFLOP/s, % of FP4 MFMA roofline"
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 / fp6 MFMA, published
+KERNEL_FILES["mxfp4"] = ("mxfp4.hip", "common.hpp")
+
+
+def bench_mxfp4(args, paro, synth, np, torch, dev):
+    """Time paro_mxfp4_linear on the workload's first layer (weights quantized
+    once with paro_mxfp4_quantize_weight), rotating through >= 512 MB of
+    distinct weight codes; the GEMM alone is timed the same way for its
+    roofline."""
+    spec = synth.WORKLOADS[args.workload]
+    lname, I, O = spec["layers"][0]
+    M, dt = max(spec["tokens"], 1), spec["act"]
+    tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
+    host = synth.make_layer(args.workload, 0, I, O, group_size=args.group)
+    D = paro.DeviceLayer(host, device=dev)
+    x = synth.make_x(args.workload, 0, M, I, dt)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
+    w = synth.make_w(args.workload, 0, O, I, dt)
+    wd = torch.from_numpy(w.view(np.int16)).to(dev).view(tdt)
+    set_bytes = O * I // 2 + O * I // 32
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // set_bytes)))
+    wcs = [torch.empty((O, I // 2), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    wss = [torch.empty((O, I // 32), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    for c, sc in zip(wcs, wss):
+        paro.paro_mxfp4_quantize_weight(D, wd, c, sc)
+    log(f"mxfp4: workload {args.workload} layer {lname} ({I} -> {O}), {M} tokens, {nsets} weight code sets")
+    y = torch.empty((M, O), dtype=tdt, device=dev)
+    work = torch.empty(max(paro.paro_mxfp4_linear_workspace_bytes(D, M), 16), dtype=torch.uint8, device=dev)
+    ac = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M, I // 32), dtype=torch.uint8, device=dev)
+    paro.paro_mxfp4_quantize_activations(D, xd, ac, as_)
+    bias = D.bias
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(n):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / n
+
+    us = timed(lambda i: paro.paro_mxfp4_linear(D, wcs[i % nsets], wss[i % nsets], xd, y, work, stream=stream),
+               args.steps)
+    g_us = None
+    if not args.no_kernel_timing:
+        g_us = timed(lambda i: paro.paro_mxfp4_gemm(ac, as_, wcs[i % nsets], wss[i % nsets], y, bias, stream=stream),
+                     args.steps)
+    flops = 2.0 * M * I * O
+    value = flops / (us * 1e-6) / 1e12
+    k_us = g_us if g_us is not None else us
+    ach = flops / (k_us * 1e-6) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        rows = min(M, 16)
+        wc_h, ws_h = ref.mxfp4_weight(host, w, dt)
+        n, t_start = 0, time.perf_counter()
+        while True:
+            a_c, a_s = ref.mxfp4_activations(host, np.ascontiguousarray(x[:rows]), dt)
+            ref.mxfp4_matmul(a_c, a_s, wc_h, ws_h, host.bias)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = {"value": 2.0 * rows * I * O / (el / n) / 1e12, "unit": "TFLOP/s", "cores": ref.threads(0),
+               "kind": "oracle", "sample": f"{n} oracle call(s) (rotate, quantize, dequantized product) on {rows} "
+                                          f"of {M} tokens of '{lname}', {el:.1f} s"}
+    out = {
+        "metric": MX_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": f"{spec['name']}-mxfp4{gsuffix(args)}", "tokens": M, "layer": [lname, I, O],
+                   "group_size": args.group, "krot": host.krot, "weight_sets": nsets, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "mx_gemm_kernel" if g_us is not None else "paro_mxfp4_linear (whole entry point)",
+                     "avg_launch_us": round(k_us, 3)},
+        "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("mxfp4"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bits_to_f64_host(bits, dt, np):
     """fp16 / bf16 bit patterns (uint16) -> float64 (the oracle takes g in double)."""
     if dt == 0:
@@ -331,11 +419,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
-    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward", "moe"), default="linear",
+    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward", "moe", "mxfp4"), default="linear",
                     help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
                          "qzeros, scales) transform of the workload's first layer; rotate_backward: the "
                          "calibration-time backward of the scaling and rotation over that layer's input; "
-                         "moe: the mixture-of-experts projection of workload 5 (synth.MOE_WORKLOADS)")
+                         "moe: the mixture-of-experts projection of workload 5 (synth.MOE_WORKLOADS); "
+                         "mxfp4: the W4A4 MXFP4 linear of the workload's first layer")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark: copy BYTES between two device buffers --steps times "
                          "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -374,6 +463,9 @@ def main():
         return
     if args.op == "moe":
         bench_moe(args, paro, synth, np, torch, dev)
+        return
+    if args.op == "mxfp4":
+        bench_mxfp4(args, paro, synth, np, torch, dev)
         return
     spec = synth.WORKLOADS[args.workload]
     M, act = spec["tokens"], spec["act"]

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARO_ABI_VERSION 4
+#define PARO_ABI_VERSION 5
 
 typedef enum {
   PARO_F16 = 0,  /* IEEE binary16 */
@@ -318,6 +318,47 @@ int paro_scale_rotate_backward(const paro_w4_layer *layer, const void *x, paro_d
 
 /* Workspace bytes paro_scale_rotate_backward needs (0 if the shape is invalid). */
 size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
+
+/*
+ * Four-bit activations after the rotation: the W4A4 extension in its MXFP4
+ * variant ("ParoQuant" blog, Bits and formats), on the block-scaled FP4
+ * matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).  Weight error
+ * compensation of the GPTQ kind needs calibration data and is not done here:
+ * weights are rounded to nearest.
+ *
+ * MXFP4 of a row of I values (OCP microscaling): blocks of 32 consecutive
+ * values share an E8M0 scale byte b (2^(b - 127)), b = floor(log2 max|v|)
+ * - 2 + 127 (0 for an all-zero block); each value is the E2M1 code (bit 3
+ * sign; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to v / 2^(b - 127),
+ * ties to the even code, clamped at 6, zero as +0.  Layout: codes [rows][I/2]
+ * bytes, element 2j in the low nibble of byte j; scales [rows][I/32] bytes.
+ * Decisions are taken in fp32 on the kernel's rotation of the rows.
+ *
+ * Quantize the transformed weight W_r = W . D . R (w [O][I], F16/BF16/F32, 4-
+ * byte aligned, 8 for F32): codes [O][I/2] (16-byte aligned), scales [O][I/32]
+ * (4-byte aligned).  Uses the layer's I, O, group_size, krot, pairs, theta,
+ * channel_scales.
+ */
+int paro_mxfp4_quantize_weight(const paro_w4_layer *layer, const void *w, paro_dtype w_dt, uint8_t *codes,
+                               uint8_t *scales, void *stream);
+/* Quantize the rotated activations X_r = X . D^-1 . R (x [tokens][I] F16/BF16). */
+int paro_mxfp4_quantize_activations(const paro_w4_layer *layer, const void *x, paro_dtype x_dt, int64_t tokens,
+                                    uint8_t *codes, uint8_t *scales, void *stream);
+/* y [tokens][out_features] = A . W^T (+ bias fp16 [out_features] or NULL)
+ * from MXFP4 codes and scales of A [tokens][in_features] and W
+ * [out_features][in_features]; fp32 accumulation, one rounding to y_dt
+ * (F16/BF16/F32).  in_features % 128 == 0, out_features % 8 == 0, and
+ * rows * in_features / 2 < 2^31 for both operands. */
+int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tokens, const uint8_t *w_codes,
+                    const uint8_t *w_scales, int64_t out_features, int64_t in_features, const uint16_t *bias,
+                    void *y, paro_dtype y_dt, void *stream);
+/* The whole W4A4 MXFP4 linear: activations rotated and quantized into the
+ * workspace, then the FP4 GEMM with layer->bias.  w_codes / w_scales from
+ * paro_mxfp4_quantize_weight; layer->qweight/qzeros/scales are not used. */
+int paro_mxfp4_linear(const paro_w4_layer *layer, const uint8_t *w_codes, const uint8_t *w_scales, const void *x,
+                      paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                      size_t workspace_bytes, void *stream);
+size_t paro_mxfp4_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,

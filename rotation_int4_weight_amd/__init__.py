@@ -15,7 +15,9 @@ from ._lib import (BF16, EXPORTS, F16, F32, PATH_AUTO, PATH_DECODE_FUSED, PATH_D
                    paro_rotation_matrix, paro_scale_rotate_tiled, paro_w4a16_linear_tiled,
                    paro_w4_quantize_pack, paro_scale_rotate_backward,
                    paro_scale_rotate_backward_workspace_bytes, paro_w4a16_moe_linear,
-                   paro_w4a16_moe_linear_workspace_bytes)
+                   paro_w4a16_moe_linear_workspace_bytes, paro_mxfp4_quantize_weight,
+                   paro_mxfp4_quantize_activations, paro_mxfp4_gemm, paro_mxfp4_linear,
+                   paro_mxfp4_linear_workspace_bytes)
 
 __all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "PATH_DECODE_SPLIT",
            "PATH_PREFILL", "DeviceLayer", "ParoError", "load", "make_workspace", "paro_abi_version",
@@ -25,4 +27,6 @@ __all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "P
            "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward",
            "paro_scale_rotate_backward_workspace_bytes", "paro_w4a16_moe_linear",
-           "paro_w4a16_moe_linear_workspace_bytes"]
+           "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
+           "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
+           "paro_mxfp4_linear_workspace_bytes"]

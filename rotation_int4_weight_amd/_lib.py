@@ -21,7 +21,9 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
-           "paro_w4a16_moe_linear_workspace_bytes",
+           "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
+           "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
+           "paro_mxfp4_linear_workspace_bytes",
            "paro_scale_rotate_backward_workspace_bytes",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
@@ -69,6 +71,12 @@ def load(path: str | None = None):
     lib.paro_w4a16_moe_linear.argtypes = [P, I32, P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_moe_linear_workspace_bytes.argtypes = [P, I64, I32]
     lib.paro_w4a16_moe_linear_workspace_bytes.restype = SZ
+    lib.paro_mxfp4_quantize_weight.argtypes = [P, P, I32, P, P, P]
+    lib.paro_mxfp4_quantize_activations.argtypes = [P, P, I32, I64, P, P, P]
+    lib.paro_mxfp4_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P, I32, P]
+    lib.paro_mxfp4_linear.argtypes = [P, P, P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_mxfp4_linear_workspace_bytes.argtypes = [P, I64]
+    lib.paro_mxfp4_linear_workspace_bytes.restype = SZ
     lib.paro_scale_rotate_backward.argtypes = [P, P, I32, P, I32, I64, P, I32, P, P, P, SZ, P]
     lib.paro_scale_rotate_backward_workspace_bytes.argtypes = [P, I64]
     lib.paro_scale_rotate_backward_workspace_bytes.restype = SZ
@@ -87,6 +95,8 @@ def load(path: str | None = None):
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
                  "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
+                 "paro_mxfp4_quantize_weight", "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm",
+                 "paro_mxfp4_linear",
                  "paro_rotation_matrix", "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
                  "paro_w4a16_linear_choose_path",
                  "paro_validate_layer", "paro_abi_version"):
@@ -232,6 +242,37 @@ def paro_w4_quantize_pack(layer: DeviceLayer, w, symmetric: bool, qweight, qzero
     scales fp16/int16 view (I/128, O)."""
     _check(load().paro_w4_quantize_pack(layer.ref, _ptr(w), _dt(w), int(bool(symmetric)), _ptr(qweight),
                                         _ptr(qzeros), _ptr(scales), _stream_handle(stream)), "paro_w4_quantize_pack")
+
+
+def paro_mxfp4_quantize_weight(layer: DeviceLayer, w, codes, scales, stream=None) -> None:
+    """w: (O, I) fp16/bf16/fp32; codes uint8 (O, I/2); scales uint8 (O, I/32)."""
+    _check(load().paro_mxfp4_quantize_weight(layer.ref, _ptr(w), _dt(w), _ptr(codes), _ptr(scales),
+                                             _stream_handle(stream)), "paro_mxfp4_quantize_weight")
+
+
+def paro_mxfp4_quantize_activations(layer: DeviceLayer, x, codes, scales, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16; codes uint8 (tokens, I/2); scales uint8 (tokens, I/32)."""
+    _check(load().paro_mxfp4_quantize_activations(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(codes),
+                                                  _ptr(scales), _stream_handle(stream)),
+           "paro_mxfp4_quantize_activations")
+
+
+def paro_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, y, bias=None, stream=None) -> None:
+    """y (tokens, O) = A . W^T (+ bias) from MXFP4 codes/scales (uint8 device tensors)."""
+    tokens, O, I = a_codes.shape[0], w_codes.shape[0], w_codes.shape[1] * 2
+    _check(load().paro_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), tokens, _ptr(w_codes), _ptr(w_scales), O, I,
+                                  _ptr(bias), _ptr(y), _dt(y), _stream_handle(stream)), "paro_mxfp4_gemm")
+
+
+def paro_mxfp4_linear_workspace_bytes(layer: DeviceLayer, tokens: int) -> int:
+    return int(load().paro_mxfp4_linear_workspace_bytes(layer.ref, tokens))
+
+
+def paro_mxfp4_linear(layer: DeviceLayer, w_codes, w_scales, x, y, workspace, stream=None) -> None:
+    """The W4A4 MXFP4 linear (rotation, activation quantization, FP4 GEMM, layer bias)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_mxfp4_linear(layer.ref, _ptr(w_codes), _ptr(w_scales), _ptr(x), _dt(x), x.shape[0], _ptr(y),
+                                    _dt(y), _ptr(workspace), ws_bytes, _stream_handle(stream)), "paro_mxfp4_linear")
 
 
 def paro_w4a16_moe_linear_workspace_bytes(layer: DeviceLayer, tokens: int, x_dt: int = F16) -> int:

@@ -108,4 +108,14 @@ hipError_t launch_rot_backward(const void *x, int x_dt, const void *g, int g_dt,
                                void *gx,
                                int gx_dt, float *gtheta, float *gcs, float *partial, hipStream_t st);
 
+// MXFP4 (32-element E8M0 blocks, E2M1 codes) after the rotation: rows
+// [rows][I] (activations times cs, or weights divided by cs when `weight`)
+// -> codes [rows][I/2] bytes, scales [rows][I/32] bytes.
+hipError_t launch_mx_quantize(const void *src, int dt, bool weight, int64_t rows, int64_t I, const int16_t *pairs,
+                              const float *theta, const float *cs, int krot, int group, uint8_t *codes,
+                              uint8_t *scales, hipStream_t st);
+// y [M][N] = A . W^T (+ bias) on the block-scaled FP4 matrix cores.
+hipError_t launch_mx_gemm(const uint8_t *ac, const uint8_t *as, int64_t M, const uint8_t *wc, const uint8_t *ws,
+                          int64_t N, int64_t K, const uint16_t *bias, void *y, int y_dt, hipStream_t st);
+
 }  // namespace paro

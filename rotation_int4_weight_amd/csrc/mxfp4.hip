@@ -1,0 +1,254 @@
+// mxfp4.hip - four-bit activations after the rotation (the W4A4 extension's
+// MXFP4 variant; "ParoQuant" blog, Bits and formats) on the CDNA4 block-scaled
+// FP4 matrix cores.
+//
+//   y = MX(x . D^-1 . R) . MX(W . D . R)^T + b
+//
+// MX(.) is the OCP microscaling format along the input channels: blocks of 32
+// consecutive values share an E8M0 scale 2^(b - 127) with
+// b = floor(log2 max|v|) - 2 + 127 (0 for an all-zero block), and each value
+// is the E2M1 number nearest to v / 2^(b - 127) (ties to the even code,
+// clamped at 6; zero stored as +0).  Codes: [rows][I/2] bytes, element 2j in
+// the low nibble of byte j; scales: [rows][I/32] bytes.
+//
+// mx_quant_kernel rotates rows of one 128-channel block in LDS with the staged
+// rotation (fp32) and quantizes them: lane p holds channels 2p, 2p+1, a block
+// of 32 channels is 16 lanes, so its max is four lane shuffles away.  The same
+// kernel takes activations (x times cs) and weights (W divided by cs).
+//
+// mx_gemm_kernel runs v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 A and B: lane
+// l supplies row (column) l%16 and the 32 elements of K block l/16 of a
+// 128-wide k step, 16 bytes loaded straight from the row-major codes, with
+// the E8M0 scale of exactly that 32-element block; the 16x16 fp32 result has
+// row 4(l/16)+r, column l%16 in register r.  (The order of the 32 elements
+// inside a lane's block does not matter as long as A and B agree.)
+#include "common.hpp"
+#include "launch.hpp"
+#include "mfma.hpp"
+
+namespace paro {
+
+constexpr int kMxRS = kG + 4;  // LDS row stride (floats)
+
+template <int DT>
+__device__ __forceinline__ float2 load_pair_any(const void *p, int64_t idx) {
+  if constexpr (DT == kF32) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(p) + idx);
+  } else {
+    const uint32_t b = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(p) + idx);
+    return float2{act_to_f32<DT>(b & 0xffffu), act_to_f32<DT>(b >> 16)};
+  }
+}
+
+// E2M1 code of a (already divided by the block scale): the count of rounding
+// boundaries below |a|, ties to the even code (0, 1.0, 1.0, 2.0, 2.0, 4.0,
+// 4.0), saturating at 6; sign in bit 3 unless the magnitude is zero.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+  const float m = fabsf(a);
+  const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
+                     (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+  return (a < 0.0f && c != 0) ? (c | 8u) : c;
+}
+
+// rows [rows][I] (x dtype, or the weight's dtype); WEIGHT: divide by cs
+template <int DT, bool WEIGHT>
+__global__ void __launch_bounds__(256)
+mx_quant_kernel(const void *__restrict__ src, int64_t rows, int64_t I, const int16_t *__restrict__ pairs,
+                const float *__restrict__ theta, const float *__restrict__ cscale, int krot, int gmask,
+                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  constexpr int RW = 16;
+  __shared__ float lds[4][RW * kMxRS];
+  const int lane = lane_id(), wave = wave_id();
+  const int64_t g = blockIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64 + wave * RW;
+  if (r0 >= rows) return;  // wave-uniform; no workgroup barrier below
+  float *xs = lds[wave];
+
+  RotParams rp;
+  rp.load(pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
+  const float2 csv = *reinterpret_cast<const float2 *>(cscale + g * kG + 2 * lane);
+#pragma unroll
+  for (int m = 0; m < RW; ++m) {
+    float2 v{0.f, 0.f};
+    if (r0 + m < rows) v = load_pair_any<DT>(src, (r0 + m) * I + g * kG + 2 * lane);
+    xs[m * kMxRS + 2 * lane] = WEIGHT ? v.x / csv.x : v.x * csv.x;
+    xs[m * kMxRS + 2 * lane + 1] = WEIGHT ? v.y / csv.y : v.y * csv.y;
+  }
+  wave_lds_sync();
+  rotate_rows_lds<RW>(xs, kMxRS, rp, pairs + g * kG, I, theta + g * kPairs, I / 2, krot, lane, gmask);
+
+#pragma unroll
+  for (int m = 0; m < RW; ++m) {
+    if (r0 + m >= rows) break;
+    const float v0 = xs[m * kMxRS + 2 * lane], v1 = xs[m * kMxRS + 2 * lane + 1];
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // the 16 lanes of a block
+    // floor(log2 amax) = exponent field - 127 (normal amax); the block
+    // exponent is 2 less; subnormal or zero amax gives the smallest scale
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    const int biased = amax > 0.0f && ef > 2 ? ef - 2 : 0;
+    const float q0 = __builtin_ldexpf(v0, 127 - biased), q1 = __builtin_ldexpf(v1, 127 - biased);  // exact
+    const uint32_t byte = e2m1_code(q0) | (e2m1_code(q1) << 4);
+    codes[(r0 + m) * (I / 2) + g * kPairs + lane] = (uint8_t)byte;
+    if ((lane & 15) == 0) scales[(r0 + m) * (I / 32) + g * 4 + (lane >> 4)] = (uint8_t)biased;
+  }
+}
+
+// c += A . B on one 16x16 tile with FP4 (E2M1) A and B and their E8M0 block
+// scales, c tied to an AGPR quadruple (as mfma_acc: no accumulator moves
+// between loop iterations).  The compiler does not see this as an MFMA: the
+// scale operands are computed by VALU some instructions earlier and separated
+// from the first MFMA by s_nop, and results are read only after mfma_drain.
+__device__ __forceinline__ void mfma_fp4(const u32x4 &a, const u32x4 &b, uint32_t sa, uint32_t sb, f32x4 &c) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+               : "+a"(c)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// y[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]); a workgroup of 4 waves takes a
+// 128 x 128 tile, a wave 64 x 64 (4 x 4 MFMA tiles), k steps of 128, the
+// next step's fragments loaded while the current one computes.
+template <int ODT>
+__global__ void __launch_bounds__(256)
+mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
+               const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, int64_t N, int64_t K,
+               const uint16_t *__restrict__ bias, void *__restrict__ y) {
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int n_tiles = (int)((N + 127) / 128);
+  const int lwg = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * 128 + (wave & 1) * 64;
+  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * 128 + (wave >> 1) * 64;
+  const int fr = lane & 15, q = lane >> 4;
+  const int64_t kb = K / 2, ks = K / 32;  // code bytes and scale bytes per row
+  // raw buffers over the whole operands: rows past the end read as zeros
+  const __amdgpu_buffer_rsrc_t ra = raw_rsrc(ac, (uint32_t)(M * kb));
+  const __amdgpu_buffer_rsrc_t rw = raw_rsrc(wc, (uint32_t)(N * kb));
+  const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(as, (uint32_t)(M * ks));
+  const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(ws, (uint32_t)(N * ks));
+  uint32_t aoff[4], woff[4], asoff[4], wsoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ar = m0 + 16 * i + fr, wr = n0 + 16 * i + fr;
+    aoff[i] = (uint32_t)(ar * kb + 16 * q);
+    woff[i] = (uint32_t)(wr * kb + 16 * q);
+    asoff[i] = (uint32_t)(ar * ks);
+    wsoff[i] = (uint32_t)(wr * ks);
+  }
+  u32x4 fa[2][4], fw[2][4];
+  uint32_t sa[2][4], sw[2][4];
+  auto load = [&](int buf, int64_t step) {
+    const uint32_t cb = (uint32_t)(step * 64), sb = (uint32_t)(step * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[buf][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + cb, 0, 0);
+      fw[buf][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + cb, 0, 0);
+      sa[buf][i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, asoff[i] + sb, 0, 0);
+      sw[buf][i] = __builtin_amdgcn_raw_buffer_load_b32(rsw, wsoff[i] + sb, 0, 0);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_fence(acc[i][j]);
+    }
+  asm volatile("s_nop 7");
+  auto step = [&](int b) {
+    // this lane's block scales (byte q of each 4-block dword), then the MFMAs
+    uint32_t sca[4], scw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sca[i] = (sa[b][i] >> (8 * q)) & 0xffu;
+      scw[i] = (sw[b][i] >> (8 * q)) & 0xffu;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma_fp4(fa[b][i], fw[b][j], sca[i], scw[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int64_t nsteps = K / 128, npairs = nsteps / 2;
+  load(0, 0);
+  if (npairs > 0) {
+    int64_t s = 0;
+    do {
+      load(1, s + 1);
+      step(0);
+      if (s + 2 < nsteps) load(0, s + 2);
+      step(1);
+      s += 2;
+    } while (s < 2 * npairs);
+  }
+  if (nsteps & 1) step(0);  // buffer 0 holds the last step
+  mfma_drain();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc_fence(acc[i][j]);
+  // lane l of tile (i, j): rows 16i + 4q + r, column 16j + l%16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + 16 * j + fr;
+    if (n >= N) continue;
+    const float bv = bias ? f16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + 16 * i + 4 * q + r;
+        if (m >= M) continue;
+        const float v = acc[i][j][r] + bv;
+        if constexpr (ODT == kF32)
+          reinterpret_cast<float *>(y)[m * N + n] = v;
+        else if constexpr (ODT == kF16)
+          reinterpret_cast<uint16_t *>(y)[m * N + n] = f32_to_f16_bits(v);
+        else
+          reinterpret_cast<uint16_t *>(y)[m * N + n] = f32_to_bf16_bits(v);
+      }
+  }
+}
+
+template <int DT, bool WEIGHT>
+static void launch_mxq(dim3 grid, hipStream_t st, const void *src, int64_t rows, int64_t I, const int16_t *pairs,
+                       const float *theta, const float *cs, int krot, int gm, uint8_t *codes, uint8_t *scales) {
+  hipLaunchKernelGGL((mx_quant_kernel<DT, WEIGHT>), grid, dim3(256), 0, st, src, rows, I, pairs, theta, cs, krot, gm,
+                     codes, scales);
+}
+
+hipError_t launch_mx_quantize(const void *src, int dt, bool weight, int64_t rows, int64_t I, const int16_t *pairs,
+                              const float *theta, const float *cs, int krot, int group, uint8_t *codes,
+                              uint8_t *scales, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)(I / kG), (unsigned)((rows + 63) / 64));
+  const int gm = kG - group;
+  if (weight) {
+    if (dt == kF16) launch_mxq<kF16, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+    else if (dt == kBF16) launch_mxq<kBF16, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+    else launch_mxq<kF32, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+  } else {
+    if (dt == kF16) launch_mxq<kF16, false>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+    else launch_mxq<kBF16, false>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t *ac, const uint8_t *as, int64_t M, const uint8_t *wc, const uint8_t *ws,
+                          int64_t N, int64_t K, const uint16_t *bias, void *y, int y_dt, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
+  if (y_dt == kF32)
+    hipLaunchKernelGGL((mx_gemm_kernel<kF32>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+  else if (y_dt == kF16)
+    hipLaunchKernelGGL((mx_gemm_kernel<kF16>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<kBF16>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+  return hipGetLastError();
+}
+
+}  // namespace paro

@@ -380,6 +380,134 @@ size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *L, int64_
   return paro::rot_backward_partial_bytes(tokens, L->in_features, L->krot);  // > 0 even for 0 tokens
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMxMaxBytes = (int64_t(1) << 31) - 1;  // 32-bit buffer offsets in the FP4 GEMM
+
+bool overlap(const void *a, size_t an, const void *b, size_t bn) {
+  const char *pa = (const char *)a, *pb = (const char *)b;
+  return an && bn && pa < pb + bn && pb < pa + an;
+}
+
+int check_mx_rows(int64_t rows, int64_t I) {
+  if (rows < 0) return fail(PARO_ERR_SHAPE, "rows=%lld is negative", (long long)rows);
+  if (rows * (I / 2) > kMxMaxBytes)
+    return fail(PARO_ERR_UNSUPPORTED, "rows * in_features / 2 = %lld exceeds %lld", (long long)(rows * (I / 2)),
+                (long long)kMxMaxBytes);
+  return PARO_OK;
+}
+
+int mx_quantize_impl(const paro_w4_layer *L, const void *src, paro_dtype dt, int64_t rows, bool weight,
+                     uint8_t *codes, uint8_t *scales, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (rc) return rc;
+  const int64_t I = L->in_features;
+  rc = check_mx_rows(rows, I);
+  if (rc) return rc;
+  if (weight ? (!act_dtype(dt) && dt != PARO_F32) : !act_dtype(dt))
+    return fail(PARO_ERR_DTYPE, "%s dtype %d invalid", weight ? "w" : "x", (int)dt);
+  if (rows == 0) return ok();
+  if (!src || !codes || !scales) return fail(PARO_ERR_NULL, "input, codes and scales are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  if (!aligned(src, dt == PARO_F32 ? 8 : 4) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(PARO_ERR_ALIGN, "input 4-byte (8 for F32), codes 16-byte and scales 4-byte aligned");
+  const size_t sb = (size_t)rows * I * (dt == PARO_F32 ? 4 : 2), cb = (size_t)rows * I / 2, scb = (size_t)rows * I / 32;
+  if (overlap(codes, cb, src, sb) || overlap(scales, scb, src, sb) || overlap(codes, cb, scales, scb))
+    return fail(PARO_ERR_SHAPE, "codes, scales and the input must not overlap");
+  hipError_t e = paro::launch_mx_quantize(src, (int)dt, weight, rows, I, L->pairs, L->theta, L->channel_scales,
+                                          L->krot, (int)group_of(L), codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 quantize launch");
+  return ok();
+}
+
+int mx_gemm_checks(const uint8_t *ac, const uint8_t *as, int64_t tokens, const uint8_t *wc, const uint8_t *ws,
+                   int64_t O, int64_t I, const uint16_t *bias, void *y, paro_dtype y_dt) {
+  if (I <= 0 || I % 128 || O <= 0 || O % 8)
+    return fail(PARO_ERR_SHAPE, "in_features %% 128 == 0 and out_features %% 8 == 0 required");
+  int rc = check_mx_rows(tokens, I);
+  if (!rc) rc = check_mx_rows(O, I);
+  if (rc) return rc;
+  if (y_dt != PARO_F16 && y_dt != PARO_BF16 && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d invalid", (int)y_dt);
+  if (tokens == 0) return PARO_OK;
+  if (!ac || !as || !wc || !ws || !y) return fail(PARO_ERR_NULL, "codes, scales and y are required");
+  if (!aligned(ac, 16) || !aligned(wc, 16) || !aligned(as, 4) || !aligned(ws, 4) || !aligned(y, 4) ||
+      (bias && !aligned(bias, 2)))
+    return fail(PARO_ERR_ALIGN, "codes 16-byte, scales and y 4-byte aligned");
+  const size_t yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+  const void *ins[5] = {ac, as, wc, ws, bias};
+  const size_t inb[5] = {(size_t)tokens * I / 2, (size_t)tokens * I / 32, (size_t)O * I / 2, (size_t)O * I / 32,
+                         bias ? (size_t)O * 2 : 0};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(y, yb, ins[i], inb[i])) return fail(PARO_ERR_SHAPE, "y overlaps an input");
+  return PARO_OK;
+}
+
+size_t mx_codes_region(int64_t tokens, int64_t I) { return align_up((size_t)tokens * I / 2, 256); }
+
+}  // namespace
+
+extern "C" {
+
+int paro_mxfp4_quantize_weight(const paro_w4_layer *L, const void *w, paro_dtype w_dt, uint8_t *codes,
+                               uint8_t *scales, void *stream) {
+  if (!L) return fail(PARO_ERR_NULL, "layer is NULL");
+  return mx_quantize_impl(L, w, w_dt, L->out_features, true, codes, scales, stream);
+}
+
+int paro_mxfp4_quantize_activations(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens,
+                                    uint8_t *codes, uint8_t *scales, void *stream) {
+  return mx_quantize_impl(L, x, x_dt, tokens, false, codes, scales, stream);
+}
+
+int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tokens, const uint8_t *w_codes,
+                    const uint8_t *w_scales, int64_t out_features, int64_t in_features, const uint16_t *bias,
+                    void *y, paro_dtype y_dt, void *stream) {
+  int rc = mx_gemm_checks(a_codes, a_scales, tokens, w_codes, w_scales, out_features, in_features, bias, y, y_dt);
+  if (rc) return rc;
+  if (tokens == 0) return ok();
+  hipError_t e = paro::launch_mx_gemm(a_codes, a_scales, tokens, w_codes, w_scales, out_features, in_features, bias,
+                                      y, (int)y_dt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 GEMM launch");
+  return ok();
+}
+
+size_t paro_mxfp4_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
+  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
+  return mx_codes_region(tokens, L->in_features) + align_up((size_t)tokens * L->in_features / 32, 256);
+}
+
+int paro_mxfp4_linear(const paro_w4_layer *L, const uint8_t *w_codes, const uint8_t *w_scales, const void *x,
+                      paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  const int64_t I = L->in_features, O = L->out_features;
+  if (tokens == 0) return ok();
+  const size_t need = paro_mxfp4_linear_workspace_bytes(L, tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
+  uint8_t *ac = (uint8_t *)workspace, *as = ac + mx_codes_region(tokens, I);
+  rc = mx_gemm_checks(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, y_dt);
+  if (rc) return rc;
+  if (overlap(y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2), x, (size_t)tokens * I * 2) ||
+      overlap(workspace, need, x, (size_t)tokens * I * 2) ||
+      overlap(workspace, need, y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2)))
+    return fail(PARO_ERR_SHAPE, "x, y and the workspace must not overlap");
+  rc = mx_quantize_impl(L, x, x_dt, tokens, false, ac, as, stream);
+  if (rc) return rc;
+  hipError_t e = paro::launch_mx_gemm(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, (int)y_dt,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 GEMM launch");
+  return ok();
+}
+
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {
   (void)L;
   return auto_path(tokens);

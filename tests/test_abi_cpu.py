@@ -32,7 +32,7 @@ def test_libparo_exports_every_declared_symbol():
     assert set(_lib.EXPORTS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.paro_abi_version() == 4
+    assert lib.paro_abi_version() == 5
 
 
 def test_oracle_exports_every_declared_symbol():
@@ -300,3 +300,38 @@ def test_moe_linear_argument_checks():
     assert call(y=FAKE + 64) == 2                    # y overlaps x
     assert call(L=fake_layer(G=16)) == 5
     assert call(tokens=0, x=0, y=0) == 0             # nothing to do
+
+
+@needs_no_gpu
+def test_mxfp4_argument_checks():
+    lib = _lib.load()
+    L = fake_layer(I=256, O=64)
+    qw = lambda w=FAKE * 8, dt=1, c=FAKE * 9, s=FAKE * 10, L=L: lib.paro_mxfp4_quantize_weight(
+        ctypes.byref(L), w, dt, c, s, None)
+    assert qw(dt=5) == 3
+    assert qw(w=0) == 1
+    assert qw(c=FAKE * 9 + 4) == 4                  # codes 16-byte aligned
+    assert qw(s=FAKE * 10 + 2) == 4
+    assert qw(c=FAKE * 8 + 64) == 2                 # codes overlap w
+    assert qw(L=fake_layer(G=16)) == 5
+    qa = lambda x=FAKE * 8, dt=0, t=4, c=FAKE * 9, s=FAKE * 10: lib.paro_mxfp4_quantize_activations(
+        ctypes.byref(L), x, dt, t, c, s, None)
+    assert qa(dt=2) == 3                            # activations are 16-bit
+    assert qa(t=-1) == 2
+    assert qa(t=0, x=0, c=0, s=0) == 0
+    gm = lambda ac=FAKE, as_=FAKE * 2, t=4, wc=FAKE * 3, ws=FAKE * 4, O=64, I=256, b=0, y=FAKE * 5, ydt=2: \
+        lib.paro_mxfp4_gemm(ac, as_, t, wc, ws, O, I, b, y, ydt, None)
+    assert gm(I=200) == 2
+    assert gm(O=60) == 2
+    assert gm(ydt=7) == 3
+    assert gm(wc=0) == 1
+    assert gm(ac=FAKE + 8) == 4
+    assert gm(y=FAKE * 3 + 16) == 2                 # y overlaps the weight codes
+    assert gm(t=1 << 24, I=1 << 12) == 5            # beyond 32-bit buffer offsets
+    need = lib.paro_mxfp4_linear_workspace_bytes(ctypes.byref(L), 4)
+    assert need == 512 + 256                        # 4 x 128 code bytes, 4 x 8 scale bytes, each 256-aligned
+    ln = lambda wsb=need, ws=FAKE * 6, xdt=0: lib.paro_mxfp4_linear(
+        ctypes.byref(L), FAKE * 3, FAKE * 4, FAKE, xdt, 4, FAKE * 5, 0, ws, wsb, None)
+    assert ln(wsb=need - 1) == 7
+    assert ln(ws=0) == 7
+    assert ln(xdt=2) == 3

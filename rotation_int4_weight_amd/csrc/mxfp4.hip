@@ -18,7 +18,7 @@
 //
 // mx_gemm_kernel runs v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 A and B: lane
 // l supplies row (column) l%16 and the 32 elements of K block l/16 of a
-// 128-wide k step, 16 bytes loaded straight from the row-major codes, with
+// 128-wide k step, 16 bytes of the row-major codes (staged through LDS), with
 // the E8M0 scale of exactly that 32-element block; the 16x16 fp32 result has
 // row 4(l/16)+r, column l%16 in register r.  (The order of the 32 elements
 // inside a lane's block does not matter as long as A and B agree.)
@@ -106,47 +106,65 @@ __device__ __forceinline__ void mfma_fp4(const u32x4 &a, const u32x4 &b, uint32_
                : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
 
-// y[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]); a workgroup of 4 waves takes a
-// 128 x 128 tile, a wave 64 x 64 (4 x 4 MFMA tiles), k steps of 128, the
-// next step's fragments loaded while the current one computes.
+// y[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]).  A workgroup of 8 waves takes
+// a 128 x 256 tile (waves 2 x 4, 64 x 64 each: 4 x 4 MFMA tiles) over k steps
+// of 128.  Each step's A and W code panels (128 and 256 rows x 64 bytes) and
+// their scale dwords go through LDS once per workgroup (rows padded to 80
+// bytes so the 16-byte fragment reads of 16 rows spread over the banks),
+// double-buffered: the next step's global loads are in flight while this
+// step computes, and one barrier per step separates the buffers.
+// Workgroups run M-fastest in XCD-local order, so the M tiles that share a
+// weight panel meet in one L2.
+constexpr int kMxBM = 128, kMxBN = 256, kMxRow = 80;  // LDS row pitch (bytes)
+constexpr int kMxA = kMxBM * kMxRow, kMxW = kMxBN * kMxRow;
+constexpr int kMxBuf = kMxA + kMxW + (kMxBM + kMxBN) * 4;  // codes + scale dwords of one step
+
 template <int ODT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
                const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, int64_t N, int64_t K,
                const uint16_t *__restrict__ bias, void *__restrict__ y) {
-  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
-  const int n_tiles = (int)((N + 127) / 128);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kMxBuf];
+  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int m_tiles = (int)((M + kMxBM - 1) / kMxBM);
   const int lwg = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
-  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * 128 + (wave & 1) * 64;
-  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * 128 + (wave >> 1) * 64;
+  const int64_t mt0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % m_tiles) * kMxBM;
+  const int64_t nt0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg / m_tiles) * kMxBN;
+  const int wm = wave >> 2, wn = wave & 3;  // wave's 64 x 64 sub-tile
   const int fr = lane & 15, q = lane >> 4;
-  const int64_t kb = K / 2, ks = K / 32;  // code bytes and scale bytes per row
-  // raw buffers over the whole operands: rows past the end read as zeros
+  const int64_t kb = K / 2, ks = K / 32;
   const __amdgpu_buffer_rsrc_t ra = raw_rsrc(ac, (uint32_t)(M * kb));
   const __amdgpu_buffer_rsrc_t rw = raw_rsrc(wc, (uint32_t)(N * kb));
   const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(as, (uint32_t)(M * ks));
   const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(ws, (uint32_t)(N * ks));
-  uint32_t aoff[4], woff[4], asoff[4], wsoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t ar = m0 + 16 * i + fr, wr = n0 + 16 * i + fr;
-    aoff[i] = (uint32_t)(ar * kb + 16 * q);
-    woff[i] = (uint32_t)(wr * kb + 16 * q);
-    asoff[i] = (uint32_t)(ar * ks);
-    wsoff[i] = (uint32_t)(wr * ks);
-  }
-  u32x4 fa[2][4], fw[2][4];
-  uint32_t sa[2][4], sw[2][4];
-  auto load = [&](int buf, int64_t step) {
+
+  // global -> register staging of one step: A chunks c = tid (row c/4, part
+  // c%4), W chunks tid and tid + 512, one scale dword (A rows for tid < 128,
+  // W rows for 128 <= tid < 384)
+  const int a_row = tid >> 2, part = tid & 3;
+  const uint32_t a_goff = (uint32_t)((mt0 + a_row) * kb + 16 * part);
+  const uint32_t w_goff0 = (uint32_t)((nt0 + a_row) * kb + 16 * part);
+  const uint32_t w_goff1 = (uint32_t)((nt0 + 128 + a_row) * kb + 16 * part);
+  const bool sc_a = tid < kMxBM, sc_w = tid >= kMxBM && tid < kMxBM + kMxBN;
+  const uint32_t s_goff = sc_a ? (uint32_t)((mt0 + tid) * ks) : (uint32_t)((nt0 + (tid - kMxBM)) * ks);
+  u32x4 ga, gw0, gw1;
+  uint32_t gs;
+  auto gload = [&](int64_t step) {
     const uint32_t cb = (uint32_t)(step * 64), sb = (uint32_t)(step * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[buf][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + cb, 0, 0);
-      fw[buf][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + cb, 0, 0);
-      sa[buf][i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, asoff[i] + sb, 0, 0);
-      sw[buf][i] = __builtin_amdgcn_raw_buffer_load_b32(rsw, wsoff[i] + sb, 0, 0);
-    }
+    ga = __builtin_amdgcn_raw_buffer_load_b128(ra, a_goff + cb, 0, 0);
+    gw0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_goff0 + cb, 0, 0);
+    gw1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_goff1 + cb, 0, 0);
+    gs = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb, 0, 0)
+              : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb, 0, 0) : 0u);
   };
+  auto sstore = [&](int buf) {
+    uint8_t *b = lds[buf];
+    *reinterpret_cast<u32x4 *>(b + a_row * kMxRow + 16 * part) = ga;
+    *reinterpret_cast<u32x4 *>(b + kMxA + a_row * kMxRow + 16 * part) = gw0;
+    *reinterpret_cast<u32x4 *>(b + kMxA + (128 + a_row) * kMxRow + 16 * part) = gw1;
+    if (tid < kMxBM + kMxBN) *reinterpret_cast<uint32_t *>(b + kMxA + kMxW + 4 * tid) = gs;
+  };
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -156,42 +174,51 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
       acc_fence(acc[i][j]);
     }
   asm volatile("s_nop 7");
-  auto step = [&](int b) {
-    // this lane's block scales (byte q of each 4-block dword), then the MFMAs
+
+  auto compute = [&](int buf) {
+    const uint8_t *b = lds[buf];
+    u32x4 fa[4], fw[4];
     uint32_t sca[4], scw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sca[i] = (sa[b][i] >> (8 * q)) & 0xffu;
-      scw[i] = (sw[b][i] >> (8 * q)) & 0xffu;
+      const int ar = wm * 64 + 16 * i + fr, wr = wn * 64 + 16 * i + fr;
+      fa[i] = *reinterpret_cast<const u32x4 *>(b + ar * kMxRow + 16 * q);
+      fw[i] = *reinterpret_cast<const u32x4 *>(b + kMxA + wr * kMxRow + 16 * q);
+      sca[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 4 * ar) >> (8 * q)) & 0xffu;
+      scw[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 4 * (kMxBM + wr)) >> (8 * q)) & 0xffu;
     }
+    // the scale operands come from VALU: padding before the asm MFMAs read them
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 4");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_fp4(fa[b][i], fw[b][j], sca[i], scw[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mfma_fp4(fa[i], fw[j], sca[i], scw[j], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
   };
-  const int64_t nsteps = K / 128, npairs = nsteps / 2;
-  load(0, 0);
-  if (npairs > 0) {
-    int64_t s = 0;
-    do {
-      load(1, s + 1);
-      step(0);
-      if (s + 2 < nsteps) load(0, s + 2);
-      step(1);
-      s += 2;
-    } while (s < 2 * npairs);
-  }
-  if (nsteps & 1) step(0);  // buffer 0 holds the last step
+
+  const int64_t nsteps = K / 128;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  int64_t s = 0;
+  do {
+    const int buf = (int)(s & 1);
+    if (s + 1 < nsteps) gload(s + 1);
+    compute(buf);
+    if (s + 1 < nsteps) sstore(buf ^ 1);  // buf ^ 1 was last read in step s - 1
+    __syncthreads();
+    ++s;
+  } while (s < nsteps);
   mfma_drain();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc_fence(acc[i][j]);
+
   // lane l of tile (i, j): rows 16i + 4q + r, column 16j + l%16
+  const int64_t m0 = mt0 + wm * 64, n0 = nt0 + wn * 64;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + 16 * j + fr;
@@ -241,13 +268,13 @@ hipError_t launch_mx_quantize(const void *src, int dt, bool weight, int64_t rows
 hipError_t launch_mx_gemm(const uint8_t *ac, const uint8_t *as, int64_t M, const uint8_t *wc, const uint8_t *ws,
                           int64_t N, int64_t K, const uint16_t *bias, void *y, int y_dt, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
+  const dim3 grid((unsigned)(((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN)));
   if (y_dt == kF32)
-    hipLaunchKernelGGL((mx_gemm_kernel<kF32>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+    hipLaunchKernelGGL((mx_gemm_kernel<kF32>), grid, dim3(512), 0, st, ac, as, M, wc, ws, N, K, bias, y);
   else if (y_dt == kF16)
-    hipLaunchKernelGGL((mx_gemm_kernel<kF16>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+    hipLaunchKernelGGL((mx_gemm_kernel<kF16>), grid, dim3(512), 0, st, ac, as, M, wc, ws, N, K, bias, y);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<kBF16>), grid, dim3(256), 0, st, ac, as, M, wc, ws, N, K, bias, y);
+    hipLaunchKernelGGL((mx_gemm_kernel<kBF16>), grid, dim3(512), 0, st, ac, as, M, wc, ws, N, K, bias, y);
   return hipGetLastError();
 }
 

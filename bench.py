@@ -343,7 +343,8 @@ def bench_mxfp4(args, paro, synth, np, torch, dev):
     work = torch.empty(max(paro.paro_mxfp4_linear_workspace_bytes(D, M), 16), dtype=torch.uint8, device=dev)
     ac = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
     as_ = torch.empty((M, I // 32), dtype=torch.uint8, device=dev)
-    paro.paro_mxfp4_quantize_activations(D, xd, ac, as_)
+    aws = torch.empty(paro.paro_mxfp4_activation_workspace_bytes(D), dtype=torch.uint8, device=dev)
+    paro.paro_mxfp4_quantize_activations(D, xd, ac, as_, aws)
     bias = D.bias
     stream = torch.cuda.current_stream()
 

@@ -332,7 +332,8 @@ size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *layer, in
  * sign; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to v / 2^(b - 127),
  * ties to the even code, clamped at 6, zero as +0.  Layout: codes [rows][I/2]
  * bytes, element 2j in the low nibble of byte j; scales [rows][I/32] bytes.
- * Decisions are taken in fp32 on the kernel's rotation of the rows.
+ * Decisions are taken in fp32 on the kernel's rotation of the rows (the
+ * staged rotation for weights, the dense one for activations).
  *
  * Quantize the transformed weight W_r = W . D . R (w [O][I], F16/BF16/F32, 4-
  * byte aligned, 8 for F32): codes [O][I/2] (16-byte aligned), scales [O][I/32]
@@ -341,9 +342,15 @@ size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *layer, in
  */
 int paro_mxfp4_quantize_weight(const paro_w4_layer *layer, const void *w, paro_dtype w_dt, uint8_t *codes,
                                uint8_t *scales, void *stream);
-/* Quantize the rotated activations X_r = X . D^-1 . R (x [tokens][I] F16/BF16). */
+/* Quantize the rotated activations X_r = X . D^-1 . R (x [tokens][I] F16/BF16,
+ * 16-byte aligned; codes [tokens][I/2] 16-byte, scales [tokens][I/32] 4-byte
+ * aligned).  The rotation runs as the dense per-group R' = diag(cs) . R on the
+ * matrix cores (built into the workspace, paro_mxfp4_activation_workspace_bytes
+ * bytes, 16-byte aligned) and the blocks are quantized in its epilogue. */
 int paro_mxfp4_quantize_activations(const paro_w4_layer *layer, const void *x, paro_dtype x_dt, int64_t tokens,
-                                    uint8_t *codes, uint8_t *scales, void *stream);
+                                    uint8_t *codes, uint8_t *scales, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+size_t paro_mxfp4_activation_workspace_bytes(const paro_w4_layer *layer);
 /* y [tokens][out_features] = A . W^T (+ bias fp16 [out_features] or NULL)
  * from MXFP4 codes and scales of A [tokens][in_features] and W
  * [out_features][in_features]; fp32 accumulation, one rounding to y_dt

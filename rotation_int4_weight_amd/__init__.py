@@ -17,7 +17,7 @@ from ._lib import (BF16, EXPORTS, F16, F32, PATH_AUTO, PATH_DECODE_FUSED, PATH_D
                    paro_scale_rotate_backward_workspace_bytes, paro_w4a16_moe_linear,
                    paro_w4a16_moe_linear_workspace_bytes, paro_mxfp4_quantize_weight,
                    paro_mxfp4_quantize_activations, paro_mxfp4_gemm, paro_mxfp4_linear,
-                   paro_mxfp4_linear_workspace_bytes)
+                   paro_mxfp4_linear_workspace_bytes, paro_mxfp4_activation_workspace_bytes)
 
 __all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "PATH_DECODE_SPLIT",
            "PATH_PREFILL", "DeviceLayer", "ParoError", "load", "make_workspace", "paro_abi_version",
@@ -29,4 +29,4 @@ __all__ = ["BF16", "EXPORTS", "F16", "F32", "PATH_AUTO", "PATH_DECODE_FUSED", "P
            "paro_scale_rotate_backward_workspace_bytes", "paro_w4a16_moe_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
            "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
-           "paro_mxfp4_linear_workspace_bytes"]
+           "paro_mxfp4_linear_workspace_bytes", "paro_mxfp4_activation_workspace_bytes"]

@@ -23,7 +23,7 @@ EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
            "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
-           "paro_mxfp4_linear_workspace_bytes",
+           "paro_mxfp4_linear_workspace_bytes", "paro_mxfp4_activation_workspace_bytes",
            "paro_scale_rotate_backward_workspace_bytes",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
@@ -72,7 +72,9 @@ def load(path: str | None = None):
     lib.paro_w4a16_moe_linear_workspace_bytes.argtypes = [P, I64, I32]
     lib.paro_w4a16_moe_linear_workspace_bytes.restype = SZ
     lib.paro_mxfp4_quantize_weight.argtypes = [P, P, I32, P, P, P]
-    lib.paro_mxfp4_quantize_activations.argtypes = [P, P, I32, I64, P, P, P]
+    lib.paro_mxfp4_quantize_activations.argtypes = [P, P, I32, I64, P, P, P, SZ, P]
+    lib.paro_mxfp4_activation_workspace_bytes.argtypes = [P]
+    lib.paro_mxfp4_activation_workspace_bytes.restype = SZ
     lib.paro_mxfp4_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P, I32, P]
     lib.paro_mxfp4_linear.argtypes = [P, P, P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_mxfp4_linear_workspace_bytes.argtypes = [P, I64]
@@ -250,10 +252,16 @@ def paro_mxfp4_quantize_weight(layer: DeviceLayer, w, codes, scales, stream=None
                                              _stream_handle(stream)), "paro_mxfp4_quantize_weight")
 
 
-def paro_mxfp4_quantize_activations(layer: DeviceLayer, x, codes, scales, stream=None) -> None:
-    """x: (tokens, I) fp16/bf16; codes uint8 (tokens, I/2); scales uint8 (tokens, I/32)."""
+def paro_mxfp4_activation_workspace_bytes(layer: DeviceLayer) -> int:
+    return int(load().paro_mxfp4_activation_workspace_bytes(layer.ref))
+
+
+def paro_mxfp4_quantize_activations(layer: DeviceLayer, x, codes, scales, workspace, stream=None) -> None:
+    """x: (tokens, I) fp16/bf16; codes uint8 (tokens, I/2); scales uint8 (tokens, I/32); workspace: device
+    buffer of paro_mxfp4_activation_workspace_bytes() bytes."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().paro_mxfp4_quantize_activations(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(codes),
-                                                  _ptr(scales), _stream_handle(stream)),
+                                                  _ptr(scales), _ptr(workspace), ws_bytes, _stream_handle(stream)),
            "paro_mxfp4_quantize_activations")
 
 

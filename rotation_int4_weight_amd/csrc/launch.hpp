@@ -82,6 +82,10 @@ hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const flo
                             int krot, int group, uint16_t *hl, hipStream_t st);
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st);
+// The same product with an MXFP4 epilogue: codes [tokens][I/2], scales
+// [tokens][I/32] (see mx.hpp) instead of the tiled X_r.
+hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
+                               uint8_t *codes, uint8_t *scales, hipStream_t st);
 // Row-major [tokens][I] (2-byte elements) -> tiled layout (pad rows zero).
 hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64_t I, hipStream_t st);
 
@@ -108,12 +112,11 @@ hipError_t launch_rot_backward(const void *x, int x_dt, const void *g, int g_dt,
                                void *gx,
                                int gx_dt, float *gtheta, float *gcs, float *partial, hipStream_t st);
 
-// MXFP4 (32-element E8M0 blocks, E2M1 codes) after the rotation: rows
-// [rows][I] (activations times cs, or weights divided by cs when `weight`)
-// -> codes [rows][I/2] bytes, scales [rows][I/32] bytes.
-hipError_t launch_mx_quantize(const void *src, int dt, bool weight, int64_t rows, int64_t I, const int16_t *pairs,
-                              const float *theta, const float *cs, int krot, int group, uint8_t *codes,
-                              uint8_t *scales, hipStream_t st);
+// MXFP4 (32-element E8M0 blocks, E2M1 codes; mx.hpp) of the transformed
+// weight rows W . D . R: w [rows][I] -> codes [rows][I/2], scales [rows][I/32].
+hipError_t launch_mx_quantize_weight(const void *w, int dt, int64_t rows, int64_t I, const int16_t *pairs,
+                                     const float *theta, const float *cs, int krot, int group, uint8_t *codes,
+                                     uint8_t *scales, hipStream_t st);
 // y [M][N] = A . W^T (+ bias) on the block-scaled FP4 matrix cores.
 hipError_t launch_mx_gemm(const uint8_t *ac, const uint8_t *as, int64_t M, const uint8_t *wc, const uint8_t *ws,
                           int64_t N, int64_t K, const uint16_t *bias, void *y, int y_dt, hipStream_t st);

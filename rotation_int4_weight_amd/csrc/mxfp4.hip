@@ -11,10 +11,11 @@
 // clamped at 6; zero stored as +0).  Codes: [rows][I/2] bytes, element 2j in
 // the low nibble of byte j; scales: [rows][I/32] bytes.
 //
-// mx_quant_kernel rotates rows of one 128-channel block in LDS with the staged
-// rotation (fp32) and quantizes them: lane p holds channels 2p, 2p+1, a block
-// of 32 channels is 16 lanes, so its max is four lane shuffles away.  The same
-// kernel takes activations (x times cs) and weights (W divided by cs).
+// mx_quant_kernel rotates weight rows of one 128-channel block in LDS with the
+// staged rotation (fp32, W divided by cs) and quantizes them: lane p holds
+// channels 2p, 2p+1, a block of 32 channels is 16 lanes, so its max is four
+// lane shuffles away.  Activations are quantized in the epilogue of the dense
+// rotation on the matrix cores (rot_apply_kernel<., true>).
 //
 // mx_gemm_kernel runs v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 A and B: lane
 // l supplies row (column) l%16 and the 32 elements of K block l/16 of a
@@ -25,6 +26,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
+#include "mx.hpp"
 
 namespace paro {
 
@@ -38,16 +40,6 @@ __device__ __forceinline__ float2 load_pair_any(const void *p, int64_t idx) {
     const uint32_t b = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(p) + idx);
     return float2{act_to_f32<DT>(b & 0xffffu), act_to_f32<DT>(b >> 16)};
   }
-}
-
-// E2M1 code of a (already divided by the block scale): the count of rounding
-// boundaries below |a|, ties to the even code (0, 1.0, 1.0, 2.0, 2.0, 4.0,
-// 4.0), saturating at 6; sign in bit 3 unless the magnitude is zero.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-  const float m = fabsf(a);
-  const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
-                     (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
-  return (a < 0.0f && c != 0) ? (c | 8u) : c;
 }
 
 // rows [rows][I] (x dtype, or the weight's dtype); WEIGHT: divide by cs
@@ -84,12 +76,8 @@ mx_quant_kernel(const void *__restrict__ src, int64_t rows, int64_t I, const int
     float amax = fmaxf(fabsf(v0), fabsf(v1));
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // the 16 lanes of a block
-    // floor(log2 amax) = exponent field - 127 (normal amax); the block
-    // exponent is 2 less; subnormal or zero amax gives the smallest scale
-    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-    const int biased = amax > 0.0f && ef > 2 ? ef - 2 : 0;
-    const float q0 = __builtin_ldexpf(v0, 127 - biased), q1 = __builtin_ldexpf(v1, 127 - biased);  // exact
-    const uint32_t byte = e2m1_code(q0) | (e2m1_code(q1) << 4);
+    const int biased = mx_block_exponent(amax);
+    const uint32_t byte = e2m1_code(mx_scaled(v0, biased)) | (e2m1_code(mx_scaled(v1, biased)) << 4);
     codes[(r0 + m) * (I / 2) + g * kPairs + lane] = (uint8_t)byte;
     if ((lane & 15) == 0) scales[(r0 + m) * (I / 32) + g * 4 + (lane >> 4)] = (uint8_t)biased;
   }
@@ -241,27 +229,22 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
   }
 }
 
-template <int DT, bool WEIGHT>
+template <int DT>
 static void launch_mxq(dim3 grid, hipStream_t st, const void *src, int64_t rows, int64_t I, const int16_t *pairs,
                        const float *theta, const float *cs, int krot, int gm, uint8_t *codes, uint8_t *scales) {
-  hipLaunchKernelGGL((mx_quant_kernel<DT, WEIGHT>), grid, dim3(256), 0, st, src, rows, I, pairs, theta, cs, krot, gm,
+  hipLaunchKernelGGL((mx_quant_kernel<DT, true>), grid, dim3(256), 0, st, src, rows, I, pairs, theta, cs, krot, gm,
                      codes, scales);
 }
 
-hipError_t launch_mx_quantize(const void *src, int dt, bool weight, int64_t rows, int64_t I, const int16_t *pairs,
-                              const float *theta, const float *cs, int krot, int group, uint8_t *codes,
-                              uint8_t *scales, hipStream_t st) {
+hipError_t launch_mx_quantize_weight(const void *w, int dt, int64_t rows, int64_t I, const int16_t *pairs,
+                                     const float *theta, const float *cs, int krot, int group, uint8_t *codes,
+                                     uint8_t *scales, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)(I / kG), (unsigned)((rows + 63) / 64));
   const int gm = kG - group;
-  if (weight) {
-    if (dt == kF16) launch_mxq<kF16, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
-    else if (dt == kBF16) launch_mxq<kBF16, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
-    else launch_mxq<kF32, true>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
-  } else {
-    if (dt == kF16) launch_mxq<kF16, false>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
-    else launch_mxq<kBF16, false>(grid, st, src, rows, I, pairs, theta, cs, krot, gm, codes, scales);
-  }
+  if (dt == kF16) launch_mxq<kF16>(grid, st, w, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+  else if (dt == kBF16) launch_mxq<kBF16>(grid, st, w, rows, I, pairs, theta, cs, krot, gm, codes, scales);
+  else launch_mxq<kF32>(grid, st, w, rows, I, pairs, theta, cs, krot, gm, codes, scales);
   return hipGetLastError();
 }
 

@@ -399,27 +399,26 @@ int check_mx_rows(int64_t rows, int64_t I) {
   return PARO_OK;
 }
 
-int mx_quantize_impl(const paro_w4_layer *L, const void *src, paro_dtype dt, int64_t rows, bool weight,
-                     uint8_t *codes, uint8_t *scales, void *stream) {
+int mx_quantize_weight_impl(const paro_w4_layer *L, const void *w, paro_dtype w_dt, uint8_t *codes,
+                            uint8_t *scales, void *stream) {
   int rc = check_gpu_shape(L);
   if (rc) return rc;
-  const int64_t I = L->in_features;
+  const int64_t I = L->in_features, rows = L->out_features;
   rc = check_mx_rows(rows, I);
   if (rc) return rc;
-  if (weight ? (!act_dtype(dt) && dt != PARO_F32) : !act_dtype(dt))
-    return fail(PARO_ERR_DTYPE, "%s dtype %d invalid", weight ? "w" : "x", (int)dt);
-  if (rows == 0) return ok();
-  if (!src || !codes || !scales) return fail(PARO_ERR_NULL, "input, codes and scales are required");
+  if (!act_dtype(w_dt) && w_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "w dtype %d invalid", (int)w_dt);
+  if (!w || !codes || !scales) return fail(PARO_ERR_NULL, "w, codes and scales are required");
   rc = check_rotation_tensors(L);
   if (rc) return rc;
-  if (!aligned(src, dt == PARO_F32 ? 8 : 4) || !aligned(codes, 16) || !aligned(scales, 4))
-    return fail(PARO_ERR_ALIGN, "input 4-byte (8 for F32), codes 16-byte and scales 4-byte aligned");
-  const size_t sb = (size_t)rows * I * (dt == PARO_F32 ? 4 : 2), cb = (size_t)rows * I / 2, scb = (size_t)rows * I / 32;
-  if (overlap(codes, cb, src, sb) || overlap(scales, scb, src, sb) || overlap(codes, cb, scales, scb))
-    return fail(PARO_ERR_SHAPE, "codes, scales and the input must not overlap");
-  hipError_t e = paro::launch_mx_quantize(src, (int)dt, weight, rows, I, L->pairs, L->theta, L->channel_scales,
-                                          L->krot, (int)group_of(L), codes, scales, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "mxfp4 quantize launch");
+  if (!aligned(w, w_dt == PARO_F32 ? 8 : 4) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(PARO_ERR_ALIGN, "w 4-byte (8 for F32), codes 16-byte and scales 4-byte aligned");
+  const size_t wb = (size_t)rows * I * (w_dt == PARO_F32 ? 4 : 2), cb = (size_t)rows * I / 2,
+               scb = (size_t)rows * I / 32;
+  if (overlap(codes, cb, w, wb) || overlap(scales, scb, w, wb) || overlap(codes, cb, scales, scb))
+    return fail(PARO_ERR_SHAPE, "codes, scales and w must not overlap");
+  hipError_t e = paro::launch_mx_quantize_weight(w, (int)w_dt, rows, I, L->pairs, L->theta, L->channel_scales,
+                                                 L->krot, (int)group_of(L), codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 weight quantize launch");
   return ok();
 }
 
@@ -453,13 +452,45 @@ extern "C" {
 
 int paro_mxfp4_quantize_weight(const paro_w4_layer *L, const void *w, paro_dtype w_dt, uint8_t *codes,
                                uint8_t *scales, void *stream) {
-  if (!L) return fail(PARO_ERR_NULL, "layer is NULL");
-  return mx_quantize_impl(L, w, w_dt, L->out_features, true, codes, scales, stream);
+  return mx_quantize_weight_impl(L, w, w_dt, codes, scales, stream);
+}
+
+size_t paro_mxfp4_activation_workspace_bytes(const paro_w4_layer *L) {
+  if (!L || check_gpu_shape(L)) return 0;
+  return align_up(paro::rot_mat_bytes(L->in_features), 256);
 }
 
 int paro_mxfp4_quantize_activations(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens,
-                                    uint8_t *codes, uint8_t *scales, void *stream) {
-  return mx_quantize_impl(L, x, x_dt, tokens, false, codes, scales, stream);
+                                    uint8_t *codes, uint8_t *scales, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  int rc = check_gpu_shape(L);
+  if (rc) return rc;
+  const int64_t I = L->in_features;
+  rc = check_mx_rows(tokens, I);
+  if (rc) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (tokens == 0) return ok();
+  if (!x || !codes || !scales) return fail(PARO_ERR_NULL, "x, codes and scales are required");
+  rc = check_rotation_tensors(L);
+  if (rc) return rc;
+  const size_t need = paro_mxfp4_activation_workspace_bytes(L);
+  if (!workspace || workspace_bytes < need)
+    return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(workspace, 16))
+    return fail(PARO_ERR_ALIGN, "x, codes and workspace 16-byte, scales 4-byte aligned");
+  const size_t xb = (size_t)tokens * I * 2, cb = (size_t)tokens * I / 2, sb = (size_t)tokens * I / 32;
+  if (overlap(codes, cb, x, xb) || overlap(scales, sb, x, xb) || overlap(codes, cb, scales, sb) ||
+      overlap(workspace, need, x, xb) || overlap(workspace, need, codes, cb) || overlap(workspace, need, scales, sb))
+    return fail(PARO_ERR_SHAPE, "x, codes, scales and the workspace must not overlap");
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t *hl = (uint16_t *)workspace;
+  hipError_t e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot,
+                                        (int)group_of(L), hl, st);
+  if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+  e = paro::launch_rot_apply_mx((const uint16_t *)x, (int)x_dt, tokens, I, hl, codes, scales, st);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 activation launch");
+  return ok();
 }
 
 int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tokens, const uint8_t *w_codes,
@@ -476,7 +507,8 @@ int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tok
 
 size_t paro_mxfp4_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
   if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
-  return mx_codes_region(tokens, L->in_features) + align_up((size_t)tokens * L->in_features / 32, 256);
+  return mx_codes_region(tokens, L->in_features) + align_up((size_t)tokens * L->in_features / 32, 256) +
+         paro_mxfp4_activation_workspace_bytes(L);
 }
 
 int paro_mxfp4_linear(const paro_w4_layer *L, const uint8_t *w_codes, const uint8_t *w_scales, const void *x,
@@ -494,13 +526,15 @@ int paro_mxfp4_linear(const paro_w4_layer *L, const uint8_t *w_codes, const uint
                 need);
   if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
   uint8_t *ac = (uint8_t *)workspace, *as = ac + mx_codes_region(tokens, I);
+  uint8_t *hl = as + align_up((size_t)tokens * I / 32, 256);
   rc = mx_gemm_checks(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, y_dt);
   if (rc) return rc;
   if (overlap(y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2), x, (size_t)tokens * I * 2) ||
       overlap(workspace, need, x, (size_t)tokens * I * 2) ||
       overlap(workspace, need, y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2)))
     return fail(PARO_ERR_SHAPE, "x, y and the workspace must not overlap");
-  rc = mx_quantize_impl(L, x, x_dt, tokens, false, ac, as, stream);
+  rc = paro_mxfp4_quantize_activations(L, x, x_dt, tokens, ac, as, hl, paro_mxfp4_activation_workspace_bytes(L),
+                                       stream);
   if (rc) return rc;
   hipError_t e = paro::launch_mx_gemm(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, (int)y_dt,
                                       (hipStream_t)stream);

@@ -14,6 +14,7 @@
 // dependent LDS stages).
 #include "common.hpp"
 #include "launch.hpp"
+#include "mx.hpp"
 #include "mfma.hpp"
 
 namespace paro {
@@ -167,10 +168,14 @@ constexpr int kHS = kG + 8;
 constexpr int kApplyRows = 512;
 constexpr int kApplyTiles = 4;  // row tiles per wave and batch
 
-template <int XDT>
+// MX = true: instead of the tiled X_r, each row's 32-channel blocks are
+// quantized to MXFP4 in the epilogue (codes [tokens][I/2], E8M0 scales
+// [tokens][I/32]): a lane holds 8 consecutive channels of a block, and the
+// block's other 24 are in lanes l ^ 16, l ^ 32, l ^ 48 (same token).
+template <int XDT, bool MX>
 __global__ void __launch_bounds__(256, 2)
 rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int64_t tokens, int64_t I,
-                 const uint16_t *__restrict__ hl) {
+                 const uint16_t *__restrict__ hl, uint8_t *__restrict__ mx_codes, uint8_t *__restrict__ mx_scales) {
   __shared__ __attribute__((aligned(16))) uint16_t hlds[2 * kG * kHS];
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t g = blockIdx.x;
@@ -256,6 +261,31 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc_fence(acc[t][ct]);
     // lane l, tile t, 32-channel block b: token l%16, channels 32b + 8(l/16) .. +7.
+    if constexpr (MX) {
+#pragma unroll
+      for (int t = 0; t < kApplyTiles; ++t) {
+        const int64_t tok = (mt0 + t) * 16 + fr;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const f32x4 lo = acc[t][2 * b], hi = acc[t][2 * b + 1];
+          const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          float am = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+          am = fmaxf(am, __shfl_xor(am, 16));
+          am = fmaxf(am, __shfl_xor(am, 32));
+          const int biased = mx_block_exponent(am);
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) word |= e2m1_code(mx_scaled(v[e], biased)) << (4 * e);
+          if (tok < tokens) {
+            *reinterpret_cast<uint32_t *>(mx_codes + tok * (I / 2) + g * (kG / 2) + 16 * b + (fk >> 1)) = word;
+            if (fk == 0) mx_scales[tok * (I / 32) + g * 4 + b] = (uint8_t)biased;
+          }
+        }
+      }
+      continue;
+    }
     // Streaming (non-temporal) stores: X_r is not read again by this kernel,
     // and keeping it out of the caches leaves them to the x stream (measured
     // a third faster than ordinary stores).
@@ -290,9 +320,24 @@ hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t t
                             const uint16_t *hl, hipStream_t st) {
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + kApplyRows - 1) / kApplyRows));
   if (x_dt == kF16)
-    hipLaunchKernelGGL((rot_apply_kernel<kF16>), grid, dim3(256), 0, st, x, xt, tokens, I, hl);
+    hipLaunchKernelGGL((rot_apply_kernel<kF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
+                       nullptr);
   else
-    hipLaunchKernelGGL((rot_apply_kernel<kBF16>), grid, dim3(256), 0, st, x, xt, tokens, I, hl);
+    hipLaunchKernelGGL((rot_apply_kernel<kBF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
+                       nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
+                               uint8_t *codes, uint8_t *scales, hipStream_t st) {
+  if (tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + kApplyRows - 1) / kApplyRows));
+  if (x_dt == kF16)
+    hipLaunchKernelGGL((rot_apply_kernel<kF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL((rot_apply_kernel<kBF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,
+                       scales);
   return hipGetLastError();
 }
 

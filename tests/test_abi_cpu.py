@@ -314,11 +314,16 @@ def test_mxfp4_argument_checks():
     assert qw(s=FAKE * 10 + 2) == 4
     assert qw(c=FAKE * 8 + 64) == 2                 # codes overlap w
     assert qw(L=fake_layer(G=16)) == 5
-    qa = lambda x=FAKE * 8, dt=0, t=4, c=FAKE * 9, s=FAKE * 10: lib.paro_mxfp4_quantize_activations(
-        ctypes.byref(L), x, dt, t, c, s, None)
+    aws = lib.paro_mxfp4_activation_workspace_bytes(ctypes.byref(L))
+    assert aws == 2 * 2 * 128 * 128 * 2             # the dense R' (H and L) of two groups
+    qa = lambda x=FAKE * 8, dt=0, t=4, c=FAKE * 9, s=FAKE * 10, ws=FAKE * 11, wsb=aws: \
+        lib.paro_mxfp4_quantize_activations(ctypes.byref(L), x, dt, t, c, s, ws, wsb, None)
     assert qa(dt=2) == 3                            # activations are 16-bit
     assert qa(t=-1) == 2
     assert qa(t=0, x=0, c=0, s=0) == 0
+    assert qa(wsb=aws - 1) == 7
+    assert qa(x=FAKE * 8 + 4) == 4
+    assert qa(ws=FAKE * 8 + 64) == 2                # workspace overlaps x
     gm = lambda ac=FAKE, as_=FAKE * 2, t=4, wc=FAKE * 3, ws=FAKE * 4, O=64, I=256, b=0, y=FAKE * 5, ydt=2: \
         lib.paro_mxfp4_gemm(ac, as_, t, wc, ws, O, I, b, y, ydt, None)
     assert gm(I=200) == 2
@@ -329,7 +334,7 @@ def test_mxfp4_argument_checks():
     assert gm(y=FAKE * 3 + 16) == 2                 # y overlaps the weight codes
     assert gm(t=1 << 24, I=1 << 12) == 5            # beyond 32-bit buffer offsets
     need = lib.paro_mxfp4_linear_workspace_bytes(ctypes.byref(L), 4)
-    assert need == 512 + 256                        # 4 x 128 code bytes, 4 x 8 scale bytes, each 256-aligned
+    assert need == 512 + 256 + aws                  # 4 x 128 code bytes, 4 x 8 scale bytes, R' (each 256-aligned)
     ln = lambda wsb=need, ws=FAKE * 6, xdt=0: lib.paro_mxfp4_linear(
         ctypes.byref(L), FAKE * 3, FAKE * 4, FAKE, xdt, 4, FAKE * 5, 0, ws, wsb, None)
     assert ln(wsb=need - 1) == 7

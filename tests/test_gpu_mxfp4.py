@@ -1,8 +1,9 @@
 """GPU parity of the MXFP4 (four-bit activations) path against the fp64
 oracle, through the C-ABI.
 
-Quantization: the kernel decides on its fp32 rotation of the rows, the oracle
-on its exact one; they differ by about 1e-6 relative.  A block scale may
+Quantization: the kernel decides on its fp32 rotation of the rows (staged for
+weights; for activations the dense R' = H + L on the matrix cores, good to
+about 2^-16 relative), the oracle on its exact one.  A block scale may
 differ (by one) only where the oracle's block maximum lies within 1e-4
 (relative) of a power of two, and a code only where the oracle's v / scale
 lies within 1e-4 of an E2M1 rounding boundary (then by one step); such places
@@ -27,6 +28,11 @@ paro = pytest.importorskip("rotation_int4_weight_amd")
 pytestmark = pytest.mark.gpu
 
 TIE = 1e-4
+# activations go through the dense R' = H + L (bf16 parts: each entry to about
+# 2^-17), so a rotated value errs by up to about 2^-17 * sum |x_i R'_ij|, which
+# for a group holding an x20 outlier column reaches ~1e-4 of the block scale:
+# decisions within 2e-3 of a boundary may differ
+TIE_ACT = 2e-3
 BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
@@ -47,19 +53,21 @@ def magnitude_index(c):
     return np.where(c & 8, -(c & 7), c & 7)
 
 
-def compare_quantized(v_ref, codes_g, scales_g):
-    """v_ref: the oracle's exact rotated rows [rows][K]."""
+def compare_quantized(v_ref, codes_g, scales_g, tie=TIE):
+    """v_ref: the oracle's exact rotated rows [rows][K]; tie: the decision
+    window (relative to the block scale) that the kernel's rotation error can
+    reach."""
     codes_o, scales_o = ref.mxfp4_quantize(v_ref)
     rows, K = v_ref.shape
     amax = np.abs(v_ref.reshape(rows, K // 32, 32)).max(axis=2)
     frac = np.log2(np.where(amax > 0, amax, 1.0))
-    near_pow2 = np.abs(frac - np.round(frac)) < TIE / np.log(2)
+    near_pow2 = np.abs(frac - np.round(frac)) < tie / np.log(2)
     ds = scales_g.astype(int) - scales_o.astype(int)
     bad_s = (ds != 0) & ~(near_pow2 & (np.abs(ds) == 1))
     assert not bad_s.any(), f"block scales differ off powers of two at {np.argwhere(bad_s)[:5]}"
     X = np.repeat(2.0 ** (scales_o.astype(float) - 127), 32, axis=1)
     qv = np.abs(v_ref / X)
-    near_b = (np.abs(qv[..., None] - BOUNDS) < TIE).any(axis=-1)
+    near_b = (np.abs(qv[..., None] - BOUNDS) < tie).any(axis=-1)
     ng, no = nibbles(codes_g), nibbles(codes_o)
     diff = magnitude_index(ng) - magnitude_index(no)
     same_scale = np.repeat(ds == 0, 32, axis=1)
@@ -73,7 +81,8 @@ def gpu_quant_acts(D, x, dt, I):
     M = x.shape[0]
     c = torch.full((M, I // 2), 0xAA, dtype=torch.uint8, device="cuda")
     s = torch.full((M, I // 32), 0xAA, dtype=torch.uint8, device="cuda")
-    paro.paro_mxfp4_quantize_activations(D, x_to_device(x, dt), c, s)
+    ws = torch.empty(paro.paro_mxfp4_activation_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    paro.paro_mxfp4_quantize_activations(D, x_to_device(x, dt), c, s, ws)
     torch.cuda.synchronize()
     return c, s
 
@@ -93,7 +102,7 @@ def test_activation_quantization_matches_oracle(I, M, dt, G):
     x = synth.make_x(701, 1, M, I, dt)
     say(f"mxfp4 activations I={I} M={M} dt={dt} G={G}")
     c, s = gpu_quant_acts(paro.DeviceLayer(L), x, dt, I)
-    nc, ns = compare_quantized(ref.scale_rotate(L, x, dt), c.cpu().numpy(), s.cpu().numpy())
+    nc, ns = compare_quantized(ref.scale_rotate(L, x, dt), c.cpu().numpy(), s.cpu().numpy(), TIE_ACT)
     say(f"  codes at boundaries that differ: {nc}, scales at powers of two that differ: {ns}")
 
 

@@ -240,7 +240,7 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
 
 
 MOE_METRIC = "ParoQuant MoE projection (shared rotation, stacked experts): TFLOP/s, % of MFMA roofline"
-KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp")
+KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp", "mx.hpp")
 
 
 def bench_moe(args, paro, synth, np, torch, dev):
@@ -304,7 +304,8 @@ def bench_moe(args, paro, synth, np, torch, dev):
                    "top_k": spec["top_k"], "group_size": args.group, "krot": host.krot, "weight_sets": nsets,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(value, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(value / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(value / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(f"moe-{wl}{gsuffix(args)}", kernel_source_hash("moe")),
                      "kernel": "rot_build + rot_apply + prefill_gemm_kernel<MoE> (one entry point)",
                      "avg_launch_us": round(us, 3)},
         "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("moe"),
@@ -314,7 +315,7 @@ def bench_moe(args, paro, synth, np, torch, dev):
 
 MX_METRIC = "ParoQuant W4A4 MXFP4 linear (rotation, activation quantization, FP4 GEMM): TFLOP/s, % of FP4 MFMA roofline"
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 / fp6 MFMA, published
-KERNEL_FILES["mxfp4"] = ("mxfp4.hip", "common.hpp")
+KERNEL_FILES["mxfp4"] = ("mxfp4.hip", "common.hpp", "mx.hpp")
 
 
 def bench_mxfp4(args, paro, synth, np, torch, dev):
@@ -393,7 +394,9 @@ def bench_mxfp4(args, paro, synth, np, torch, dev):
         "config": {"workload": f"{spec['name']}-mxfp4{gsuffix(args)}", "tokens": M, "layer": [lname, I, O],
                    "group_size": args.group, "krot": host.krot, "weight_sets": nsets, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / FP4_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(f"mxfp4-{args.workload}{gsuffix(args)}", kernel_source_hash("mxfp4"))
+                     if g_us is not None else None,
                      "kernel": "mx_gemm_kernel" if g_us is not None else "paro_mxfp4_linear (whole entry point)",
                      "avg_launch_us": round(k_us, 3)},
         "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("mxfp4"),

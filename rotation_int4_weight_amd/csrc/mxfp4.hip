@@ -95,17 +95,17 @@ __device__ __forceinline__ void mfma_fp4(const u32x4 &a, const u32x4 &b, uint32_
 }
 
 // y[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]).  A workgroup of 8 waves takes
-// a 128 x 256 tile (waves 2 x 4, 64 x 64 each: 4 x 4 MFMA tiles) over k steps
-// of 128.  Each step's A and W code panels (128 and 256 rows x 64 bytes) and
-// their scale dwords go through LDS once per workgroup (rows padded to 80
-// bytes so the 16-byte fragment reads of 16 rows spread over the banks),
-// double-buffered: the next step's global loads are in flight while this
-// step computes, and one barrier per step separates the buffers.
-// Workgroups run M-fastest in XCD-local order, so the M tiles that share a
-// weight panel meet in one L2.
-constexpr int kMxBM = 128, kMxBN = 256, kMxRow = 80;  // LDS row pitch (bytes)
+// a 128 x 256 tile (waves 2 x 4, 64 x 64 each: 4 x 4 MFMA tiles) over stages
+// of 256 k (two 128-wide MFMA steps).  Each stage's A and W code panels (128
+// and 256 rows x 128 bytes: whole cache lines) and their two scale dwords per
+// row go through LDS once per workgroup (rows padded to 144 bytes so the
+// 16-byte fragment reads of 8 rows hit distinct banks), double-buffered, with
+// the global loads of stage s + 2 requested while stage s computes and one
+// barrier per stage.  Workgroups run M-fastest in XCD-local order, so the M
+// tiles that share a weight panel meet in one L2.
+constexpr int kMxBM = 128, kMxBN = 256, kMxRow = 144;  // LDS row pitch (bytes): 128 code bytes + pad
 constexpr int kMxA = kMxBM * kMxRow, kMxW = kMxBN * kMxRow;
-constexpr int kMxBuf = kMxA + kMxW + (kMxBM + kMxBN) * 4;  // codes + scale dwords of one step
+constexpr int kMxBuf = kMxA + kMxW + (kMxBM + kMxBN) * 8;  // codes + two scale dwords per row
 
 template <int ODT>
 __global__ void __launch_bounds__(512)
@@ -121,36 +121,59 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
   const int wm = wave >> 2, wn = wave & 3;  // wave's 64 x 64 sub-tile
   const int fr = lane & 15, q = lane >> 4;
   const int64_t kb = K / 2, ks = K / 32;
+  const int64_t ksteps = K / 128, nstages = (ksteps + 1) / 2;
   const __amdgpu_buffer_rsrc_t ra = raw_rsrc(ac, (uint32_t)(M * kb));
   const __amdgpu_buffer_rsrc_t rw = raw_rsrc(wc, (uint32_t)(N * kb));
   const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(as, (uint32_t)(M * ks));
   const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(ws, (uint32_t)(N * ks));
 
-  // global -> register staging of one step: A chunks c = tid (row c/4, part
-  // c%4), W chunks tid and tid + 512, one scale dword (A rows for tid < 128,
-  // W rows for 128 <= tid < 384)
-  const int a_row = tid >> 2, part = tid & 3;
-  const uint32_t a_goff = (uint32_t)((mt0 + a_row) * kb + 16 * part);
-  const uint32_t w_goff0 = (uint32_t)((nt0 + a_row) * kb + 16 * part);
-  const uint32_t w_goff1 = (uint32_t)((nt0 + 128 + a_row) * kb + 16 * part);
+  // global -> register staging of one stage: 16-byte chunk c = tid + 512u is
+  // row c/8, part c%8 of the A panel (u < 2) and of the W panel (u < 4); row
+  // tid (< 384) of the scales: 8 bytes, the stage's eight 32-blocks.  Parts
+  // past the end of K (an odd last step) are re-read in bounds and unused.
+  uint32_t a_goff[2], w_goff[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    a_goff[u] = (uint32_t)((mt0 + ((tid + 512 * u) >> 3)) * kb + 16 * ((tid + 512 * u) & 7));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    w_goff[u] = (uint32_t)((nt0 + ((tid + 512 * u) >> 3)) * kb + 16 * ((tid + 512 * u) & 7));
   const bool sc_a = tid < kMxBM, sc_w = tid >= kMxBM && tid < kMxBM + kMxBN;
   const uint32_t s_goff = sc_a ? (uint32_t)((mt0 + tid) * ks) : (uint32_t)((nt0 + (tid - kMxBM)) * ks);
-  u32x4 ga, gw0, gw1;
-  uint32_t gs;
-  auto gload = [&](int64_t step) {
-    const uint32_t cb = (uint32_t)(step * 64), sb = (uint32_t)(step * 4);
-    ga = __builtin_amdgcn_raw_buffer_load_b128(ra, a_goff + cb, 0, 0);
-    gw0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_goff0 + cb, 0, 0);
-    gw1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_goff1 + cb, 0, 0);
-    gs = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb, 0, 0)
-              : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb, 0, 0) : 0u);
+  u32x4 ga[2][2], gw[2][4];
+  uint32_t gs[2][2];
+  auto gload = [&](int r, int64_t st) {
+    // the last stage of an odd step count holds one step: its second half is
+    // clamped onto the first (in bounds, never used)
+    const int64_t hi_ok = 2 * st + 1 < ksteps;
+    const uint32_t cb = (uint32_t)(st * 128);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t part = (uint32_t)((tid + 512 * u) & 7);
+      const uint32_t o = a_goff[u] + cb - ((part >= 4 && !hi_ok) ? 64u : 0u);
+      ga[r][u] = __builtin_amdgcn_raw_buffer_load_b128(ra, o, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t part = (uint32_t)((tid + 512 * u) & 7);
+      const uint32_t o = w_goff[u] + cb - ((part >= 4 && !hi_ok) ? 64u : 0u);
+      gw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0);
+    }
+    const uint32_t sb = (uint32_t)(st * 8), sb1 = hi_ok ? sb + 4 : sb;
+    gs[r][0] = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb, 0, 0)
+                    : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb, 0, 0) : 0u);
+    gs[r][1] = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb1, 0, 0)
+                    : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb1, 0, 0) : 0u);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int r, int buf) {
     uint8_t *b = lds[buf];
-    *reinterpret_cast<u32x4 *>(b + a_row * kMxRow + 16 * part) = ga;
-    *reinterpret_cast<u32x4 *>(b + kMxA + a_row * kMxRow + 16 * part) = gw0;
-    *reinterpret_cast<u32x4 *>(b + kMxA + (128 + a_row) * kMxRow + 16 * part) = gw1;
-    if (tid < kMxBM + kMxBN) *reinterpret_cast<uint32_t *>(b + kMxA + kMxW + 4 * tid) = gs;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<u32x4 *>(b + ((tid + 512 * u) >> 3) * kMxRow + 16 * ((tid + 512 * u) & 7)) = ga[r][u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<u32x4 *>(b + kMxA + ((tid + 512 * u) >> 3) * kMxRow + 16 * ((tid + 512 * u) & 7)) = gw[r][u];
+    if (tid < kMxBM + kMxBN) *reinterpret_cast<u32x2 *>(b + kMxA + kMxW + 8 * tid) = u32x2{gs[r][0], gs[r][1]};
   };
 
   f32x4 acc[4][4];
@@ -163,17 +186,17 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
     }
   asm volatile("s_nop 7");
 
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf, int h) {  // the 128-wide step h (0, 1) of the stage in buffer buf
     const uint8_t *b = lds[buf];
     u32x4 fa[4], fw[4];
     uint32_t sca[4], scw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ar = wm * 64 + 16 * i + fr, wr = wn * 64 + 16 * i + fr;
-      fa[i] = *reinterpret_cast<const u32x4 *>(b + ar * kMxRow + 16 * q);
-      fw[i] = *reinterpret_cast<const u32x4 *>(b + kMxA + wr * kMxRow + 16 * q);
-      sca[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 4 * ar) >> (8 * q)) & 0xffu;
-      scw[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 4 * (kMxBM + wr)) >> (8 * q)) & 0xffu;
+      fa[i] = *reinterpret_cast<const u32x4 *>(b + ar * kMxRow + 64 * h + 16 * q);
+      fw[i] = *reinterpret_cast<const u32x4 *>(b + kMxA + wr * kMxRow + 64 * h + 16 * q);
+      sca[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 8 * ar + 4 * h) >> (8 * q)) & 0xffu;
+      scw[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 8 * (kMxBM + wr) + 4 * h) >> (8 * q)) & 0xffu;
     }
     // the scale operands come from VALU: padding before the asm MFMAs read them
     __builtin_amdgcn_sched_barrier(0);
@@ -186,19 +209,25 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int64_t nsteps = K / 128;
-  gload(0);
-  sstore(0);
+  // stage s: LDS buffer s & 1 holds it, register set (s + 1) & 1 holds stage
+  // s + 1, set s & 1 is free (its stage went to LDS one stage ago)
+  gload(0, 0);
+  if (nstages > 1) gload(1, 1);
+  sstore(0, 0);
   __syncthreads();
+  auto iter = [&](int64_t st, int r) {  // r == st & 1, a compile-time constant
+    if (st + 2 < nstages) gload(r, st + 2);
+    compute(r, 0);
+    if (2 * st + 1 < ksteps) compute(r, 1);
+    if (st + 1 < nstages) sstore(r ^ 1, r ^ 1);  // buffer r ^ 1 was last read in stage st - 1
+    __syncthreads();
+  };
   int64_t s = 0;
   do {
-    const int buf = (int)(s & 1);
-    if (s + 1 < nsteps) gload(s + 1);
-    compute(buf);
-    if (s + 1 < nsteps) sstore(buf ^ 1);  // buf ^ 1 was last read in step s - 1
-    __syncthreads();
-    ++s;
-  } while (s < nsteps);
+    iter(s, 0);
+    if (s + 1 < nstages) iter(s + 1, 1);
+    s += 2;
+  } while (s < nstages);
   mfma_drain();
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -232,7 +232,7 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
                      "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(f"rotate_backward-{args.workload}{gsuffix(args)}",
                                              kernel_source_hash("rotate_backward")),
-                     "kernel": "bwd_gram + bwd_walk + bwd_dx + bwd_theta_reduce kernels (one entry point)",
+                     "kernel": "bwd_rrow + bwd_gram_dx + bwd_walk + bwd_theta_reduce kernels (one entry point)",
                      "avg_launch_us": round(us, 3)},
         "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("rotate_backward"),
     }

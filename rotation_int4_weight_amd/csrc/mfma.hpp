@@ -24,6 +24,28 @@ __device__ __forceinline__ void mfma_acc(const u32x4 &a, const u32x4 &b, f32x4 &
   else
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+// mfma_acc for operands that a VALU instruction may have written just before
+// the MFMA, e.g. a copy out of an AGPR that the register allocator inserts
+// under pressure: the hardware needs wait states between a VALU write of a
+// VGPR and an MFMA reading it, and the compiler inserts none before asm.
+template <int DT>
+__device__ __forceinline__ void mfma_acc_after_valu(const u32x4 &a, const u32x4 &b, f32x4 &c) {
+  if constexpr (DT == kF16)
+    asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// D = A * B + c on one 16x16 tile through the builtin (the compiler tracks
+// its latency); for short-lived products whose result a VALU reads next.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, f32x4 c) {
+  if constexpr (DT == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
 // 64 wait states: more than any MFMA needs before a VALU reads its result.
 __device__ __forceinline__ void mfma_drain() {
   __builtin_amdgcn_sched_barrier(0);

@@ -13,34 +13,32 @@
 // Also dL/dcs_j = (R . C)[j][j] and dL/dx = g . R'^T with R' = diag(cs) . R.
 //
 // So every token enters only two contractions on the matrix cores, C = g^T x
-// (bwd_gram_kernel) and g . R'^T (bwd_dx_kernel), and the stage walk runs on
-// the 128 rows of C per group instead of on every token (bwd_walk_kernel).
+// and g . R'^T, both taken in one pass over the tokens (bwd_gram_dx_kernel:
+// x and g are read once, dL/dx written once), and the stage walk runs on the
+// 128 rows of C per group instead of on every token (bwd_walk_kernel).  R'
+// depends only on the angles and scales, so it is formed first
+// (bwd_rrow_kernel: row i of R is e_i pushed forward through the stages).
 // The walk is row-parallel: with u_i = column i of C,
 //   (R . C)[:, i]   = R u_i          (stages applied to u_i as a column,
 //                                     last stage first: inverse rotations)
 //   row i of N_0^T  = v_i = cs_i (R u_i)
 //   row i of F_t    = f_i = e_i . R_1 ... R_t      (forward rotations)
 //   dL/dtheta_t(p)  = sum over i of f_i[b] (v_i R_1..R_t)[a] - f_i[a] (v_i R_1..R_t)[b]
-// (from N_t^T = F_t^T N_0^T F_t), and after the last stage f_i is row i of R,
-// which gives R' for the dL/dx product.  Sums over tokens and over rows are
-// taken in a fixed order, so results are identical from call to call.
+// (from N_t^T = F_t^T N_0^T F_t).  Sums over tokens and over rows are taken
+// in a fixed order, so results are identical from call to call.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
 
 namespace paro {
 
-constexpr int kBwdTok = 64;                  // token granule of the Gram splits
-// tokens per LDS tile of the Gram kernel (128-token tiles measured slower:
-// fewer splits in flight, the same transposing LDS writes per token)
-__host__ __device__ constexpr int gram_tile(int) { return kBwdTok; }
+constexpr int kFT = 64;                      // tokens per tile of the fused kernel (the split granule)
 constexpr int kWalkRows = 8;                 // rows of C per wave in the walk
 constexpr int kWalkParts = kG / kWalkRows;   // dtheta partial rows per group
-constexpr int kBwdRS = kG + 4;               // walk LDS row stride (floats)
-constexpr int kDxHS = kG + 8;                // dx LDS row stride of H / L (halves)
-constexpr int kDxRows = 512;                 // tokens per dx workgroup
+constexpr int kBwdRS = kG + 4;               // walk / build LDS row stride (floats)
+constexpr int kRowsPerBuild = 16;            // rows of R' per one-wave build workgroup
 constexpr int64_t kBwdMat = 2 * kG * kG;     // H and L of one group (halves)
-constexpr int kGramTarget = 512;             // Gram workgroups to aim for
+constexpr int kGramResident = 256;           // fused workgroups that fit the chip at once
 
 // Matrix-core dtype of each product: fp16 when both operands are fp16
 // (exact), otherwise bf16 with fp16 / fp32 operands split into a bf16 high
@@ -48,184 +46,356 @@ constexpr int kGramTarget = 512;             // Gram workgroups to aim for
 __host__ __device__ constexpr int gram_mdt(int xdt, int gdt) { return (xdt == kF16 && gdt == kF16) ? kF16 : kBF16; }
 __host__ __device__ constexpr int dx_mdt(int gdt) { return gdt == kF16 ? kF16 : kBF16; }
 
-__device__ __forceinline__ int mfma_row_of_channel(int j) {
-  // inverse of the dx output order: MFMA row 32b + 16h + 4q + r holds channel 32b + 8q + 4h + r
-  return (j & ~31) | (((j >> 2) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3);
+// MFMA row 32b + 16h + 4q + r (b < 4, h < 2, q < 4, r < 4) of R' holds
+// channel 32b + 8q + 4h + r: the dL/dx accumulators of row tiles 2b and 2b+1
+// then give each lane 8 consecutive channels of one token.
+__device__ __forceinline__ int channel_of_row(int r) {
+  return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
 // ---------------------------------------------------------------------------
-// Gram kernel: C^T[i][k] = sum over tokens of x[m][i] * g[m][k], one 128 x 128
-// fp32 partial per (group, token split).  Tiles of 64 tokens are loaded with
-// coalesced 16-byte reads and written to LDS transposed (channel-major, eight
-// tokens per 16-byte block, blocks XOR-swizzled by the channel's 8-block), so
-// that each MFMA fragment (one channel, eight consecutive tokens) is one
-// 16-byte LDS read.  Wave w owns C^T rows 32w..32w+31 (two 16-row tiles) and
-// all 128 columns: 16 accumulator tiles.
+// R' build: one wave forms rows r0 = 16 * blockIdx.y .. r0+15 (MFMA order) of
+// R' = diag(cs) . R for group blockIdx.x.  Row i of R is the unit row e_i
+// through the forward stages (the same staged fp32 code as the forward
+// rotation); times cs_i it is stored as H + L in dtype MDT, H = rne(R'),
+// L = rne(R' - H).
+// hl: [group][2 (H, L)][128 (MFMA row)][128 (channel j)], R'[i][j].
 // ---------------------------------------------------------------------------
-template <int T>
-__device__ __forceinline__ int gram_off(int ch, int tok) {
-  return ch * T + ((((tok >> 3) ^ (ch >> 3)) & (T / 8 - 1)) << 3) + (tok & 7);
+template <int MDT>
+__global__ void __launch_bounds__(64)
+bwd_rrow_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__restrict__ theta,
+                const float *__restrict__ cscale, int krot, int gmask, uint16_t *__restrict__ hl) {
+  constexpr int RW = kRowsPerBuild;
+  __shared__ float xs[RW * kBwdRS];
+  const int lane = lane_id();
+  const int64_t g = blockIdx.x;
+  const int r0 = blockIdx.y * RW;
+  const int16_t *pairs_g = pairs + g * kG;
+  const float *theta_g = theta + g * kPairs;
+  RotParams rp;
+  rp.load(pairs_g, I, theta_g, I / 2, krot, lane, gmask);
+  float csr[RW];
+#pragma unroll
+  for (int m = 0; m < RW; ++m) {
+    const int i = channel_of_row(r0 + m);
+    csr[m] = cscale[g * kG + i];
+    xs[m * kBwdRS + 2 * lane] = 2 * lane == i ? 1.0f : 0.0f;
+    xs[m * kBwdRS + 2 * lane + 1] = 2 * lane + 1 == i ? 1.0f : 0.0f;
+  }
+  wave_lds_sync();
+  rotate_rows_lds<RW>(xs, kBwdRS, rp, pairs_g, I, theta_g, I / 2, krot, lane, gmask);
+  uint32_t *hg = reinterpret_cast<uint32_t *>(hl + g * kBwdMat) + lane;
+#pragma unroll
+  for (int m = 0; m < RW; ++m) {
+    const float v0 = xs[m * kBwdRS + 2 * lane] * csr[m], v1 = xs[m * kBwdRS + 2 * lane + 1] * csr[m];
+    const uint32_t hb = pack2<MDT>(v0, v1);
+    const float e0 = v0 - act_to_f32<MDT>(hb & 0xffffu), e1 = v1 - act_to_f32<MDT>(hb >> 16);  // exact
+    hg[(r0 + m) * (kG / 2)] = hb;
+    hg[(kG + r0 + m) * (kG / 2)] = pack2<MDT>(e0, e1);
+  }
 }
+
+// ---------------------------------------------------------------------------
+// Fused Gram + dL/dx kernel: one workgroup of 8 waves per (group, token
+// split); tiles of 64 tokens of x and g are read once (coalesced 16-byte
+// loads), two tiles ahead of the products (two register sets, the tile loop
+// unrolled by two so that each set keeps its registers; one tile ahead for
+// fp32 g, whose fragments take twice the registers).
+//
+//  * Loads: wave w takes tokens 32s .. 32s+31 (s = w / 4) and channels
+//    32c .. 32c+31 (c = w % 4) of the tile, as MFMA A fragments in natural
+//    order (lane l: token l%16 of a 16-token block, 8 consecutive channels).
+//  * Transpose on the matrix cores: an MFMA of such a fragment with a one-hot
+//    B (B[k][n] = 1 where k = 16h + n) returns, exactly in fp32, lane l's
+//    channel 16h + l%16 at tokens 4(l/16) .. +3 of the block.  Two blocks'
+//    results packed together are one 16-byte, channel-major LDS store: eight
+//    tokens of one channel, the k-slots of a Gram fragment.  x and g go
+//    through the same token-to-slot map, so their products pair up right.
+//    (A non-finite input value spreads through the zeros of the one-hot
+//    operand to its 16-channel block of that token.)
+//  * Gram: wave w owns the 32 x 64 block of C^T at rows 32(w/2) (x channels)
+//    and columns 64(w%2) (g channels): 8 accumulator tiles over the split.
+//  * dL/dx = g . R'^T as its transpose R' . g^T: wave w holds rows 32(w%4) ..
+//    +31 of R' (H and L, MFMA order) in registers as A fragments and takes
+//    tokens 32(w/4) .. +31; g in natural order from LDS gives the B
+//    fragments.  Lane l's accumulators are then 8 consecutive channels of one
+//    token: a 16-byte (fp32: 32-byte) store.
+//  LDS slots are XOR-swizzled so that every 16-lane quarter of a 16-byte LDS
+//  access covers all 64 banks.  Under register pressure (fp32 g) the
+//  allocator keeps some R' fragments in AGPRs and copies them out right
+//  before use, so every product here waits out a VALU write first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split_to_bf16(const float *v, u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = pack2<kBF16>(v[2 * e], v[2 * e + 1]);
+    hi[e] = h;
+    lo[e] = pack2<kBF16>(v[2 * e] - bf16_bits_to_f32(h & 0xffffu), v[2 * e + 1] - bf16_bits_to_f32(h >> 16));
+  }
+}
+
+template <int N>
+struct Const {
+  static constexpr int value = N;
+};
 
 template <int XDT, int GDT>
-__global__ void __launch_bounds__(256, 2)
-bwd_gram_kernel(const void *__restrict__ x, const void *__restrict__ gin, int64_t tokens, int64_t I,
-                int64_t chunk, float *__restrict__ cpart) {
-  constexpr int MD = gram_mdt(XDT, GDT);
-  constexpr int XP = (XDT == kF16 && MD == kBF16) ? 2 : 1;  // parts of x
-  constexpr int GP = (GDT == kF32 || (GDT == kF16 && MD == kBF16)) ? 2 : 1;
-  constexpr int T = gram_tile(GDT);
-  constexpr int XCH = T / 16;                          // 16-byte chunks of x per thread and tile
-  constexpr int GCH = GDT == kF32 ? T / 8 : T / 16;    // and of g
-  __shared__ __attribute__((aligned(16))) uint16_t xt[XP][kG * T];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[GP][kG * T];
+__global__ void __launch_bounds__(512)
+bwd_gram_dx_kernel(const void *__restrict__ x, const void *__restrict__ gin, void *__restrict__ gx, int gx_f32,
+                   int64_t tokens, int64_t I, int64_t chunk, const uint16_t *__restrict__ hl,
+                   float *__restrict__ cpart) {
+  constexpr int MG = gram_mdt(XDT, GDT), MX = dx_mdt(GDT);
+  constexpr bool F32G = GDT == kF32;
+  constexpr int XP = XDT == MG ? 1 : 2;  // parts of x in MG
+  constexpr int GP = F32G ? 2 : 1;       // parts of g (in MG = MX for fp32 g)
+  constexpr int gsz = F32G ? 4 : 2;
+  constexpr int PF = F32G ? 1 : 2;  // tiles in flight ahead of the products (register sets)
+  __shared__ __attribute__((aligned(16))) uint16_t xt[XP][kG * kFT];  // [channel][8 slots of 8 tokens]
+  __shared__ __attribute__((aligned(16))) uint16_t gt[GP][kG * kFT];
+  __shared__ __attribute__((aligned(16))) uint16_t gn[GP][kFT * kG];  // [token][16 slots of 8 channels]
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int fr = lane & 15, q = lane >> 4;
   const int64_t g = blockIdx.x, groups = I / kG;
   const int64_t m_begin = (int64_t)blockIdx.y * chunk;
   const int64_t m_end = tokens < m_begin + chunk ? tokens : m_begin + chunk;
-  const int gsz = GDT == kF32 ? 4 : 2;
+  const int ls = wave >> 2, lc = wave & 3;   // load role
+  const int gi = wave >> 1, gk = wave & 1;   // Gram role
+  const int dr = wave & 3, dt = wave >> 2;   // dL/dx role
 
-  u32x4 xr[XCH], gr[GCH];
-  auto load_tile = [&](int64_t m0) {
-    const int64_t rows = m_end - m0 < T ? m_end - m0 : T;  // > 0
+  // rows 32 dr + 16it + fr of R' (H, L): A fragments of the dL/dx product
+  u32x4 ar[2][4][2];
+  {
+    const uint16_t *hg = hl + g * kBwdMat;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          ar[it][ks][p] =
+              *reinterpret_cast<const u32x4 *>(hg + ((int64_t)p * kG + 32 * dr + 16 * it + fr) * kG + 32 * ks + 8 * q);
+  }
+  // one-hot B fragments: element e of lane l is 1 where 8(l/16) + e = 16h + l%16
+  constexpr uint32_t kOne = MG == kF16 ? 0x3c00u : 0x3f80u;
+  u32x4 oh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 16 * h + fr - 8 * q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) oh[h][k] = (e >> 1) == k ? kOne << (16 * (e & 1)) : 0u;
+  }
+
+  u32x4 xr[PF][2], gr[PF][2][GP];  // [register set][16-token block][...]
+  auto load_tile = [&](auto set, int64_t m0) {
+    constexpr int S = decltype(set)::value;
+    const int64_t rows = m_end - m0 < kFT ? m_end - m0 : kFT;  // > 0; later rows read as zeros
     const __amdgpu_buffer_rsrc_t rx =
         raw_rsrc(reinterpret_cast<const uint16_t *>(x) + m0 * I + g * kG, (uint32_t)(rows * I * 2));
     const __amdgpu_buffer_rsrc_t rg =
         raw_rsrc(reinterpret_cast<const char *>(gin) + (m0 * I + g * kG) * gsz, (uint32_t)(rows * I * gsz));
 #pragma unroll
-    for (int u = 0; u < XCH; ++u) {
-      const int c = tid + 256 * u, row = c >> 4, cb = c & 15;
-      xr[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((row * I + cb * 8) * 2), 0, 0);
-    }
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t e = (uint32_t)((32 * ls + 16 * tt + fr) * I + 32 * lc + 8 * q);
+      xr[S][tt] = __builtin_amdgcn_raw_buffer_load_b128(rx, e * 2, 0, 0);
 #pragma unroll
-    for (int u = 0; u < GCH; ++u) {
-      const int c = tid + 256 * u;
-      const int row = GDT == kF32 ? c >> 5 : c >> 4, cb = GDT == kF32 ? c & 31 : c & 15;
-      gr[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)((row * I) * gsz + cb * 16), 0, 0);
+      for (int h = 0; h < GP; ++h) gr[S][tt][h] = __builtin_amdgcn_raw_buffer_load_b128(rg, e * gsz + 16 * h, 0, 0);
     }
   };
 
-  auto put = [&](uint16_t *arr, int ch, int tok, uint32_t v) { arr[gram_off<T>(ch, tok)] = (uint16_t)v; };
-  auto store_tile = [&]() {
+  // parts, the natural copy of g, the transposes
+  auto store_tile = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+    u32x4 xp[2][XP], gp[2][GP];
 #pragma unroll
-    for (int u = 0; u < XCH; ++u) {
-      const int c = tid + 256 * u, tok = c >> 4, cb = c & 15;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (xr[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        if constexpr (XP == 1) {
-          put(xt[0], 8 * cb + e, tok, h);
-        } else {  // fp16 -> bf16 high part + exact bf16 remainder
-          const float v = f16_bits_to_f32(h);
-          const uint32_t hi = f32_to_bf16_bits(v);
-          put(xt[0], 8 * cb + e, tok, hi);
-          put(xt[XP - 1], 8 * cb + e, tok, f32_to_bf16_bits(v - bf16_bits_to_f32(hi)));
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < GCH; ++u) {
-      const int c = tid + 256 * u;
-      if constexpr (GDT == kF32) {
-        const int tok = c >> 5, cb = c & 31;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = __uint_as_float(gr[u][e]);
-          const uint32_t hi = f32_to_bf16_bits(v);
-          put(gt[0], 4 * cb + e, tok, hi);
-          put(gt[GP - 1], 4 * cb + e, tok, f32_to_bf16_bits(v - bf16_bits_to_f32(hi)));
-        }
+    for (int tt = 0; tt < 2; ++tt) {
+      if constexpr (XP == 1) {
+        xp[tt][0] = xr[S][tt];
       } else {
-        const int tok = c >> 4, cb = c & 15;
+        float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t h = (gr[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          if constexpr (GP == 1) {
-            put(gt[0], 8 * cb + e, tok, h);
-          } else {
-            const float v = f16_bits_to_f32(h);
-            const uint32_t hi = f32_to_bf16_bits(v);
-            put(gt[0], 8 * cb + e, tok, hi);
-            put(gt[GP - 1], 8 * cb + e, tok, f32_to_bf16_bits(v - bf16_bits_to_f32(hi)));
-          }
-        }
+        for (int e = 0; e < 8; ++e) v[e] = f16_bits_to_f32((xr[S][tt][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        split_to_bf16(v, xp[tt][0], xp[tt][1]);
+      }
+      if constexpr (F32G) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(gr[S][tt][e >> 2][e & 3]);
+        split_to_bf16(v, gp[tt][0], gp[tt][1]);
+      } else {
+        gp[tt][0] = gr[S][tt][0];
+      }
+      const int tok = 32 * ls + 16 * tt + fr;
+#pragma unroll
+      for (int p = 0; p < GP; ++p)
+        *reinterpret_cast<u32x4 *>(gn[p] + tok * kG + 8 * ((4 * lc + q) ^ fr)) = gp[tt][p];
+    }
+    const int slot = (4 * ls + q) ^ (fr >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = 32 * lc + 16 * h + fr;
+      const f32x4 z{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < XP; ++p) {
+        const f32x4 d0 = mfma16x16x32<MG>(xp[0][p], oh[h], z), d1 = mfma16x16x32<MG>(xp[1][p], oh[h], z);
+        *reinterpret_cast<u32x4 *>(xt[p] + ch * kFT + 8 * slot) =
+            u32x4{pack2<MG>(d0[0], d0[1]), pack2<MG>(d0[2], d0[3]), pack2<MG>(d1[0], d1[1]), pack2<MG>(d1[2], d1[3])};
+      }
+#pragma unroll
+      for (int p = 0; p < GP; ++p) {
+        const f32x4 d0 = mfma16x16x32<MG>(gp[0][p], oh[h], z), d1 = mfma16x16x32<MG>(gp[1][p], oh[h], z);
+        *reinterpret_cast<u32x4 *>(gt[p] + ch * kFT + 8 * slot) =
+            u32x4{pack2<MG>(d0[0], d0[1]), pack2<MG>(d0[2], d0[3]), pack2<MG>(d1[0], d1[1]), pack2<MG>(d1[2], d1[3])};
       }
     }
   };
 
-  f32x4 acc[2][8];
+  f32x4 acc[2][4];
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
+    for (int kt = 0; kt < 4; ++kt) {
       acc[it][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc_fence(acc[it][kt]);
     }
   asm volatile("s_nop 7");
 
-  const int fr = lane & 15, fj = lane >> 4;
-  auto frag = [&](const uint16_t *arr, int ch, int j) {
-    return *reinterpret_cast<const u32x4 *>(arr + ch * T + (((j ^ (ch >> 3)) & (T / 8 - 1)) << 3));
+  auto read_n = [&](int tt, int ks, int p) {
+    const int tok = 16 * tt + fr;
+    return *reinterpret_cast<const u32x4 *>(gn[p] + tok * kG + 8 * ((4 * ks + q) ^ fr));
+  };
+  auto read_t = [&](const uint16_t *arr, int ch, int sp) {
+    return *reinterpret_cast<const u32x4 *>(arr + ch * kFT + 8 * ((4 * sp + q) ^ (fr >> 1)));
   };
 
-  if (m_begin < m_end) load_tile(m_begin);
-  for (int64_t m0 = m_begin; m0 < m_end; m0 += T) {
-    __syncthreads();  // the previous tile's fragments are read
+  // one tile: transposes into LDS, the next-but-one tile's loads, products, dL/dx stores
+  auto tile = [&](auto set, int64_t m0) {
+    __syncthreads();          // the previous tile's fragments are read
     asm volatile("s_nop 7");  // before VALU reuses registers the last asm MFMAs read
     __builtin_amdgcn_sched_barrier(0);
-    store_tile();
-    if (m0 + T < m_end) load_tile(m0 + T);  // in flight during the products below
+    store_tile(set);
+    if (m0 + PF * kFT < m_end) load_tile(set, m0 + PF * kFT);  // in flight for PF tiles' products
     __syncthreads();
+
+    // dL/dx^T tiles (it: 16 rows of R', t2: 16 tokens of 32 dt ..), k over the 128 channels
+    f32x4 acc2[2][2];
 #pragma unroll
-    for (int ks = 0; ks < T / 32; ++ks) {
-      const int j = 4 * ks + fj;
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        acc2[it][t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_fence(acc2[it][t2]);
+      }
+    asm volatile("s_nop 7");
+    // B fragment ring (step = 4 t2 + ks), filled two steps ahead: a load never
+    // targets registers that the asm MFMAs just issued may still be reading
+    constexpr int NB = 3;
+    u32x4 bn[NB][GP];
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+#pragma unroll
+      for (int p = 0; p < GP; ++p) bn[b][p] = read_n(2 * dt, b, p);
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+      const int nx = step + NB - 1;
+      if (nx < 8) {
+#pragma unroll
+        for (int p = 0; p < GP; ++p) bn[nx % NB][p] = read_n(2 * dt + (nx >> 2), nx & 3, p);
+      }
+      const int t2 = step >> 2, ks = step & 3;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        mfma_acc_after_valu<MX>(ar[it][ks][0], bn[step % NB][0], acc2[it][t2]);
+        mfma_acc_after_valu<MX>(ar[it][ks][1], bn[step % NB][0], acc2[it][t2]);
+        if constexpr (GP == 2) mfma_acc_after_valu<MX>(ar[it][ks][0], bn[step % NB][1], acc2[it][t2]);
+      }
+    }
+
+    // Gram: k-step sp = tokens 32sp .. 32sp+31 of the tile
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
       u32x4 a[2][XP];
 #pragma unroll
       for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int p = 0; p < XP; ++p) a[it][p] = frag(xt[p], 32 * wave + 16 * it + fr, j);
+        for (int p = 0; p < XP; ++p) a[it][p] = read_t(xt[p], 32 * gi + 16 * it + fr, sp);
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
+      for (int kt = 0; kt < 4; ++kt) {
         u32x4 b[GP];
 #pragma unroll
-        for (int p = 0; p < GP; ++p) b[p] = frag(gt[p], 16 * kt + fr, j);
+        for (int p = 0; p < GP; ++p) b[p] = read_t(gt[p], 64 * gk + 16 * kt + fr, sp);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
           for (int xp = 0; xp < XP; ++xp)
 #pragma unroll
-            for (int gp = 0; gp < GP; ++gp) mfma_acc<MD>(a[it][xp], b[gp], acc[it][kt]);
+            for (int gp = 0; gp < GP; ++gp) mfma_acc_after_valu<MG>(a[it][xp], b[gp], acc[it][kt]);
       }
     }
+
+    mfma_drain();
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) acc_fence(acc2[it][t2]);
+    // lane l of tile (it, t2): token 32 dt + 16 t2 + l%16, channels 32 dr + 8(l/16) + 4it + r
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int64_t tok = m0 + 32 * dt + 16 * t2 + fr;
+      if (tok < m_end) {
+        const int64_t off = tok * I + g * kG + 32 * dr + 8 * q;
+        const f32x4 lo4 = acc2[0][t2], hi4 = acc2[1][t2];
+        if (gx_f32) {
+          float *o = reinterpret_cast<float *>(gx) + off;
+          __builtin_nontemporal_store(lo4, reinterpret_cast<f32x4 *>(o));
+          __builtin_nontemporal_store(hi4, reinterpret_cast<f32x4 *>(o + 4));
+        } else {
+          const u32x4 v{pack2<XDT>(lo4[0], lo4[1]), pack2<XDT>(lo4[2], lo4[3]), pack2<XDT>(hi4[0], hi4[1]),
+                        pack2<XDT>(hi4[2], hi4[3])};
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(gx) + off));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (m_begin < m_end) load_tile(Const<0>{}, m_begin);
+  if constexpr (PF == 2) {
+    if (m_begin + kFT < m_end) load_tile(Const<PF - 1>{}, m_begin + kFT);
+    for (int64_t m0 = m_begin; m0 < m_end; m0 += 2 * kFT) {
+      tile(Const<0>{}, m0);
+      if (m0 + kFT >= m_end) break;
+      tile(Const<PF - 1>{}, m0 + kFT);
+    }
+  } else {
+    for (int64_t m0 = m_begin; m0 < m_end; m0 += kFT) tile(Const<0>{}, m0);
   }
   mfma_drain();
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) acc_fence(acc[it][kt]);
+    for (int kt = 0; kt < 4; ++kt) acc_fence(acc[it][kt]);
 
-  // lane l of tile (it, kt): rows 32w + 16it + 4(l/16) + r, column 16kt + l%16
+  // lane l of tile (it, kt): rows 32 gi + 16it + 4(l/16) + r, column 64 gk + 16kt + l%16
   float *out = cpart + ((int64_t)blockIdx.y * groups + g) * (kG * kG);
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(32 * wave + 16 * it + 4 * fj + r) * kG + 16 * kt + fr] = acc[it][kt][r];
+      for (int r = 0; r < 4; ++r)
+        out[(32 * gi + 16 * it + 4 * q + r) * kG + 64 * gk + 16 * kt + fr] = acc[it][kt][r];
 }
 
 // ---------------------------------------------------------------------------
 // Walk kernel: rows i of C^T (columns of C) of one group, 8 per wave, four
 // workgroups per group.  Lane p owns pair p of every stage (as in the forward
-// rotation).  Writes dL/dcs_i, the wave's dtheta partial sums and row i of
-// R' = diag(cs) R as H + L (dtype MDT) at its MFMA row for the dx product.
+// rotation).  Writes dL/dcs_i and the wave's dtheta partial sums.
 // ---------------------------------------------------------------------------
-template <int MDT>
 __global__ void __launch_bounds__(256)
 bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const int16_t *__restrict__ pairs,
                 const float *__restrict__ theta, const float *__restrict__ cscale, int krot, int gmask,
-                float *__restrict__ gcs, float *__restrict__ tpart, uint16_t *__restrict__ hl) {
+                float *__restrict__ gcs, float *__restrict__ tpart) {
   constexpr int RW = kWalkRows;
   __shared__ float lds[4][2][RW * kBwdRS];
   const int lane = lane_id(), wave = wave_id();
@@ -356,168 +526,6 @@ bwd_walk_kernel(const float *__restrict__ cpart, int splits, int64_t I, const in
     prow[(int64_t)t * (I / 2)] = dth;
     wave_lds_sync();
   }
-
-  // f_i is now row i of R: R'[i][:] = cs_i f_i as H + L at MFMA row r(i)
-  uint32_t *hg = reinterpret_cast<uint32_t *>(hl + g * kBwdMat) + lane;
-#pragma unroll
-  for (int m = 0; m < RW; ++m) {
-    const int r = mfma_row_of_channel(i0 + m);
-    const float v0 = fs[m * kBwdRS + 2 * lane] * csr[m], v1 = fs[m * kBwdRS + 2 * lane + 1] * csr[m];
-    const uint32_t hb = pack2<MDT>(v0, v1);
-    const float e0 = v0 - act_to_f32<MDT>(hb & 0xffffu), e1 = v1 - act_to_f32<MDT>(hb >> 16);  // exact
-    hg[r * (kG / 2)] = hb;
-    hg[(kG + r) * (kG / 2)] = pack2<MDT>(e0, e1);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dx kernel: dL/dx = g . R'^T per group on the matrix cores, computed as its
-// transpose R' . g^T with H / L (rows of R' in MFMA order) as the A operand
-// and g's rows as B fragments.  Lane l of row tile t then holds, for its token
-// l%16, the 8 consecutive channels 32b + 8(l/16) .. +7 of each 32-channel
-// block b: one 16-byte (32-byte for fp32) row-major store each.  fp32 g is
-// split into a bf16 high part and remainder: H.hi + H.lo + L.hi.
-// ---------------------------------------------------------------------------
-template <int GDT, int ODT>
-__global__ void __launch_bounds__(256, 2)
-bwd_dx_kernel(const void *__restrict__ gin, void *__restrict__ gx, int64_t tokens, int64_t I,
-              const uint16_t *__restrict__ hl) {
-  constexpr int MD = dx_mdt(GDT);
-  constexpr bool F32G = GDT == kF32;
-  constexpr int TB = F32G ? 2 : 4;  // row tiles per wave and batch
-  constexpr int gsz = F32G ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t hlds[2 * kG * kDxHS];
-  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
-  const int64_t g = blockIdx.x;
-  const int64_t mt_end = (tokens + 15) / 16;
-  const int64_t mt_first = (int64_t)blockIdx.y * (kDxRows / 16);
-  const int64_t mt_last = mt_first + kDxRows / 16 < mt_end ? mt_first + kDxRows / 16 : mt_end;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const uint32_t lane_off = (uint32_t)((fr * I + fk) * gsz);
-
-  // raw g fragments: [tile][k-step][1 or 2 x 16 bytes]
-  constexpr int NPC = F32G ? 2 : 1;
-  u32x4 raw[TB][4][NPC];
-  auto load_g = [&](int64_t mt0, int ks, bool all) {
-    const int64_t row0 = mt0 * 16;
-    const int64_t rows = tokens - row0 < 16 * TB ? tokens - row0 : 16 * TB;
-    const __amdgpu_buffer_rsrc_t r =
-        raw_rsrc(reinterpret_cast<const char *>(gin) + (row0 * I + g * kG) * gsz, (uint32_t)(rows * I * gsz));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (!all && k != ks) continue;
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-#pragma unroll
-        for (int h = 0; h < NPC; ++h)
-          raw[t][k][h] = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, (int)((t * 16 * I + k * 32) * gsz + 16 * h), 0);
-    }
-  };
-
-  int64_t mt0 = mt_first + wave * TB;
-  if (mt0 < mt_last) load_g(mt0, 0, true);
-
-  const uint16_t *hg = hl + g * kBwdMat;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = threadIdx.x + 256 * (8 * half + u);  // matrix row c/16 (of 256), 16-byte part c%16
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(hg + (int64_t)c * 8);
-      *reinterpret_cast<u32x4 *>(hlds + (c >> 4) * kDxHS + (c & 15) * 8) = v;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();
-
-  constexpr int kStride = 4 * TB;
-  for (; mt0 < mt_last; mt0 += kStride) {
-    const int64_t next = mt0 + kStride;
-    const bool more = next < mt_last;
-    f32x4 acc[TB][8];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc_fence(acc[t][ct]);
-      }
-    asm volatile("s_nop 7");
-    auto read_a = [&](int step) {
-      const int ks = step >> 4, ct = (step >> 1) & 7, hlm = step & 1;
-      return *reinterpret_cast<const u32x4 *>(hlds + (hlm * kG + ct * 16 + fr) * kDxHS + ks * 32 + fk);
-    };
-    u32x4 ar[3];
-    ar[0] = read_a(0);
-    ar[1] = read_a(1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      // this k-step's B fragments (fp32 g: bf16 high part and remainder)
-      u32x4 hi[TB], lo[TB];
-      if constexpr (F32G) {
-        // the conversion writes registers that the previous k-step's MFMAs
-        // read; the compiler does not see those asm MFMAs
-        if (ks > 0) asm volatile("s_nop 7");
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        if constexpr (F32G) {
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const u32x4 &src = raw[t][ks][e >> 1];
-            const float v0 = __uint_as_float(src[2 * (e & 1)]), v1 = __uint_as_float(src[2 * (e & 1) + 1]);
-            h[e] = pack2<kBF16>(v0, v1);
-            l[e] = pack2<kBF16>(v0 - bf16_bits_to_f32(h[e] & 0xffffu), v1 - bf16_bits_to_f32(h[e] >> 16));
-          }
-          hi[t] = u32x4{h[0], h[1], h[2], h[3]};
-          lo[t] = u32x4{l[0], l[1], l[2], l[3]};
-        } else {
-          hi[t] = raw[t][ks][0];
-        }
-      }
-#pragma unroll
-      for (int sub = 0; sub < 16; ++sub) {
-        const int step = ks * 16 + sub, ct = sub >> 1, hlm = sub & 1;
-        if (step + 2 < 64) ar[(step + 2) % 3] = read_a(step + 2);
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          mfma_acc<MD>(ar[step % 3], hi[t], acc[t][ct]);
-          if constexpr (F32G) {
-            if (hlm == 0) mfma_acc<MD>(ar[step % 3], lo[t], acc[t][ct]);
-          }
-        }
-        if (sub == 15 && more) load_g(next, ks, false);  // k-step consumed: next batch's fragments
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    mfma_drain();
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc_fence(acc[t][ct]);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      const int64_t tok = (mt0 + t) * 16 + fr;
-      if (tok < tokens) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x4 l4 = acc[t][2 * b], h4 = acc[t][2 * b + 1];
-          const int64_t off = tok * I + g * kG + 32 * b + fk;
-          if constexpr (ODT == kF32) {
-            float *o = reinterpret_cast<float *>(gx) + off;
-            __builtin_nontemporal_store(l4, reinterpret_cast<f32x4 *>(o));
-            __builtin_nontemporal_store(h4, reinterpret_cast<f32x4 *>(o + 4));
-          } else {
-            const u32x4 v{pack2<ODT>(l4[0], l4[1]), pack2<ODT>(l4[2], l4[3]), pack2<ODT>(h4[0], h4[1]),
-                          pack2<ODT>(h4[2], h4[3])};
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(gx) + off));
-          }
-        }
-      }
-    }
-  }
 }
 
 // gtheta[e] = sum over the kWalkParts partial rows, in order
@@ -535,9 +543,10 @@ bwd_theta_reduce_kernel(const float *__restrict__ tpart, int64_t n, float *__res
 // host side
 // ---------------------------------------------------------------------------
 namespace {
+// token splits: as many as keep every fused workgroup resident at once
 int64_t gram_splits(int64_t tokens, int64_t I) {
-  const int64_t groups = I / kG, tiles = (tokens + kBwdTok - 1) / kBwdTok;
-  int64_t s = (kGramTarget + groups - 1) / groups;
+  const int64_t groups = I / kG, tiles = (tokens + kFT - 1) / kFT;
+  int64_t s = kGramResident / groups;
   if (s > tiles) s = tiles;
   return s < 1 ? 1 : s;
 }
@@ -549,9 +558,9 @@ struct BwdLayout {
 BwdLayout bwd_layout(int64_t tokens, int64_t I, int krot) {
   BwdLayout L;
   L.splits = gram_splits(tokens, I);
-  const int64_t tiles = (tokens + kBwdTok - 1) / kBwdTok;
-  L.chunk = ((tiles + L.splits - 1) / L.splits) * kBwdTok;
-  if (L.chunk == 0) L.chunk = kBwdTok;
+  const int64_t tiles = (tokens + kFT - 1) / kFT;
+  L.chunk = ((tiles + L.splits - 1) / L.splits) * kFT;
+  if (L.chunk == 0) L.chunk = kFT;
   L.hl_off = 0;
   L.c_off = align256((size_t)(I / kG) * kBwdMat * 2);
   L.t_off = L.c_off + align256((size_t)L.splits * (size_t)(I / kG) * kG * kG * 4);
@@ -563,20 +572,10 @@ BwdLayout bwd_layout(int64_t tokens, int64_t I, int krot) {
 size_t rot_backward_partial_bytes(int64_t tokens, int64_t I, int krot) { return bwd_layout(tokens, I, krot).total; }
 
 template <int XDT, int GDT>
-static void launch_gram(dim3 grid, hipStream_t st, const void *x, const void *g, int64_t tokens, int64_t I,
-                        int64_t chunk, float *cpart) {
-  hipLaunchKernelGGL((bwd_gram_kernel<XDT, GDT>), grid, dim3(256), 0, st, x, g, tokens, I, chunk, cpart);
-}
-
-template <int GDT>
-static void launch_dx(int gx_dt, dim3 grid, hipStream_t st, const void *g, void *gx, int64_t tokens, int64_t I,
-                      const uint16_t *hl) {
-  if (gx_dt == kF32)
-    hipLaunchKernelGGL((bwd_dx_kernel<GDT, kF32>), grid, dim3(256), 0, st, g, gx, tokens, I, hl);
-  else if (gx_dt == kF16)
-    hipLaunchKernelGGL((bwd_dx_kernel<GDT, kF16>), grid, dim3(256), 0, st, g, gx, tokens, I, hl);
-  else
-    hipLaunchKernelGGL((bwd_dx_kernel<GDT, kBF16>), grid, dim3(256), 0, st, g, gx, tokens, I, hl);
+static void launch_gram_dx(dim3 grid, hipStream_t st, const void *x, const void *g, void *gx, int gx_f32,
+                           int64_t tokens, int64_t I, int64_t chunk, const uint16_t *hl, float *cpart) {
+  hipLaunchKernelGGL((bwd_gram_dx_kernel<XDT, GDT>), grid, dim3(512), 0, st, x, g, gx, gx_f32, tokens, I, chunk, hl,
+                     cpart);
 }
 
 hipError_t launch_rot_backward(const void *x, int x_dt, const void *gin, int g_dt, int64_t tokens, int64_t I,
@@ -588,39 +587,36 @@ hipError_t launch_rot_backward(const void *x, int x_dt, const void *gin, int g_d
   float *cpart = reinterpret_cast<float *>(ws + L.c_off);
   float *tpart = reinterpret_cast<float *>(ws + L.t_off);
   const unsigned groups = (unsigned)(I / kG);
+  const int gm = kG - group;
 
-  // 1. Gram partials (with no tokens: one split of zeros)
-  const dim3 ggrid(groups, (unsigned)L.splits);
-  if (x_dt == kF16) {
-    if (g_dt == kF32) launch_gram<kF16, kF32>(ggrid, st, x, gin, tokens, I, L.chunk, cpart);
-    else launch_gram<kF16, kF16>(ggrid, st, x, gin, tokens, I, L.chunk, cpart);
-  } else {
-    if (g_dt == kF32) launch_gram<kBF16, kF32>(ggrid, st, x, gin, tokens, I, L.chunk, cpart);
-    else launch_gram<kBF16, kBF16>(ggrid, st, x, gin, tokens, I, L.chunk, cpart);
-  }
+  // 1. R' = diag(cs) R as H + L, rows in MFMA order
+  const dim3 rgrid(groups, kG / kRowsPerBuild);
+  if (dx_mdt(g_dt) == kF16)
+    hipLaunchKernelGGL((bwd_rrow_kernel<kF16>), rgrid, dim3(64), 0, st, I, pairs, theta, cs, krot, gm, hl);
+  else
+    hipLaunchKernelGGL((bwd_rrow_kernel<kBF16>), rgrid, dim3(64), 0, st, I, pairs, theta, cs, krot, gm, hl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // 2. the stage walk: dL/dcs, dtheta partials, R' for the dx product
-  const dim3 wgrid(groups, kG / (4 * kWalkRows));
-  if (dx_mdt(g_dt) == kF16)
-    hipLaunchKernelGGL((bwd_walk_kernel<kF16>), wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta, cs,
-                       krot, kG - group, gcs, tpart, hl);
-  else
-    hipLaunchKernelGGL((bwd_walk_kernel<kBF16>), wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta,
-                       cs, krot, kG - group, gcs, tpart, hl);
+  // 2. Gram partials and dL/dx in one pass (with no tokens: one split of zeros)
+  const dim3 ggrid(groups, (unsigned)L.splits);
+  const int f32 = gx_dt == kF32;
+  if (x_dt == kF16) {
+    if (g_dt == kF32) launch_gram_dx<kF16, kF32>(ggrid, st, x, gin, gx, f32, tokens, I, L.chunk, hl, cpart);
+    else launch_gram_dx<kF16, kF16>(ggrid, st, x, gin, gx, f32, tokens, I, L.chunk, hl, cpart);
+  } else {
+    if (g_dt == kF32) launch_gram_dx<kBF16, kF32>(ggrid, st, x, gin, gx, f32, tokens, I, L.chunk, hl, cpart);
+    else launch_gram_dx<kBF16, kBF16>(ggrid, st, x, gin, gx, f32, tokens, I, L.chunk, hl, cpart);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // 3. dL/dx
-  if (tokens > 0) {
-    const dim3 dgrid(groups, (unsigned)((tokens + kDxRows - 1) / kDxRows));
-    if (g_dt == kF32) launch_dx<kF32>(gx_dt, dgrid, st, gin, gx, tokens, I, hl);
-    else if (g_dt == kF16) launch_dx<kF16>(gx_dt, dgrid, st, gin, gx, tokens, I, hl);
-    else launch_dx<kBF16>(gx_dt, dgrid, st, gin, gx, tokens, I, hl);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // 3. the stage walk: dL/dcs and dtheta partials
+  const dim3 wgrid(groups, kG / (4 * kWalkRows));
+  hipLaunchKernelGGL(bwd_walk_kernel, wgrid, dim3(256), 0, st, cpart, (int)L.splits, I, pairs, theta, cs, krot, gm,
+                     gcs, tpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
 
   // 4. dL/dtheta
   const int64_t n = (int64_t)krot * (I / 2);

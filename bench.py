@@ -53,7 +53,7 @@ def layer_bytes(I, O, krot, G=128, bias=True):
 # Sources of the dominant kernel of each path (counter readings are valid
 # only for the code they were taken on).
 KERNEL_FILES = {1: ("decode.hip", "common.hpp"), 2: ("decode.hip", "common.hpp"),
-                3: ("prefill.hip", "common.hpp")}
+                3: ("prefill.hip", "common.hpp", "mfma.hpp")}
 
 
 def gsuffix(args):
@@ -163,7 +163,7 @@ def bench_quantize(args, paro, synth, np, torch, dev):
 
 
 BWD_METRIC = "ParoQuant rotation backward (dL/dx, dL/dtheta, dL/dcs): activation GB/s, % of HBM roofline"
-KERNEL_FILES["rotate_backward"] = ("rotate_backward.hip", "common.hpp")
+KERNEL_FILES["rotate_backward"] = ("rotate_backward.hip", "common.hpp", "mfma.hpp")
 
 
 def bench_rotate_backward(args, paro, synth, np, torch, dev):
@@ -240,7 +240,7 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
 
 
 MOE_METRIC = "ParoQuant MoE projection (shared rotation, stacked experts): TFLOP/s, % of MFMA roofline"
-KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp", "mx.hpp")
+KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp", "mx.hpp", "mfma.hpp")
 
 
 def bench_moe(args, paro, synth, np, torch, dev):
@@ -315,7 +315,7 @@ def bench_moe(args, paro, synth, np, torch, dev):
 
 MX_METRIC = "ParoQuant W4A4 MXFP4 linear (rotation, activation quantization, FP4 GEMM): TFLOP/s, % of FP4 MFMA roofline"
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 / fp6 MFMA, published
-KERNEL_FILES["mxfp4"] = ("mxfp4.hip", "common.hpp", "mx.hpp")
+KERNEL_FILES["mxfp4"] = ("mxfp4.hip", "common.hpp", "mx.hpp", "mfma.hpp")
 
 
 def bench_mxfp4(args, paro, synth, np, torch, dev):

@@ -12,6 +12,8 @@
 // RW is 16 for many tokens (the pair/angle loads and sin/cos are amortised
 // over more rows) and 1..4 for few tokens (more waves, shorter chains of
 // dependent LDS stages).
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mx.hpp"
@@ -159,13 +161,17 @@ rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__re
   }
 }
 
-// One workgroup: group g = blockIdx.x, token rows [512*blockIdx.y, +512); each
+// One workgroup: group g = blockIdx.x, token rows [R*blockIdx.y, +R) with
+// R = 16 * wg_tiles (kApplyRows unless overridden); each
 // wave takes batches of 4 row tiles (64 rows) and prefetches the next batch's
 // x fragments as the current ones retire.  LDS holds H_T and L_T of the group
 // (row stride 136 halves: the 16-byte fragment reads of 16 lanes spread over
 // the banks).
 constexpr int kHS = kG + 8;
-constexpr int kApplyRows = 512;
+// default token rows per workgroup (a multiple of 256); on 2048 x 14336 bf16
+// 1024 measured 32.7 us against 34.6 us at 512 (the group's H / L pair is
+// loaded into LDS once per workgroup) and 48.9 us at 2048 (too few workgroups)
+constexpr int kApplyRows = 1024;
 constexpr int kApplyTiles = 4;  // row tiles per wave and batch
 
 // MX = true: instead of the tiled X_r, each row's 32-channel blocks are
@@ -175,12 +181,13 @@ constexpr int kApplyTiles = 4;  // row tiles per wave and batch
 template <int XDT, bool MX>
 __global__ void __launch_bounds__(256, 2)
 rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int64_t tokens, int64_t I,
-                 const uint16_t *__restrict__ hl, uint8_t *__restrict__ mx_codes, uint8_t *__restrict__ mx_scales) {
+                 const uint16_t *__restrict__ hl, uint8_t *__restrict__ mx_codes, uint8_t *__restrict__ mx_scales,
+                 int wg_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t hlds[2 * kG * kHS];
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t g = blockIdx.x;
   const int64_t mt_end = tiled_rows(tokens) / 16;  // row tiles of the tiled buffer
-  const int64_t mt_first = (int64_t)blockIdx.y * (kApplyRows / 16);
+  const int64_t mt_first = (int64_t)blockIdx.y * wg_tiles;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const uint32_t lane_off = (uint32_t)((fr * I + fk) * 2);
 
@@ -218,9 +225,9 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
   __syncthreads();
 
   constexpr int kStride = 4 * kApplyTiles;  // row tiles per batch of the workgroup
-  for (; mt0 < mt_end && mt0 < mt_first + kApplyRows / 16; mt0 += kStride) {
+  for (; mt0 < mt_end && mt0 < mt_first + wg_tiles; mt0 += kStride) {
     const int64_t next = mt0 + kStride;
-    const bool more = next < mt_end && next < mt_first + kApplyRows / 16;
+    const bool more = next < mt_end && next < mt_first + wg_tiles;
     f32x4 acc[kApplyTiles][8];
 #pragma unroll
     for (int t = 0; t < kApplyTiles; ++t)
@@ -316,28 +323,41 @@ hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const flo
   return hipGetLastError();
 }
 
+// token rows per apply workgroup; tuning override PARO_APPLY_ROWS (256, 512,
+// 1024, 2048 or 4096), read once per process
+static int apply_rows() {
+  static const int r = [] {
+    const char *v = getenv("PARO_APPLY_ROWS");
+    const int n = (v && *v) ? atoi(v) : 0;
+    return (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) ? n : kApplyRows;
+  }();
+  return r;
+}
+
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st) {
-  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + kApplyRows - 1) / kApplyRows));
+  const int rows = apply_rows();
+  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
-                       nullptr);
+                       nullptr, rows / 16);
   else
     hipLaunchKernelGGL((rot_apply_kernel<kBF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
-                       nullptr);
+                       nullptr, rows / 16);
   return hipGetLastError();
 }
 
 hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
   if (tokens == 0) return hipSuccess;
-  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + kApplyRows - 1) / kApplyRows));
+  const int rows = apply_rows();
+  const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,
-                       scales);
+                       scales, rows / 16);
   else
     hipLaunchKernelGGL((rot_apply_kernel<kBF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,
-                       scales);
+                       scales, rows / 16);
   return hipGetLastError();
 }
 

@@ -98,22 +98,35 @@ __device__ __forceinline__ void mfma_fp4(const u32x4 &a, const u32x4 &b, uint32_
 // a 128 x 256 tile (waves 2 x 4, 64 x 64 each: 4 x 4 MFMA tiles) over stages
 // of 256 k (two 128-wide MFMA steps).  Each stage's A and W code panels (128
 // and 256 rows x 128 bytes: whole cache lines) and their two scale dwords per
-// row go through LDS once per workgroup (rows padded to 144 bytes so the
-// 16-byte fragment reads of 8 rows hit distinct banks), double-buffered, with
-// the global loads of stage s + 2 requested while stage s computes and one
-// barrier per stage.  Workgroups run M-fastest in XCD-local order, so the M
-// tiles that share a weight panel meet in one L2.
-constexpr int kMxBM = 128, kMxBN = 256, kMxRow = 144;  // LDS row pitch (bytes): 128 code bytes + pad
+// row go through LDS once per workgroup, loaded straight into LDS (no
+// register staging, no LDS store instructions) into a ring of three stage
+// buffers, two stages ahead of the products, with one barrier per stage.
+// 16-byte chunks are XOR-swizzled by row, so that the fragment reads of 16
+// rows cover all banks.  Workgroups run M-fastest in XCD-local order, so the
+// M tiles that share a weight panel meet in one L2.
+constexpr int kMxBM = 128, kMxBN = 256, kMxRow = 128;  // LDS row pitch (bytes): one 128-byte code line
+// 16-byte chunk c of row r sits at slot c ^ ((r / 2) % 8): the fragment read
+// of 16 rows at one chunk covers all 64 banks
+__device__ __forceinline__ int mx_slot(int row, int c) { return row * kMxRow + 16 * (c ^ ((row >> 1) & 7)); }
 constexpr int kMxA = kMxBM * kMxRow, kMxW = kMxBN * kMxRow;
-constexpr int kMxBuf = kMxA + kMxW + (kMxBM + kMxBN) * 8;  // codes + two scale dwords per row
+constexpr int kMxS = 4096;                  // scales: two dwords per row (3 KB) and 1 KB of padding
+constexpr int kMxBuf = kMxA + kMxW + kMxS;  // one stage
+constexpr int kMxStages = 3;                // LDS ring: 156 KB
+constexpr int kMxDma = 8;                   // direct-to-LDS loads per wave and stage
+static_assert(kMxDma == 8, "the stage wait below is written as vmcnt(8)");
+
+template <int N>
+struct MxConst {
+  static constexpr int value = N;
+};
 
 template <int ODT>
 __global__ void __launch_bounds__(512)
 mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
                const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws, int64_t N, int64_t K,
                const uint16_t *__restrict__ bias, void *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kMxBuf];
-  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMxStages][kMxBuf];
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int m_tiles = (int)((M + kMxBM - 1) / kMxBM);
   const int lwg = xcd_local_order((int)blockIdx.x, (int)gridDim.x);
   const int64_t mt0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % m_tiles) * kMxBM;
@@ -127,53 +140,62 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
   const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(as, (uint32_t)(M * ks));
   const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(ws, (uint32_t)(N * ks));
 
-  // global -> register staging of one stage: 16-byte chunk c = tid + 512u is
-  // row c/8, part c%8 of the A panel (u < 2) and of the W panel (u < 4); row
-  // tid (< 384) of the scales: 8 bytes, the stage's eight 32-blocks.  Parts
-  // past the end of K (an odd last step) are re-read in bounds and unused.
-  uint32_t a_goff[2], w_goff[4];
+  // Direct global -> LDS loads of one stage (buffer_load ... lds: lane l's 16
+  // (4) bytes land at the window base + 16l (4l)).  A wave fills 1 KB windows
+  // of 8 code rows: lane l takes slot l of the window, i.e. row l/8 and the
+  // global chunk whose swizzled slot is l%8.  A: windows wave, wave + 8 (128
+  // rows); W: wave + 8u, u < 4 (256 rows).  Scales: 256-byte windows of 32
+  // rows (two dwords each), wave and wave + 8 of 16: windows 0..3 are A's
+  // rows, 4..11 W's, 12..15 re-read row 0 into the padding, so every wave
+  // issues kMxDma loads per stage.  Chunks past the end of K (an odd last
+  // step) are re-read in bounds and unused.
+  uint32_t a_off[2], w_off[4], s_off[2];
+  bool s_isa[2], s_hi[2];
+  const int wrow = lane >> 3, wslot = lane & 7;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    a_goff[u] = (uint32_t)((mt0 + ((tid + 512 * u) >> 3)) * kb + 16 * ((tid + 512 * u) & 7));
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * (wave + 8 * u) + wrow;
+    a_off[u] = (uint32_t)((mt0 + row) * kb + 16 * (wslot ^ ((row >> 1) & 7)));
+  }
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    w_goff[u] = (uint32_t)((nt0 + ((tid + 512 * u) >> 3)) * kb + 16 * ((tid + 512 * u) & 7));
-  const bool sc_a = tid < kMxBM, sc_w = tid >= kMxBM && tid < kMxBM + kMxBN;
-  const uint32_t s_goff = sc_a ? (uint32_t)((mt0 + tid) * ks) : (uint32_t)((nt0 + (tid - kMxBM)) * ks);
-  u32x4 ga[2][2], gw[2][4];
-  uint32_t gs[2][2];
-  auto gload = [&](int r, int64_t st) {
-    // the last stage of an odd step count holds one step: its second half is
-    // clamped onto the first (in bounds, never used)
-    const int64_t hi_ok = 2 * st + 1 < ksteps;
+  for (int u = 0; u < 4; ++u) {
+    const int row = 8 * (wave + 8 * u) + wrow;
+    w_off[u] = (uint32_t)((nt0 + row) * kb + 16 * (wslot ^ ((row >> 1) & 7)));
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int win = wave + 8 * u, d = 64 * win + lane;  // dword d of the scale region
+    const int row = win < 12 ? d >> 1 : 0, half = win < 12 ? d & 1 : 0;
+    s_isa[u] = row < kMxBM;
+    s_hi[u] = half == 1;
+    s_off[u] = (uint32_t)((s_isa[u] ? (mt0 + row) : (nt0 + row - kMxBM)) * ks + 4 * half);
+  }
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  auto dma = [&](int buf, int64_t st) {
+    const bool hi_ok = 2 * st + 1 < ksteps;
     const uint32_t cb = (uint32_t)(st * 128);
+    uint8_t *b = lds[buf];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint32_t part = (uint32_t)((tid + 512 * u) & 7);
-      const uint32_t o = a_goff[u] + cb - ((part >= 4 && !hi_ok) ? 64u : 0u);
-      ga[r][u] = __builtin_amdgcn_raw_buffer_load_b128(ra, o, 0, 0);
+      const int row = 8 * (wave + 8 * u) + wrow, c = wslot ^ ((row >> 1) & 7);
+      const uint32_t o = a_off[u] + cb - ((c >= 4 && !hi_ok) ? 64u : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(b + 1024 * (wave + 8 * u)), 16, o, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t part = (uint32_t)((tid + 512 * u) & 7);
-      const uint32_t o = w_goff[u] + cb - ((part >= 4 && !hi_ok) ? 64u : 0u);
-      gw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0);
+      const int row = 8 * (wave + 8 * u) + wrow, c = wslot ^ ((row >> 1) & 7);
+      const uint32_t o = w_off[u] + cb - ((c >= 4 && !hi_ok) ? 64u : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(b + kMxA + 1024 * (wave + 8 * u)), 16, o, 0, 0, 0);
     }
-    const uint32_t sb = (uint32_t)(st * 8), sb1 = hi_ok ? sb + 4 : sb;
-    gs[r][0] = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb, 0, 0)
-                    : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb, 0, 0) : 0u);
-    gs[r][1] = sc_a ? __builtin_amdgcn_raw_buffer_load_b32(rsa, s_goff + sb1, 0, 0)
-                    : (sc_w ? __builtin_amdgcn_raw_buffer_load_b32(rsw, s_goff + sb1, 0, 0) : 0u);
-  };
-  auto sstore = [&](int r, int buf) {
-    uint8_t *b = lds[buf];
+    const uint32_t sb = (uint32_t)(st * 8);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<u32x4 *>(b + ((tid + 512 * u) >> 3) * kMxRow + 16 * ((tid + 512 * u) & 7)) = ga[r][u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<u32x4 *>(b + kMxA + ((tid + 512 * u) >> 3) * kMxRow + 16 * ((tid + 512 * u) & 7)) = gw[r][u];
-    if (tid < kMxBM + kMxBN) *reinterpret_cast<u32x2 *>(b + kMxA + kMxW + 8 * tid) = u32x2{gs[r][0], gs[r][1]};
+    for (int u = 0; u < 2; ++u) {
+      // the second dword of a row is the step's second half: the first one again past K
+      const uint32_t o = s_off[u] + sb - ((!hi_ok && s_hi[u]) ? 4u : 0u);
+      lds_ptr dst = (lds_ptr)(b + kMxA + kMxW + 256 * (wave + 8 * u));
+      if (s_isa[u]) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 4, o, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, dst, 4, o, 0, 0, 0);
+    }
   };
 
   f32x4 acc[4][4];
@@ -193,8 +215,8 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ar = wm * 64 + 16 * i + fr, wr = wn * 64 + 16 * i + fr;
-      fa[i] = *reinterpret_cast<const u32x4 *>(b + ar * kMxRow + 64 * h + 16 * q);
-      fw[i] = *reinterpret_cast<const u32x4 *>(b + kMxA + wr * kMxRow + 64 * h + 16 * q);
+      fa[i] = *reinterpret_cast<const u32x4 *>(b + mx_slot(ar, 4 * h + q));
+      fw[i] = *reinterpret_cast<const u32x4 *>(b + kMxA + mx_slot(wr, 4 * h + q));
       sca[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 8 * ar + 4 * h) >> (8 * q)) & 0xffu;
       scw[i] = (*reinterpret_cast<const uint32_t *>(b + kMxA + kMxW + 8 * (kMxBM + wr) + 4 * h) >> (8 * q)) & 0xffu;
     }
@@ -209,24 +231,33 @@ mx_gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, i
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // stage s: LDS buffer s & 1 holds it, register set (s + 1) & 1 holds stage
-  // s + 1, set s & 1 is free (its stage went to LDS one stage ago)
-  gload(0, 0);
-  if (nstages > 1) gload(1, 1);
-  sstore(0, 0);
-  __syncthreads();
-  auto iter = [&](int64_t st, int r) {  // r == st & 1, a compile-time constant
-    if (st + 2 < nstages) gload(r, st + 2);
-    compute(r, 0);
-    if (2 * st + 1 < ksteps) compute(r, 1);
-    if (st + 1 < nstages) sstore(r ^ 1, r ^ 1);  // buffer r ^ 1 was last read in stage st - 1
-    __syncthreads();
+  // stage s in LDS buffer s % 3: its loads were issued two stages earlier.
+  // Each stage waits for this wave's loads of the stage (the next stage's
+  // kMxDma stay in flight), then one barrier makes every wave's loads visible
+  // and orders the refill of buffer (s + 2) % 3 (read by stage s - 1) after
+  // every wave's products of stage s - 1.
+  dma(0, 0);
+  if (nstages > 1) dma(1, 1);
+  auto iter = [&](int64_t st, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    // this wave's loads of stage st are in LDS (those of st + 1 may still be
+    // in flight), then the barrier.  Not __syncthreads(): its fence would
+    // also wait for the next stage's loads.  LDS needs no cache maintenance
+    // between waves; the memory clobber keeps LDS accesses on their side.
+    if (st + 1 < nstages) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (st + 2 < nstages) dma((B + 2) % kMxStages, st + 2);
+    compute(B, 0);
+    if (2 * st + 1 < ksteps) compute(B, 1);
   };
   int64_t s = 0;
   do {
-    iter(s, 0);
-    if (s + 1 < nstages) iter(s + 1, 1);
-    s += 2;
+    iter(s, MxConst<0>{});
+    if (s + 1 >= nstages) break;
+    iter(s + 1, MxConst<1>{});
+    if (s + 2 >= nstages) break;
+    iter(s + 2, MxConst<2>{});
+    s += 3;
   } while (s < nstages);
   mfma_drain();
 #pragma unroll

@@ -172,6 +172,9 @@ constexpr int kHS = kG + 8;
 // 1024 measured 32.7 us against 34.6 us at 512 (the group's H / L pair is
 // loaded into LDS once per workgroup) and 48.9 us at 2048 (too few workgroups)
 constexpr int kApplyRows = 1024;
+// with the MXFP4 epilogue (VALU-heavy) two workgroups per CU overlap it with
+// the other's products: 42.1 us at 512 rows against 56.9 us at 1024
+constexpr int kApplyRowsMx = 512;
 constexpr int kApplyTiles = 4;  // row tiles per wave and batch
 
 // MX = true: instead of the tiled X_r, each row's 32-channel blocks are
@@ -325,18 +328,18 @@ hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const flo
 
 // token rows per apply workgroup; tuning override PARO_APPLY_ROWS (256, 512,
 // 1024, 2048 or 4096), read once per process
-static int apply_rows() {
+static int apply_rows(int dflt) {
   static const int r = [] {
     const char *v = getenv("PARO_APPLY_ROWS");
     const int n = (v && *v) ? atoi(v) : 0;
-    return (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) ? n : kApplyRows;
+    return (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) ? n : 0;
   }();
-  return r;
+  return r ? r : dflt;
 }
 
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st) {
-  const int rows = apply_rows();
+  const int rows = apply_rows(kApplyRows);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
@@ -350,7 +353,7 @@ hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t t
 hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
   if (tokens == 0) return hipSuccess;
-  const int rows = apply_rows();
+  const int rows = apply_rows(kApplyRowsMx);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,

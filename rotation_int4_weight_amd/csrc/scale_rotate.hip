@@ -327,19 +327,24 @@ hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const flo
 }
 
 // token rows per apply workgroup; tuning override PARO_APPLY_ROWS (256, 512,
-// 1024, 2048 or 4096), read once per process
-static int apply_rows(int dflt) {
+// 1024, 2048 or 4096), read once per process.  Without it the default is
+// halved (down to 256) while the launch would have fewer than 192
+// workgroups, so narrow layers still spread over the chip.
+static int apply_rows(int dflt, int64_t tokens, int64_t I) {
   static const int r = [] {
     const char *v = getenv("PARO_APPLY_ROWS");
     const int n = (v && *v) ? atoi(v) : 0;
     return (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) ? n : 0;
   }();
-  return r ? r : dflt;
+  if (r) return r;
+  int rows = dflt;
+  while (rows > 256 && (I / kG) * ((tiled_rows(tokens) + rows - 1) / rows) < 192) rows /= 2;
+  return rows;
 }
 
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st) {
-  const int rows = apply_rows(kApplyRows);
+  const int rows = apply_rows(kApplyRows, tokens, I);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
@@ -353,7 +358,7 @@ hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t t
 hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
   if (tokens == 0) return hipSuccess;
-  const int rows = apply_rows(kApplyRowsMx);
+  const int rows = apply_rows(kApplyRowsMx, tokens, I);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,

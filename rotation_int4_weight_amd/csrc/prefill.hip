@@ -36,12 +36,13 @@
 //     rows into the LDS tile [column][k].  fp16: a byte permute and an OR
 //     with 0x6400 make 1024+q exactly, then one packed add of -(1024+z) and
 //     one packed multiply by s give (q-z)*s rounded once, two weights per
-//     instruction.  bf16 (no packed bf16 arithmetic): byte-to-float converts,
-//     an fma q*s + (-z*s) that is exact in fp32, and a paired round to bf16.
-//     Within each column the four 8-row blocks of k are XOR-permuted by
-//     (column/16)&3, which spreads the 4-byte stores over all banks and
-//     leaves each fragment read (8 consecutive k, two 8-byte loads)
-//     contiguous.
+//     instruction.  bf16 (no packed bf16 arithmetic): the same masks give
+//     1024+q or 1024+16q per fp16 half, one v_fma_mix_f32 per weight turns
+//     that into the exact fp32 (q-z)*s, and a paired round makes bf16.
+//     Columns are 80 bytes apart and within each column the four 8-row
+//     blocks of k are XOR-permuted by (column/16)&3: the 4-byte stores
+//     spread over the banks and each fragment read (8 consecutive k) is one
+//     aligned 16-byte load with no bank conflicts.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -51,10 +52,11 @@ namespace paro {
 constexpr int kBM = 256, kBN = 128, kBK = 32;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
 constexpr int kStepsPerGroup = kG / kBK;
-constexpr int kBStride = kBK + 4;  // halves per LDS column (72 bytes)
+constexpr int kBStride = kBK + 8;  // halves per LDS column (80 bytes: 16-byte aligned fragment reads)
 constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k steps)
 constexpr int kWordRing = 8;        // packed weight words in flight per producer thread (steps)
 constexpr int kASlots = 4;          // A fragments in flight per consumer wave (steps)
+constexpr int kGroupM = 2;          // M blocks per group of the tile order (dense layers)
 constexpr int kStageRS = kBN + 4;   // epilogue staging row stride (floats): the four row groups of a store hit distinct banks
 static_assert(kTiles == 8 && kWordRing == 8, "the producer's ring slot arithmetic assumes rings of 8");
 
@@ -83,14 +85,33 @@ struct GroupConsts<kF16> {
 };
 template <>
 struct GroupConsts<kBF16> {
-  float zs[8], sc[8];
+  // Slot s is the low nibble of its byte for even s and the high nibble for
+  // odd s; expand_pair_to_lds builds the fp16 numbers 1024 + q and 1024 + 16q
+  // from them.  b, c make b * that + c = (q - z) * s exactly in one fma:
+  //   even: b = s,      c = -(1024 + z) * s   (11-bit x 11-bit: exact in fp32)
+  //   odd:  b = s / 16, c = -(64 + z) * s     (a power-of-two scaling and a
+  //                                            7-bit x 11-bit product: exact)
+  // and (q - z) * s itself has at most 15 significant bits.
+  float b[8], c[8];
   __device__ __forceinline__ void decode(u32x4 sw, uint32_t zw) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int c = awq_col(s);
-      sc[s] = f16_bits_to_f32((sw[c >> 1] >> (16 * (c & 1))) & 0xffffu);
-      zs[s] = -(float)((zw >> (4 * s)) & 0xfu) * sc[s];  // exact: 4-bit x 11-bit
+      const int col = awq_col(s);
+      const float sc = f16_bits_to_f32((sw[col >> 1] >> (16 * (col & 1))) & 0xffffu);
+      const uint32_t z = (zw >> (4 * s)) & 0xfu;
+      b[s] = (s & 1) ? sc * 0.0625f : sc;
+      c[s] = -(float)(((s & 1) ? 64u : 1024u) + z) * sc;
     }
+  }
+};
+
+// Nibble masks and the fp16 exponent pattern, held in VGPRs for the whole
+// producer: v_and_or_b32 takes no literal operand, and with the constants in
+// registers each 1024+q (or 1024+16q) pair costs one instruction.
+struct NibbleMasks {
+  uint32_t lo, hi, e;
+  __device__ __forceinline__ NibbleMasks() : lo(0x000f000fu), hi(0x00f000f0u), e(0x64006400u) {
+    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(e));
   }
 };
 
@@ -98,14 +119,14 @@ struct GroupConsts<kBF16> {
 // tile: slot s goes to column 8w + awq_col(s), k-pair rp (swizzled) as one u32.
 template <int DT>
 __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, const GroupConsts<DT> &gc,
-                                                   uint16_t *bl, int w, int rp) {
+                                                   const NibbleMasks &nm, uint16_t *bl, int w, int rp) {
   uint32_t v[8];
   if constexpr (DT == kF16) {
     // P = [ra.b0, ra.b2, rb.b0, rb.b2], Q = [ra.b1, ra.b3, rb.b1, rb.b3]: after
     // the shifts below, bits 0..3 and 16..19 hold slot s of ra and of rb.
     const uint32_t P = __builtin_amdgcn_perm(ra, rb, 0x02000604u);
     const uint32_t Q = __builtin_amdgcn_perm(ra, rb, 0x03010705u);
-    const uint32_t M = 0x000f000fu, E = 0x64006400u;
+    const uint32_t M = nm.lo, E = nm.e;
     const uint32_t e[8] = {(P & M) | E,         ((P >> 4) & M) | E, (Q & M) | E,         ((Q >> 4) & M) | E,
                            ((P >> 8) & M) | E, ((P >> 12) & M) | E, ((Q >> 8) & M) | E, ((Q >> 12) & M) | E};
 #pragma unroll
@@ -115,19 +136,21 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
       v[s] = __builtin_bit_cast(uint32_t, h);
     }
   } else {
-    // bytes of lo_* hold slots 0,2,4,6 and of hi_* slots 1,3,5,7.  The empty
-    // asm keeps the optimizer from merging the masks into per-nibble
-    // bit-field extracts instead of using the byte-to-float converts
-    // (v_cvt_f32_ubyte0..3).
-    uint32_t lo_a = ra & 0x0f0f0f0fu, hi_a = (ra >> 4) & 0x0f0f0f0fu;
-    uint32_t lo_b = rb & 0x0f0f0f0fu, hi_b = (rb >> 4) & 0x0f0f0f0fu;
-    asm volatile("" : "+v"(lo_a), "+v"(hi_a), "+v"(lo_b), "+v"(hi_b));
+    // Same byte gathers as fp16: P's halves hold bytes 0 and 2 of ra (low
+    // half) and of rb (high half), Q's bytes 1 and 3.  A low nibble masked in
+    // and OR-ed with 0x6400 is the fp16 number 1024 + q, a high nibble
+    // 1024 + 16q; v_fma_mix_f32 takes each half as an fp16 operand, so one
+    // instruction per weight gives the exact fp32 (q - z) * s.
+    const uint32_t P = __builtin_amdgcn_perm(ra, rb, 0x02000604u);
+    const uint32_t Q = __builtin_amdgcn_perm(ra, rb, 0x03010705u);
+    const uint32_t P8 = P >> 8, Q8 = Q >> 8;
+    const uint32_t L = nm.lo, H = nm.hi, E = nm.e;
+    const uint32_t e[8] = {(P & L) | E,  (P & H) | E,  (Q & L) | E,  (Q & H) | E,
+                           (P8 & L) | E, (P8 & H) | E, (Q8 & L) | E, (Q8 & H) | E};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint32_t wa = (s & 1) ? hi_a : lo_a, wb = (s & 1) ? hi_b : lo_b;
-      const int sh = 8 * (s >> 1);
-      const float qa = (float)((wa >> sh) & 0xffu), qb = (float)((wb >> sh) & 0xffu);
-      const f32x2 d = {__builtin_fmaf(qa, gc.sc[s], gc.zs[s]), __builtin_fmaf(qb, gc.sc[s], gc.zs[s])};
+      const f16x2 h = __builtin_bit_cast(f16x2, e[s]);
+      const f32x2 d = {__builtin_fmaf((float)h[0], gc.b[s], gc.c[s]), __builtin_fmaf((float)h[1], gc.b[s], gc.c[s])};
       v[s] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));  // one paired RNE
     }
   }
@@ -159,7 +182,18 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   const int n_tiles = (int)((O + kBN - 1) / kBN);
   const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + kBM - 1) / kBM);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
-  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(lwg % n_tiles) * kBN;
+  // Dense layers: logical tiles go in groups of kGroupM M blocks, the M block
+  // fastest, so an XCD's share of consecutive tiles spans kGroupM blocks of
+  // rows and 1/kGroupM as many weight columns as a row-major order would.
+  int tn = lwg % n_tiles, tm = lwg / n_tiles;
+  if constexpr (!MOE) {
+    const int first = (lwg / (kGroupM * n_tiles)) * kGroupM;
+    const int gsz = m_tiles - first < kGroupM ? m_tiles - first : kGroupM;
+    const int r = lwg % (kGroupM * n_tiles);
+    tm = first + r % gsz;
+    tn = r / gsz;
+  }
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * kBN;
   int64_t mb, row_lo = 0, row_hi = M;
   const int32_t *qweight = a.qweight, *qzeros = a.qzeros;
   const uint16_t *scales = a.scales, *bias = a.bias;
@@ -194,7 +228,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     scales += (int64_t)e * (I / G) * O;
     if (bias) bias += (int64_t)e * O;
   } else {
-    mb = (int64_t)__builtin_amdgcn_readfirstlane(lwg / n_tiles) * kBM;
+    mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * kBM;
   }
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
   const int nsteps = (int)(I / kBK), ngroups = (int)(I / (kBK * GK));
@@ -248,6 +282,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     // slot index below is a compile-time constant: the step's value mod 8 is.
     constexpr int NSLOT = GK == 1 ? 4 : 2;
     GroupConsts<DT> gc;
+    const NibbleMasks nm;
     GroupRaw graw[NSLOT];
     Words wd[kWordRing];
 #pragma unroll
@@ -267,7 +302,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       enter_group(k, k);
-      expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, bl[k], dw, drp);
+      expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, nm, bl[k], dw, drp);
       load_words(k + kWordRing, wd[k]);
       __builtin_amdgcn_sched_barrier(0);  // one expansion's temporaries live at a time
     }
@@ -287,7 +322,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
         const int slot = (2 * kk + 4 + u) % kTiles;  // == (2S+4+u) % 8
         enter_group(slot, 2 * S + 4 + u);
         Words &w = wd[slot];
-        expand_pair_to_lds<DT>(w.ra, w.rb, gc, bl[slot], dw, drp);
+        expand_pair_to_lds<DT>(w.ra, w.rb, gc, nm, bl[slot], dw, drp);
         load_words(2 * S + 4 + u + kWordRing, w);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -317,7 +352,9 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     for (int i = 0; i < 4; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
   };
   // B fragment of column tile j of one k step: column 16j + fr, k
-  // block fk (physical block (fk/8) ^ (j&3)), two 8-byte LDS reads each.
+  // block fk (physical block (fk/8) ^ (j&3)), one 16-byte LDS read.  With
+  // 20-dword columns the 16 lanes of each read phase land on 16 distinct
+  // 16-byte bank groups.
   // Only the four lane offsets for j&3 live in registers; the tile and j>=4
   // are constant offsets folded into the LDS instructions.
   uint32_t fcol[4];
@@ -325,9 +362,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   for (int jj = 0; jj < 4; ++jj) fcol[jj] = (uint32_t)((jj * 16 + fr) * kBStride + 8 * ((fk >> 3) ^ jj));
   auto read_frag = [&](int tile, int j, u32x4 &b) {
     const uint16_t *col = &bl[0][0] + tile * (kBN * kBStride) + fcol[j & 3] + (j >> 2) * 64 * kBStride;
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(col);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(col + 4);
-    b = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    b = *reinterpret_cast<const u32x4 *>(col);
   };
 
   f32x4 acc[4][8];

@@ -17,11 +17,12 @@
 //     ahead;
 //   * producer waves 4..7 load the packed weight words eight steps before
 //     they are needed, decode each group's scales and zero points and
-//     dequantize each tile four steps ahead into a ring of eight LDS tiles.
+//     dequantize each tile one super-step before its first reader, five to
+//     eight steps ahead, into a ring of eight LDS tiles.
 // On gfx950 a SIMD hides only about one VALU instruction per 16-cycle MFMA
 // from the same wave but about two from a second wave, so the split keeps
 // the matrix pipe fed while the dequantization runs beside it.  Both roles
-// meet at one barrier per super-step of two k steps (64 MFMAs per consumer
+// meet at one barrier per super-step of four k steps (128 MFMAs per consumer
 // wave between barriers).
 //
 // Operand layouts are chosen for whole-cache-line loads (the texture/L1 path
@@ -299,10 +300,10 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
         load_group(st / GK + NSLOT, gr);
       }
     };
-    // tiles 0..3 before the first barrier: the consumers' first super-step
-    // computes steps 0, 1 and reads the fragments of steps 2 and 3
+    // tiles 0..4 before the first barrier: the consumers' first super-step
+    // computes steps 0..3 and reads the fragments of steps 1..4
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 5; ++k) {
       enter_group(k, k);
       expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, nm, bl[k], dw, drp);
       load_words(k + kWordRing, wd[k]);
@@ -310,35 +311,31 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     }
     __syncthreads();
 
-    // Super-step S (the consumers' steps 2S, 2S+1): expand steps 2S+4 and
-    // 2S+5 into tiles (2S+4)%8, (2S+5)%8.  Their first reader runs in
-    // super-step S+1, after the barrier that ends S; their slots' previous
-    // tiles (2S-4, 2S-3) were last read in super-step S-2.  Each word slot is
-    // refilled kWordRing steps ahead.  Past the end everything runs on
-    // clamped, in-bounds addresses into tiles no consumer uses.
-    // kk: position of S in a four-super-step iteration whose first S is a
-    // multiple of 4, so that the ring slots (2kk+4+u) % 8 are constants.
+    // Super-step S (the consumers' steps 4S..4S+3): expand steps 4S+5..4S+8
+    // into tiles (4S+5..4S+8) % 8.  Their first reader runs in super-step
+    // S+1, after the barrier that ends S.  Their slots' previous tiles
+    // (4S-3..4S) were last read in super-step S-1, and the consumers wait for
+    // their own LDS reads before each barrier.  Each word slot is refilled
+    // kWordRing steps ahead.  Past the end everything runs on clamped,
+    // in-bounds addresses into tiles no consumer uses.  kk: parity of S in a
+    // two-super-step iteration, so that the ring slots (4kk+5+u) % 8 are
+    // constants.
     auto psuper = [&](int S, int kk) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int slot = (2 * kk + 4 + u) % kTiles;  // == (2S+4+u) % 8
-        enter_group(slot, 2 * S + 4 + u);
+      for (int u = 0; u < 4; ++u) {
+        const int slot = (4 * kk + 5 + u) % kTiles;  // == (4S+5+u) % 8
+        enter_group(slot, 4 * S + 5 + u);
         Words &w = wd[slot];
         expand_pair_to_lds<DT>(w.ra, w.rb, gc, nm, bl[slot], dw, drp);
-        load_words(2 * S + 4 + u + kWordRing, w);
+        load_words(4 * S + 5 + u + kWordRing, w);
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
     };
-    const int nsuper = nsteps / 2;  // a multiple of 2 (I % 128 == 0)
-    for (int S0 = 0; S0 < nsuper; S0 += 4) {
-      // four super-steps (eight k-steps) per iteration
+    const int nsuper = nsteps / 4;  // I % 128 == 0
+    for (int S0 = 0; S0 < nsuper; S0 += 2) {
       psuper(S0, 0);
-      psuper(S0 + 1, 1);
-      if (S0 + 2 < nsuper) {
-        psuper(S0 + 2, 2);
-        psuper(S0 + 3, 3);
-      }
+      if (S0 + 1 < nsuper) psuper(S0 + 1, 1);
     }
     return;
   }
@@ -383,8 +380,11 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
   // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at
   // least one barrier earlier), which has the other seven tiles' MFMAs to
-  // arrive in; then the refill of the A slot with step s+4, and a barrier
-  // after odd steps.  The scheduling barriers keep each refill after the
+  // arrive in; then the refill of the A slot with step s+4, and after every
+  // fourth step a barrier, once this wave's LDS reads have landed (the
+  // producer rewrites the slot of the last tile read in the next
+  // super-step).  Halving the barriers of a two-step super-step measured
+  // 202 -> 197.5 us at 2048 x 14336 -> 4096.  The scheduling barriers keep each refill after the
   // MFMAs that read the old fragment (an MFMA reads its sources when issued).
   auto cstep = [&](int step, u32x4(&A)[4], bool barrier) {
     const int next = (step + 1) % kTiles;
@@ -396,11 +396,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       read_frag(next, j, bf[j]);
     }
     load_a(step + kASlots, A);
-    // One barrier per super-step of two k steps, without waiting for this
-    // wave's own LDS reads: the tiles they read are rewritten only two
-    // barriers later.  The memory clobber keeps the compiler from moving LDS
-    // accesses across it.
-    if (barrier) asm volatile("s_barrier" ::: "memory");
+    if (barrier) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   // (unrolled by kASlots: the A slots need constant indices; nsteps is a
   // positive multiple of 4.  A do-while has no zero-trip path, whose join
@@ -408,7 +404,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   int step = 0;
   do {
 #pragma unroll
-    for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], (k & 1) != 0);
+    for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3);
     step += kASlots;
   } while (step < nsteps);
   __builtin_amdgcn_s_setprio(0);

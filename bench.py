@@ -1,22 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the rotated W4A16 linear (ParoQuant inference hot path) on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
 One step = one pass of the whole path (channel scale, pairwise rotation, AWQ
 unpack, dequant, contraction, bias, output rounding) over one batch of seeded
 synthetic input, through libparo's C-ABI.  The default workload is the
-Llama-3-8B q_proj decode layer (4096 -> 4096, 1 token, fp16).  Every timed
-step reads a different copy of the layer's tensors (a rotation through at
-least 512 MB of distinct buffers, twice the 256 MB MALL) so the weight stream
-comes from HBM, with every input already resident in device memory.
+largest single-GPU configuration: the seven linears of a Llama-3-8B decoder
+layer (q, k, v, o, gate, up, down) at 4096 tokens in bf16, run back to back.
+Every timed step reads a different copy of the layers' tensors (a rotation
+through at least 512 MB of distinct buffers, twice the 256 MB MALL) with
+every input already resident in device memory.
 
 Prints ONE JSON line: metric, value (decode: weight GB/s = (qweight + qzeros +
-scales bytes) / step time; prefill: TFLOP/s = 2*M*I*O / step time), the
-roofline of the dominant kernel (its algorithmic bytes or flops per launch
-over its average launch duration, timed live with HIP events on the stream
-it runs on), and the fp64 CPU oracle timed on a bounded sample of the same
-workload as a baseline.
+scales bytes) / step time; prefill: TFLOP/s = 2*M*I*O summed over the layers
+/ step time), the step time's p10 / p50 / p90, the roofline of the dominant
+kernel (its algorithmic bytes or flops per launch over its average launch
+duration, timed live with HIP events on the stream it runs on, beside a
+ceiling measured live on the same GPU), and the fp64 CPU oracle timed on a
+bounded sample of the same workload as a baseline.
 """
 from __future__ import annotations
 
@@ -404,6 +406,46 @@ def bench_mxfp4(args, paro, synth, np, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def measured_ceiling(decode, layers, M, tdt, torch, dev, stream, achieved):
+    """What this GPU delivers, measured live beside the spec peak.
+    decode (HBM-bound): a plain device-to-device copy of 512 MiB, bytes read
+    plus bytes written per second.  prefill (MFMA-bound): the library's dense
+    GEMM (torch.matmul, hipBLASLt) on the workload's own shapes in the
+    activation dtype, each layer's X [M][I] times a dense [I][O] weight --
+    the same flops with a weight four times larger and no dequantization.
+    Returns {"kind", "value", "unit", "frac"} with frac = achieved / value."""
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
+    if decode:
+        src = torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        t = timed(lambda: dst.copy_(src), 20)
+        val = 2 * src.numel() * 4 / t / 1e9
+        del src, dst
+        return {"kind": "device copy of 512 MiB (read + write bytes / s)", "value": round(val, 1),
+                "unit": "GB/s", "frac": round(achieved / val, 4)}
+    ops = []
+    for _, I, O, _, _ in layers:
+        a = torch.randn((M, I), device=dev).to(tdt)
+        w = torch.randn((I, O), device=dev).to(tdt)
+        ops.append((a, w))
+    t = timed(lambda: [torch.matmul(a, w) for a, w in ops], 10)
+    flops = sum(2.0 * M * I * O for _, I, O, _, _ in layers)
+    val = flops / t / 1e12
+    del ops
+    return {"kind": "dense GEMM of the library (torch.matmul) on the same shapes and dtype", "value": round(val, 1),
+            "unit": "TFLOP/s", "frac": round(achieved / val, 4)}
+
+
 def bits_to_f64_host(bits, dt, np):
     """fp16 / bf16 bit patterns (uint16) -> float64 (the oracle takes g in double)."""
     if dt == 0:
@@ -416,13 +458,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=1, help="0..4 (synth.WORKLOADS)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="0..4 (synth.WORKLOADS); 4, the seven linears of a Llama-3-8B decoder layer at "
+                         "4096 tokens, is the largest single-GPU configuration and the default")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode_fused, 2 decode_split, 3 prefill")
     ap.add_argument("--group", type=int, default=128, choices=(32, 64, 128),
                     help="rotation / quantization group size G of the synthetic layers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
+    ap.add_argument("--rebuild-rotation", action="store_true",
+                    help="prefill: rebuild each layer's dense rotation in every call (paro_w4a16_linear) "
+                         "instead of building it once per layer (paro_w4a16_linear_prepared)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured ceiling (device copy for decode, library dense GEMM for prefill)")
     ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward", "moe", "mxfp4"), default="linear",
                     help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
                          "qzeros, scales) transform of the workload's first layer; rotate_backward: the "
@@ -502,23 +551,44 @@ def main():
     ws = paro.make_workspace(ws_bytes, device=dev)
     stream = torch.cuda.current_stream()
 
+    # Prefill: each layer's dense rotation R' = diag(cs) R is built once, like
+    # its packed weight (it depends on the layer alone), and every step runs
+    # paro_w4a16_linear_prepared: rotation applied, then the GEMM.  With
+    # --rebuild-rotation every call rebuilds it (paro_w4a16_linear).
+    prepared = path == 3 and not args.rebuild_rotation
+    hls = None
+    if prepared:
+        hls = []
+        for row in sets:
+            hl_row = []
+            for D, _ in row:
+                hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
+                paro.paro_rotation_matrix(D, act, hl, stream=stream)
+                hl_row.append(hl)
+            hls.append(hl_row)
+
     def step(i):
         row = sets[i % nsets]
         for l, (D, xd) in enumerate(row):
-            paro.paro_w4a16_linear(D, xd, ys[l], ws, stream=stream, path=path)
+            if prepared:
+                paro.paro_w4a16_linear_prepared(D, hls[i % nsets][l], xd, ys[l], ws, stream=stream)
+            else:
+                paro.paro_w4a16_linear(D, xd, ys[l], ws, stream=stream, path=path)
 
-    # ---- whole-path timing ----
+    # ---- whole-path timing: one event at every step boundary ----
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0.record(stream)
+    marks[0].record(stream)
     for i in range(args.steps):
         step(i)
-    t1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
 
     weight_bytes = sum(layer_bytes(I, O, 8, G=args.group)[0] for _, I, O, _, _ in layers)
     flops = sum(2.0 * M * I * O for _, I, O, _, _ in layers)
@@ -559,11 +629,14 @@ def main():
             launches_per_call = len(layers)
         else:  # prefill: the GEMM kernel alone, over X_r already in its tiled layout
             xts = []
-            for row in sets:
+            for si, row in enumerate(sets):
                 xt_row = []
-                for D, xd in row:
-                    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
-                    paro.paro_rotation_matrix(D, act, hl, stream=stream)
+                for l, (D, xd) in enumerate(row):
+                    if hls is not None:
+                        hl = hls[si][l]
+                    else:
+                        hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
+                        paro.paro_rotation_matrix(D, act, hl, stream=stream)
                     xt = torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device=dev)
                     paro.paro_scale_rotate_tiled(D, hl, xd, xt, stream=stream)
                     xt_row.append(xt)
@@ -587,7 +660,7 @@ def main():
         torch.cuda.synchronize()
         us = k0.elapsed_time(k1) * 1e3 / (n_launch * launches_per_call)
         kern = {"name": {1: "decode_kernel<fused>", 2: "decode_kernel", 3: "prefill_gemm_kernel"}[path],
-                "avg_us": us, "launches": n_launch * launches_per_call,
+                "avg_us": us, "launches": n_launch * launches_per_call, "launches_per_step": launches_per_call,
                 "bytes_per_launch": per_launch_bytes / launches_per_call,
                 "flops_per_launch": per_launch_flops / launches_per_call}
 
@@ -605,38 +678,46 @@ def main():
         roofline["traffic"] = load_traffic(f"{args.workload}{gsuffix(args)}", khash)
         roofline["kernel"] = kern["name"]
         roofline["avg_launch_us"] = round(kern["avg_us"], 3)
+        roofline["launches_per_step"] = kern["launches_per_step"]
+        if not args.no_ceiling:
+            roofline["measured_ceiling"] = measured_ceiling(decode, layers, M, tdt, torch, dev, stream, ach)
 
     # ---- CPU baseline: the oracle as it stands, on a bounded sample ----
+    # decode: whole calls of every layer; prefill: the first `rows` token rows
+    # of every layer (rows are independent), one pass over all layers per round
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import ref
-        lname, I, O, host, x = layers[0]
-        rows = M if decode else min(M, 32)
-        xs = np.ascontiguousarray(x[:rows])
+        rows = M if decode else min(M, 16)
+        xs = [np.ascontiguousarray(x[:rows]) for _, _, _, _, x in layers]
         n, t_start = 0, time.perf_counter()
         while True:
-            ref.linear(host, xs, act)
+            for (lname, I, O, host, _), xr in zip(layers, xs):
+                ref.linear(host, xr, act)
             n += 1
             el = time.perf_counter() - t_start
             if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
                 break
-        per_call = el / n
+        per_round = el / n
+        names = ", ".join(l[0] for l in layers)
         if decode:
-            w_b = layer_bytes(I, O, host.krot, G=args.group)[0]
-            cval, cunit = w_b / per_call / 1e9, "GB/s"
-            sample = f"{n} full oracle calls on layer '{lname}' ({rows} token(s)), {el:.1f} s"
+            cval, cunit = weight_bytes / per_round / 1e9, "GB/s"
+            sample = f"{n} round(s) of full oracle calls on {names} ({rows} token(s)), {el:.1f} s"
         else:
-            cval, cunit = 2.0 * rows * I * O / per_call / 1e12, "TFLOP/s"
-            sample = f"{n} oracle call(s) on {rows} of {M} token rows of layer '{lname}', {el:.1f} s"
+            cval, cunit = sum(2.0 * rows * I * O for _, I, O, _, _ in layers) / per_round / 1e12, "TFLOP/s"
+            sample = f"{n} round(s) of oracle calls on the first {rows} of {M} token rows of {names}, {el:.1f} s"
         cpu = {"value": cval, "unit": cunit, "cores": ref.threads(0), "kind": "oracle", "sample": sample}
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step_p10_p50_p90": [round(p10, 6), round(p50, 6), round(p90, 6)], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if act == synth.F16 else "bf16", "data": "synthetic",
         "config": {"workload": spec["name"] + gsuffix(args), "layers": [[n, I, O] for n, I, O, _, _ in layers], "tokens": M,
                    "group_size": args.group, "krot": 8, "path": PATH_NAMES[path], "buffer_sets": nsets,
+                   "rotation_matrix": ("built once per layer (paro_rotation_matrix), applied every step"
+                                       if prepared else "built in every call" if path == 3 else None),
                    "parallelism": "single-gpu"},
         "roofline": roofline, "cpu_baseline": cpu, "kernel_sources": khash,
     }

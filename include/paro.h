@@ -40,7 +40,7 @@
  *     the host before anything is enqueued; on error nothing is launched and
  *     paro_last_error() (thread-local) describes the failure.  Launch errors
  *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
- *   - GPU limits: G = 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^22,
+ *   - GPU limits: G = 32, 64 or 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^22,
  *     O a multiple of 8 and <= 2^21, tokens <= 2^21; x, y, x_r, w_out,
  *     qweight and scales 16-byte aligned, bias 8-byte aligned, qzeros,
  *     pairs, theta and channel_scales 4-byte aligned.  Other values give
@@ -62,10 +62,16 @@ extern "C" {
 
 #define PARO_ABI_VERSION 5
 
+/* The _RANGE_MIN / _RANGE_MAX members of the two argument enums are not
+ * values to pass: they widen the enums to every int32, so that the library
+ * (C++) can receive any int a caller passes and reject it with a status code
+ * instead of holding an out-of-range enum value. */
 typedef enum {
   PARO_F16 = 0,  /* IEEE binary16 */
   PARO_BF16 = 1, /* bfloat16      */
-  PARO_F32 = 2   /* IEEE binary32 */
+  PARO_F32 = 2,  /* IEEE binary32 */
+  PARO_DTYPE_RANGE_MIN = -2147483647 - 1,
+  PARO_DTYPE_RANGE_MAX = 2147483647
 } paro_dtype;
 
 typedef enum {
@@ -87,16 +93,18 @@ typedef enum {
                                  prologue + split-K MFMA GEMV; tokens <= 16      */
   PARO_PATH_DECODE_SPLIT = 2, /* scale_rotate into the workspace, then the same
                                  GEMV reading X_r; tokens <= 16                  */
-  PARO_PATH_PREFILL = 3       /* scale_rotate into the workspace (in the GEMM's
+  PARO_PATH_PREFILL = 3,      /* scale_rotate into the workspace (in the GEMM's
                                  16-row tiled layout), then the MFMA GEMM with
                                  LDS-staged dequantized weight tiles            */
+  PARO_PATH_RANGE_MIN = -2147483647 - 1,
+  PARO_PATH_RANGE_MAX = 2147483647
 } paro_path;
 
 /* One rotated W4 linear layer: sizes plus device pointers to its tensors. */
 typedef struct {
   int64_t in_features;         /* I                                          */
   int64_t out_features;        /* O                                          */
-  int32_t group_size;          /* G (128 on the GPU; -1 means I)             */
+  int32_t group_size;          /* G (32, 64 or 128 on the GPU; -1 means I)   */
   int32_t krot;                /* number of rotation stages                  */
   const int16_t *pairs;        /* [krot][I]   local pair indices             */
   const float *theta;          /* [krot][I/2] angles (radians)               */
@@ -159,6 +167,31 @@ int paro_w4a16_linear(const paro_w4_layer *layer, const void *x, paro_dtype x_dt
 int paro_w4a16_linear_path(const paro_w4_layer *layer, const void *x, paro_dtype x_dt,
                            int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
                            size_t workspace_bytes, void *stream, paro_path path);
+
+/*
+ * paro_w4a16_linear with the layer's dense rotation built once beforehand.
+ * The rotation is a fixed linear map per 128-channel group ("ParoQuant" wiki,
+ * Concepts / Pairwise Givens rotations: the stages compose to one orthogonal
+ * map local to each group; Activation and weight transforms: D^-1 then R),
+ * so R'_g = diag(cs_g) . R_g depends on the layer alone, like the packed
+ * weight: paro_rotation_matrix(layer, x_dt, hl) builds it once, and every
+ * later call passes it here instead of rebuilding it.
+ *   hl : from paro_rotation_matrix for this layer and x_dt (I * 512 bytes,
+ *        16-byte aligned, caller-owned, not written).
+ * The path is chosen as by paro_w4a16_linear: many tokens run the PREFILL
+ * kernels (hl applied on the matrix cores, then the GEMM); up to 16 tokens
+ * run the decode kernels, which rotate stage by stage and do not read hl.
+ * Results equal paro_w4a16_linear's bit for bit.  workspace: zero-filled
+ * before first use as for paro_w4a16_linear, of
+ * paro_w4a16_linear_prepared_workspace_bytes(layer, tokens) bytes (the
+ * prefill path needs no room for the rotation matrix); it must not overlap
+ * x, y or hl.  Errors as paro_w4a16_linear, plus PARO_ERR_NULL for hl and
+ * PARO_ERR_ALIGN / _SHAPE for its alignment and overlaps.
+ */
+int paro_w4a16_linear_prepared(const paro_w4_layer *layer, const void *hl, const void *x, paro_dtype x_dt,
+                               int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                               size_t workspace_bytes, void *stream);
+size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /*
  * The quantized projection alone, over activations that are already scaled
@@ -268,15 +301,15 @@ size_t paro_w4a16_moe_linear_workspace_bytes(const paro_w4_layer *layer, int64_t
  * and RTN" wiki, quantizer: q = clamp(round(x / scale) + zero, 0, 15), range
  * including zero, symmetric midpoint zero, affine zero = round(-xmin/scale),
  * finite sentinel range for all-zero groups; Stored tensors: AWQ layout).
- * Per output row n and group g of 128 input channels, all decisions in fp32
+ * Per output row n and group g of G input channels, all decisions in fp32
  * with correctly rounded division, rounding half to even.
  *   w        : [O][I] w_dt in {F16, BF16, F32}, row-major (out_features
  *              first), 4-byte aligned (8 for F32).
  *   symmetric: nonzero = symmetric (zero point 8), 0 = affine.
- *   qweight  : [I][O/8] int32 AWQ words, qzeros [I/128][O/8] int32, scales
- *              [I/128][O] fp16 bits; caller-owned device memory that must not
- *              overlap w or each other.
- * Uses layer->in_features, out_features, group_size (128), krot, pairs, theta,
+ *   qweight  : [I][O/8] int32 AWQ words, qzeros [I/G][O/8] int32, scales
+ *              [I/G][O] fp16 bits; caller-owned device memory that must not
+ *              overlap w or each other (PARO_ERR_SHAPE otherwise).
+ * Uses layer->in_features, out_features, group_size, krot, pairs, theta,
  * channel_scales; layer->qweight/qzeros/scales/bias are ignored.  The outputs
  * plus the layer's rotation tensors form a layer for paro_w4a16_linear.
  */
@@ -308,7 +341,7 @@ int paro_w4_quantize_pack(const paro_w4_layer *layer, const void *w, paro_dtype 
  * C per group, dL/dx = g . R'^T on the matrix cores.
  * x, g and gx are 16-byte aligned; no output overlaps an input, the workspace
  * or another output.  Caller-owned device memory; enqueued on `stream`.
- * Uses layer->in_features, group_size (128), krot, pairs, theta,
+ * Uses layer->in_features, group_size, krot, pairs, theta,
  * channel_scales.  Errors: PARO_ERR_NULL, _DTYPE, _ALIGN, _SHAPE,
  * _UNSUPPORTED, _WORKSPACE, _HIP.
  */

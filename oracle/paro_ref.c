@@ -339,77 +339,81 @@ int paro_ref_scale_rotate_backward(const paro_ref_layer *L, const void *x, int x
     free(cs_tab);
     return PARO_REF_ERR_NOMEM;
   }
-  int failed = 0;
+  /* per-thread work rows, allocated before the parallel region so that every
+   * thread reaches the worksharing loop below */
+  double *work = (double *)malloc(sizeof(double) * (size_t)nt * (size_t)(krot + 2) * (size_t)I);
+  if (!work) {
+    free(acc);
+    free(cs_tab);
+    return PARO_REF_ERR_NOMEM;
+  }
 #pragma omp parallel num_threads(nt)
   {
+#ifdef _OPENMP
     const int tid = omp_get_thread_num();
+#else
+    const int tid = 0;
+#endif
     double *gth = acc + (size_t)tid * (size_t)(nang + I), *gc = gth + nang;
     /* states[t][k]: the row before stage t (states[krot] = x_r) */
-    double *states = (double *)malloc(sizeof(double) * (size_t)(krot + 1) * (size_t)I);
-    double *grad = (double *)malloc(sizeof(double) * (size_t)I);
-    if (!states || !grad) {
-#pragma omp atomic write
-      failed = 1;
-    } else {
+    double *states = work + (size_t)tid * (size_t)(krot + 2) * (size_t)I;
+    double *grad = states + (size_t)(krot + 1) * (size_t)I;
 #pragma omp for schedule(static)
-      for (int64_t m = 0; m < tokens; ++m) {
-        /* forward, keeping every intermediate row: x_s = x * cs, then the
-         * stages in order ([P1] Concepts / Pairwise Givens rotations) */
-        for (int64_t k = 0; k < I; ++k)
-          states[k] = load_elem(x, x_dt, m * I + k) * (double)L->channel_scales[k];
-        for (int t = 0; t < krot; ++t) {
-          double *in = states + (size_t)t * I, *out = states + (size_t)(t + 1) * I;
-          for (int64_t k = 0; k < I; ++k) out[k] = in[k];
-          for (int64_t gi = 0; gi < ngroups; ++gi)
-            for (int64_t p = 0; p < G / 2; ++p) {
-              const int64_t i = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p];
-              const int64_t j = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p + 1];
-              const int64_t ang = (int64_t)t * (I / 2) + gi * (G / 2) + p;
-              const double c = cs_tab[2 * ang], sn = cs_tab[2 * ang + 1];
-              out[i] = in[i] * c + in[j] * sn;
-              out[j] = -in[i] * sn + in[j] * c;
-            }
-        }
-        /* backward, stages in reverse: the chain rule through
-         *   a' = a c + b s,  b' = -a s + b c
-         * gives  dL/da = ga' c - gb' s,  dL/db = ga' s + gb' c  and, with
-         * d a'/d theta = -a s + b c = b', d b'/d theta = -a c - b s = -a',
-         *   dL/dtheta = ga' b' - gb' a'                                    */
-        for (int64_t k = 0; k < I; ++k) grad[k] = g[m * I + k];
-        for (int t = krot - 1; t >= 0; --t) {
-          const double *out = states + (size_t)(t + 1) * I;
-          for (int64_t gi = 0; gi < ngroups; ++gi)
-            for (int64_t p = 0; p < G / 2; ++p) {
-              const int64_t i = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p];
-              const int64_t j = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p + 1];
-              const int64_t ang = (int64_t)t * (I / 2) + gi * (G / 2) + p;
-              const double c = cs_tab[2 * ang], sn = cs_tab[2 * ang + 1];
-              const double ga = grad[i], gb = grad[j];
-              gth[ang] += ga * out[j] - gb * out[i];
-              grad[i] = ga * c - gb * sn;
-              grad[j] = ga * sn + gb * c;
-            }
-        }
-        /* channel scaling x_s = x * cs: dL/dx = dL/dx_s * cs, dL/dcs = dL/dx_s * x */
-        for (int64_t k = 0; k < I; ++k) {
-          const double xk = load_elem(x, x_dt, m * I + k);
-          gx[m * I + k] = grad[k] * (double)L->channel_scales[k];
-          gc[k] += grad[k] * xk;
-        }
+    for (int64_t m = 0; m < tokens; ++m) {
+      /* forward, keeping every intermediate row: x_s = x * cs, then the
+       * stages in order ([P1] Concepts / Pairwise Givens rotations) */
+      for (int64_t k = 0; k < I; ++k)
+        states[k] = load_elem(x, x_dt, m * I + k) * (double)L->channel_scales[k];
+      for (int t = 0; t < krot; ++t) {
+        double *in = states + (size_t)t * I, *out = states + (size_t)(t + 1) * I;
+        for (int64_t k = 0; k < I; ++k) out[k] = in[k];
+        for (int64_t gi = 0; gi < ngroups; ++gi)
+          for (int64_t p = 0; p < G / 2; ++p) {
+            const int64_t i = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p];
+            const int64_t j = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p + 1];
+            const int64_t ang = (int64_t)t * (I / 2) + gi * (G / 2) + p;
+            const double c = cs_tab[2 * ang], sn = cs_tab[2 * ang + 1];
+            out[i] = in[i] * c + in[j] * sn;
+            out[j] = -in[i] * sn + in[j] * c;
+          }
+      }
+      /* backward, stages in reverse: the chain rule through
+       *   a' = a c + b s,  b' = -a s + b c
+       * gives  dL/da = ga' c - gb' s,  dL/db = ga' s + gb' c  and, with
+       * d a'/d theta = -a s + b c = b', d b'/d theta = -a c - b s = -a',
+       *   dL/dtheta = ga' b' - gb' a'                                    */
+      for (int64_t k = 0; k < I; ++k) grad[k] = g[m * I + k];
+      for (int t = krot - 1; t >= 0; --t) {
+        const double *out = states + (size_t)(t + 1) * I;
+        for (int64_t gi = 0; gi < ngroups; ++gi)
+          for (int64_t p = 0; p < G / 2; ++p) {
+            const int64_t i = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p];
+            const int64_t j = gi * G + L->pairs[(int64_t)t * I + gi * G + 2 * p + 1];
+            const int64_t ang = (int64_t)t * (I / 2) + gi * (G / 2) + p;
+            const double c = cs_tab[2 * ang], sn = cs_tab[2 * ang + 1];
+            const double ga = grad[i], gb = grad[j];
+            gth[ang] += ga * out[j] - gb * out[i];
+            grad[i] = ga * c - gb * sn;
+            grad[j] = ga * sn + gb * c;
+          }
+      }
+      /* channel scaling x_s = x * cs: dL/dx = dL/dx_s * cs, dL/dcs = dL/dx_s * x */
+      for (int64_t k = 0; k < I; ++k) {
+        const double xk = load_elem(x, x_dt, m * I + k);
+        gx[m * I + k] = grad[k] * (double)L->channel_scales[k];
+        gc[k] += grad[k] * xk;
       }
     }
-    free(states);
-    free(grad);
   }
-  if (!failed)
-    for (int tid = 0; tid < nt; ++tid) {
-      const double *gth = acc + (size_t)tid * (size_t)(nang + I), *gc = gth + nang;
-      for (int64_t e = 0; e < nang; ++e) gtheta[e] += gth[e];
-      for (int64_t k = 0; k < I; ++k) gcs[k] += gc[k];
-    }
+  free(work);
+  for (int tid = 0; tid < nt; ++tid) {
+    const double *gth = acc + (size_t)tid * (size_t)(nang + I), *gc = gth + nang;
+    for (int64_t e = 0; e < nang; ++e) gtheta[e] += gth[e];
+    for (int64_t k = 0; k < I; ++k) gcs[k] += gc[k];
+  }
   free(acc);
   free(cs_tab);
-  return failed ? PARO_REF_ERR_NOMEM : PARO_REF_OK;
+  return PARO_REF_OK;
 }
 
 /* ------------------------------------------------------------------------ */

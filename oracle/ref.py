@@ -21,9 +21,10 @@ F16, BF16, F32, F64 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PAIRS, ERR_CHECK_FAILED, ERR_NOMEM = range(7)
 
 
-def build(out_path: str = LIB_PATH, src_path: str = SRC_PATH, extra=()) -> str:
-    """Compile the oracle with gcc (plain C99 + OpenMP)."""
-    cmd = ["gcc", "-std=gnu99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+def build(out_path: str = LIB_PATH, src_path: str = SRC_PATH, extra=(), openmp: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99, threaded with OpenMP unless
+    openmp is False)."""
+    cmd = ["gcc", "-std=gnu99", "-O2", *(["-fopenmp"] if openmp else []), "-fPIC", "-shared", "-Wall",
            "-I", os.path.join(ROOT, "include"), src_path, "-o", out_path, "-lm", *extra]
     subprocess.run(cmd, check=True)
     return out_path

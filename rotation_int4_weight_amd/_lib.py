@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libparo.so")
+# PARO_LIB names another build of the same library (e.g. one with host-side
+# sanitizers); by default the in-tree libparo.so is loaded.
+LIB_PATH = os.environ.get("PARO_LIB") or os.path.join(PKG, "libparo.so")
 
 F16, BF16, F32 = 0, 1, 2
 PATH_AUTO, PATH_DECODE_FUSED, PATH_DECODE_SPLIT, PATH_PREFILL = 0, 1, 2, 3
@@ -20,6 +22,7 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
           7: "PARO_ERR_WORKSPACE", 8: "PARO_ERR_HIP"}
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+           "paro_w4a16_linear_prepared", "paro_w4a16_linear_prepared_workspace_bytes",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
            "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
@@ -65,6 +68,9 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear.argtypes = [P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_linear_path.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
     lib.paro_w4a16_linear_prerotated.argtypes = [P, P, I32, I64, P, I32, P, SZ, P, I32]
+    lib.paro_w4a16_linear_prepared.argtypes = [P, P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_w4a16_linear_prepared_workspace_bytes.argtypes = [P, I64]
+    lib.paro_w4a16_linear_prepared_workspace_bytes.restype = SZ
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
     lib.paro_w4_quantize_pack.argtypes = [P, P, I32, I32, P, P, P, P]
@@ -95,7 +101,7 @@ def load(path: str | None = None):
     lib.paro_last_error.restype = ctypes.c_char_p
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
-                 "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
+                 "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated", "paro_w4a16_linear_prepared",
                  "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
                  "paro_mxfp4_quantize_weight", "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm",
                  "paro_mxfp4_linear",
@@ -222,6 +228,18 @@ def paro_w4a16_linear(layer: DeviceLayer, x, y, workspace=None, stream=None, pat
         rc = lib.paro_w4a16_linear_path(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y), ws_ptr,
                                         ws_bytes, _stream_handle(stream), path)
     _check(rc, "paro_w4a16_linear")
+
+
+def paro_w4a16_linear_prepared_workspace_bytes(layer: DeviceLayer, tokens: int) -> int:
+    return int(load().paro_w4a16_linear_prepared_workspace_bytes(layer.ref, tokens))
+
+
+def paro_w4a16_linear_prepared(layer: DeviceLayer, hl, x, y, workspace=None, stream=None) -> None:
+    """The linear with the layer's dense rotation hl prebuilt by paro_rotation_matrix (for x's dtype)."""
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_w4a16_linear_prepared(layer.ref, _ptr(hl), _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
+                                             ws_ptr, ws_bytes, _stream_handle(stream)), "paro_w4a16_linear_prepared")
 
 
 def paro_w4a16_linear_prerotated(layer: DeviceLayer, x_r, y, workspace=None, stream=None,

@@ -95,8 +95,8 @@ hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStrea
 int64_t moe_work_tiles(int64_t tokens, int experts);
 
 // W_r = W D R, group quantization and AWQ packing (the offline step):
-// w [O][I] (F16, BF16 or F32); qweight [I][O/8], qzeros [I/128][O/8],
-// scales [I/128][O] fp16.
+// w [O][I] (F16, BF16 or F32); qweight [I][O/8], qzeros [I/G][O/8],
+// scales [I/G][O] fp16 (G = group).
 hipError_t launch_quantize_pack(const void *w, int w_dt, bool sym, int64_t O, int64_t I, const int16_t *pairs,
                                 const float *theta, const float *cs, int krot, int group, int32_t *qweight,
                                 int32_t *qzeros,

@@ -112,6 +112,11 @@ int hip_fail(hipError_t e, const char *what) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+bool overlap(const void *a, size_t an, const void *b, size_t bn) {
+  const char *pa = (const char *)a, *pb = (const char *)b;
+  return an && bn && pa < pb + bn && pb < pa + an;
+}
+
 paro::LinearArgs linear_args(const paro_w4_layer *L, int64_t tokens, const void *x, paro_dtype x_dt, void *y,
                              paro_dtype y_dt) {
   paro::LinearArgs a;
@@ -309,11 +314,12 @@ int paro_w4_quantize_pack(const paro_w4_layer *L, const void *w, paro_dtype w_dt
   if (rc) return rc;
   if (!aligned(w, w_dt == PARO_F32 ? 8 : 4) || !aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2))
     return fail(PARO_ERR_ALIGN, "w must be 4-byte (8 for F32) and qweight/qzeros/scales 4/4/2-byte aligned");
-  const int64_t I = L->in_features, O = L->out_features;
+  const int64_t I = L->in_features, O = L->out_features, G = group_of(L);
   const size_t wb = (size_t)I * O * (w_dt == PARO_F32 ? 4 : 2);
   const char *ws = (const char *)w;
   const char *outs[3] = {(const char *)qweight, (const char *)qzeros, (const char *)scales};
-  const size_t outb[3] = {(size_t)I * O / 2, (size_t)(I / 128) * O / 2, (size_t)(I / 128) * O * 2};
+  // the kernel writes qzeros [I/G][O/8] int32 and scales [I/G][O] fp16
+  const size_t outb[3] = {(size_t)I * O / 2, (size_t)(I / G) * O / 2, (size_t)(I / G) * O * 2};
   for (int i = 0; i < 3; ++i) {
     if (ws < outs[i] + outb[i] && outs[i] < ws + wb) return fail(PARO_ERR_SHAPE, "an output overlaps w");
     for (int j = 0; j < i; ++j)
@@ -385,11 +391,6 @@ size_t paro_scale_rotate_backward_workspace_bytes(const paro_w4_layer *L, int64_
 namespace {
 
 constexpr int64_t kMxMaxBytes = (int64_t(1) << 31) - 1;  // 32-bit buffer offsets in the FP4 GEMM
-
-bool overlap(const void *a, size_t an, const void *b, size_t bn) {
-  const char *pa = (const char *)a, *pb = (const char *)b;
-  return an && bn && pa < pb + bn && pb < pa + an;
-}
 
 int check_mx_rows(int64_t rows, int64_t I) {
   if (rows < 0) return fail(PARO_ERR_SHAPE, "rows=%lld is negative", (long long)rows);
@@ -562,9 +563,12 @@ namespace {
 // Shared body of the linear entry points.  prerotated: x already holds X_r.
 constexpr int kMaxExperts = 1024;  // each workgroup scans the expert offsets once
 
+// hl_pre: the layer's dense rotation prebuilt by paro_rotation_matrix (for
+// x_dt), used by the prefill path instead of building it in the workspace.
 int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
                 paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream, paro_path path,
-                bool prerotated, int experts = 0, const int64_t *expert_offsets = nullptr) {
+                bool prerotated, int experts = 0, const int64_t *expert_offsets = nullptr,
+                const void *hl_pre = nullptr) {
   int rc = check_gpu_shape(L);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
@@ -598,12 +602,19 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     const size_t xb = (size_t)tokens * I * 2, yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
     if (xs < ys + yb && ys < xs + xb) return fail(PARO_ERR_SHAPE, "y overlaps x");
   }
-  const size_t need = workspace_for(L, tokens, path);
+  const bool prebuilt = hl_pre && path == PARO_PATH_PREFILL && !prerotated;
+  if (prebuilt && !aligned(hl_pre, 16)) return fail(PARO_ERR_ALIGN, "the rotation matrix must be 16-byte aligned");
+  const size_t need = prebuilt ? kCounterBytes + xr_region(L, tokens, path) : workspace_for(L, tokens, path);
   if (need > 0) {
     if (!workspace) return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
       return fail(PARO_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t xb = (size_t)tokens * I * 2, yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+    if (overlap(workspace, need, x, xb) || overlap(workspace, need, y, yb))
+      return fail(PARO_ERR_SHAPE, "the workspace overlaps x or y");
+    if (prebuilt && overlap(workspace, need, hl_pre, paro::rot_mat_bytes(I)))
+      return fail(PARO_ERR_SHAPE, "the workspace overlaps the rotation matrix");
   }
 
   paro::LinearArgs a = linear_args(L, tokens, x, x_dt, y, y_dt);
@@ -642,9 +653,13 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     e = paro::launch_retile((const uint16_t *)x, xt, tokens, I, st);
     if (e != hipSuccess) return hip_fail(e, "retile launch");
   } else {
-    uint16_t *hl = (uint16_t *)((char *)xr + xr_region(L, tokens, path));
-    e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot, a.group, hl, st);
-    if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+    const uint16_t *hl = (const uint16_t *)hl_pre;
+    if (!prebuilt) {
+      uint16_t *hw = (uint16_t *)((char *)xr + xr_region(L, tokens, path));
+      e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot, a.group, hw, st);
+      if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+      hl = hw;
+    }
     e = paro::launch_rot_apply((const uint16_t *)x, (int)x_dt, xt, tokens, I, hl, st);
     if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
   }
@@ -672,6 +687,20 @@ int paro_w4a16_linear_prerotated(const paro_w4_layer *L, const void *x_r, paro_d
 int paro_w4a16_linear(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
                       paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream) {
   return paro_w4a16_linear_path(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, PARO_PATH_AUTO);
+}
+
+int paro_w4a16_linear_prepared(const paro_w4_layer *L, const void *hl, const void *x, paro_dtype x_dt,
+                               int64_t tokens, void *y, paro_dtype y_dt, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  if (!hl) return fail(PARO_ERR_NULL, "the prebuilt rotation matrix is required");
+  return linear_impl(L, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream, PARO_PATH_AUTO, false, 0,
+                     nullptr, hl);
+}
+
+size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
+  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
+  const paro_path path = auto_path(tokens);
+  return path == PARO_PATH_PREFILL ? kCounterBytes + xr_region(L, tokens, path) : workspace_for(L, tokens, path);
 }
 
 int paro_w4a16_moe_linear(const paro_w4_layer *L, int num_experts, const int64_t *expert_offsets, const void *x,

@@ -54,7 +54,6 @@ namespace paro {
 
 constexpr int kBM = 256, kBN = 128, kBK = 32;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
-constexpr int kStepsPerGroup = kG / kBK;
 constexpr int kBStride = kBK + 8;  // halves per LDS column (80 bytes: 16-byte aligned fragment reads)
 constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k steps)
 constexpr int kWordRing = 8;        // packed weight words in flight per producer thread (steps)
@@ -310,12 +309,19 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       __builtin_amdgcn_sched_barrier(0);  // one expansion's temporaries live at a time
     }
     __syncthreads();
+    // The consumers read tile 0 (slot 0) after that barrier, and super-step 0
+    // below rewrites slot 0 with step 8: a second barrier, which they pass
+    // once their reads of tile 0 have landed, keeps the two apart.  (From
+    // super-step 1 on, a slot's previous tile was read a whole super-step
+    // earlier.)
+    __syncthreads();
 
     // Super-step S (the consumers' steps 4S..4S+3): expand steps 4S+5..4S+8
     // into tiles (4S+5..4S+8) % 8.  Their first reader runs in super-step
     // S+1, after the barrier that ends S.  Their slots' previous tiles
-    // (4S-3..4S) were last read in super-step S-1, and the consumers wait for
-    // their own LDS reads before each barrier.  Each word slot is refilled
+    // (4S-3..4S) were last read in super-step S-1 (tile 0: before the extra
+    // barrier above), and the consumers wait for their own LDS reads before
+    // each barrier.  Each word slot is refilled
     // kWordRing steps ahead.  Past the end everything runs on clamped,
     // in-bounds addresses into tiles no consumer uses.  kk: parity of S in a
     // two-super-step iteration, so that the ring slots (4kk+5+u) % 8 are
@@ -376,6 +382,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_frag(0, j, bf[j]);
+  // tile 0's slot is rewritten in the producer's first super-step
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
   // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at

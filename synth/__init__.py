@@ -75,8 +75,9 @@ def rng_for(workload: int, layer: int, tensor: str, base: int = 0) -> np.random.
 
 def f32_to_bf16_bits(a) -> np.ndarray:
     """bf16 bit patterns of fp32 values, round to nearest even (finite inputs)."""
-    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    # in 32 bits: the largest finite pattern, 0xFF7FFFFF, plus 0x8000 fits
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return b.astype(np.uint16)
 
 

@@ -17,7 +17,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-@functools.lru_cache(maxsize=8)
+@functools.lru_cache(maxsize=16)
 def workload(cfg: int, li: int = 0):
     spec = synth.WORKLOADS[cfg]
     lname, I, O = spec["layers"][li]
@@ -53,6 +53,25 @@ def sample_rows(M, n=48, seed=0):
         return np.arange(M)
     r = np.random.default_rng(seed).choice(np.arange(1, M - 1), size=n - 2, replace=False)
     return np.unique(np.concatenate([[0, M - 1], r]))
+
+
+def stratified_rows(M, per_tile=3, seed=0, tile=256):
+    """Rows that cover every `tile`-row block of M (the prefill GEMM's M tile)
+    with `per_tile` rows each, whose residues mod 16 (the row inside an MFMA
+    fragment) run through 0..15 in turn across the sample, plus rows 0 and
+    M - 1.  Each row sits in a seeded random 16-row block of its tile."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    n = 0
+    for t0 in range(0, M, tile):
+        span = min(tile, M - t0)
+        for _ in range(per_tile):
+            res = n % 16
+            n += 1
+            blocks = [b for b in range((span + 15) // 16) if t0 + 16 * b + res < M]
+            if blocks:
+                rows.add(t0 + 16 * int(rng.choice(blocks)) + res)
+    return np.array(sorted(rows))
 
 
 def bits_to_f64(bits, dt):

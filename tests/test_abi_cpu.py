@@ -240,6 +240,12 @@ def test_quantize_pack_argument_checks():
     assert call(qz=FAKE + 64) == 2                # qzeros inside qweight
     assert call(L=fake_layer(I=256, O=64, G=16)) == 5
     assert call(L=fake_layer(I=256, O=64, pairs=0)) == 1
+    # G = 32: qzeros [I/32][O/8] int32 = 8 * 8 * 4 = 256 bytes, so scales
+    # starting 128 bytes into them overlap (with I/128 groups, 64 bytes, they
+    # would not); and scales [I/32][O] fp16 = 1 KB reach a buffer 512 bytes on
+    g32 = fake_layer(I=256, O=64, G=32)
+    assert call(L=g32, sc=FAKE + qz_off + 128) == 2, _lib.paro_last_error()
+    assert call(L=g32, sc=FAKE * 8 - 512, w=FAKE * 8) == 2, _lib.paro_last_error()
 
 
 @needs_no_gpu

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import synth
-from _helpers import (LIN_TOL, ROT_TOL, U, bits_to_f64, sample_rows, say, to_host_bits,
+from _helpers import (LIN_TOL, ROT_TOL, U, bits_to_f64, sample_rows, say, stratified_rows, to_host_bits,
                       torch_dtype, workload, x_to_device)
 from oracle import ref
 
@@ -78,9 +78,12 @@ def check_linear(L, x, dt, path, rows=None, label=""):
 # unpack + dequant
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
-def test_unpack_dequant_bitexact(cfg):
-    lname, L, x, dt = workload(cfg)
+UNPACK_CASES = [(0, 0), (1, 0), (2, 0), (3, 0)] + [(4, li) for li in range(7)]
+
+
+@pytest.mark.parametrize("cfg,li", UNPACK_CASES)
+def test_unpack_dequant_bitexact(cfg, li):
+    lname, L, x, dt = workload(cfg, li)
     I, O = L.in_features, L.out_features
     say(f"unpack_dequant cfg{cfg} {lname} I={I} O={O}")
     D = paro.DeviceLayer(L)
@@ -193,13 +196,44 @@ def test_identity_state_rotation_is_exact():
                                       (3, "prefill")])
 def test_linear_workloads(cfg, path):
     lname, L, x, dt = workload(cfg)
-    check_linear(L, x, dt, path, sample_rows(x.shape[0], 48, seed=cfg), f"cfg{cfg} {lname}")
+    # prefill at full size: rows in every 256-row M tile, all residues mod 16
+    rows = stratified_rows(x.shape[0], 4, seed=cfg) if path == "prefill" else sample_rows(x.shape[0], 48, seed=cfg)
+    check_linear(L, x, dt, path, rows, f"cfg{cfg} {lname}")
 
 
 @pytest.mark.parametrize("li", range(7))
 def test_linear_decoder_layer_prefill(li):
     lname, L, x, dt = workload(4, li)
-    check_linear(L, x, dt, "prefill", sample_rows(x.shape[0], 24, seed=40 + li), f"cfg4 {lname}")
+    check_linear(L, x, dt, "prefill", stratified_rows(x.shape[0], 3, seed=40 + li), f"cfg4 {lname}")
+
+
+def tiled_rows_of(bits, M, I, rows):
+    """Rows `rows` of a tiled X_r buffer (layout of include/paro.h), row-major."""
+    a = np.asarray(bits).reshape((M + 15) // 16, I // 32, 4, 16, 8)
+    return np.stack([a[r // 16, :, :, r % 16, :].reshape(I) for r in rows])
+
+
+@pytest.mark.parametrize("cfg,li", [(3, 0)] + [(4, li) for li in range(7)])
+def test_dense_rotation_full_size(cfg, li):
+    """The prefill rotation as the linear runs it (dense H + L on the matrix
+    cores, the full token count, so the launch takes the large-workgroup
+    row split) meets the rotated-activation gate on stratified rows."""
+    lname, L, x, dt = workload(cfg, li)
+    M, I = x.shape
+    say(f"dense rotation cfg{cfg} {lname} I={I} M={M}")
+    D = paro.DeviceLayer(L)
+    xd = x_to_device(x, dt)
+    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
+    xt = torch.full((paro.paro_tiled_bytes(D, M) // 2,), -1, dtype=torch.int16, device="cuda")
+    paro.paro_scale_rotate_tiled(D, hl, xd, xt)
+    torch.cuda.synchronize()
+    rows = stratified_rows(M, 3, seed=60 + 7 * cfg + li)
+    got = bits_to_f64(tiled_rows_of(xt.cpu().numpy().view(np.uint16), M, I, rows), dt)
+    want = ref.scale_rotate(L, np.ascontiguousarray(x[rows]), dt)
+    err = np.abs(got - want).max(axis=1) / np.abs(want).max(axis=1)
+    say(f"  worst row max|dX_r|/max|X_r| = {float(err.max()):.3e}")
+    assert float(err.max()) <= ROT_TOL + U[dt]
 
 
 # ---------------------------------------------------------------------------

@@ -755,3 +755,84 @@ def test_mxfp4_round_trip_of_canonical_blocks():
     # -0 (code 8) is stored as +0: compare the values they stand for
     assert np.array_equal(s2, scales)
     assert np.array_equal(ref.mxfp4_dequant(c2, s2), back)
+
+
+def e2m1_decode_by_hand(codes, scales):
+    """Values of MXFP4 rows from the format's definition (not the oracle's
+    dequant): element 2j is the low nibble of byte j, bit 3 of a nibble is
+    the sign and bits 0..2 index the E2M1 magnitudes; block b of 32 elements
+    is scaled by 2^(scales[b] - 127)."""
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((rows, K))
+    for r in range(rows):
+        for e in range(K):
+            nib = (int(codes[r, e // 2]) >> (4 * (e % 2))) & 15
+            mag = E2M1_VALUES[nib & 7]
+            out[r, e] = (-mag if nib & 8 else mag) * 2.0 ** (int(scales[r, e // 32]) - 127)
+    return out
+
+
+def mx_row(K, entries, scales):
+    """codes and scales of one MXFP4 row with nibble `code` at element e."""
+    codes = np.zeros(K // 2, dtype=np.uint8)
+    for e, code in entries.items():
+        codes[e // 2] |= code << (4 * (e % 2))
+    return codes, np.asarray(scales, dtype=np.uint8)
+
+
+def test_mxfp4_matmul_worked_one_block():
+    """A (1 x 32): 6 (code 7) and -1.5 (code 11) at elements 0, 1, scale byte
+    128 (x2): 12 and -3.  W (1 x 32): 0.5 (code 1) and 3 (code 5), scale 126
+    (x0.5): 0.25 and 1.5.  y = 12 * 0.25 - 3 * 1.5 = -1.5, plus the fp16 bias
+    1.0 (0x3C00): -0.5."""
+    ac, as_ = mx_row(32, {0: 7, 1: 11}, [128])
+    wc, ws = mx_row(32, {0: 1, 1: 5}, [126])
+    y = ref.mxfp4_matmul(ac[None], as_[None], wc[None], ws[None], np.array([0x3C00], np.uint16))
+    assert y.shape == (1, 1) and y[0, 0] == -0.5
+    assert ref.mxfp4_matmul(ac[None], as_[None], wc[None], ws[None])[0, 0] == -1.5
+
+
+def test_mxfp4_matmul_worked_two_by_two():
+    """Two rows and two blocks each, so that a transposed product, a swapped
+    block scale or a dropped bias all change the result.
+      A row 0: 1.0 at k=0 (code 2, block scale 127), 1.0 at k=32 (code 2,
+               block scale 129: x4)                    -> 1 at k=0, 4 at k=32
+      A row 1: -2.0 at k=1 (code 12, scale 126: x0.5)  -> -1 at k=1
+      W row 0: 0.5 at k=0 (code 1, scale 127), 6 at k=32 (code 7, scale 125:
+               x0.25)                                   -> 0.5 at k=0, 1.5 at k=32
+      W row 1: 4 at k=1 (code 6, scale 128: x2), -1 at k=32 (code 10, scale
+               127)                                     -> 8 at k=1, -1 at k=32
+    A . W^T = [[1*0.5 + 4*1.5, 4*-1], [0, -1*8]] = [[6.5, -4], [0, -8]];
+    bias fp16 (0.25, -2) = (0x3400, 0xC000) -> [[6.75, -6], [0.25, -10]]."""
+    a0 = mx_row(64, {0: 2, 32: 2}, [127, 129])
+    a1 = mx_row(64, {1: 12}, [126, 127])
+    w0 = mx_row(64, {0: 1, 32: 7}, [127, 125])
+    w1 = mx_row(64, {1: 6, 32: 10}, [128, 127])
+    ac, as_ = np.stack([a0[0], a1[0]]), np.stack([a0[1], a1[1]])
+    wc, ws = np.stack([w0[0], w1[0]]), np.stack([w0[1], w1[1]])
+    y = ref.mxfp4_matmul(ac, as_, wc, ws, np.array([0x3400, 0xC000], np.uint16))
+    assert np.array_equal(y, np.array([[6.75, -6.0], [0.25, -10.0]]))
+
+
+def test_mxfp4_matmul_brute_force():
+    """Random codes and scales: a triple loop over values decoded by hand from
+    the format equals the oracle's product (powers of two times E2M1 values
+    multiply exactly; only the order of the fp64 sums differs)."""
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 5, 64
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    as_ = rng.integers(120, 135, size=(M, K // 32), dtype=np.uint8)
+    ws = rng.integers(120, 135, size=(N, K // 32), dtype=np.uint8)
+    bias = np.array([0x3C00, 0xBC00, 0x0000, 0x4000, 0x3555], np.uint16)  # 1, -1, 0, 2, 0.333...
+    bias_v = [1.0, -1.0, 0.0, 2.0, 1365.0 / 4096]                          # 0x3555 = 1.3330078125 / 4
+    a, w = e2m1_decode_by_hand(ac, as_), e2m1_decode_by_hand(wc, ws)
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            s = 0.0
+            for k in range(K):
+                s += a[m, k] * w[n, k]
+            want[m, n] = s + bias_v[n]
+    got = ref.mxfp4_matmul(ac, as_, wc, ws, bias)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-13 * np.abs(want).max())

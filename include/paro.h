@@ -194,6 +194,31 @@ int paro_w4a16_linear_prepared(const paro_w4_layer *layer, const void *hl, const
 size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /*
+ * paro_w4a16_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation with no workspace argument.  The
+ * library holds the workspace itself, one device array of 64 MiB per GPU
+ * (PARO_NOALLOC_SCRATCH_BYTES), kept until the process ends; the call makes
+ * no allocation of any kind.  Results equal paro_w4a16_linear's bit for bit.
+ *   - Shapes whose workspace (paro_w4a16_linear_workspace_bytes for the
+ *     AUTO path) exceeds the scratch give PARO_ERR_UNSUPPORTED, with nothing
+ *     launched: e.g. 4096 tokens of a 14336-channel input (117 MB of rotated
+ *     activations).  Up to 16 tokens every supported layer fits.
+ *   - The first call on a device sets its scratch up (its address, and a
+ *     fill kernel on `stream` that zeroes the split-K counters); it must not
+ *     be made under graph capture (PARO_ERR_UNSUPPORTED).  Later calls may
+ *     be captured.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (different streams, or graphs replayed concurrently)
+ *     race and give wrong results.  The scratch keeps the last call's
+ *     contents; its split-K counters are left zero by every completed call.
+ * Other arguments and errors as paro_w4a16_linear.
+ */
+#define PARO_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paro_w4a16_linear_noalloc(const paro_w4_layer *layer, const void *x, paro_dtype x_dt, int64_t tokens,
+                              void *y, paro_dtype y_dt, void *stream);
+
+/*
  * The quantized projection alone, over activations that are already scaled
  * and rotated (x_r, e.g. from paro_scale_rotate with xr_dt == x_dt):
  *   y[m][n] = sum_k x_r[m][k] * (q[k][n] - z[k/G][n]) * s[k/G][n] + bias[n].

@@ -23,6 +23,7 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
            "paro_w4a16_linear_prepared", "paro_w4a16_linear_prepared_workspace_bytes",
+           "paro_w4a16_linear_noalloc",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
            "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
@@ -71,6 +72,7 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear_prepared.argtypes = [P, P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_linear_prepared_workspace_bytes.argtypes = [P, I64]
     lib.paro_w4a16_linear_prepared_workspace_bytes.restype = SZ
+    lib.paro_w4a16_linear_noalloc.argtypes = [P, P, I32, I64, P, I32, P]
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
     lib.paro_w4_quantize_pack.argtypes = [P, P, I32, I32, P, P, P, P]
@@ -102,6 +104,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated", "paro_w4a16_linear_prepared",
+                 "paro_w4a16_linear_noalloc",
                  "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
                  "paro_mxfp4_quantize_weight", "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm",
                  "paro_mxfp4_linear",
@@ -240,6 +243,12 @@ def paro_w4a16_linear_prepared(layer: DeviceLayer, hl, x, y, workspace=None, str
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().paro_w4a16_linear_prepared(layer.ref, _ptr(hl), _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
                                              ws_ptr, ws_bytes, _stream_handle(stream)), "paro_w4a16_linear_prepared")
+
+
+def paro_w4a16_linear_noalloc(layer: DeviceLayer, x, y, stream=None) -> None:
+    """The linear with the library-held workspace (no allocation in the call)."""
+    _check(load().paro_w4a16_linear_noalloc(layer.ref, _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
+                                            _stream_handle(stream)), "paro_w4a16_linear_noalloc")
 
 
 def paro_w4a16_linear_prerotated(layer: DeviceLayer, x_r, y, workspace=None, stream=None,

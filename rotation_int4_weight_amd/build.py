@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build", "paro")
 LIB = os.path.join(PKG, "libparo.so")
 ARCH = "gfx950"
 
-SOURCES = ["paro_abi.cpp", "scale_rotate.hip", "unpack_dequant.hip", "decode.hip", "prefill.hip", "quantize.hip", "rotate_backward.hip", "mxfp4.hip"]
+SOURCES = ["paro_abi.cpp", "scale_rotate.hip", "unpack_dequant.hip", "decode.hip", "prefill.hip", "quantize.hip", "rotate_backward.hip", "mxfp4.hip", "noalloc.hip"]
 
 # Packed-FP32 instructions are switched off for all device code: hipcc would
 # otherwise form v_pk_{add,mul,fma}_f32 from scalar float code.

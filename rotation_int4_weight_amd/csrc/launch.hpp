@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "paro.h"
+
 namespace paro {
 
 // `group`: the rotation / quantization group size G (32, 64 or 128); the
@@ -120,5 +122,14 @@ hipError_t launch_mx_quantize_weight(const void *w, int dt, int64_t rows, int64_
 // y [M][N] = A . W^T (+ bias) on the block-scaled FP4 matrix cores.
 hipError_t launch_mx_gemm(const uint8_t *ac, const uint8_t *as, int64_t M, const uint8_t *wc, const uint8_t *ws,
                           int64_t N, int64_t K, const uint16_t *bias, void *y, int y_dt, hipStream_t st);
+
+// The allocation-free linear's scratch (noalloc.hip): one device array of
+// kNoallocScratchBytes per GPU, held until the process ends.  noalloc_scratch
+// returns the address of the stream's device's copy, setting it up on the
+// first call on that device (hipGetSymbolAddress with the device current,
+// then the first zero_bytes cleared by a fill kernel on `st`); that first call
+// must not be made under graph capture (hipErrorStreamCaptureUnsupported).
+constexpr size_t kNoallocScratchBytes = PARO_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t st, size_t zero_bytes, void **ptr);
 
 }  // namespace paro

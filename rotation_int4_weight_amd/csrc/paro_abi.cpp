@@ -697,6 +697,29 @@ int paro_w4a16_linear_prepared(const paro_w4_layer *L, const void *hl, const voi
                      nullptr, hl);
 }
 
+int paro_w4a16_linear_noalloc(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                              paro_dtype y_dt, void *stream) {
+  // the same checks as the workspace variant first, so that a bad call
+  // touches no device state
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  if (tokens == 0) return ok();
+  const size_t need = workspace_for(L, tokens, auto_path(tokens));
+  if (need > paro::kNoallocScratchBytes)
+    return fail(PARO_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of workspace; the allocation-free linear holds %zu "
+                "(use paro_w4a16_linear with a caller workspace)",
+                need, paro::kNoallocScratchBytes);
+  void *scratch = nullptr;
+  const hipError_t e = paro::noalloc_scratch((hipStream_t)stream, kCounterBytes, &scratch);
+  if (e == hipErrorStreamCaptureUnsupported)
+    return fail(PARO_ERR_UNSUPPORTED, "the first allocation-free call on a device must not be graph-captured");
+  if (e != hipSuccess) return hip_fail(e, "allocation-free scratch set-up");
+  return linear_impl(L, x, x_dt, tokens, y, y_dt, scratch, paro::kNoallocScratchBytes, stream, PARO_PATH_AUTO,
+                     false);
+}
+
 size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
   if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
   const paro_path path = auto_path(tokens);

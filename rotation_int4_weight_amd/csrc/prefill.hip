@@ -46,13 +46,16 @@
 //     reads about five times the cycles of 72-byte columns read as two
 //     8-byte halves, with no measurable change in the kernel's time: LDS is
 //     not what bounds it.)
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
 
 namespace paro {
 
-constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kBM = 256, kBN = 128, kBK = 32;  // kBM: the MoE grouped GEMM's rows per tile
+constexpr int kCUs = 256;                       // compute units of an MI355X
 constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
 constexpr int kBStride = kBK + 8;  // halves per LDS column (80 bytes: 16-byte aligned fragment reads)
 constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k steps)
@@ -170,9 +173,15 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
 // row: rows of neighbouring experts in its tiles are computed and dropped.
 // Offsets are clamped into [0, tokens] and made nondecreasing, so no offsets
 // can take a workgroup outside its buffers.
-template <int DT, int GK, bool MOE>
+// RT: 16-row tiles per consumer wave, so the workgroup tile is BM = 64 RT
+// rows: 4 (256 rows) by default, 2 (128 rows) for dense layers whose
+// 256-row grid would leave CUs idle (each weight tile then serves half as
+// many MFMAs, and twice as many workgroups fill the chip).
+template <int DT, int GK, bool MOE, int RT>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
+  static_assert(RT == 4 || (RT == 2 && !MOE), "256-row tiles, or 128-row tiles for dense layers");
+  constexpr int BM = 64 * RT;
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
   __shared__ __attribute__((aligned(16))) float stage[4][32 * kStageRS];  // epilogue, one per consumer wave
   const int lane = lane_id(), wave = wave_id();
@@ -182,7 +191,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // moves them (computed with VALU division) to scalar registers so that the
   // buffer descriptors derived from them stay scalar too.
   const int n_tiles = (int)((O + kBN - 1) / kBN);
-  const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + kBM - 1) / kBM);
+  const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + BM - 1) / BM);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
   // Dense layers: logical tiles go in groups of kGroupM M blocks, the M block
   // fastest, so an XCD's share of consecutive tiles spans kGroupM blocks of
@@ -230,7 +239,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     scales += (int64_t)e * (I / G) * O;
     if (bias) bias += (int64_t)e * O;
   } else {
-    mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * kBM;
+    mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM;
   }
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
   const int nsteps = (int)(I / kBK), ngroups = (int)(I / (kBK * GK));
@@ -238,7 +247,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
   // the (16-row padded) tiled buffer; later ones read as zeros.
   const int64_t rtiles = (row_hi + 15) / 16 - mb / 16;
-  const int tiles = (int)(rtiles < kBM / 16 ? rtiles : kBM / 16);
+  const int tiles = (int)(rtiles < BM / 16 ? rtiles : BM / 16);
   const uint32_t tile_bytes = (uint32_t)nsteps * 1024u;  // one row tile over all of k
   const uint32_t a_bytes = (uint32_t)tiles * tile_bytes;
   const char *a_base = reinterpret_cast<const char *>(xt + (mb / 16) * (I / 32) * 512);
@@ -348,13 +357,13 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 
   // ------------------------------ consumer ------------------------------
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // lane row / k block of each 16 x 32 fragment
-  uint32_t a_off[4];
+  uint32_t a_off[RT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (uint32_t)(wave * 4 + i) * tile_bytes + (uint32_t)lane * 16u;
-  auto load_a = [&](int step, u32x4 af[4]) {
+  for (int i = 0; i < RT; ++i) a_off[i] = (uint32_t)(wave * RT + i) * tile_bytes + (uint32_t)lane * 16u;
+  auto load_a = [&](int step, u32x4 af[RT]) {
     const __amdgpu_buffer_rsrc_t r = a_rsrc(step);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
+    for (int i = 0; i < RT; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
   };
   // B fragment of column tile j of one k step: column 16j + fr, k
   // block fk (physical block (fk/8) ^ (j&3)), one 16-byte LDS read.
@@ -368,12 +377,12 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     b = *reinterpret_cast<const u32x4 *>(col);
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[RT][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ab[kASlots][4], bf[8];
+  u32x4 ab[kASlots][RT], bf[8];
 #pragma unroll
   for (int k = 0; k < kASlots; ++k) load_a(k, ab[k]);
   __syncthreads();
@@ -394,12 +403,12 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // super-step).  Halving the barriers of a two-step super-step measured
   // 202 -> 197.5 us at 2048 x 14336 -> 4096.  The scheduling barriers keep each refill after the
   // MFMAs that read the old fragment (an MFMA reads its sources when issued).
-  auto cstep = [&](int step, u32x4(&A)[4], bool barrier) {
+  auto cstep = [&](int step, u32x4(&A)[RT], bool barrier) {
     const int next = (step + 1) % kTiles;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
+      for (int i = 0; i < RT; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       read_frag(next, j, bf[j]);
     }
@@ -418,16 +427,16 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __builtin_amdgcn_s_setprio(0);
   mfma_drain();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
 
-  // Epilogue.  Each consumer wave stages its 64 x 128 fp32 tile through its
+  // Epilogue.  Each consumer wave stages its 16 RT x 128 fp32 tile through its
   // own LDS region, 32 rows at a time; a lane then holds 4 consecutive columns
   // of one row: bias added in fp32, one rounding, one 8-byte store (16 bytes
   // for fp32 output), so every row's 128 columns leave as whole cache lines.
   float *stg = stage[wave];
-  const int64_t m0 = mb + wave * 64;
+  const int64_t m0 = mb + wave * 16 * RT;
   const int sc = (lane & 31) * 4, srow = lane >> 5;  // quad column, row parity of this lane
   const int64_t n = n0 + sc;
   const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
@@ -438,7 +447,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
                   f16_bits_to_f32(bb[1] >> 16)};
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < RT / 2; ++p) {
     // D of tile (i, j): row 16i + 4(lane/16) + r, column 16j + lane%16
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
@@ -467,19 +476,33 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   }
 }
 
-template <int GK, bool MOE>
+template <int GK, bool MOE, int RT>
 static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
   if (a.x_dt == kF16)
-    hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK, MOE>), grid, dim3(kThreads), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK, MOE, RT>), grid, dim3(kThreads), 0, st, a, x);
   else
-    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16, GK, MOE>), grid, dim3(kThreads), 0, st, a, x);
+    hipLaunchKernelGGL((prefill_gemm_kernel<kBF16, GK, MOE, RT>), grid, dim3(kThreads), 0, st, a, x);
 }
 
-template <bool MOE>
+template <bool MOE, int RT>
 static void launch_prefill_moe(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
-  if (a.group == 32) launch_prefill_gk<1, MOE>(a, x, grid, st);
-  else if (a.group == 64) launch_prefill_gk<2, MOE>(a, x, grid, st);
-  else launch_prefill_gk<4, MOE>(a, x, grid, st);
+  if (a.group == 32) launch_prefill_gk<1, MOE, RT>(a, x, grid, st);
+  else if (a.group == 64) launch_prefill_gk<2, MOE, RT>(a, x, grid, st);
+  else launch_prefill_gk<4, MOE, RT>(a, x, grid, st);
+}
+
+// Rows per workgroup tile of a dense layer: 256, or 128 when a 256-row
+// grid would not give every CU a workgroup (k_proj / v_proj of Llama-3-8B at
+// 4096 tokens: 16 x 8 = 128 workgroups of 256 rows on 256 CUs).
+// PARO_PREFILL_BM=128|256 forces one (tuning), read once per process.
+static int dense_tile_rows(int64_t tokens, int64_t n_tiles) {
+  static const int forced = [] {
+    const char *v = getenv("PARO_PREFILL_BM");
+    const int n = (v && *v) ? atoi(v) : 0;
+    return (n == 128 || n == 256) ? n : 0;
+  }();
+  if (forced) return forced;
+  return ((tokens + 255) / 256) * n_tiles < kCUs ? 128 : 256;
 }
 
 int64_t moe_work_tiles(int64_t tokens, int experts) {
@@ -490,9 +513,13 @@ int64_t moe_work_tiles(int64_t tokens, int experts) {
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
   const int64_t n_tiles = (a.O + kBN - 1) / kBN;
   if (a.experts > 0) {
-    launch_prefill_moe<true>(a, x, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
+    launch_prefill_moe<true, 4>(a, x, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
   } else {
-    launch_prefill_moe<false>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + kBM - 1) / kBM))), st);
+    const int bm = dense_tile_rows(a.tokens, n_tiles);
+    if (bm == 128)
+      launch_prefill_moe<false, 2>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + 127) / 128))), st);
+    else
+      launch_prefill_moe<false, 4>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + 255) / 256))), st);
   }
   return hipGetLastError();
 }

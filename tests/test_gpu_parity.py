@@ -487,3 +487,32 @@ def test_split_k_handoff_alternating_inputs(I, O, M, path):
     torch.cuda.synchronize()
     for i, yi in enumerate(ys):
         assert torch.equal(yi.view(torch.int32), outs[i % 2][1].view(torch.int32)), f"call {i} differs"
+
+
+@pytest.mark.parametrize("cfg,li", [(0, 0), (1, 0), (2, 0), (3, 0), (4, 1), ("edge", 0)])
+def test_prepared_linear_matches_linear(cfg, li):
+    """paro_w4a16_linear_prepared with the layer's rotation matrix built once
+    == paro_w4a16_linear, bit for bit, on every path the shape selects, and
+    the matrix stays usable for later calls (it is read, never written)."""
+    if cfg == "edge":
+        L = synth.make_layer(208, 0, 640, 1000)
+        x = synth.make_x(208, 0, 300, 640, synth.BF16)
+        dt = synth.BF16
+    else:
+        _, L, x, dt = workload(cfg, li)
+    M, I, O = x.shape[0], L.in_features, L.out_features
+    say(f"prepared linear cfg={cfg} layer={li} I={I} O={O} M={M}")
+    D = paro.DeviceLayer(L)
+    xd = x_to_device(x, dt)
+    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
+    hl0 = hl.clone()
+    ws = paro.make_workspace(paro.paro_w4a16_linear_prepared_workspace_bytes(D, M))
+    for ydt in (synth.F32, dt):
+        ref_y = to_host_bits(run_linear(D, xd, O, ydt, 0))
+        for _ in range(2):
+            y = torch.full((M, O), float("nan"), dtype=torch_dtype(ydt), device="cuda")
+            paro.paro_w4a16_linear_prepared(D, hl, xd, y, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host_bits(y).view(np.uint8), ref_y.view(np.uint8))
+    assert torch.equal(hl, hl0)

@@ -41,7 +41,13 @@
  *     paro_last_error() (thread-local) describes the failure.  Launch errors
  *     map to PARO_ERR_HIP.  No C++ exception crosses the ABI.
  *   - GPU limits: G = 32, 64 or 128, 1 <= krot <= 64, I a multiple of 128 and <= 2^22,
- *     O a multiple of 8 and <= 2^21, tokens <= 2^21; x, y, x_r, w_out,
+ *     O a multiple of 8 and <= 2^21, tokens <= 2^21.  G = -1 (or G = I: one
+ *     rotation and quantization group over the whole row; Concepts / Pairwise
+ *     Givens rotations) is taken by paro_scale_rotate, the linear on its
+ *     DECODE_SPLIT and PREFILL paths (AUTO picks them), the allocation-free
+ *     linear, paro_w4a16_linear_prerotated / _tiled and
+ *     paro_w4_unpack_dequant, with I <= 16384 (whole rows are staged in LDS);
+ *     the other entry points return PARO_ERR_UNSUPPORTED for it.  x, y, x_r, w_out,
  *     qweight and scales 16-byte aligned, bias 8-byte aligned, qzeros,
  *     pairs, theta and channel_scales 4-byte aligned.  Other values give
  *     PARO_ERR_UNSUPPORTED / _SHAPE / _ALIGN.
@@ -104,7 +110,7 @@ typedef enum {
 typedef struct {
   int64_t in_features;         /* I                                          */
   int64_t out_features;        /* O                                          */
-  int32_t group_size;          /* G (32, 64 or 128 on the GPU; -1 means I)   */
+  int32_t group_size;          /* G (32, 64, 128 or -1 = I on the GPU)       */
   int32_t krot;                /* number of rotation stages                  */
   const int16_t *pairs;        /* [krot][I]   local pair indices             */
   const float *theta;          /* [krot][I/2] angles (radians)               */

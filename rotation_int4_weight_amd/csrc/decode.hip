@@ -205,8 +205,12 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
 
   if (nk > 0) {
     // 128-channel rotation blocks hold 4 k-steps; quantization groups hold
-    // G/32 = 1 << gsh (with G < 128 the plan gives each wave one k-step)
-    const int gsh = __builtin_ctz((unsigned)a.group) - 5, gmask = kG - a.group;
+    // G/32 = 1 << gsh (with G < 128 the plan gives each wave one k-step).  One
+    // group over the whole row (G = I > 128, any multiple of 128): a shift
+    // past every k-step, so all fall in group 0 and each wave folds once, at
+    // its last k-step (its rotation ran in a separate pass).
+    const bool row_group = a.group == I && a.group > kG;
+    const int gsh = row_group ? 30 : __builtin_ctz((unsigned)a.group) - 5, gmask = kG - a.group;
     const int64_t g_first = ks0 / 4, q_first = ks0 >> gsh, nq = I / a.group;
     float *xs = smem + wave * (MT * kDecodeRS);  // fused rotation rows of this wave
     // ---- fused: the first group's rotation inputs, before the weight stream ----

@@ -19,6 +19,17 @@ hipError_t launch_scale_rotate(const uint16_t *x, int x_dt, void *xr, int xr_dt,
                                const int16_t *pairs, const float *theta, const float *cs, int krot, int group,
                                hipStream_t st);
 
+// One rotation group over the whole row (G = I): scaled rows staged in LDS
+// (full_row_rows(I) rows per workgroup, R * I * 4 <= kFullRowLdsBytes), the
+// stages applied across the workgroup.  tiled: output in the prefill GEMM's
+// tiled layout (activation dtype, pad rows zero); else row-major in xr_dt.
+constexpr int64_t kFullRowLdsBytes = 65536;
+constexpr int64_t kMaxFullRowDim = kFullRowLdsBytes / 4;  // I <= 16384
+int full_row_rows(int64_t I);
+hipError_t launch_scale_rotate_full(const uint16_t *x, int x_dt, void *xr, int xr_dt, bool tiled, int64_t tokens,
+                                    int64_t I, const int16_t *pairs, const float *theta, const float *cs, int krot,
+                                    hipStream_t st);
+
 hipError_t launch_unpack_dequant(const int32_t *qweight, const int32_t *qzeros, const uint16_t *scales,
                                  int64_t I, int64_t O, int64_t G, uint8_t *q_out, uint8_t *z_out,
                                  void *w_out, int w_dt, hipStream_t st);
@@ -27,7 +38,7 @@ hipError_t launch_unpack_dequant(const int32_t *qweight, const int32_t *qzeros, 
 struct LinearArgs {
   int64_t I, O, tokens;
   int krot;
-  int group;  // G: 32, 64 or 128 (rotation pairs and quantization groups)
+  int group;  // G: 32, 64 or 128 (rotation pairs and quantization groups), or I (one group per row)
   // MoE (prefill only): experts > 0 stacked experts sharing the rotation,
   // rows of expert e in [expert_offsets[e], expert_offsets[e+1]) (device)
   int experts;

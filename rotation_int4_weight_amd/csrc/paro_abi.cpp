@@ -64,13 +64,33 @@ int check_method_shape(const paro_w4_layer *L) {
   return PARO_OK;
 }
 
-// What the GPU kernels support on top of the method's rules.
-int check_gpu_shape(const paro_w4_layer *L) {
+// One rotation and quantization group over the whole row: group_size -1
+// (or G == I) beyond the 128-channel block sizes.
+bool full_row(const paro_w4_layer *L) {
+  const int64_t G = group_of(L);
+  return G == L->in_features && G != 32 && G != 64 && G != 128;
+}
+
+// What the GPU kernels support on top of the method's rules.  rows: the
+// entry point also takes one group over the whole row (the linear, the
+// row-major rotation, the tiled contraction, the unpack).
+int check_gpu_shape(const paro_w4_layer *L, bool rows = false) {
   int rc = check_method_shape(L);
   if (rc) return rc;
   const int64_t G = group_of(L);
-  if (G != 32 && G != 64 && G != 128)
-    return fail(PARO_ERR_UNSUPPORTED, "group_size=%d: the GPU path supports 32, 64 and 128", L->group_size);
+  if (full_row(L)) {
+    if (!rows)
+      return fail(PARO_ERR_UNSUPPORTED,
+                  "group_size=%d (one group over all %lld channels): this entry point takes 32, 64 and 128; the "
+                  "linear, paro_scale_rotate, paro_w4a16_linear_tiled and paro_w4_unpack_dequant take it",
+                  L->group_size, (long long)L->in_features);
+    if (L->in_features > paro::kMaxFullRowDim)
+      return fail(PARO_ERR_UNSUPPORTED, "one group over the row: in_features=%lld exceeds %lld",
+                  (long long)L->in_features, (long long)paro::kMaxFullRowDim);
+  } else if (G != 32 && G != 64 && G != 128) {
+    return fail(PARO_ERR_UNSUPPORTED, "group_size=%d: the GPU path supports 32, 64, 128 and -1 (the whole row)",
+                L->group_size);
+  }
   if (L->in_features % 128)
     return fail(PARO_ERR_UNSUPPORTED, "in_features=%lld: the GPU path rotates 128-channel blocks",
                 (long long)L->in_features);
@@ -141,8 +161,10 @@ paro::LinearArgs linear_args(const paro_w4_layer *L, int64_t tokens, const void 
   return a;
 }
 
-paro_path auto_path(int64_t tokens) {
-  if (tokens <= 4) return PARO_PATH_DECODE_FUSED;
+// rows: one group over the whole row, whose rotation the fused decode
+// prologue (one 128-channel block per wave) cannot do
+paro_path auto_path(int64_t tokens, bool rows = false) {
+  if (tokens <= 4 && !rows) return PARO_PATH_DECODE_FUSED;
   if (tokens <= 16) return PARO_PATH_DECODE_SPLIT;
   return PARO_PATH_PREFILL;
 }
@@ -161,8 +183,8 @@ size_t workspace_for(const paro_w4_layer *L, int64_t tokens, paro_path path) {
   size_t bytes = kCounterBytes + xr_region(L, tokens, path);
   if (path != PARO_PATH_PREFILL)
     bytes += paro::decode_partial_bytes(paro::plan_decode(I, O, tokens, path == PARO_PATH_DECODE_FUSED, (int)group_of(L)), tokens, O);
-  else
-    bytes += paro::rot_mat_bytes(I);
+  else if (!full_row(L))
+    bytes += paro::rot_mat_bytes(I);  // the dense rotation (one group over the row is rotated stage by stage)
   return bytes;
 }
 
@@ -198,7 +220,7 @@ int paro_validate_layer(const paro_w4_layer *L) {
 
 int paro_scale_rotate(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens, void *x_r,
                       paro_dtype xr_dt, void *stream) {
-  int rc = check_gpu_shape(L);
+  int rc = check_gpu_shape(L, true);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
@@ -214,9 +236,12 @@ int paro_scale_rotate(const paro_w4_layer *L, const void *x, paro_dtype x_dt, in
   const bool overlap = xs < os + ob && os < xs + xb;
   if (overlap && !(x == x_r && x_dt == xr_dt))
     return fail(PARO_ERR_SHAPE, "x_r overlaps x (only exact in-place with equal dtypes is allowed)");
-  hipError_t e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, x_r, (int)xr_dt, tokens, I, L->pairs,
-                                           L->theta, L->channel_scales, L->krot, (int)group_of(L),
-                                           (hipStream_t)stream);
+  hipError_t e = full_row(L) ? paro::launch_scale_rotate_full((const uint16_t *)x, (int)x_dt, x_r, (int)xr_dt, false,
+                                                               tokens, I, L->pairs, L->theta, L->channel_scales,
+                                                               L->krot, (hipStream_t)stream)
+                             : paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, x_r, (int)xr_dt, tokens, I,
+                                                         L->pairs, L->theta, L->channel_scales, L->krot,
+                                                         (int)group_of(L), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
   return ok();
 }
@@ -268,7 +293,7 @@ int paro_scale_rotate_tiled(const paro_w4_layer *L, const void *hl, const void *
 
 int paro_w4a16_linear_tiled(const paro_w4_layer *L, const void *x_t, paro_dtype x_dt, int64_t tokens, void *y,
                             paro_dtype y_dt, void *stream) {
-  int rc = check_gpu_shape(L);
+  int rc = check_gpu_shape(L, true);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
@@ -290,7 +315,7 @@ int paro_w4a16_linear_tiled(const paro_w4_layer *L, const void *x_t, paro_dtype 
 
 int paro_w4_unpack_dequant(const paro_w4_layer *L, uint8_t *q_out, uint8_t *z_out, void *w_out, paro_dtype w_dt,
                            void *stream) {
-  int rc = check_gpu_shape(L);
+  int rc = check_gpu_shape(L, true);
   if (rc) return rc;
   if (w_out && !act_dtype(w_dt) && w_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "w dtype %d invalid", (int)w_dt);
   if (!q_out && !z_out && !w_out) return ok();
@@ -544,15 +569,14 @@ int paro_mxfp4_linear(const paro_w4_layer *L, const uint8_t *w_codes, const uint
 }
 
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {
-  (void)L;
-  return auto_path(tokens);
+  return auto_path(tokens, L && full_row(L));
 }
 
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens, paro_dtype x_dt,
                                          paro_path path) {
   (void)x_dt;
-  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
-  if (path == PARO_PATH_AUTO) path = auto_path(tokens);
+  if (!L || tokens <= 0 || check_gpu_shape(L, true)) return 0;
+  if (path == PARO_PATH_AUTO) path = auto_path(tokens, full_row(L));
   return workspace_for(L, tokens, path);
 }
 
@@ -569,7 +593,8 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
                 paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream, paro_path path,
                 bool prerotated, int experts = 0, const int64_t *expert_offsets = nullptr,
                 const void *hl_pre = nullptr) {
-  int rc = check_gpu_shape(L);
+  const bool rows = full_row(L);
+  int rc = check_gpu_shape(L, !hl_pre && experts == 0);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
@@ -584,9 +609,12 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
     if (!aligned(expert_offsets, 8)) return fail(PARO_ERR_ALIGN, "expert_offsets must be 8-byte aligned");
     path = PARO_PATH_PREFILL;  // the grouped GEMM runs on the prefill kernel
   }
+  if (rows && path == PARO_PATH_DECODE_FUSED)
+    return fail(PARO_ERR_UNSUPPORTED, "one group over the whole row: the fused decode path rotates 128-channel "
+                                      "blocks; use AUTO, DECODE_SPLIT or PREFILL");
   if (tokens == 0) return ok();
   if (path == PARO_PATH_AUTO) {
-    path = auto_path(tokens);
+    path = auto_path(tokens, rows);
     if (prerotated && path == PARO_PATH_DECODE_FUSED) path = PARO_PATH_DECODE_SPLIT;
   }
   if ((path == PARO_PATH_DECODE_FUSED || path == PARO_PATH_DECODE_SPLIT) && tokens > 16)
@@ -635,8 +663,10 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
   if (path == PARO_PATH_DECODE_SPLIT) {  // row-major X_r into the workspace, then the split-K GEMV over it
     const void *xin = x;
     if (!prerotated) {
-      e = paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs, L->theta,
-                                    L->channel_scales, L->krot, a.group, st);
+      e = rows ? paro::launch_scale_rotate_full((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, false, tokens, I,
+                                                L->pairs, L->theta, L->channel_scales, L->krot, st)
+               : paro::launch_scale_rotate((const uint16_t *)x, (int)x_dt, xr, (int)x_dt, tokens, I, L->pairs,
+                                           L->theta, L->channel_scales, L->krot, a.group, st);
       if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
       xin = xr;
     }
@@ -652,6 +682,10 @@ int linear_impl(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t 
   if (prerotated) {
     e = paro::launch_retile((const uint16_t *)x, xt, tokens, I, st);
     if (e != hipSuccess) return hip_fail(e, "retile launch");
+  } else if (rows) {  // one group over the row: staged rotation straight into the tiled layout
+    e = paro::launch_scale_rotate_full((const uint16_t *)x, (int)x_dt, xt, (int)x_dt, true, tokens, I, L->pairs,
+                                       L->theta, L->channel_scales, L->krot, st);
+    if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
   } else {
     const uint16_t *hl = (const uint16_t *)hl_pre;
     if (!prebuilt) {
@@ -701,11 +735,11 @@ int paro_w4a16_linear_noalloc(const paro_w4_layer *L, const void *x, paro_dtype 
                               paro_dtype y_dt, void *stream) {
   // the same checks as the workspace variant first, so that a bad call
   // touches no device state
-  int rc = check_gpu_shape(L);
+  int rc = check_gpu_shape(L, true);
   if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
   if (tokens == 0) return ok();
-  const size_t need = workspace_for(L, tokens, auto_path(tokens));
+  const size_t need = workspace_for(L, tokens, auto_path(tokens, full_row(L)));
   if (need > paro::kNoallocScratchBytes)
     return fail(PARO_ERR_UNSUPPORTED,
                 "this shape needs %zu bytes of workspace; the allocation-free linear holds %zu "

@@ -242,7 +242,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM;
   }
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
-  const int nsteps = (int)(I / kBK), ngroups = (int)(I / (kBK * GK));
+  // (GK = 0: one quantization group over the whole row)
+  const int nsteps = (int)(I / kBK), ngroups = GK ? (int)(I / (kBK * GK)) : 1;
 
   // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
   // the (16-row padded) tiled buffer; later ones read as zeros.
@@ -291,7 +292,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     // q % NSLOT; it is decoded just before the first k-step of the group is
     // expanded, and the slot is refilled at once with group q + NSLOT.  Every
     // slot index below is a compile-time constant: the step's value mod 8 is.
-    constexpr int NSLOT = GK == 1 ? 4 : 2;
+    // One group over the whole row (GK = 0): decoded once, at step 0.
+    constexpr int NSLOT = GK == 0 ? 1 : GK == 1 ? 4 : 2;
     GroupConsts<DT> gc;
     const NibbleMasks nm;
     GroupRaw graw[NSLOT];
@@ -302,7 +304,9 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     for (int k = 0; k < kWordRing; ++k) load_words(k, wd[k]);
     // step st (st % 8 == sm): enter its group if it is the group's first step
     auto enter_group = [&](int sm, int st) {
-      if (sm % GK == 0) {
+      if constexpr (GK == 0) {
+        if (sm == 0 && st == 0) gc.decode(graw[0].sw, graw[0].zw);
+      } else if (sm % GK == 0) {
         GroupRaw &gr = graw[(sm / GK) % NSLOT];
         gc.decode(gr.sw, gr.zw);
         load_group(st / GK + NSLOT, gr);
@@ -486,6 +490,12 @@ static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid,
 
 template <bool MOE, int RT>
 static void launch_prefill_moe(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
+  if constexpr (!MOE) {  // one group over the whole row (dense layers only)
+    if (a.group == a.I && a.group > kG) {
+      launch_prefill_gk<0, MOE, RT>(a, x, grid, st);
+      return;
+    }
+  }
   if (a.group == 32) launch_prefill_gk<1, MOE, RT>(a, x, grid, st);
   else if (a.group == 64) launch_prefill_gk<2, MOE, RT>(a, x, grid, st);
   else launch_prefill_gk<4, MOE, RT>(a, x, grid, st);

@@ -393,6 +393,122 @@ hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// One rotation group over the whole row (group_size -1, i.e. G = I).
+//
+// "ParoQuant" wiki, Concepts / Pairwise Givens rotations: group_size -1 is one
+// group of all in_features channels, so a stage's pairs may join any two
+// channels of the row and the 128-channel blocks above do not apply (nor
+// does the dense per-block form).  A workgroup holds R scaled rows of x in
+// LDS (fp32, R * I * 4 <= 64 KB); at each stage its threads take the I/2
+// pairs in turn and apply them to all R rows with the same fp32 operations
+// as rotate_stage; a barrier separates the stages.  Pair indices past the
+// row are read as 0, so a bad schedule cannot leave the row's LDS.  The
+// result goes out row-major (xr dtype) or, TILED, in the prefill GEMM's
+// tiled layout: the grid then covers every 16-row tile of it, pad rows
+// (zero in, zero out) included, with R dividing 16.
+// ---------------------------------------------------------------------------
+constexpr int kFullThreads = 256;
+
+template <int XDT, int ODT, bool TILED>
+__global__ void __launch_bounds__(kFullThreads)
+scale_rotate_full_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64_t tokens, int64_t I, int R,
+                         const int16_t *__restrict__ pairs, const float *__restrict__ theta,
+                         const float *__restrict__ cscale, int krot) {
+  extern __shared__ __attribute__((aligned(16))) float rows[];  // [R][I]
+  const int64_t m0 = (int64_t)blockIdx.x * R;
+  const int64_t half = I / 2;
+  for (int64_t e = threadIdx.x; e < R * half; e += kFullThreads) {
+    const int r = (int)(e / half);
+    const int64_t k = 2 * (e - r * half);
+    float v0 = 0.0f, v1 = 0.0f;
+    if (m0 + r < tokens) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(x + (m0 + r) * I + k);
+      v0 = act_to_f32<XDT>(w & 0xffffu) * cscale[k];
+      v1 = act_to_f32<XDT>(w >> 16) * cscale[k + 1];
+    }
+    rows[r * I + k] = v0;
+    rows[r * I + k + 1] = v1;
+  }
+  __syncthreads();
+  for (int t = 0; t < krot; ++t) {
+    const int16_t *pt = pairs + (int64_t)t * I;
+    const float *tt = theta + (int64_t)t * half;
+    for (int64_t p = threadIdx.x; p < half; p += kFullThreads) {
+      const uint32_t pw = *reinterpret_cast<const uint32_t *>(pt + 2 * p);
+      const int64_t ia = pw & 0xffffu, ib = pw >> 16;
+      const int64_t a = ia < I ? ia : 0, b = ib < I ? ib : 0;
+      float c, sn;
+      __sincosf(tt[p], &sn, &c);
+      for (int r = 0; r < R; ++r) {
+        const float va = rows[r * I + a], vb = rows[r * I + b];
+        rows[r * I + a] = __builtin_fmaf(va, c, vb * sn);
+        rows[r * I + b] = __builtin_fmaf(vb, c, -(va * sn));
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (TILED) {
+    // 8 consecutive channels of one row per thread and pass: one 16-byte piece
+    const int64_t chunks = I / 8;
+    for (int64_t e = threadIdx.x; e < R * chunks; e += kFullThreads) {
+      const int r = (int)(e / chunks);
+      const int64_t c = e - r * chunks, k = 8 * c, m = m0 + r;
+      const float *v = rows + r * I + k;
+      const u32x4 q{pack2<ODT>(v[0], v[1]), pack2<ODT>(v[2], v[3]), pack2<ODT>(v[4], v[5]), pack2<ODT>(v[6], v[7])};
+      const int64_t idx = ((m / 16) * (I / 32) + k / 32) * 512 + (((k % 32) / 8) * 16 + m % 16) * 8;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(xr) + idx) = q;
+    }
+  } else {
+    for (int64_t e = threadIdx.x; e < R * half; e += kFullThreads) {
+      const int r = (int)(e / half);
+      const int64_t k = 2 * (e - r * half);
+      if (m0 + r >= tokens) continue;
+      const float v0 = rows[r * I + k], v1 = rows[r * I + k + 1];
+      const int64_t o = (m0 + r) * I + k;
+      if constexpr (ODT == kF32)
+        *reinterpret_cast<float2 *>(reinterpret_cast<float *>(xr) + o) = make_float2(v0, v1);
+      else
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(xr) + o) = pack2<ODT>(v0, v1);
+    }
+  }
+}
+
+int full_row_rows(int64_t I) {
+  int r = 16;
+  while (r > 1 && (int64_t)r * I * 4 > kFullRowLdsBytes) r /= 2;
+  return r;
+}
+
+template <int XDT, int ODT, bool TILED>
+static hipError_t launch_full_t(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
+                                const float *theta, const float *cs, int krot, hipStream_t st) {
+  const int R = full_row_rows(I);
+  const int64_t rows = TILED ? tiled_rows(tokens) : tokens;
+  const dim3 grid((unsigned)((rows + R - 1) / R));
+  hipLaunchKernelGGL((scale_rotate_full_kernel<XDT, ODT, TILED>), grid, dim3(kFullThreads),
+                     (size_t)R * I * sizeof(float), st, x, xr, tokens, I, R, pairs, theta, cs, krot);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_rotate_full(const uint16_t *x, int x_dt, void *xr, int xr_dt, bool tiled, int64_t tokens,
+                                    int64_t I, const int16_t *pairs, const float *theta, const float *cs, int krot,
+                                    hipStream_t st) {
+  if (tokens == 0) return hipSuccess;
+  if (tiled) {  // the tiled layout holds the activation dtype
+    if (x_dt == kF16) return launch_full_t<kF16, kF16, true>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+    return launch_full_t<kBF16, kBF16, true>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  }
+  if (x_dt == kF16) {
+    if (xr_dt == kF16) return launch_full_t<kF16, kF16, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+    if (xr_dt == kBF16) return launch_full_t<kF16, kBF16, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+    return launch_full_t<kF16, kF32, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  }
+  if (xr_dt == kF16) return launch_full_t<kBF16, kF16, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  if (xr_dt == kBF16) return launch_full_t<kBF16, kBF16, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+  return launch_full_t<kBF16, kF32, false>(x, xr, tokens, I, pairs, theta, cs, krot, st);
+}
+
 template <int XDT, int ODT, int RW>
 static hipError_t launch_rot_rw(const uint16_t *x, void *xr, int64_t tokens, int64_t I, const int16_t *pairs,
                                 const float *theta, const float *cs, int krot, int gm, hipStream_t st) {

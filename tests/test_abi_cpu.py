@@ -107,7 +107,9 @@ def lin(L, x=FAKE, xdt=0, tokens=4, y=FAKE * 2, ydt=0, ws=FAKE * 4, wsb=1 << 30,
     (dict(L=dict(G=16)), 5),             # G in {32, 64, 128} on the GPU
     (dict(L=dict(G=256, I=512)), 5),
     (dict(L=dict(G=64, I=320)), 5),      # 128-channel rotation blocks: I % 128 == 0
-    (dict(L=dict(G=-1, I=256)), 5),      # G = I = 256
+    (dict(L=dict(G=-1, I=256), path=1), 5),      # one group over the row: no fused decode
+    (dict(L=dict(G=-1, I=16384 + 128)), 5),      # one group over the row: I <= 16384 (LDS)
+    (dict(L=dict(G=256, I=256), path=1), 5),     # G == I is the same layer as G = -1
     (dict(L=dict(O=60)), 2),             # O % 8
     (dict(L=dict(G=100)), 2),            # G does not divide I
     (dict(L=dict(krot=0)), 2),
@@ -198,6 +200,7 @@ def test_tiled_entry_point_argument_checks():
     assert mat(L=fake_layer(pairs=0)) == 1
     assert mat(L=fake_layer(theta=0)) == 1
     assert mat(L=fake_layer(G=16)) == 5
+    assert mat(L=fake_layer(G=-1)) == 5      # no dense form of one group over the whole row
     rot = lambda x=FAKE, dt=0, tokens=4, xt=FAKE * 2, hl=FAKE * 8, L=L: lib.paro_scale_rotate_tiled(
         ctypes.byref(L), hl, x, dt, tokens, xt, None)
     assert rot(dt=2) == 3                      # fp32 activations not accepted
@@ -239,6 +242,7 @@ def test_quantize_pack_argument_checks():
     assert call(w=FAKE) == 2                      # w overlaps qweight
     assert call(qz=FAKE + 64) == 2                # qzeros inside qweight
     assert call(L=fake_layer(I=256, O=64, G=16)) == 5
+    assert call(L=fake_layer(I=256, O=64, G=-1)) == 5
     assert call(L=fake_layer(I=256, O=64, pairs=0)) == 1
     # G = 32: qzeros [I/32][O/8] int32 = 8 * 8 * 4 = 256 bytes, so scales
     # starting 128 bytes into them overlap (with I/128 groups, 64 bytes, they
@@ -258,6 +262,7 @@ def test_scale_rotate_backward_argument_checks():
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 65) == need + 2 * 128 * 128 * 4
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(L), 0) == need   # the walk still runs
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=16)), 4) == 0
+    assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=-1)), 4) == 0
     assert lib.paro_scale_rotate_backward_workspace_bytes(ctypes.byref(fake_layer(G=64)), 4) == need
 
     def call(x=FAKE * 8, xdt=0, g=FAKE * 9, gdt=2, tokens=4, gx=FAKE * 10, gxdt=2, gth=FAKE * 11,
@@ -346,3 +351,19 @@ def test_mxfp4_argument_checks():
     assert ln(wsb=need - 1) == 7
     assert ln(ws=0) == 7
     assert ln(xdt=2) == 3
+
+
+@needs_no_gpu
+def test_whole_row_group_workspace_and_path():
+    """group_size -1 (one group over all I channels): decode takes the split
+    path, and the prefill workspace holds no dense rotation matrix."""
+    lib = _lib.load()
+    L = fake_layer(I=4096, O=1024, G=-1)
+    assert lib.paro_w4a16_linear_choose_path(ctypes.byref(L), 1) == 2
+    assert lib.paro_w4a16_linear_choose_path(ctypes.byref(L), 16) == 2
+    assert lib.paro_w4a16_linear_choose_path(ctypes.byref(L), 17) == 3
+    L128 = fake_layer(I=4096, O=1024, G=128)
+    counters = (1 << 21) // 128 * 128
+    assert lib.paro_w4a16_linear_workspace_bytes(ctypes.byref(L), 32, 1, 3) == counters + 32 * 4096 * 2
+    assert lib.paro_w4a16_linear_workspace_bytes(ctypes.byref(L128), 32, 1, 3) == counters + 32 * 4096 * 2 + 4096 * 512
+    assert lib.paro_w4a16_linear_prepared_workspace_bytes(ctypes.byref(L), 32) == 0   # no prebuilt form

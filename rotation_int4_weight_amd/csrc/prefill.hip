@@ -48,6 +48,8 @@
 //     not what bounds it.)
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -64,6 +66,7 @@ constexpr int kASlots = 4;          // A fragments in flight per consumer wave (
 constexpr int kGroupM = 2;          // M blocks per group of the tile order (dense layers)
 constexpr int kStageRS = kBN + 4;   // epilogue staging row stride (floats): the four row groups of a store hit distinct banks
 static_assert(kTiles == 8 && kWordRing == 8, "the producer's ring slot arithmetic assumes rings of 8");
+static_assert(kASlots == 4, "a tile's last super-step loads two A steps of the next tile, the epilogue the other two");
 
 // Physical k-pair index of k-pair rp (k = 2rp, 2rp+1) in column col: the
 // four 8-row blocks are XOR-permuted by (col/16)&3.
@@ -177,6 +180,13 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
 // rows: 4 (256 rows) by default, 2 (128 rows) for dense layers whose
 // 256-row grid would leave CUs idle (each weight tile then serves half as
 // many MFMAs, and twice as many workgroups fill the chip).
+//
+// Dense layers run persistent workgroups: workgroup b takes the output tiles
+// b, b + G, b + 2G, ... (G workgroups, at most one per CU) in turn.  Steps
+// are numbered across its tiles, so the weight ring simply continues: while
+// the consumers finish a tile (its epilogue), the producers already expand
+// the first steps of the next one, and the consumers' A loads for it are in
+// flight, instead of every tile starting from an empty pipeline.
 template <int DT, int GK, bool MOE, int RT>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
@@ -186,139 +196,191 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __shared__ __attribute__((aligned(16))) float stage[4][32 * kStageRS];  // epilogue, one per consumer wave
   const int lane = lane_id(), wave = wave_id();
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
-  // XCD-local order: consecutive logical tiles (the N tiles of one M block)
-  // share an XCD and its L2.  The tile indices are uniform; readfirstlane
-  // moves them (computed with VALU division) to scalar registers so that the
-  // buffer descriptors derived from them stay scalar too.
   const int n_tiles = (int)((O + kBN - 1) / kBN);
   const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + BM - 1) / BM);
-  const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * m_tiles);
-  // Dense layers: logical tiles go in groups of kGroupM M blocks, the M block
-  // fastest, so an XCD's share of consecutive tiles spans kGroupM blocks of
-  // rows and 1/kGroupM as many weight columns as a row-major order would.
-  int tn = lwg % n_tiles, tm = lwg / n_tiles;
-  if constexpr (!MOE) {
-    const int first = (lwg / (kGroupM * n_tiles)) * kGroupM;
-    const int gsz = m_tiles - first < kGroupM ? m_tiles - first : kGroupM;
-    const int r = lwg % (kGroupM * n_tiles);
-    tm = first + r % gsz;
-    tn = r / gsz;
-  }
-  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * kBN;
-  int64_t mb, row_lo = 0, row_hi = M;
-  const int32_t *qweight = a.qweight, *qzeros = a.qzeros;
-  const uint16_t *scales = a.scales, *bias = a.bias;
-  if constexpr (MOE) {
-    // work item (expert, 256-row tile) number lwg / n_tiles, experts in order
-    const int64_t wi = __builtin_amdgcn_readfirstlane(lwg / n_tiles);
-    int64_t cum = 0, prev = a.expert_offsets[0];
-    prev = prev < 0 ? 0 : (prev > M ? M : prev);
-    int e = -1;
-    int64_t lo = 0, hi = 0, j = 0;
-    for (int k = 0; k < a.experts; ++k) {
-      int64_t o1 = a.expert_offsets[k + 1];
-      o1 = o1 < prev ? prev : (o1 > M ? M : o1);
-      const int64_t t = o1 > prev ? (o1 - (prev & ~(int64_t)15) + kBM - 1) / kBM : 0;
-      if (wi < cum + t) {
-        e = k;
-        lo = prev;
-        hi = o1;
-        j = wi - cum;
-        break;
-      }
-      cum += t;
-      prev = o1;
-    }
-    if (e < 0) return;  // past the last tile: the whole workgroup leaves before any barrier
-    mb = (lo & ~(int64_t)15) + j * kBM;
-    row_lo = lo > mb ? lo : mb;
-    row_hi = hi < mb + kBM ? hi : mb + kBM;
-    const int64_t G = (int64_t)kBK * GK;
-    qweight += (int64_t)e * I * W;
-    qzeros += (int64_t)e * (I / G) * W;
-    scales += (int64_t)e * (I / G) * O;
-    if (bias) bias += (int64_t)e * O;
-  } else {
-    mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM;
-  }
+  const int total = n_tiles * m_tiles;
+  // tiles of this workgroup (the grid never exceeds the tile count)
+  const int my_tiles = MOE ? 1 : (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
   // (GK = 0: one quantization group over the whole row)
   const int nsteps = (int)(I / kBK), ngroups = GK ? (int)(I / (kBK * GK)) : 1;
+  const int wg_steps = my_tiles * nsteps;
 
-  // A row tiles of this workgroup: 16 from mb/16, of which `tiles` exist in
-  // the (16-row padded) tiled buffer; later ones read as zeros.
-  const int64_t rtiles = (row_hi + 15) / 16 - mb / 16;
-  const int tiles = (int)(rtiles < BM / 16 ? rtiles : BM / 16);
+  // The output tile of this workgroup's iteration it (uniform values; the
+  // tile indices go through readfirstlane so that everything derived from
+  // them stays in scalar registers).
+  struct Tile {
+    int64_t n0, mb, row_lo, row_hi;
+    const int32_t *qweight, *qzeros;
+    const uint16_t *scales, *bias;
+  };
+  auto tile_of = [&](int it, Tile &t) -> bool {
+    t.qweight = a.qweight;
+    t.qzeros = a.qzeros;
+    t.scales = a.scales;
+    t.bias = a.bias;
+    t.row_lo = 0;
+    t.row_hi = M;
+    // XCD-local order: consecutive logical tiles (the N tiles of one M block)
+    // share an XCD and its L2.  Workgroup b's iteration it stands for launch
+    // id b + it G, which lies on b's XCD when G is a multiple of 8.
+    const int lwg = xcd_local_order((int)blockIdx.x + it * (int)gridDim.x, total);
+    // Dense layers: logical tiles go in groups of kGroupM M blocks, the M
+    // block fastest, so an XCD's share of consecutive tiles spans kGroupM
+    // blocks of rows and 1/kGroupM as many weight columns as a row-major
+    // order would.
+    int tn = lwg % n_tiles, tm = lwg / n_tiles;
+    if constexpr (!MOE) {
+      const int first = (lwg / (kGroupM * n_tiles)) * kGroupM;
+      const int gsz = m_tiles - first < kGroupM ? m_tiles - first : kGroupM;
+      const int r = lwg % (kGroupM * n_tiles);
+      tm = first + r % gsz;
+      tn = r / gsz;
+    }
+    t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * kBN;
+    if constexpr (MOE) {
+      // work item (expert, 256-row tile) number lwg / n_tiles, experts in order
+      const int64_t wi = __builtin_amdgcn_readfirstlane(lwg / n_tiles);
+      int64_t cum = 0, prev = a.expert_offsets[0];
+      prev = prev < 0 ? 0 : (prev > M ? M : prev);
+      int e = -1;
+      int64_t lo = 0, hi = 0, j = 0;
+      for (int k = 0; k < a.experts; ++k) {
+        int64_t o1 = a.expert_offsets[k + 1];
+        o1 = o1 < prev ? prev : (o1 > M ? M : o1);
+        const int64_t c = o1 > prev ? (o1 - (prev & ~(int64_t)15) + kBM - 1) / kBM : 0;
+        if (wi < cum + c) {
+          e = k;
+          lo = prev;
+          hi = o1;
+          j = wi - cum;
+          break;
+        }
+        cum += c;
+        prev = o1;
+      }
+      if (e < 0) return false;
+      t.mb = (lo & ~(int64_t)15) + j * kBM;
+      t.row_lo = lo > t.mb ? lo : t.mb;
+      t.row_hi = hi < t.mb + kBM ? hi : t.mb + kBM;
+      const int64_t G = (int64_t)kBK * GK;
+      t.qweight += (int64_t)e * I * W;
+      t.qzeros += (int64_t)e * (I / G) * W;
+      t.scales += (int64_t)e * (I / G) * O;
+      if (t.bias) t.bias += (int64_t)e * O;
+    } else {
+      t.mb = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM;
+    }
+    return true;
+  };
   const uint32_t tile_bytes = (uint32_t)nsteps * 1024u;  // one row tile over all of k
-  const uint32_t a_bytes = (uint32_t)tiles * tile_bytes;
-  const char *a_base = reinterpret_cast<const char *>(xt + (mb / 16) * (I / 32) * 512);
-  auto a_rsrc = [&](int step) {
-    const int st = step < nsteps ? step : nsteps - 1;  // past the end: any in-bounds step, unused
-    const uint32_t kb = (uint32_t)st * 1024u;
-    return raw_rsrc(a_base + kb, a_bytes - kb);
+
+  Tile t0;
+  if (!tile_of(0, t0)) return;  // MoE past the last tile: the whole workgroup leaves before any barrier
+  // (a MoE workgroup has one tile: its expert scan is not repeated)
+  auto tile_at = [&](int it, Tile &t) {
+    if (MOE || it == 0)
+      t = t0;
+    else
+      tile_of(it, t);
+  };
+  // A position in the workgroup's sequence of (tile, k step) or (tile,
+  // group) pairs.  Every load stream below takes its positions in order, one
+  // at a time, so each keeps its own cursor and looks a tile up only when
+  // it enters one: no division in the loops.  Past the end a cursor stays
+  // on the last position (in-bounds loads whose values are never used).
+  struct Cursor {
+    int it, pos;
+    Tile t;
+  };
+  auto advance = [&](Cursor &c, int len) {
+    if (c.pos + 1 < len) {
+      ++c.pos;
+    } else if (c.it + 1 < my_tiles) {
+      ++c.it;
+      c.pos = 0;
+      tile_at(c.it, c.t);
+    }
   };
 
   if (wave >= 4) {
     // ------------------------------ producer ------------------------------
     const int tp = threadIdx.x - 256;
     const int dw = tp & 15, drp = tp >> 4;  // word dw of the tile's 16, rows 2drp, 2drp+1 of a step
-    const int64_t dword = n0 / 8 + dw;
-    const uint32_t dwc = (uint32_t)(dword < W ? dword : W - 1);  // tail tile: any in-bounds word
-    const uint32_t w_off = (uint32_t)((2 * drp) * W + dwc) * 4u;
     const uint32_t w_step_bytes = (uint32_t)(kBK * W * 4);
+    // this thread's packed word of a tile's column block (tail tile: any
+    // in-bounds word)
+    auto word_of = [&](int64_t n0) -> uint32_t {
+      const int64_t dword = n0 / 8 + dw;
+      return (uint32_t)(dword < W ? dword : W - 1);
+    };
 
     struct Words {
       uint32_t ra, rb;
     };
-    auto load_words = [&](int step, Words &wd) {
-      const int st = step < nsteps ? step : nsteps - 1;
-      const __amdgpu_buffer_rsrc_t r = raw_rsrc(qweight + (int64_t)st * kBK * W, w_step_bytes);
+    // packed words of the next step of the sequence (steps in order)
+    Cursor cw{0, 0, t0};
+    auto load_words = [&](Words &wd) {
+      const uint32_t w_off = (uint32_t)((2 * drp) * W + word_of(cw.t.n0)) * 4u;
+      const __amdgpu_buffer_rsrc_t r = raw_rsrc(cw.t.qweight + (int64_t)cw.pos * kBK * W, w_step_bytes);
       wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
       wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
+      advance(cw, nsteps);
     };
     struct GroupRaw {
       u32x4 sw;
       uint32_t zw;
     };
-    auto load_group = [&](int g, GroupRaw &gr) {
-      const int gg = g < ngroups ? g : ngroups - 1;
-      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(scales + (int64_t)gg * O, (uint32_t)(O * 2));
+    // scales and zeros of the next group of the sequence (groups in order)
+    Cursor cg{0, 0, t0};
+    auto load_group = [&](GroupRaw &gr) {
+      const uint32_t dwc = word_of(cg.t.n0);
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(cg.t.scales + (int64_t)cg.pos * O, (uint32_t)(O * 2));
       gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
-      const __amdgpu_buffer_rsrc_t rz = raw_rsrc(qzeros + (int64_t)gg * W, (uint32_t)(W * 4));
+      const __amdgpu_buffer_rsrc_t rz = raw_rsrc(cg.t.qzeros + (int64_t)cg.pos * W, (uint32_t)(W * 4));
       gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
+      advance(cg, ngroups);
     };
 
     // Scales and zeros: a ring of NSLOT groups.  Group q sits in slot
     // q % NSLOT; it is decoded just before the first k-step of the group is
     // expanded, and the slot is refilled at once with group q + NSLOT.  Every
-    // slot index below is a compile-time constant: the step's value mod 8 is.
-    // One group over the whole row (GK = 0): decoded once, at step 0.
+    // slot index below is a compile-time constant: the step's value mod 8 is
+    // (nsteps is a multiple of 4 and of GK, so a group never straddles two
+    // tiles).  One group over the whole row (GK = 0): decoded at the first
+    // step of each tile, the next tile's loaded meanwhile.
     constexpr int NSLOT = GK == 0 ? 1 : GK == 1 ? 4 : 2;
     GroupConsts<DT> gc;
     const NibbleMasks nm;
     GroupRaw graw[NSLOT];
     Words wd[kWordRing];
 #pragma unroll
-    for (int q = 0; q < NSLOT; ++q) load_group(q, graw[q]);
+    for (int q = 0; q < NSLOT; ++q) load_group(graw[q]);
 #pragma unroll
-    for (int k = 0; k < kWordRing; ++k) load_words(k, wd[k]);
-    // step st (st % 8 == sm): enter its group if it is the group's first step
-    auto enter_group = [&](int sm, int st) {
+    for (int k = 0; k < kWordRing; ++k) load_words(wd[k]);
+    // The step being expanded (st % 8 == sm, steps in order): entering its
+    // group if it is the group's first step.
+    Cursor ce{0, 0, t0};
+    auto enter_group = [&](int sm) {
       if constexpr (GK == 0) {
-        if (sm == 0 && st == 0) gc.decode(graw[0].sw, graw[0].zw);
+        if (ce.pos == 0) {  // a tile's first step
+          gc.decode(graw[0].sw, graw[0].zw);
+          load_group(graw[0]);
+        }
       } else if (sm % GK == 0) {
         GroupRaw &gr = graw[(sm / GK) % NSLOT];
         gc.decode(gr.sw, gr.zw);
-        load_group(st / GK + NSLOT, gr);
+        load_group(gr);
       }
+      advance(ce, nsteps);
     };
     // tiles 0..4 before the first barrier: the consumers' first super-step
     // computes steps 0..3 and reads the fragments of steps 1..4
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
-      enter_group(k, k);
+      enter_group(k);
       expand_pair_to_lds<DT>(wd[k].ra, wd[k].rb, gc, nm, bl[k], dw, drp);
-      load_words(k + kWordRing, wd[k]);
+      load_words(wd[k]);  // step k + kWordRing
       __builtin_amdgcn_sched_barrier(0);  // one expansion's temporaries live at a time
     }
     __syncthreads();
@@ -334,40 +396,49 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     // S+1, after the barrier that ends S.  Their slots' previous tiles
     // (4S-3..4S) were last read in super-step S-1 (tile 0: before the extra
     // barrier above), and the consumers wait for their own LDS reads before
-    // each barrier.  Each word slot is refilled
-    // kWordRing steps ahead.  Past the end everything runs on clamped,
-    // in-bounds addresses into tiles no consumer uses.  kk: parity of S in a
-    // two-super-step iteration, so that the ring slots (4kk+5+u) % 8 are
-    // constants.
-    auto psuper = [&](int S, int kk) {
+    // each barrier.  Each word slot is refilled kWordRing steps ahead.  Steps
+    // run on across the workgroup's tiles; past its last step everything
+    // runs on clamped, in-bounds addresses into tiles no consumer uses.  kk:
+    // parity of S in a two-super-step iteration, so that the ring slots
+    // (4kk+5+u) % 8 are constants.
+    auto psuper = [&](int kk) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int slot = (4 * kk + 5 + u) % kTiles;  // == (4S+5+u) % 8
-        enter_group(slot, 4 * S + 5 + u);
+        enter_group(slot);  // step 4S+5+u
         Words &w = wd[slot];
         expand_pair_to_lds<DT>(w.ra, w.rb, gc, nm, bl[slot], dw, drp);
-        load_words(4 * S + 5 + u + kWordRing, w);
+        load_words(w);      // step 4S+5+u + kWordRing
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
     };
-    const int nsuper = nsteps / 4;  // I % 128 == 0
+    const int nsuper = wg_steps / 4;  // I % 128 == 0
     for (int S0 = 0; S0 < nsuper; S0 += 2) {
-      psuper(S0, 0);
-      if (S0 + 1 < nsuper) psuper(S0 + 1, 1);
+      psuper(0);
+      if (S0 + 1 < nsuper) psuper(1);
     }
     return;
   }
 
   // ------------------------------ consumer ------------------------------
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // lane row / k block of each 16 x 32 fragment
-  uint32_t a_off[RT];
+  // A fragment i of this wave: row tile wave RT + i (a scalar offset) and
+  // lane's 16 bytes of it (the one per-lane offset)
+  const uint32_t a_lane = (uint32_t)lane * 16u;
+  const uint32_t a_wave = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * RT * tile_bytes;
+  // A of k step ls of tile t: 16-row tiles from mb/16 of its M block, of
+  // which those in the (16-row padded) tiled buffer exist; the buffer
+  // descriptor ends there, so later ones read as zeros.
+  auto load_a = [&](const Tile &t, int ls, u32x4 af[RT]) {
+    const int64_t rtiles = (t.row_hi + 15) / 16 - t.mb / 16;
+    const int tiles = (int)(rtiles < BM / 16 ? rtiles : BM / 16);
+    const uint32_t kb = (uint32_t)ls * 1024u;
+    const char *a_base = reinterpret_cast<const char *>(xt + (t.mb / 16) * (I / 32) * 512);
+    const __amdgpu_buffer_rsrc_t r = raw_rsrc(a_base + kb, (uint32_t)tiles * tile_bytes - kb);
 #pragma unroll
-  for (int i = 0; i < RT; ++i) a_off[i] = (uint32_t)(wave * RT + i) * tile_bytes + (uint32_t)lane * 16u;
-  auto load_a = [&](int step, u32x4 af[RT]) {
-    const __amdgpu_buffer_rsrc_t r = a_rsrc(step);
-#pragma unroll
-    for (int i = 0; i < RT; ++i) af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_off[i], 0, 0);
+    for (int i = 0; i < RT; ++i)
+      af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_lane, (int)(a_wave + (uint32_t)i * tile_bytes), 0);
   };
   // B fragment of column tile j of one k step: column 16j + fr, k
   // block fk (physical block (fk/8) ^ (j&3)), one 16-byte LDS read.
@@ -381,102 +452,157 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     b = *reinterpret_cast<const u32x4 *>(col);
   };
 
-  f32x4 acc[RT][8];
-#pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 ab[kASlots][RT], bf[8];
 #pragma unroll
-  for (int k = 0; k < kASlots; ++k) load_a(k, ab[k]);
+  for (int k = 0; k < kASlots; ++k) load_a(t0, k, ab[k]);
   __syncthreads();
-  // When both waves of a SIMD are ready, issue the consumer's MFMAs first;
-  // the producer's VALU work fills the cycles in between.
-  __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_frag(0, j, bf[j]);
   // tile 0's slot is rewritten in the producer's first super-step
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
-  // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at
-  // least one barrier earlier), which has the other seven tiles' MFMAs to
-  // arrive in; then the refill of the A slot with step s+4, and after every
-  // fourth step a barrier, once this wave's LDS reads have landed (the
-  // producer rewrites the slot of the last tile read in the next
-  // super-step).  Halving the barriers of a two-step super-step measured
-  // 202 -> 197.5 us at 2048 x 14336 -> 4096.  The scheduling barriers keep each refill after the
-  // MFMAs that read the old fragment (an MFMA reads its sources when issued).
-  auto cstep = [&](int step, u32x4(&A)[RT], bool barrier) {
-    const int next = (step + 1) % kTiles;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int i = 0; i < RT; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frag(next, j, bf[j]);
-    }
-    load_a(step + kASlots, A);
-    if (barrier) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  // (unrolled by kASlots: the A slots need constant indices; nsteps is a
-  // positive multiple of 4.  A do-while has no zero-trip path, whose join
-  // would let the compiler copy accumulators out before the drain below.)
   int step = 0;
-  do {
+  Tile t = t0;
+  for (int it = 0;;) {
+    // the next tile (this one again past the last: its A loads go unused)
+    Tile tn;
+    tile_at(it + 1 < my_tiles ? it + 1 : it, tn);
+    // This tile's accumulators (AGPRs; declared per tile, so that nothing
+    // carries them around the loop)
+    f32x4 acc[RT][8];
 #pragma unroll
-    for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3);
-    step += kASlots;
-  } while (step < nsteps);
-  __builtin_amdgcn_s_setprio(0);
-  mfma_drain();
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
-
-  // Epilogue.  Each consumer wave stages its 16 RT x 128 fp32 tile through its
-  // own LDS region, 32 rows at a time; a lane then holds 4 consecutive columns
-  // of one row: bias added in fp32, one rounding, one 8-byte store (16 bytes
-  // for fp32 output), so every row's 128 columns leave as whole cache lines.
-  float *stg = stage[wave];
-  const int64_t m0 = mb + wave * 16 * RT;
-  const int sc = (lane & 31) * 4, srow = lane >> 5;  // quad column, row parity of this lane
-  const int64_t n = n0 + sc;
-  const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
-  f32x4 bias4{0.f, 0.f, 0.f, 0.f};
-  if (bias && n_ok) {
-    const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
-    bias4 = f32x4{f16_bits_to_f32(bb[0] & 0xffffu), f16_bits_to_f32(bb[0] >> 16), f16_bits_to_f32(bb[1] & 0xffffu),
-                  f16_bits_to_f32(bb[1] >> 16)};
-  }
-#pragma unroll
-  for (int p = 0; p < RT / 2; ++p) {
-    // D of tile (i, j): row 16i + 4(lane/16) + r, column 16j + lane%16
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          stg[(16 * ii + (lane >> 4) * 4 + r) * kStageRS + 16 * j + fr] = acc[2 * p + ii][j][r];
-    wave_lds_sync();
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int lr = 2 * rr + srow;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + lr * kStageRS + sc) + bias4;
-      const int64_t row = m0 + 32 * p + lr;
-      if (row >= row_lo && row < row_hi && n_ok) {
-        if (a.y_dt == kF32) {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * O + n) = v;
-        } else {
-          const u32x2 o = a.y_dt == kF16 ? u32x2{pack2<kF16>(v[0], v[1]), pack2<kF16>(v[2], v[3])}
-                                         : u32x2{pack2<kBF16>(v[0], v[1]), pack2<kBF16>(v[2], v[3])};
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.y) + row * O + n) = o;
-        }
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_fence(acc[i][j]);
       }
+    asm volatile("s_nop 7");  // accumulator writes -> first MFMA
+    // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
+    // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at
+    // least one barrier earlier), which has the other seven tiles' MFMAs to
+    // arrive in; then the refill of the A slot with step s+4 (k step la of
+    // tile ta), and after every fourth step a barrier, once this wave's LDS
+    // reads have landed (the producer rewrites the slot of the last tile
+    // read in the next super-step).  Halving the barriers of a two-step
+    // super-step measured 202 -> 197.5 us at 2048 x 14336 -> 4096.  The
+    // scheduling barriers keep each refill after the MFMAs that read the old
+    // fragment (an MFMA reads its sources when issued).  Steps and ring
+    // slots run on across the workgroup's tiles: the last step of a tile
+    // refills with the first of the next.
+    auto cstep = [&](int step, u32x4(&A)[RT], bool barrier, const Tile &ta, int la, bool reload_a = true) {
+      const int next = (step + 1) % kTiles;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frag(next, j, bf[j]);
+      }
+      if (reload_a) load_a(ta, la, A);
+      if (barrier) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    // When both waves of a SIMD are ready, issue the consumer's MFMAs first;
+    // the producer's VALU work fills the cycles in between.
+    __builtin_amdgcn_s_setprio(2);
+    // Super-steps of 4 (the A slots need constant indices; nsteps is a
+    // positive multiple of 4).  All but the last load A of this tile four
+    // steps ahead; the last one loads the next tile's first four steps, so
+    // no branch on the tile sits inside the loop.
+    int ls = 0;
+    while (ls + kASlots < nsteps) {
+#pragma unroll
+      for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3, t, ls + kASlots + k);
+      step += kASlots;
+      ls += kASlots;
     }
-    wave_lds_sync();  // this pass's reads are done before the next pass's writes
+    // (the B fragments of the next tile's first step are read here, before
+    // the barrier after which the producers rewrite their slot; of its A
+    // steps only the first two are loaded before the epilogue, the other two
+    // after it, so that fewer registers are live through it)
+#pragma unroll
+    for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3, tn, k, k < 2);
+    step += kASlots;
+    __builtin_amdgcn_s_setprio(0);
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
+
+    // Epilogue.  Each consumer wave stages its 16 RT x 128 fp32 tile through
+    // its own LDS region (apart from the weight ring, which the producers
+    // keep filling), 32 rows at a time; a lane then holds 4 consecutive
+    // columns of one row: bias added in fp32, one rounding, one 8-byte store
+    // (16 bytes for fp32 output), so every row's 128 columns leave as whole
+    // cache lines.
+    // (the lane index is laundered through an empty asm so that the
+    // compiler computes the epilogue's addresses here, per tile, instead of
+    // hoisting them out of the tile loop into registers held through the
+    // main loop)
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int efr = el & 15;
+    float *stg = stage[wave];
+    const int64_t m0 = t.mb + wave * 16 * RT;
+    const int sc = (el & 31) * 4, srow = el >> 5;  // quad column, row parity of this lane
+    const int64_t n = t.n0 + sc;
+    const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
+    // rows m0 + lo .. m0 + hi - 1 of this wave's 16 RT are stored
+    const int64_t lo64 = t.row_lo - m0, hi64 = t.row_hi - m0;
+    const int lo = (int)(lo64 < 0 ? 0 : lo64 > 16 * RT ? 16 * RT : lo64);
+    const int hi = n_ok ? (int)(hi64 < 0 ? 0 : hi64 > 16 * RT ? 16 * RT : hi64) : 0;
+    f32x4 bias4{0.f, 0.f, 0.f, 0.f};
+    if (t.bias && n_ok) {
+      const u32x2 bb = *reinterpret_cast<const u32x2 *>(t.bias + n);
+      bias4 = f32x4{f16_bits_to_f32(bb[0] & 0xffffu), f16_bits_to_f32(bb[0] >> 16),
+                    f16_bits_to_f32(bb[1] & 0xffffu), f16_bits_to_f32(bb[1] >> 16)};
+    }
+    // one copy of the passes per output dtype (no dtype test per store)
+    auto epilogue = [&](auto ydt) {
+      constexpr int YD = decltype(ydt)::value;
+      typedef typename std::conditional<YD == kF32, float, uint16_t>::type YT;
+      YT *ybase = reinterpret_cast<YT *>(a.y) + m0 * O + n;
+#pragma unroll
+      for (int p = 0; p < RT / 2; ++p) {
+        // D of tile (i, j): row 16i + 4(lane/16) + r, column 16j + lane%16
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              stg[(16 * ii + (el >> 4) * 4 + r) * kStageRS + 16 * j + efr] = acc[2 * p + ii][j][r];
+            __builtin_amdgcn_sched_barrier(0);  // four accumulators in flight at a time
+          }
+        wave_lds_sync();
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int lr = 2 * rr + srow, row = 32 * p + lr;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + lr * kStageRS + sc) + bias4;
+          if (row >= lo && row < hi) {
+            YT *dst = ybase + (int64_t)row * O;
+            if constexpr (YD == kF32)
+              *reinterpret_cast<f32x4 *>(dst) = v;
+            else
+              *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2<YD>(v[0], v[1]), pack2<YD>(v[2], v[3])};
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wave_lds_sync();  // this pass's reads are done before the next pass's writes
+      }
+    };
+    if (a.y_dt == kF32)
+      epilogue(std::integral_constant<int, kF32>());
+    else if (a.y_dt == kF16)
+      epilogue(std::integral_constant<int, kF16>());
+    else
+      epilogue(std::integral_constant<int, kBF16>());
+    if (++it >= my_tiles) break;
+    t = tn;
+    load_a(t, 2, ab[2]);
+    load_a(t, 3, ab[3]);
   }
 }
 
@@ -515,6 +641,19 @@ static int dense_tile_rows(int64_t tokens, int64_t n_tiles) {
   return ((tokens + 255) / 256) * n_tiles < kCUs ? 128 : 256;
 }
 
+// Workgroups of a dense launch: one per CU, each taking every kCUs-th tile
+// (a multiple of the 8 XCDs, so that a workgroup's tiles stay on its XCD in
+// the tile order); fewer tiles than CUs give one tile per workgroup.
+// PARO_PREFILL_PERSIST=0 gives every tile its own workgroup (tuning), read
+// once per process.
+static int64_t persistent_grid(int64_t tiles) {
+  static const bool on = [] {
+    const char *v = getenv("PARO_PREFILL_PERSIST");
+    return !(v && *v && atoi(v) == 0);
+  }();
+  return on && tiles > kCUs ? kCUs : tiles;
+}
+
 int64_t moe_work_tiles(int64_t tokens, int experts) {
   // sum over experts of ceil((rows + up to 15 rows of the first 16-row tile) / 256)
   return (tokens + 15 * (int64_t)experts + kBM - 1) / kBM + experts;
@@ -526,10 +665,12 @@ hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream
     launch_prefill_moe<true, 4>(a, x, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
   } else {
     const int bm = dense_tile_rows(a.tokens, n_tiles);
+    const int64_t tiles = n_tiles * ((a.tokens + bm - 1) / bm);
+    const dim3 grid((unsigned)persistent_grid(tiles));
     if (bm == 128)
-      launch_prefill_moe<false, 2>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + 127) / 128))), st);
+      launch_prefill_moe<false, 2>(a, x, grid, st);
     else
-      launch_prefill_moe<false, 4>(a, x, dim3((unsigned)(n_tiles * ((a.tokens + 255) / 256))), st);
+      launch_prefill_moe<false, 4>(a, x, grid, st);
   }
   return hipGetLastError();
 }

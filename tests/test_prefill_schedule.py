@@ -12,14 +12,18 @@ conditions that make the ring race-free:
 The numbers below restate the kernel's schedule: the producer expands tiles
 0..4 before the first barrier, passes one extra barrier, then expands four
 tiles (4S+5 .. 4S+8) per super-step S; the consumers read tile 0 between the
-first two barriers and tiles 4S+1 .. 4S+4 during super-step S.
+first two barriers and tiles 4S+1 .. 4S+4 during super-step S.  A persistent
+workgroup numbers its steps across its output tiles, so several tiles are
+one long schedule; between two output tiles the consumers run the epilogue,
+which touches no ring slot, and they must read the next tile's first weight
+tile during the last super-step of the previous one (not after the epilogue).
 """
 import pytest
 
 SLOTS = 8
 
 
-def schedule(nsteps, extra_barrier=True):
+def schedule(nsteps, extra_barrier=True, late_refill_every=0):
     """Lists of (interval, role, tile) events; interval i lies between
     barrier i-1 and barrier i (interval 0 precedes the first barrier)."""
     ev = []
@@ -31,8 +35,13 @@ def schedule(nsteps, extra_barrier=True):
         iv = first + S
         for u in range(4):
             ev.append((iv, "w", 4 * S + 5 + u))   # past the end too: clamped tiles still land in slots
-            if 4 * S + 1 + u < nsteps:
-                ev.append((iv, "r", 4 * S + 1 + u))
+            t = 4 * S + 1 + u
+            if t >= nsteps:
+                continue
+            # late_refill_every = n: the first weight tile of every n-step
+            # output tile read after the barrier ending the previous one
+            late = late_refill_every and t % late_refill_every == 0
+            ev.append((iv + 1 if late else iv, "r", t))
     return ev
 
 
@@ -72,3 +81,16 @@ def test_model_detects_the_single_barrier_schedule():
     """Without the extra barrier, tile 8 lands in slot 0 while tile 0 is read."""
     bad = violations(schedule(8, extra_barrier=False))
     assert any("slot(s) [0]" in b for b in bad)
+
+
+@pytest.mark.parametrize("tile_steps", [4, 8, 128])
+def test_persistent_schedule_over_several_output_tiles(tile_steps):
+    """Seven output tiles of tile_steps k steps each in one workgroup."""
+    assert violations(schedule(7 * tile_steps)) == []
+
+
+def test_model_detects_a_refill_after_the_epilogue():
+    """Reading the next output tile's first weight tile after the barrier
+    that ends the previous tile races with the producers' next super-step,
+    which rewrites that slot."""
+    assert any("slot(s)" in b for b in violations(schedule(7 * 8, late_refill_every=8)))

@@ -59,6 +59,13 @@ def build(extra=(), verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel template whose host pass fails quietly leaves its launch stub
+    # undefined: the library would then not load.  Refuse such a link.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"link left {len(missing)} kernel launch stubs undefined, e.g. {missing[0]}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

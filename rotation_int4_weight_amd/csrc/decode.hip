@@ -9,26 +9,28 @@
 //
 // Work split.  A k-step is 32 rows of the weight.  A workgroup (NW waves)
 // owns a tile of 128*WPL output columns and NW*KSW consecutive k-steps; wave
-// w takes KSW consecutive k-steps of them.  For one k-step a lane loads the 8 rows of
-// its 8-row block (lane>>4) of its WPL consecutive packed words (lane&15), so
-// the 16 lanes of a block read 64*WPL contiguous bytes of each row (256 B
-// with WPL = 4).  A wave issues the loads of all its k-steps before it
-// computes, in the order it consumes them, so the MFMAs of a k-step start as
-// soon as its own loads have landed.  Each packed word turns into eight MFMA
+// w takes KSW consecutive k-steps of them.  The tile's row segments (64*WPL
+// contiguous bytes per weight row) go straight from HBM into LDS: at entry
+// every wave issues 1 KB buffer-to-LDS loads for all its k-steps, after its
+// few register loads, so the weight stream holds no VGPRs and each k-step
+// waits only for its own loads (vmcnt counts them in order).  A lane then
+// reads the 8 rows of its 8-row block (lane>>4) of its WPL packed words
+// (lane&15) from LDS.  Each packed word turns into eight MFMA
 // B fragments (one per nibble slot = one output column each), so no
-// transpose is needed: v_perm_b32 gathers the bytes of a row pair and an OR
-// with an exponent-bias constant turns a nibble into a half-precision number
+// transpose is needed: v_perm_b32 gathers the bytes of a row pair and one
+// v_and_or_b32 with an exponent-bias constant turns a nibble into a
+// half-precision number
 // (fp16: 0x6400|q = 1024+q, 0x6400|(q<<4) = 1024+16q; bf16: 0x4300|q =
 // 128+q).  The offset and the zero point are removed with the row sums of the
 // rounded activations, which one extra MFMA against a fragment of ones
 // produces in the output layout:
 //   sum_k x (off + c*q) = off*xsum + c*sum_k x q
 //   =>  sum_k x (q - z) = (acc - (off + c*z) * xsum) / c,
-// folded into the running sum with the group scale once per group (or per
-// k-step when a wave owns a single k-step; the fold is linear, so both are the
-// same sum).  v_mfma_f32_16x16x32_{f16,bf16}: lane l holds A row l&15 and B
-// column l&15 of its 8-element k block; the 16x16 fp32 result has row
-// 4*(l>>4)+r, column l&15 in register r.
+// folded into the running sum with the group scale at the end of every
+// 128-row block and of the wave's k-steps (the fold is linear, so folding a
+// group in pieces gives the same sum).  v_mfma_f32_16x16x32_{f16,bf16}: lane
+// l holds A row l&15 and B column l&15 of its 8-element k block; the 16x16
+// fp32 result has row 4*(l>>4)+r, column l&15 in register r.
 //
 // Workgroups are numbered tile-fastest (all column tiles of split 0, then of
 // split 1, ...) and that order is dealt out to the XCDs in contiguous runs
@@ -36,20 +38,23 @@
 // at the same time and their row segments merge in its L2 into long DRAM
 // bursts.
 //
-// Reduction.  The NW waves' tiles are summed in LDS in wave order, each
-// thread taking quads of 4 consecutive outputs.  With one K split the
+// Reduction.  The NW waves' tiles are summed in LDS in wave order, in
+// "slots" of 4 consecutive outputs laid out so that stores and loads are
+// consecutive 16-byte chunks (see the kernel).  With one K split the
 // workgroup adds the bias and stores y.  Otherwise it stores its fp32 partial
 // with 16-byte device-coherent stores (SC1: coherent across the XCDs' L2
 // caches without whole-cache write-backs), waits for them, and bumps a
 // device-scope counter; the last workgroup of the column tile to arrive
-// loads every split's quads with 16-byte device-coherent loads, all in flight
+// loads every split's slots with 16-byte device-coherent loads, all in flight
 // together, sums them in split order, adds the bias, stores y and resets the
 // counter.  The result is independent of arrival order (bitwise
 // deterministic).
 #include <stdlib.h>
 
-#include "common.hpp"
+#include <type_traits>
+
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace paro {
 
@@ -87,12 +92,24 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    0, 0);
 }
 
+// The nibble masks and the exponent pattern, held in VGPRs: each fragment
+// word is then one v_and_or_b32 (with literal operands the compiler emits an
+// AND and an OR, since the three-operand form takes no literal here).
+struct NibbleMasks {
+  uint32_t lo, hi, magic;
+};
+template <int DT>
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m{0x000f000fu, 0x00f000f0u, MfmaTypes<DT>::kMagic};
+  asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.magic));
+  return m;
+}
+
 // B fragment of nibble slot `s` from the 8 row words r[0..7] (rows k0..k0+7)
 // of one packed column word.  Element e of the fragment is row k0+e.
 // fp16: even slots give 1024+q, odd slots 1024+16q; bf16: 128+q everywhere.
 template <int DT>
-__device__ __forceinline__ void build_b_frags(const uint32_t r[8], u32x4 out[8]) {
-  constexpr uint32_t M = MfmaTypes<DT>::kMagic;
+__device__ __forceinline__ void build_b_frags(const uint32_t r[8], u32x4 out[8], const NibbleMasks &m) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // P = [ra.b0, ra.b2, rb.b0, rb.b2], Q = [ra.b1, ra.b3, rb.b1, rb.b3]
@@ -100,23 +117,23 @@ __device__ __forceinline__ void build_b_frags(const uint32_t r[8], u32x4 out[8])
     const uint32_t Q = __builtin_amdgcn_perm(r[2 * i], r[2 * i + 1], 0x03010705u);
     const uint32_t P8 = P >> 8, Q8 = Q >> 8;
     if constexpr (DT == kF16) {
-      out[0][i] = (P & 0x000f000fu) | M;
-      out[1][i] = (P & 0x00f000f0u) | M;
-      out[2][i] = (Q & 0x000f000fu) | M;
-      out[3][i] = (Q & 0x00f000f0u) | M;
-      out[4][i] = (P8 & 0x000f000fu) | M;
-      out[5][i] = (P8 & 0x00f000f0u) | M;
-      out[6][i] = (Q8 & 0x000f000fu) | M;
-      out[7][i] = (Q8 & 0x00f000f0u) | M;
+      out[0][i] = (P & m.lo) | m.magic;
+      out[1][i] = (P & m.hi) | m.magic;
+      out[2][i] = (Q & m.lo) | m.magic;
+      out[3][i] = (Q & m.hi) | m.magic;
+      out[4][i] = (P8 & m.lo) | m.magic;
+      out[5][i] = (P8 & m.hi) | m.magic;
+      out[6][i] = (Q8 & m.lo) | m.magic;
+      out[7][i] = (Q8 & m.hi) | m.magic;
     } else {
-      out[0][i] = (P & 0x000f000fu) | M;
-      out[1][i] = ((P >> 4) & 0x000f000fu) | M;
-      out[2][i] = (Q & 0x000f000fu) | M;
-      out[3][i] = ((Q >> 4) & 0x000f000fu) | M;
-      out[4][i] = (P8 & 0x000f000fu) | M;
-      out[5][i] = ((P >> 12) & 0x000f000fu) | M;
-      out[6][i] = (Q8 & 0x000f000fu) | M;
-      out[7][i] = ((Q >> 12) & 0x000f000fu) | M;
+      out[0][i] = (P & m.lo) | m.magic;
+      out[1][i] = ((P >> 4) & m.lo) | m.magic;
+      out[2][i] = (Q & m.lo) | m.magic;
+      out[3][i] = ((Q >> 4) & m.lo) | m.magic;
+      out[4][i] = (P8 & m.lo) | m.magic;
+      out[5][i] = ((P >> 12) & m.lo) | m.magic;
+      out[6][i] = (Q8 & m.lo) | m.magic;
+      out[7][i] = ((Q >> 12) & m.lo) | m.magic;
     }
   }
 }
@@ -127,17 +144,28 @@ __device__ __forceinline__ constexpr float slot_mult(int s) {
   return (DT == kF16 && (s & 1)) ? 16.0f : 1.0f;
 }
 
-// Load WPL consecutive packed words of one row (one vector load when WPL > 1).
-template <int WPL>
-__device__ __forceinline__ void load_words(const int32_t *__restrict__ p, uint32_t out[WPL]) {
-  if constexpr (WPL == 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-  } else if constexpr (WPL == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
-    out[0] = v[0]; out[1] = v[1];
-  } else {
-    out[0] = (uint32_t)p[0];
+// Bytes of weight rows one wave holds in LDS: KSW k-steps of 32 rows of the
+// tile's 64*WPL-byte row segment.
+constexpr int decode_wave_lds(int wpl, int ksw) { return ksw * 32 * 64 * wpl; }
+
+// s_waitcnt immediate for "at most n vector-memory loads outstanding", the
+// other counters left open (gfx9-family encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// One 1 KB global -> LDS load: lane l's 16 bytes at `voff` land at lds + 16l.
+// (A plain device function: inside a kernel template the builtin would keep
+// the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void dma_1k(__amdgpu_buffer_rsrc_t r, unsigned char *lds, uint32_t voff) {
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, 0, 0, 0);
+}
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -150,15 +178,21 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   constexpr int FR = MT < 4 ? MT : 4;
   constexpr int NT = 8 * WPL;                 // MFMA column tiles per wave
   constexpr int NG = KSW < 4 ? 1 : KSW / 4;   // groups a wave touches (its k-steps are aligned)
-  // k-steps of loads kept in flight (16-wave groups have half the registers)
-  constexpr int PD = KSW < (NW >= 16 ? 2 : 4) ? KSW : (NW >= 16 ? 2 : 4);
   constexpr int NTH = 64 * NW;
   constexpr int NTILE = 128 * WPL;
-  constexpr int QUADS = MT * NTILE / 4;                 // 4-column output quads of the tile
-  constexpr int QPT = (QUADS + NTH - 1) / NTH;          // quads per thread
-  extern __shared__ __attribute__((aligned(16))) float smem[];
+  constexpr int KBV = (MT + 3) / 4;                     // lane groups (kb) holding real rows
+  constexpr int QUADS = MT * NTILE / 4;                 // output slots of the tile (16 bytes each)
+  constexpr int QPT = (QUADS + NTH - 1) / NTH;          // slots per thread
+  static_assert(QUADS == 2 * WPL * FR * 16 * KBV, "slot numbering covers the tile");
+  constexpr int RB = 64 * WPL;                          // bytes of one weight row of the tile
+  constexpr int LPR = 4 * WPL;                          // 16-byte lanes per row in one DMA load
+  constexpr int RPI = 64 / LPR;                         // rows per DMA load (1 KB)
+  constexpr int NI = 32 / RPI;                          // DMA loads per k-step
+  constexpr int WLDS = decode_wave_lds(WPL, KSW);
+  static_assert(KSW * NI <= 63, "the k-step waits count at most 63 loads");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
-  const int lane = lane_id(), wave = wave_id();
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int cl = lane & 15, kb = lane >> 4;
   const int n_tiles = (int)((a.O + NTILE - 1) / NTILE);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * splits);
@@ -171,28 +205,44 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   const uint16_t *__restrict__ x = reinterpret_cast<const uint16_t *>(a.x);
   const int64_t n0 = (int64_t)tile * NTILE;
 
+  // ---- output slots ----
+  // A slot is a 16-byte chunk of 4 consecutive columns of one row of the
+  // tile: the chunk that lane (kb, cl) holds for its store number instr in
+  // the reduction below,
+  //   s = instr * 16 * KBV + kb * 16 + cl,   instr = (w * FR + i) * 2 + h,
+  //   row = 4 * kb + i,   column = (cl * WPL + w) * 8 + 4 * h,
+  // where KBV = ceil(MT / 4) lane groups hold real rows.  The LDS reduction
+  // tiles and the split-K partials are slot-major, so every wave's stores and
+  // every thread's loads there are consecutive 16-byte chunks (no LDS bank
+  // conflicts); thread t owns slots t, t + NTH, ...
+  auto slot_pos = [](int sl, int &row, int &col) {
+    const int instr = sl / (16 * KBV), r = sl % (16 * KBV);
+    const int h = instr % 2, i = (instr / 2) % FR, w = instr / (2 * FR);
+    row = 4 * (r / 16) + i;
+    col = ((r % 16) * WPL + w) * 8 + 4 * h;
+  };
+
   // ---- small early loads: this thread's bias values ----
-  // Quad q holds outputs 4q..4q+3 of the tile ([row][col], NTILE columns per
-  // row); a quad is entirely inside or entirely past O (O % 8 == 0).
   // Branch-free: every load reads a valid address (a stand-in tensor when
   // there is no bias, a clamped column past O) and the value is selected
-  // afterwards.  A conditional load would make the compiler wait for it at
-  // the join, i.e. one full memory round trip before the weight stream.
+  // afterwards.  A slot is entirely inside or entirely past O (O % 8 == 0).
   float bias_v[QPT][4];
   const uint16_t *bias_src = a.bias ? a.bias : a.scales;
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
-    const int q = threadIdx.x + j * NTH;
-    const int64_t n = n0 + (4 * q) % NTILE;
-    const bool use = a.bias && q < M * NTILE / 4 && n < O;
+    const int sl = threadIdx.x + j * NTH;
+    int row, col;
+    slot_pos(sl, row, col);
+    const int64_t n = n0 + col;
+    const bool use = a.bias && sl < QUADS && row < M && n < O;
     const u32x2 b = *reinterpret_cast<const u32x2 *>(bias_src + (n < O ? n : O - 4));
 #pragma unroll
     for (int c = 0; c < 4; ++c) bias_v[j][c] = use ? f16_bits_to_f32((b[c >> 1] >> (16 * (c & 1))) & 0xffffu) : 0.0f;
   }
 
-  // Columns past O (last tile only) read an in-bounds word and are zeroed;
-  // their outputs are never stored.  WPL words never straddle O (O % 16 == 0
-  // for WPL == 2, O % 32 == 0 for WPL == 4).
+  // Columns past O (last tile only) get zero scales, so whatever weight bits
+  // they read contribute nothing; their outputs are never stored.  WPL words
+  // never straddle O (O % 16 == 0 for WPL == 2, O % 32 == 0 for WPL == 4).
   const int64_t wbase = (int64_t)tile * 16 * WPL + cl * WPL;
   const bool wok = wbase < W;
   const int64_t wcl = wok ? wbase : W - WPL;
@@ -207,13 +257,13 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     // 128-channel rotation blocks hold 4 k-steps; quantization groups hold
     // G/32 = 1 << gsh (with G < 128 the plan gives each wave one k-step).  One
     // group over the whole row (G = I > 128, any multiple of 128): a shift
-    // past every k-step, so all fall in group 0 and each wave folds once, at
-    // its last k-step (its rotation ran in a separate pass).
+    // past every k-step, so all fall in group 0 (its rotation ran in a
+    // separate pass).
     const bool row_group = a.group == I && a.group > kG;
     const int gsh = row_group ? 30 : __builtin_ctz((unsigned)a.group) - 5, gmask = kG - a.group;
     const int64_t g_first = ks0 / 4, q_first = ks0 >> gsh, nq = I / a.group;
-    float *xs = smem + wave * (MT * kDecodeRS);  // fused rotation rows of this wave
-    // ---- fused: the first group's rotation inputs, before the weight stream ----
+    float *xs = reinterpret_cast<float *>(smem + NW * WLDS) + wave * (MT * kDecodeRS);  // fused rotation rows
+    // ---- fused: the first group's rotation inputs ----
     RotParams rp;
     float xin[MT][2];
     float cs0 = 0.f, cs1 = 0.f;
@@ -231,18 +281,15 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     };
     if constexpr (FUSED) load_rot_inputs(g_first);
 
-    // ---- A fragments (non-fused), group scales / zeros, then the weights of
-    //      the first PD k-steps, in the order they are consumed ----
+    // ---- A fragments (non-fused), group scales and zeros ----
     u32x4 af[KSW];
     const int arow = cl < M ? cl : 0;
-    auto load_a = [&](int k) {  // non-fused: rotated activations from the workspace
-      const int64_t ks = ks0 + (k < nk ? k : 0);
-      af[k] = *reinterpret_cast<const u32x4 *>(xr + (int64_t)arow * I + ks * 32 + kb * 8);
-      if (cl >= M) af[k] = u32x4{0u, 0u, 0u, 0u};
-    };
     if constexpr (!FUSED) {
 #pragma unroll
-      for (int k = 0; k < PD; ++k) load_a(k);
+      for (int k = 0; k < KSW; ++k) {
+        const int64_t ks = ks0 + (k < nk ? k : 0);
+        af[k] = *reinterpret_cast<const u32x4 *>(xr + (int64_t)arow * I + ks * 32 + kb * 8);
+      }
     }
     u32x4 sv[NG][WPL];
     uint32_t zv[NG][WPL];
@@ -253,19 +300,50 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
 #pragma unroll
       for (int w = 0; w < WPL; ++w) {
         sv[gi][w] = *reinterpret_cast<const u32x4 *>(a.scales + g * O + 8 * (wcl + w));  // wcl is in bounds
-        if (!wok) sv[gi][w] = u32x4{0u, 0u, 0u, 0u};
         zv[gi][w] = (uint32_t)a.qzeros[g * W + wcl + w];
       }
     }
-    uint32_t qv[KSW][8][WPL];
-    auto load_ks = [&](int k) {
-      const int64_t ks = ks0 + (k < nk ? k : 0);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) load_words<WPL>(a.qweight + (ks * 32 + kb * 8 + r) * W + wcl, qv[k][r]);
-    };
-#pragma unroll
-    for (int k = 0; k < PD; ++k) load_ks(k);
 
+    // ---- the weight rows of every k-step, straight into LDS ----
+    // Issued after every other load of the prologue, so the per-k-step waits
+    // below count only these.  One DMA load moves 1 KB: lane l's 16 bytes
+    // land at slot l, i.e. LDS row position pos = j*RPI + l/LPR, chunk l%LPR.
+    // Position pos holds k-step row (pos%4)*8 + pos/4, so the rows that the
+    // four 8-row blocks read together sit in different LDS banks.  The raw
+    // buffer covers this wave's rows only: offsets past them (columns past O
+    // in the last row) read zeros instead of memory.
+    const uint32_t W4 = (uint32_t)(W * 4);
+    const __amdgpu_buffer_rsrc_t rw =
+        raw_rsrc(a.qweight + ks0 * 32 * W, (uint32_t)nk * 32u * W4);
+    unsigned char *wl = smem + wave * WLDS;
+    uint32_t voff[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int pos = j * RPI + lane / LPR;
+      const int row = (pos & 3) * 8 + (pos >> 2);
+      voff[j] = (uint32_t)row * W4 + (uint32_t)tile * RB + (uint32_t)(lane % LPR) * 16u;
+    }
+    // Every wave issues all KSW k-steps (those past nk fall outside the
+    // buffer and move zeros), so each k-step below waits for a fixed count.
+#pragma unroll
+    for (int k = 0; k < KSW; ++k)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        dma_1k(rw, wl + k * 32 * RB + j * 1024, voff[j] + (uint32_t)k * 32u * W4);
+
+    // Nothing above may wait for a load: the weight stream starts first.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int w = 0; w < WPL; ++w)
+        if (!wok) sv[gi][w] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!FUSED) {  // rows past M multiply as zeros
+#pragma unroll
+      for (int k = 0; k < KSW; ++k)
+        if (cl >= M) af[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const NibbleMasks nm = nibble_masks<DT>();
     const u32x4 ones = {MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes, MfmaTypes<DT>::kOnes,
                         MfmaTypes<DT>::kOnes};
     f32x4 acc[NT];
@@ -273,12 +351,16 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int k = 0; k < KSW; ++k) {
+    static_for<0, KSW>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
       if (k < nk) {
         const int64_t ks = ks0 + k;
-        const int64_t g = ks / 4;                     // rotation block
-        const int gi = (int)((ks >> gsh) - q_first);  // quantization group of this wave
+        const int64_t g = ks / 4;  // rotation block
+        // quantization group of this wave: k-step k of a wave lies in its
+        // group k/4 (G = 128: the wave's first k-step starts a group when it
+        // owns more than two; G < 128: one k-step; one group over the row:
+        // every entry holds group 0)
+        constexpr int gi = k / 4;
         if constexpr (FUSED) {
           if (k == 0 || (ks % 4) == 0) {  // entering a group: rotate it into LDS
             if (k != 0) load_rot_inputs(g);
@@ -299,24 +381,35 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
                         pack2<DT>(hi.z, hi.w)};
           if (cl >= M) af[k] = u32x4{0u, 0u, 0u, 0u};
         }
-        if (k + PD < KSW) {  // keep PD k-steps in flight
-          if constexpr (!FUSED) load_a(k + PD);
-          load_ks(k + PD);
+        // this k-step's rows have landed in LDS (later k-steps may still be in flight)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((KSW - 1 - k) * NI));
+        const unsigned char *wk = wl + k * 32 * RB + cl * WPL * 4;
+        uint32_t rw8[WPL][8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const unsigned char *p = wk + (r * 4 + kb) * RB;
+          if constexpr (WPL == 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+            rw8[0][r] = v[0]; rw8[1][r] = v[1]; rw8[2][r] = v[2]; rw8[3][r] = v[3];
+          } else if constexpr (WPL == 2) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+            rw8[0][r] = v[0]; rw8[1][r] = v[1];
+          } else {
+            rw8[0][r] = *reinterpret_cast<const uint32_t *>(p);
+          }
         }
         xsum = mfma16<DT>(af[k], ones, xsum);
 #pragma unroll
         for (int w = 0; w < WPL; ++w) {
-          uint32_t rw[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) rw[r] = qv[k][r][w];
           u32x4 bf[8];
-          build_b_frags<DT>(rw, bf);
+          build_b_frags<DT>(rw8[w], bf, nm);
 #pragma unroll
           for (int s = 0; s < 8; ++s) acc[w * 8 + s] = mfma16<DT>(af[k], bf[s], acc[w * 8 + s]);
         }
-        // fold at the end of a group or of this wave's k-steps:
+        // fold at the end of a 128-row block or of this wave's k-steps (a
+        // whole-row group folds once per block, the fold being linear):
         //   tot += s/c * (acc - (off + c*z) * xsum)
-        if (((ks + 1) & ((1 << gsh) - 1)) == 0 || k == nk - 1) {
+        if (k % 4 == 3 || k == nk - 1) {
 #pragma unroll
           for (int w = 0; w < WPL; ++w) {
 #pragma unroll
@@ -328,56 +421,57 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
               const float zz = MfmaTypes<DT>::kOff + c * (float)((zv[gi][w] >> (4 * s)) & 0xfu);
 #pragma unroll
               for (int i = 0; i < FR; ++i) tot[w * 8 + s][i] += sc * (acc[w * 8 + s][i] - zz * xsum[i]);
-              acc[w * 8 + s] = f32x4{0.f, 0.f, 0.f, 0.f};
+              if (k + 1 < KSW) acc[w * 8 + s] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
           }
-          xsum = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (k + 1 < KSW) xsum = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
-    }
+    });
   }
 
-  // ---- reduce the NW waves' tiles in LDS (wave order) ----
-  __syncthreads();   // every wave is done with its rotation rows
-  float *red = smem; // [NW][MT][NTILE]
+  // ---- reduce the NW waves' tiles in LDS (wave order), slot-major ----
+  __syncthreads();  // every wave is done with its weight and rotation rows
+  f32x4 *red = reinterpret_cast<f32x4 *>(smem);  // [NW][QUADS]
+  if (kb < KBV) {
 #pragma unroll
-  for (int w = 0; w < WPL; ++w) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int col = (cl * WPL + w) * 8 + awq_col(s);
+    for (int w = 0; w < WPL; ++w) {
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
-        const int row = 4 * kb + i;
-        if (row < MT) red[(wave * MT + row) * NTILE + col] = tot[w * 8 + s][i];
+        // column c of the word is nibble slot 4 * (c & 1) + c / 2
+        f32x4 *dst = red + wave * QUADS + ((w * FR + i) * 2) * 16 * KBV + kb * 16 + cl;
+        dst[0] = f32x4{tot[w * 8 + 0][i], tot[w * 8 + 4][i], tot[w * 8 + 1][i], tot[w * 8 + 5][i]};
+        dst[16 * KBV] = f32x4{tot[w * 8 + 2][i], tot[w * 8 + 6][i], tot[w * 8 + 3][i], tot[w * 8 + 7][i]};
       }
     }
   }
   __syncthreads();
 
-  // quads of this thread: sum over the waves in wave order
-  const int nq = M * NTILE / 4;  // quads holding real rows
+  // this thread's slots: sum over the waves in wave order
   f32x4 v[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
-    const int q = threadIdx.x + j * NTH;
+    const int sl = threadIdx.x + j * NTH;
     v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (q < nq) {
+    if (sl < QUADS) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v[j] += *reinterpret_cast<const f32x4 *>(red + w * MT * NTILE + 4 * q);
+      for (int w = 0; w < NW; ++w) v[j] += red[w * QUADS + sl];
     }
   }
-  auto quad_out = [&](int j, int &row, int64_t &n) {
-    const int q = threadIdx.x + j * NTH;
-    row = (4 * q) / NTILE;
-    n = n0 + (4 * q - row * NTILE);
-    return q < nq && n < O;
+  // slot j of this thread: its row and output column, and whether it is stored
+  auto slot_out = [&](int j, int &row, int64_t &n) {
+    const int sl = threadIdx.x + j * NTH;
+    int col;
+    slot_pos(sl, row, col);
+    n = n0 + col;
+    return sl < QUADS && row < M && n < O;
   };
-  auto store_quads = [&](const f32x4 *val) {
+  auto store_slots = [&](const f32x4 *val) {
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       int row;
       int64_t n;
-      if (quad_out(j, row, n)) {
+      if (slot_out(j, row, n)) {
         const float o0 = val[j][0] + bias_v[j][0], o1 = val[j][1] + bias_v[j][1];
         const float o2 = val[j][2] + bias_v[j][2], o3 = val[j][3] + bias_v[j][3];
         if (a.y_dt == kF32) {
@@ -392,24 +486,25 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     }
   };
   if (splits == 1) {
-    store_quads(v);
+    store_slots(v);
     return;
   }
 
   // ---- split-K handoff (see the header) ----
-  // partial: [tile][split][M][NTILE] fp32.  One raw buffer per tile: its
-  // splits * M * NTILE * 4 bytes (at most 2^14 * 16 * 512 * 4 = 2^29) keep
-  // every offset in 32 bits.
-  const uint32_t sstride = (uint32_t)(M * NTILE);  // floats per split
+  // partial: [tile][split][QUADS] 16-byte slots.  One raw buffer per tile:
+  // its splits * QUADS * 16 bytes (at most 2^14 * 2048 * 16 = 2^29) keep every
+  // offset in 32 bits.
+  constexpr uint32_t sstride = (uint32_t)QUADS * 16u;  // bytes per split
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      partial + (int64_t)tile * splits * sstride, (short)0, (int)((uint32_t)splits * sstride * 4u), 0x00020000);
+      reinterpret_cast<char *>(partial) + (int64_t)tile * splits * sstride, (short)0,
+      (int)((uint32_t)splits * sstride), 0x00020000);
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     int row;
     int64_t n;
-    if (quad_out(j, row, n))
+    if (slot_out(j, row, n))
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[j]), prs,
-                                             ((uint32_t)split * sstride + 4u * (uint32_t)(threadIdx.x + j * NTH)) * 4u,
+                                             (uint32_t)split * sstride + 16u * (uint32_t)(threadIdx.x + j * NTH),
                                              0, kDeviceCoherent);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
@@ -421,9 +516,9 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   }
   __syncthreads();
   if (!s_last) return;
-  // Gather every split's quads, all loads of a batch in flight together (the
-  // addresses of splits past the last are clamped and their values dropped),
-  // summing in split order.
+  // Gather every split's slots, all loads of a batch in flight together (the
+  // addresses of splits past the last are clamped and their values dropped,
+  // unstored slots are read and not used), summing in split order.
   constexpr int SB = QPT >= 16 ? 1 : 16 / QPT;  // splits per batch
   f32x4 sum[QPT];
 #pragma unroll
@@ -432,13 +527,13 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
     f32x4 t[QPT][SB];
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
-      const uint32_t q = (uint32_t)(threadIdx.x + j * NTH);
-      const uint32_t off = 16u * (q < (uint32_t)nq ? q : 0u);
+      const uint32_t sl = (uint32_t)(threadIdx.x + j * NTH);
+      const uint32_t off = 16u * (sl < (uint32_t)QUADS ? sl : 0u);
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         const uint32_t spc = (uint32_t)(sp + u < splits ? sp + u : splits - 1);
-        t[j][u] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off + spc * sstride * 4u, 0, kDeviceCoherent));
+        t[j][u] = __builtin_bit_cast(f32x4,
+                                     __builtin_amdgcn_raw_buffer_load_b128(prs, off + spc * sstride, 0, kDeviceCoherent));
       }
     }
 #pragma unroll
@@ -447,7 +542,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
       for (int u = 0; u < SB; ++u)
         if (sp + u < splits) sum[j] += t[j][u];
   }
-  store_quads(sum);
+  store_slots(sum);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -456,8 +551,21 @@ static int env_int(const char *name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
+static int token_rows(int64_t tokens) {
+  return tokens <= 1 ? 1 : tokens <= 2 ? 2 : tokens <= 4 ? 4 : tokens <= 8 ? 8 : 16;
+}
+
+// LDS of one workgroup: the waves' weight rows (and, fused, their rotation
+// rows) during the k-steps, then the NW slot-major fp32 reduction tiles
+// (MT * NTILE floats each) in the same space.
+static size_t decode_lds_bytes(int wpl, int ksw, int nw, int mt, bool fused) {
+  const size_t stream = (size_t)nw * decode_wave_lds(wpl, ksw) + (fused ? (size_t)nw * mt * kDecodeRS * 4 : 0);
+  const size_t red = (size_t)nw * mt * 128 * wpl * 4;
+  return stream > red ? stream : red;
+}
+constexpr size_t kDecodeMaxLds = 160 * 1024 - 256;  // the static s_last flag takes a little
+
 DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int group) {
-  (void)fused;
   DecodePlan p;
   const int64_t nks = I / 32;
   if (tokens <= 4) {
@@ -485,10 +593,12 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int gro
   static const int fn = env_int("PARO_DECODE_NW", 0);
   if (fw == 1 || (fw == 2 && O % 16 == 0) || (fw == 4 && O % 32 == 0)) p.wpl = fw;
   if (fk == 1 || fk == 2 || fk == 4 || fk == 8) p.ksw = fk;
-  if (fn == 4 || fn == 8 || fn == 16) p.nw = fn;
+  if (fn == 2 || fn == 4 || fn == 8 || fn == 16) p.nw = fn;
   // groups of 32 or 64 rows: one k-step per wave (the kernel keeps one
   // group's scales and zeros per wave and folds every k-step)
   if (group < kG) p.ksw = 1;
+  // the k-steps' weight rows (and fused rotation rows) must fit in LDS
+  while (p.ksw > 1 && decode_lds_bytes(p.wpl, p.ksw, p.nw, token_rows(tokens), fused) > kDecodeMaxLds) p.ksw /= 2;
   p.ntile = 128 * p.wpl;
   p.n_tiles = (int)((O + p.ntile - 1) / p.ntile);
   p.splits = (int)((nks + p.nw * p.ksw - 1) / (p.nw * p.ksw));
@@ -498,8 +608,8 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int gro
 size_t decode_partial_bytes(const DecodePlan &p, int64_t tokens, int64_t O) {
   (void)O;
   if (p.splits <= 1) return 0;
-  // [tile][split][tokens][ntile] fp32
-  return (size_t)p.n_tiles * (size_t)p.splits * (size_t)tokens * (size_t)p.ntile * 4;
+  // [tile][split][slots]: token_rows(tokens) rows of ntile fp32 each
+  return (size_t)p.n_tiles * (size_t)p.splits * (size_t)token_rows(tokens) * (size_t)p.ntile * 4;
 }
 
 template <int DT, int WPL, int KSW, int NW, bool FUSED>
@@ -507,10 +617,8 @@ static hipError_t launch_decode_t(const LinearArgs &a, const DecodePlan &p, cons
                                   float *partial, hipStream_t st) {
   dim3 grid((unsigned)(p.n_tiles * p.splits));
   const int M = (int)a.tokens;
-  const int mt = (M <= 1) ? 1 : (M <= 2) ? 2 : (M <= 4) ? 4 : (M <= 8) ? 8 : 16;
-  size_t red_bytes = (size_t)NW * mt * p.ntile * 4;
-  size_t rot_bytes = FUSED ? (size_t)NW * mt * kDecodeRS * 4 : 0;
-  size_t shmem = red_bytes > rot_bytes ? red_bytes : rot_bytes;
+  const int mt = token_rows(M);
+  const size_t shmem = decode_lds_bytes(WPL, KSW, NW, mt, FUSED);
   const uint16_t *xrp = reinterpret_cast<const uint16_t *>(xr);
 #define PARO_DECODE_LAUNCH(MT)                                                                                \
   hipLaunchKernelGGL((decode_kernel<DT, WPL, KSW, NW, FUSED, MT>), grid, dim3(64 * NW), shmem, st, a, xrp, p.splits, \
@@ -529,26 +637,23 @@ static hipError_t launch_decode_t(const LinearArgs &a, const DecodePlan &p, cons
 template <int DT, bool FUSED>
 static hipError_t launch_decode_dt(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
                                    float *partials, hipStream_t st) {
-  // every (wpl, ksw, nw) the planner produces is instantiated; other
-  // combinations (tuning overrides only) are rejected
+  // every (wpl, ksw, nw) the planner produces is instantiated, and 256-byte
+  // row segments (wpl 4) for tuning; other combinations (tuning overrides
+  // only) are rejected
 #define PARO_DECODE_CFG(WPL, KSW, NW) \
   if (p.wpl == WPL && p.ksw == KSW && p.nw == NW) return launch_decode_t<DT, WPL, KSW, NW, FUSED>(a, p, xr, counters, partials, st)
   PARO_DECODE_CFG(2, 1, 8);
   PARO_DECODE_CFG(1, 1, 8);
-  PARO_DECODE_CFG(2, 1, 16);
-  PARO_DECODE_CFG(4, 1, 8);
-  PARO_DECODE_CFG(2, 2, 4);
-  PARO_DECODE_CFG(1, 8, 16);
-  PARO_DECODE_CFG(1, 8, 8);
-  PARO_DECODE_CFG(1, 4, 8);
-  PARO_DECODE_CFG(1, 2, 8);
-  PARO_DECODE_CFG(2, 4, 8);
   PARO_DECODE_CFG(2, 2, 8);
-  PARO_DECODE_CFG(1, 4, 16);
-  PARO_DECODE_CFG(1, 2, 16);
-  PARO_DECODE_CFG(1, 1, 16);
-  PARO_DECODE_CFG(1, 8, 4);
-  PARO_DECODE_CFG(1, 4, 4);
+  PARO_DECODE_CFG(2, 4, 8);
+  PARO_DECODE_CFG(1, 2, 8);
+  PARO_DECODE_CFG(1, 4, 8);
+  PARO_DECODE_CFG(1, 8, 8);
+  PARO_DECODE_CFG(4, 1, 8);
+  PARO_DECODE_CFG(4, 2, 8);
+  PARO_DECODE_CFG(2, 2, 4);
+  PARO_DECODE_CFG(2, 4, 4);
+  PARO_DECODE_CFG(2, 8, 4);
 #undef PARO_DECODE_CFG
   return hipErrorInvalidValue;
 }

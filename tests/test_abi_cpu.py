@@ -169,7 +169,7 @@ def test_workspace_sizes_and_path_choice():
     wsb = lambda m, p: _lib.load().paro_w4a16_linear_workspace_bytes(ctypes.byref(L), m, 0, p)
     # prefill holds X_r (tokens * I * 2 bytes) after the fixed counter area
     assert wsb(2048, 3) - wsb(1024, 3) == 1024 * 4096 * 2
-    assert wsb(1, 1) > 0 and wsb(16, 2) > wsb(16, 1)
+    assert wsb(1, 1) > 0 and wsb(4, 2) > wsb(4, 1)
     assert wsb(0, 1) == 0
 
 

@@ -58,6 +58,28 @@
 
 namespace paro {
 
+// Optional per-wave timeline, compiled in only with PARO_DECODE_TIMELINE
+// (csrc/decode_timeline.hip): lane 0 of every wave stores the 100 MHz
+// realtime counter at fixed points of the kernel into
+// decode_timeline_buf[workgroup][wave][16].  Marks: 0 entry, 1 weight loads
+// issued, 2-5 k-steps 0-3 landed, 6 k-steps done, 7 reduction start (first
+// barrier), 8 reduction stores done, 9 second barrier, 10 slots summed,
+// 11 partial stores issued, 12 partial stores complete, 13 counter returned,
+// 14 gather done (finishing workgroup), 15 outputs stored.
+#ifdef PARO_DECODE_TIMELINE
+__device__ unsigned long long *decode_timeline_buf;
+#define DECODE_MARK(i)                                                                                  \
+  do {                                                                                                  \
+    if ((threadIdx.x & 63) == 0)                                                                        \
+      decode_timeline_buf[((size_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)) * 16 + (i)] =   \
+          __builtin_amdgcn_s_memrealtime();                                                             \
+  } while (0)
+#else
+#define DECODE_MARK(i) \
+  do {                 \
+  } while (0)
+#endif
+
 constexpr int kDecodeRS = kG + 4;  // fused-rotation LDS row stride (floats)
 constexpr int kCounterStride = 32; // uint32 per split-K counter: one 128-byte line each
 // Cache policy of the raw buffer loads/stores that exchange split-K partials:
@@ -193,6 +215,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  DECODE_MARK(0);
   const int cl = lane & 15, kb = lane >> 4;
   const int n_tiles = (int)((a.O + NTILE - 1) / NTILE);
   const int lwg = xcd_local_order((int)blockIdx.x, n_tiles * splits);
@@ -330,6 +353,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         dma_1k(rw, wl + k * 32 * RB + j * 1024, voff[j] + (uint32_t)k * 32u * W4);
+    DECODE_MARK(1);
 
     // Nothing above may wait for a load: the weight stream starts first.
     __builtin_amdgcn_sched_barrier(0);
@@ -383,6 +407,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
         }
         // this k-step's rows have landed in LDS (later k-steps may still be in flight)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((KSW - 1 - k) * NI));
+        if (k < 4) DECODE_MARK(2 + k);
         const unsigned char *wk = wl + k * 32 * RB + cl * WPL * 4;
         uint32_t rw8[WPL][8];
 #pragma unroll
@@ -431,7 +456,9 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   }
 
   // ---- reduce the NW waves' tiles in LDS (wave order), slot-major ----
+  DECODE_MARK(6);
   __syncthreads();  // every wave is done with its weight and rotation rows
+  DECODE_MARK(7);
   f32x4 *red = reinterpret_cast<f32x4 *>(smem);  // [NW][QUADS]
   if (kb < KBV) {
 #pragma unroll
@@ -445,7 +472,9 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
       }
     }
   }
+  DECODE_MARK(8);
   __syncthreads();
+  DECODE_MARK(9);
 
   // this thread's slots: sum over the waves in wave order
   f32x4 v[QPT];
@@ -458,6 +487,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
       for (int w = 0; w < NW; ++w) v[j] += red[w * QUADS + sl];
     }
   }
+  DECODE_MARK(10);
   // slot j of this thread: its row and output column, and whether it is stored
   auto slot_out = [&](int j, int &row, int64_t &n) {
     const int sl = threadIdx.x + j * NTH;
@@ -487,6 +517,7 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   };
   if (splits == 1) {
     store_slots(v);
+    DECODE_MARK(15);
     return;
   }
 
@@ -507,14 +538,17 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
                                              (uint32_t)split * sstride + 16u * (uint32_t)(threadIdx.x + j * NTH),
                                              0, kDeviceCoherent);
   }
+  DECODE_MARK(11);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
+  DECODE_MARK(12);
   uint32_t *cnt = counters + (int64_t)tile * kCounterStride;
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == (uint32_t)(splits - 1));
   }
   __syncthreads();
+  DECODE_MARK(13);
   if (!s_last) return;
   // Gather every split's slots, all loads of a batch in flight together (the
   // addresses of splits past the last are clamped and their values dropped,
@@ -542,7 +576,9 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
       for (int u = 0; u < SB; ++u)
         if (sp + u < splits) sum[j] += t[j][u];
   }
+  DECODE_MARK(14);
   store_slots(sum);
+  DECODE_MARK(15);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -569,13 +605,15 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int gro
   DecodePlan p;
   const int64_t nks = I / 32;
   if (tokens <= 4) {
-    // Few rows: the per-k-step fold is nearly free (one register row), so a
-    // wave owns one k-step of 128-byte row segments; eight waves per
-    // workgroup keep the K splits (whose partials the last workgroup gathers)
-    // at nks / 8 while filling the chip.
+    // Few rows: the fold is nearly free (one register row), so a workgroup
+    // owns eight k-steps of 128-byte row segments (four waves of two: one
+    // wave per SIMD measured a little faster than eight waves of one),
+    // keeping the K splits (whose partials the last workgroup gathers) at
+    // nks / 8 while filling the chip.
     p.wpl = (O % 16 == 0) ? 2 : 1;
-    p.ksw = 1;
-    p.nw = 8;
+    p.ksw = 2;
+    p.nw = 4;
+    while (p.ksw > 1 && (int64_t)p.nw * (p.ksw / 2) >= nks) p.ksw /= 2;
   } else {
     // Up to 16 rows: the partial sums cost splits * tokens * O * 8 bytes, so
     // an eight-wave workgroup covers long K ranges (several k-steps per wave,
@@ -591,14 +629,19 @@ DecodePlan plan_decode(int64_t I, int64_t O, int64_t tokens, bool fused, int gro
   static const int fw = env_int("PARO_DECODE_WPL", 0);
   static const int fk = env_int("PARO_DECODE_KSW", 0);
   static const int fn = env_int("PARO_DECODE_NW", 0);
-  if (fw == 1 || (fw == 2 && O % 16 == 0) || (fw == 4 && O % 32 == 0)) p.wpl = fw;
+  if (fw == 1 || (fw == 2 && O % 16 == 0)) p.wpl = fw;
   if (fk == 1 || fk == 2 || fk == 4 || fk == 8) p.ksw = fk;
   if (fn == 2 || fn == 4 || fn == 8 || fn == 16) p.nw = fn;
   // groups of 32 or 64 rows: one k-step per wave (the kernel keeps one
   // group's scales and zeros per wave and folds every k-step)
   if (group < kG) p.ksw = 1;
-  // the k-steps' weight rows (and fused rotation rows) must fit in LDS
-  while (p.ksw > 1 && decode_lds_bytes(p.wpl, p.ksw, p.nw, token_rows(tokens), fused) > kDecodeMaxLds) p.ksw /= 2;
+  // the k-steps' weight rows (and fused rotation rows), and then the
+  // reduction tiles, must fit in LDS
+  while ((p.ksw > 1 || p.wpl > 1) &&
+         decode_lds_bytes(p.wpl, p.ksw, p.nw, token_rows(tokens), fused) > kDecodeMaxLds) {
+    if (p.ksw > 1) p.ksw /= 2;
+    else p.wpl /= 2;
+  }
   p.ntile = 128 * p.wpl;
   p.n_tiles = (int)((O + p.ntile - 1) / p.ntile);
   p.splits = (int)((nks + p.nw * p.ksw - 1) / (p.nw * p.ksw));
@@ -637,23 +680,21 @@ static hipError_t launch_decode_t(const LinearArgs &a, const DecodePlan &p, cons
 template <int DT, bool FUSED>
 static hipError_t launch_decode_dt(const LinearArgs &a, const DecodePlan &p, const void *xr, uint32_t *counters,
                                    float *partials, hipStream_t st) {
-  // every (wpl, ksw, nw) the planner produces is instantiated, and 256-byte
-  // row segments (wpl 4) for tuning; other combinations (tuning overrides
-  // only) are rejected
+  // every (wpl, ksw, nw) the planner produces is instantiated; other
+  // combinations (tuning overrides only) are rejected
 #define PARO_DECODE_CFG(WPL, KSW, NW) \
   if (p.wpl == WPL && p.ksw == KSW && p.nw == NW) return launch_decode_t<DT, WPL, KSW, NW, FUSED>(a, p, xr, counters, partials, st)
+  PARO_DECODE_CFG(2, 2, 4);
+  PARO_DECODE_CFG(2, 1, 4);
+  PARO_DECODE_CFG(1, 2, 4);
+  PARO_DECODE_CFG(1, 1, 4);
   PARO_DECODE_CFG(2, 1, 8);
-  PARO_DECODE_CFG(1, 1, 8);
   PARO_DECODE_CFG(2, 2, 8);
   PARO_DECODE_CFG(2, 4, 8);
+  PARO_DECODE_CFG(1, 1, 8);
   PARO_DECODE_CFG(1, 2, 8);
   PARO_DECODE_CFG(1, 4, 8);
   PARO_DECODE_CFG(1, 8, 8);
-  PARO_DECODE_CFG(4, 1, 8);
-  PARO_DECODE_CFG(4, 2, 8);
-  PARO_DECODE_CFG(2, 2, 4);
-  PARO_DECODE_CFG(2, 4, 4);
-  PARO_DECODE_CFG(2, 8, 4);
 #undef PARO_DECODE_CFG
   return hipErrorInvalidValue;
 }

@@ -60,7 +60,7 @@ struct LinearArgs {
 // rotation runs fused in each workgroup's prologue; otherwise `xr` holds the
 // rotated activations ([tokens][I], x dtype) and is read directly.
 struct DecodePlan {
-  int wpl;        // packed words per lane and row (1, 2 or 4)
+  int wpl;        // packed words per lane and row (1 or 2)
   int ksw;        // 32-row k-steps per wave (a workgroup covers nw * ksw)
   int nw;         // waves per workgroup (4 or 8)
   int ntile;      // output columns per workgroup (= 128 * wpl)

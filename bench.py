@@ -241,6 +241,105 @@ def bench_rotate_backward(args, paro, synth, np, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+ROT_METRIC = "ParoQuant input scaling + rotation (X -> X_r): activation GB/s, % of HBM roofline"
+KERNEL_FILES["rotate"] = ("scale_rotate.hip", "common.hpp", "mfma.hpp")
+
+
+def bench_rotate(args, paro, synth, np, torch, dev):
+    """Time the input scaling and rotation of every layer of the workload, as
+    the prefill path runs it: the dense per-group matrix built once per layer
+    (paro_rotation_matrix) and applied on the matrix cores into the GEMM's
+    tiled layout (paro_scale_rotate_tiled), with the staged rotation
+    (paro_scale_rotate: krot Givens stages in LDS, row-major X_r) timed beside
+    it on the same inputs.  >= 512 MB of distinct inputs are rotated through."""
+    spec = synth.WORKLOADS[args.workload]
+    M, dt = spec["tokens"], spec["act"]
+    tdt = torch.float16 if dt == synth.F16 else torch.bfloat16
+    layers = spec["layers"]
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+    set_bytes = sum(M * I * 2 for _, I, _ in layers)
+    nsets = min(MAX_BUFFER_SETS, max(1, -(-MALL_ROTATION_BYTES // set_bytes)))
+    log(f"rotate: workload {args.workload}, {len(layers)} layer(s), {M} tokens, {nsets} input copies")
+    Ds, hls, xts, xrs, hosts = [], [], [], [], []
+    xs = [[] for _ in range(nsets)]
+    for li, (lname, I, O) in enumerate(layers):
+        host = synth.make_layer(args.workload, li, I, O, group_size=args.group)
+        hosts.append(host)
+        D = paro.DeviceLayer(host, device=dev)
+        Ds.append(D)
+        hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
+        paro.paro_rotation_matrix(D, dt, hl)
+        hls.append(hl)
+        xts.append(torch.empty((paro.paro_tiled_bytes(D, M) // 2,), dtype=torch.int16, device=dev))
+        xrs.append(torch.empty((M, I), dtype=tdt, device=dev))
+        x = up(synth.make_x(args.workload, li, M, I, dt))
+        for k in range(nsets):
+            xs[k].append(x.clone())
+    stream = torch.cuda.current_stream()
+
+    def dense(i):
+        for li, D in enumerate(Ds):
+            paro.paro_scale_rotate_tiled(D, hls[li], xs[i % nsets][li], xts[li], stream=stream)
+
+    def staged(i):
+        for li, D in enumerate(Ds):
+            paro.paro_scale_rotate(D, xs[i % nsets][li], xrs[li], stream=stream)
+
+    def timeit(step):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / args.steps
+
+    us = timeit(dense)
+    us_staged = timeit(staged)
+    act_b = sum(2 * M * I * 2 for _, I, _ in layers)     # X read, X_r written
+    mat_b = sum((I // 128) * 2 * 128 * 128 * 2 for _, I, _ in layers)  # H and L read
+    value = act_b / (us * 1e-6) / 1e9
+    ach = (act_b + mat_b) / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        rows = min(M, 16)
+        hx = [np.ascontiguousarray(synth.make_x(args.workload, li, M, I, dt)[:rows])
+              for li, (_, I, _) in enumerate(layers)]
+        n, t_start = 0, time.perf_counter()
+        while True:
+            for li in range(len(layers)):
+                ref.scale_rotate(hosts[li], hx[li], dt)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or (el / n) * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = {"value": sum(2 * rows * I * 2 for _, I, _ in layers) / (el / n) / 1e9, "unit": "GB/s",
+               "cores": ref.threads(0), "kind": "oracle",
+               "sample": f"{n} round(s) of oracle scale_rotate on the first {rows} of {M} token rows of every "
+                         f"layer, {el:.1f} s"}
+    wl = f"{spec['name']}-input-rotation{gsuffix(args)}"
+    out = {
+        "metric": ROT_METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl, "layers": [[n, I] for n, I, _ in layers], "tokens": M,
+                   "group_size": args.group, "input_copies": nsets, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"rotate-{args.workload}{gsuffix(args)}", kernel_source_hash("rotate")),
+                     "kernel": "rot_apply_kernel (one launch per layer)", "avg_launch_us": round(us / len(layers), 3),
+                     "launches_per_step": len(layers)},
+        "staged": {"kernel": "scale_rotate_kernel (one launch per layer)", "ms_per_step": round(us_staged / 1e3, 6),
+                   "value": round(act_b / (us_staged * 1e-6) / 1e9, 3), "unit": "GB/s"},
+        "cpu_baseline": cpu, "kernel_sources": kernel_source_hash("rotate"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 MOE_METRIC = "ParoQuant MoE projection (shared rotation, stacked experts): TFLOP/s, % of MFMA roofline"
 KERNEL_FILES["moe"] = ("prefill.hip", "scale_rotate.hip", "common.hpp", "mx.hpp", "mfma.hpp")
 
@@ -473,12 +572,14 @@ def main():
                          "instead of building it once per layer (paro_w4a16_linear_prepared)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured ceiling (device copy for decode, library dense GEMM for prefill)")
-    ap.add_argument("--op", choices=("linear", "quantize", "rotate_backward", "moe", "mxfp4"), default="linear",
+    ap.add_argument("--op", choices=("linear", "quantize", "rotate", "rotate_backward", "moe", "mxfp4"),
+                    default="linear",
                     help="linear: the inference hot path (default); quantize: the offline W -> (qweight, "
                          "qzeros, scales) transform of the workload's first layer; rotate_backward: the "
                          "calibration-time backward of the scaling and rotation over that layer's input; "
                          "moe: the mixture-of-experts projection of workload 5 (synth.MOE_WORKLOADS); "
-                         "mxfp4: the W4A4 MXFP4 linear of the workload's first layer")
+                         "mxfp4: the W4A4 MXFP4 linear of the workload's first layer; rotate: the input "
+                         "scaling and rotation of every layer (dense prefill form, staged form beside it)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark: copy BYTES between two device buffers --steps times "
                          "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -511,6 +612,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.op == "quantize":
         bench_quantize(args, paro, synth, np, torch, dev)
+        return
+    if args.op == "rotate":
+        bench_rotate(args, paro, synth, np, torch, dev)
         return
     if args.op == "rotate_backward":
         bench_rotate_backward(args, paro, synth, np, torch, dev)

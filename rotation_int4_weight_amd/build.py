@@ -1,7 +1,8 @@
 """Build libparo.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree.
 
     python -m rotation_int4_weight_amd.build        # or build() from Python
-    python -m rotation_int4_weight_amd.build --decode-timeline   # diagnostic tool
+    python -m rotation_int4_weight_amd.build --decode-timeline   # diagnostic tools
+    python -m rotation_int4_weight_amd.build --prefill-timeline
 
 Each source compiles to an object under _build/ (in parallel), then one link
 produces rotation_int4_weight_amd/libparo.so.  Always rebuilds.
@@ -73,23 +74,34 @@ def build(extra=(), verbose: bool = False) -> str:
     return LIB
 
 
-def build_decode_timeline(verbose: bool = False) -> str:
-    """The per-wave decode timeline tool (csrc/decode_timeline.hip): decode.hip
-    compiled with PARO_DECODE_TIMELINE into a standalone program under _build/."""
+def _build_tool(name: str, define: str, verbose: bool) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    out = os.path.join(BUILD, "decode_timeline")
-    cmd = [hipcc(), *[f for f in COMMON if f != "-fPIC"], "-DPARO_DECODE_TIMELINE",
-           os.path.join(CSRC, "decode_timeline.hip"), "-o", out]
+    out = os.path.join(BUILD, name)
+    cmd = [hipcc(), *[f for f in COMMON if f != "-fPIC"], f"-D{define}", os.path.join(CSRC, name + ".hip"),
+           "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for decode_timeline.hip:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {name}.hip:\n{r.stdout}\n{r.stderr}")
     if verbose:
         print(f"built {out}")
     return out
 
 
+def build_decode_timeline(verbose: bool = False) -> str:
+    """The per-wave decode timeline tool (csrc/decode_timeline.hip): decode.hip
+    compiled with PARO_DECODE_TIMELINE into a standalone program under _build/."""
+    return _build_tool("decode_timeline", "PARO_DECODE_TIMELINE", verbose)
+
+
+def build_prefill_timeline(verbose: bool = False) -> str:
+    """The per-wave prefill GEMM timeline tool (csrc/prefill_timeline.hip)."""
+    return _build_tool("prefill_timeline", "PARO_PREFILL_TIMELINE", verbose)
+
+
 if __name__ == "__main__":
     if "--decode-timeline" in sys.argv[1:]:
         build_decode_timeline(verbose=True)
+    elif "--prefill-timeline" in sys.argv[1:]:
+        build_prefill_timeline(verbose=True)
     else:
         build(verbose=True)

@@ -56,6 +56,27 @@
 
 namespace paro {
 
+// Optional per-wave timeline, compiled in only with PARO_PREFILL_TIMELINE
+// (csrc/prefill_timeline.hip): lane 0 of a wave stores the 100 MHz realtime
+// counter at fixed points into prefill_timeline_buf[workgroup][wave][48]:
+// 0 entry, 1 pipeline primed (consumers: first B fragments read; producers:
+// first super-step expanded), 46 producer done; consumer marks of tile it
+// (it < 8) at 2 + 4 it: tile start, + 1 main loop done, + 2 MFMAs drained,
+// + 3 epilogue stores issued.
+#ifdef PARO_PREFILL_TIMELINE
+__device__ unsigned long long *prefill_timeline_buf;
+#define PREFILL_MARK(i)                                                                                 \
+  do {                                                                                                  \
+    if ((threadIdx.x & 63) == 0)                                                                        \
+      prefill_timeline_buf[((size_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)) * 48 + (i)] =  \
+          __builtin_amdgcn_s_memrealtime();                                                             \
+  } while (0)
+#else
+#define PREFILL_MARK(i) \
+  do {                  \
+  } while (0)
+#endif
+
 constexpr int kBM = 256, kBN = 128, kBK = 32;  // kBM: the MoE grouped GEMM's rows per tile
 constexpr int kCUs = 256;                       // compute units of an MI355X
 constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 4 consumer + 4 producer waves
@@ -195,6 +216,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
   __shared__ __attribute__((aligned(16))) float stage[4][32 * kStageRS];  // epilogue, one per consumer wave
   const int lane = lane_id(), wave = wave_id();
+  PREFILL_MARK(0);
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
   const int n_tiles = (int)((O + kBN - 1) / kBN);
   const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + BM - 1) / BM);
@@ -416,8 +438,10 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     const int nsuper = wg_steps / 4;  // I % 128 == 0
     for (int S0 = 0; S0 < nsuper; S0 += 2) {
       psuper(0);
+      if (S0 == 0) PREFILL_MARK(1);
       if (S0 + 1 < nsuper) psuper(1);
     }
+    PREFILL_MARK(46);
     return;
   }
 
@@ -460,6 +484,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   for (int j = 0; j < 8; ++j) read_frag(0, j, bf[j]);
   // tile 0's slot is rewritten in the producer's first super-step
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  PREFILL_MARK(1);
 
   int step = 0;
   Tile t = t0;
@@ -478,6 +503,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
         acc_fence(acc[i][j]);
       }
     asm volatile("s_nop 7");  // accumulator writes -> first MFMA
+    if (it < 8) PREFILL_MARK(2 + 4 * it);
     // Step s: for each column tile j, its four MFMAs on A slot s%4, then the
     // refill of fragment j with that of step s+1 (tile (s+1)%8, expanded at
     // least one barrier earlier), which has the other seven tiles' MFMAs to
@@ -517,6 +543,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       step += kASlots;
       ls += kASlots;
     }
+    if (it < 8) PREFILL_MARK(3 + 4 * it);
     // (the B fragments of the next tile's first step are read here, before
     // the barrier after which the producers rewrite their slot; of its A
     // steps only the first two are loaded before the epilogue, the other two
@@ -530,6 +557,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
+    if (it < 8) PREFILL_MARK(4 + 4 * it);
 
     // Epilogue.  Each consumer wave stages its 16 RT x 128 fp32 tile through
     // its own LDS region (apart from the weight ring, which the producers
@@ -577,16 +605,27 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
             __builtin_amdgcn_sched_barrier(0);  // four accumulators in flight at a time
           }
         wave_lds_sync();
+        // rows in batches of four: the batch's LDS reads are issued together,
+        // so their latency is paid once per batch, not once per row
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int lr = 2 * rr + srow, row = 32 * p + lr;
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(stg + lr * kStageRS + sc) + bias4;
-          if (row >= lo && row < hi) {
-            YT *dst = ybase + (int64_t)row * O;
-            if constexpr (YD == kF32)
-              *reinterpret_cast<f32x4 *>(dst) = v;
-            else
-              *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2<YD>(v[0], v[1]), pack2<YD>(v[2], v[3])};
+        for (int rb = 0; rb < 16; rb += 4) {
+          f32x4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4 *>(stg + (2 * (rb + u) + srow) * kStageRS + sc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int row = 32 * p + 2 * (rb + u) + srow;
+            const f32x4 o = v[u] + bias4;
+            if (row >= lo && row < hi) {
+              YT *dst = ybase + (int64_t)row * O;
+              // streaming stores: y is not read again here (and a little
+              // faster on the decoder-layer step than ordinary stores)
+              if constexpr (YD == kF32)
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(dst));
+              else
+                __builtin_nontemporal_store(u32x2{pack2<YD>(o[0], o[1]), pack2<YD>(o[2], o[3])},
+                                            reinterpret_cast<u32x2 *>(dst));
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -599,6 +638,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       epilogue(std::integral_constant<int, kF16>());
     else
       epilogue(std::integral_constant<int, kBF16>());
+    if (it < 8) PREFILL_MARK(5 + 4 * it);
     if (++it >= my_tiles) break;
     t = tn;
     load_a(t, 2, ab[2]);

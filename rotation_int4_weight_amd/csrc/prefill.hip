@@ -85,7 +85,6 @@ constexpr int kTiles = 8;           // LDS ring of expanded weight tiles (k step
 constexpr int kWordRing = 8;        // packed weight words in flight per producer thread (steps)
 constexpr int kASlots = 4;          // A fragments in flight per consumer wave (steps)
 constexpr int kGroupM = 2;          // M blocks per group of the tile order (dense layers)
-constexpr int kStageRS = kBN + 4;   // epilogue staging row stride (floats): the four row groups of a store hit distinct banks
 static_assert(kTiles == 8 && kWordRing == 8, "the producer's ring slot arithmetic assumes rings of 8");
 static_assert(kASlots == 4, "a tile's last super-step loads two A steps of the next tile, the epilogue the other two");
 
@@ -214,7 +213,6 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   static_assert(RT == 4 || (RT == 2 && !MOE), "256-row tiles, or 128-row tiles for dense layers");
   constexpr int BM = 64 * RT;
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
-  __shared__ __attribute__((aligned(16))) float stage[4][32 * kStageRS];  // epilogue, one per consumer wave
   const int lane = lane_id(), wave = wave_id();
   PREFILL_MARK(0);
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
@@ -450,7 +448,8 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // A fragment i of this wave: row tile wave RT + i (a scalar offset) and
   // lane's 16 bytes of it (the one per-lane offset)
   const uint32_t a_lane = (uint32_t)lane * 16u;
-  const uint32_t a_wave = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * RT * tile_bytes;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // in a scalar register
+  const uint32_t a_wave = (uint32_t)wave_s * RT * tile_bytes;
   // A of k step ls of tile t: 16-row tiles from mb/16 of its M block, of
   // which those in the (16-row padded) tiled buffer exist; the buffer
   // descriptor ends there, so later ones read as zeros.
@@ -464,13 +463,22 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     for (int i = 0; i < RT; ++i)
       af[i] = __builtin_amdgcn_raw_buffer_load_b128(r, a_lane, (int)(a_wave + (uint32_t)i * tile_bytes), 0);
   };
-  // B fragment of column tile j of one k step: column 16j + fr, k
-  // block fk (physical block (fk/8) ^ (j&3)), one 16-byte LDS read.
+  // B fragment j of one k step: 16 of the tile's columns, k block fk
+  // (physical block (fk/8) ^ ((column/16)&3)), one 16-byte LDS read.  The
+  // weights are the MFMA's first operand, so a lane's results are four
+  // consecutive fragment columns (4(lane/16) + r) of one token; fragment
+  // column c of fragment j is tile column
+  //     32 (j/2) + 8 (c/4) + 4 (j%2) + c%4,
+  // which puts fragments 2s and 2s+1 of lane group g on the eight adjacent
+  // columns 32s + 8g .. 32s + 8g + 7 (one 16-byte store in the epilogue).
   // Only the four lane offsets for j&3 live in registers; the tile and j>=4
-  // are constant offsets folded into the LDS instructions.
+  // (64 columns on) are constant offsets folded into the LDS instructions.
   uint32_t fcol[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) fcol[jj] = (uint32_t)((jj * 16 + fr) * kBStride + 8 * ((fk >> 3) ^ jj));
+  for (int jj = 0; jj < 4; ++jj) {
+    const int col = 32 * (jj >> 1) + 8 * (fr >> 2) + 4 * (jj & 1) + (fr & 3);
+    fcol[jj] = (uint32_t)(col * kBStride + 8 * ((fk >> 3) ^ ((col >> 4) & 3)));
+  }
   auto read_frag = [&](int tile, int j, u32x4 &b) {
     const uint16_t *col = &bl[0][0] + tile * (kBN * kBStride) + fcol[j & 3] + (j >> 2) * 64 * kBStride;
     b = *reinterpret_cast<const u32x4 *>(col);
@@ -521,7 +529,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
-        for (int i = 0; i < RT; ++i) mfma_acc<DT>(A[i], bf[j], acc[i][j]);
+        for (int i = 0; i < RT; ++i) mfma_acc<DT>(bf[j], A[i], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
         read_frag(next, j, bf[j]);
       }
@@ -548,6 +556,17 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     // the barrier after which the producers rewrite their slot; of its A
     // steps only the first two are loaded before the epilogue, the other two
     // after it, so that fewer registers are live through it)
+    // The tile's bias: lane l loads columns 2l, 2l+1 (one dword; the
+    // epilogue hands each lane its eight columns per group by bpermute),
+    // before the next tile's first A loads, so that waiting for it does not
+    // wait for them.  The lane index is recomputed here by a volatile asm,
+    // so that the compiler derives the epilogue's addresses per tile
+    // instead of holding them (or spilling them) through the main loop.
+    int el;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
+    uint32_t bw = 0u;
+    if (t.bias && t.n0 + 2 * el < O) bw = *reinterpret_cast<const uint32_t *>(t.bias + t.n0 + 2 * el);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3, tn, k, k < 2);
     step += kASlots;
@@ -559,77 +578,83 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
       for (int j = 0; j < 8; ++j) acc_fence(acc[i][j]);
     if (it < 8) PREFILL_MARK(4 + 4 * it);
 
-    // Epilogue.  Each consumer wave stages its 16 RT x 128 fp32 tile through
-    // its own LDS region (apart from the weight ring, which the producers
-    // keep filling), 32 rows at a time; a lane then holds 4 consecutive
-    // columns of one row: bias added in fp32, one rounding, one 8-byte store
-    // (16 bytes for fp32 output), so every row's 128 columns leave as whole
-    // cache lines.
-    // (the lane index is laundered through an empty asm so that the
-    // compiler computes the epilogue's addresses here, per tile, instead of
-    // hoisting them out of the tile loop into registers held through the
-    // main loop)
-    int el = lane;
     asm volatile("" : "+v"(el));
-    const int efr = el & 15;
-    float *stg = stage[wave];
-    const int64_t m0 = t.mb + wave * 16 * RT;
-    const int sc = (el & 31) * 4, srow = el >> 5;  // quad column, row parity of this lane
-    const int64_t n = t.n0 + sc;
-    const bool n_ok = n < O;  // O % 8 == 0: a quad is wholly in or out
+    const int erow = el & 15, eg = el >> 4;
+    // Epilogue, straight from the accumulators: lane (g, t) = (lane/16,
+    // lane%16) holds, for each 16-row block i and column group s, the eight
+    // outputs 32s + 8g .. 32s + 8g + 7 of row 16i + t (fragments 2s, 2s+1):
+    // bias added in fp32, one rounding, one 16-byte store (two for fp32
+    // output); the four lanes of a row write its 64 contiguous bytes.  No
+    // LDS staging, so nothing waits here on the producers' LDS traffic.
+    const int64_t m0 = t.mb + wave_s * 16 * RT;
     // rows m0 + lo .. m0 + hi - 1 of this wave's 16 RT are stored
     const int64_t lo64 = t.row_lo - m0, hi64 = t.row_hi - m0;
     const int lo = (int)(lo64 < 0 ? 0 : lo64 > 16 * RT ? 16 * RT : lo64);
-    const int hi = n_ok ? (int)(hi64 < 0 ? 0 : hi64 > 16 * RT ? 16 * RT : hi64) : 0;
-    f32x4 bias4{0.f, 0.f, 0.f, 0.f};
-    if (t.bias && n_ok) {
-      const u32x2 bb = *reinterpret_cast<const u32x2 *>(t.bias + n);
-      bias4 = f32x4{f16_bits_to_f32(bb[0] & 0xffffu), f16_bits_to_f32(bb[0] >> 16),
-                    f16_bits_to_f32(bb[1] & 0xffffu), f16_bits_to_f32(bb[1] >> 16)};
-    }
-    // one copy of the passes per output dtype (no dtype test per store)
+    const int hi = (int)(hi64 < 0 ? 0 : hi64 > 16 * RT ? 16 * RT : hi64);
+    // (1 through an empty asm: the compiler would fold acc * 1 + bias into
+    // a convert and an add)
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    // one copy per output dtype (no dtype test per store)
     auto epilogue = [&](auto ydt) {
       constexpr int YD = decltype(ydt)::value;
       typedef typename std::conditional<YD == kF32, float, uint16_t>::type YT;
-      YT *ybase = reinterpret_cast<YT *>(a.y) + m0 * O + n;
+      YT *ybase = reinterpret_cast<YT *>(a.y) + (m0 + erow) * O + t.n0 + 8 * eg;
+      // Two fp32 sums -> one packed pair, RNE.  For fp16 the conversion is
+      // written as asm: the compiler would otherwise fuse it with the bias
+      // fma into one mixed fma with an fp16 result (a single rounding),
+      // whereas a 16-bit output is the rounding of the fp32 output.
+      auto pk2 = [](float lo, float hi) -> uint32_t {
+        if constexpr (YD == kF16) {
+          uint32_t r;
+          asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+          return r;
+        } else {
+          return pack2<YD>(lo, hi);
+        }
+      };
+      // The lane's bias halves of column group s4: columns 32 s4 + 8 eg + 2q,
+      // +1 are bias dword 16 s4 + 4 eg + q (bpermute), each added to its
+      // output as the fp16 operand of one mixed fma.  The next block's are
+      // fetched before this block's arithmetic, so that their latency is
+      // hidden behind it.
+      auto bias_of = [&](int s4, f16x2 (&b)[4]) {
 #pragma unroll
-      for (int p = 0; p < RT / 2; ++p) {
-        // D of tile (i, j): row 16i + 4(lane/16) + r, column 16j + lane%16
+        for (int q = 0; q < 4; ++q)
+          b[q] = __builtin_bit_cast(f16x2, __builtin_amdgcn_ds_bpermute(4 * (16 * s4 + 4 * eg + q), (int)bw));
+      };
+      f16x2 bcur[4];
+      bias_of(0, bcur);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+      for (int i = 0; i < RT; ++i) {
+        const int row = 16 * i + erow;
+        const bool row_ok = row >= lo && row < hi;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
+        for (int s4 = 0; s4 < 4; ++s4) {
+          f16x2 bnext[4];
+          if (i + 1 < RT || s4 < 3) bias_of((s4 + 1) & 3, bnext);
+          float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              stg[(16 * ii + (el >> 4) * 4 + r) * kStageRS + 16 * j + efr] = acc[2 * p + ii][j][r];
-            __builtin_amdgcn_sched_barrier(0);  // four accumulators in flight at a time
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 &c = acc[i][2 * s4 + (q >> 1)];
+            v[2 * q] = __builtin_fmaf(c[2 * (q & 1)], one, (float)bcur[q][0]);
+            v[2 * q + 1] = __builtin_fmaf(c[2 * (q & 1) + 1], one, (float)bcur[q][1]);
           }
-        wave_lds_sync();
-        // rows in batches of four: the batch's LDS reads are issued together,
-        // so their latency is paid once per batch, not once per row
-#pragma unroll
-        for (int rb = 0; rb < 16; rb += 4) {
-          f32x4 v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4 *>(stg + (2 * (rb + u) + srow) * kStageRS + sc);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int row = 32 * p + 2 * (rb + u) + srow;
-            const f32x4 o = v[u] + bias4;
-            if (row >= lo && row < hi) {
-              YT *dst = ybase + (int64_t)row * O;
-              // streaming stores: y is not read again here (and a little
-              // faster on the decoder-layer step than ordinary stores)
-              if constexpr (YD == kF32)
-                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(dst));
-              else
-                __builtin_nontemporal_store(u32x2{pack2<YD>(o[0], o[1]), pack2<YD>(o[2], o[3])},
-                                            reinterpret_cast<u32x2 *>(dst));
+          if (row_ok && t.n0 + 32 * s4 + 8 * eg < O) {
+            YT *dst = ybase + (int64_t)(16 * i) * O + 32 * s4;
+            // streaming stores: y is not read again here
+            if constexpr (YD == kF32) {
+              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
+              __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(dst + 4));
+            } else {
+              __builtin_nontemporal_store(u32x4{pk2(v[0], v[1]), pk2(v[2], v[3]), pk2(v[4], v[5]), pk2(v[6], v[7])},
+                                          reinterpret_cast<u32x4 *>(dst));
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bcur[q] = bnext[q];
+          __builtin_amdgcn_sched_barrier(0);  // one block's values live at a time
         }
-        wave_lds_sync();  // this pass's reads are done before the next pass's writes
       }
     };
     if (a.y_dt == kF32)

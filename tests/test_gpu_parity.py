@@ -253,6 +253,8 @@ EDGE = [
     (1024, 520, 16, synth.BF16, 8, "fused"),
     (1280, 392, 7, synth.F16, 8, "split"),
     (512, 256, 257, synth.F16, 8, "prefill"),
+    # 128-row tiles, ragged rows and a partial last column tile
+    (4096, 1000, 300, synth.BF16, 8, "prefill"),
 ]
 
 
@@ -261,6 +263,17 @@ def test_linear_edge_shapes(I, O, M, dt, krot, path):
     L = synth.make_layer(300 + I % 97, O % 89, I, O, krot=krot, bias=(O % 3 != 0))
     x = synth.make_x(300 + I % 97, O % 89, M, I, dt)
     check_linear(L, x, dt, path, None, f"edge")
+
+
+def test_linear_persistent_ragged_fp16():
+    """297 output tiles on at most 256 workgroups (some take two), a ragged
+    last row block and a last column tile of 8 columns, fp16.  check_linear
+    compares the whole fp16 output bit for bit with the rounding of the fp32
+    output (a fused bias-and-convert with a single rounding fails this)."""
+    I, O, M = 2304, 4104, 2100
+    L = synth.make_layer(77, 5, I, O, krot=8, bias=True)
+    x = synth.make_x(77, 5, M, I, synth.F16)
+    check_linear(L, x, synth.F16, "prefill", stratified_rows(M, 3, seed=77), "persistent ragged")
 
 
 def test_linear_identity_state_no_bias():

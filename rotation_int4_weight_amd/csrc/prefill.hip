@@ -642,13 +642,14 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
           }
           if (row_ok && t.n0 + 32 * s4 + 8 * eg < O) {
             YT *dst = ybase + (int64_t)(16 * i) * O + 32 * s4;
-            // streaming stores: y is not read again here
+            // ordinary (write-back) stores: a row's four 64-byte pieces meet
+            // in L2 and leave as whole lines (streaming stores wrote 1.4x
+            // the output bytes to HBM)
             if constexpr (YD == kF32) {
-              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
-              __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(dst + 4));
+              *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
             } else {
-              __builtin_nontemporal_store(u32x4{pk2(v[0], v[1]), pk2(v[2], v[3]), pk2(v[4], v[5]), pk2(v[6], v[7])},
-                                          reinterpret_cast<u32x4 *>(dst));
+              *reinterpret_cast<u32x4 *>(dst) = u32x4{pk2(v[0], v[1]), pk2(v[2], v[3]), pk2(v[4], v[5]), pk2(v[6], v[7])};
             }
           }
 #pragma unroll

@@ -214,6 +214,13 @@ decode_kernel(LinearArgs a, const uint16_t *__restrict__ xr, int splits, float *
   static_assert(KSW * NI <= 63, "the k-step waits count at most 63 loads");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
+  // Every argument the kernel reads, named in one empty asm at the top, so
+  // that their scalar loads go out together: otherwise the compiler loads
+  // some of them only after the first batch has returned, a second
+  // dependent round trip before the weight stream can start.
+  asm volatile("" ::"s"(a.I), "s"(a.O), "s"(a.tokens), "s"(a.krot), "s"(a.group), "s"(a.pairs), "s"(a.theta),
+               "s"(a.cs), "s"(a.qweight), "s"(a.qzeros), "s"(a.scales), "s"(a.bias), "s"(a.x), "s"(a.y),
+               "s"(a.y_dt), "s"(xr), "s"(splits), "s"(partial), "s"(counters));
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
   DECODE_MARK(0);
   const int cl = lane & 15, kb = lane >> 4;

@@ -29,6 +29,9 @@ scale_rotate_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, int64
                     const int16_t *__restrict__ pairs, const float *__restrict__ theta,
                     const float *__restrict__ cscale, int krot, int gmask) {
   __shared__ float lds[4][RW * kRotRS];
+  // all arguments in one batch of scalar loads (see decode_kernel)
+  asm volatile("" ::"s"(x), "s"(xr), "s"(tokens), "s"(I), "s"(pairs), "s"(theta), "s"(cscale), "s"(krot),
+               "s"(gmask));
   const int lane = lane_id(), wave = wave_id();
   const int64_t g = blockIdx.x;
   const int64_t m0 = ((int64_t)blockIdx.y * 4 + wave) * RW;
@@ -416,6 +419,8 @@ scale_rotate_full_kernel(const uint16_t *__restrict__ x, void *__restrict__ xr, 
                          const int16_t *__restrict__ pairs, const float *__restrict__ theta,
                          const float *__restrict__ cscale, int krot) {
   extern __shared__ __attribute__((aligned(16))) float rows[];  // [R][I]
+  // all arguments in one batch of scalar loads (see decode_kernel)
+  asm volatile("" ::"s"(x), "s"(xr), "s"(tokens), "s"(I), "s"(R), "s"(pairs), "s"(theta), "s"(cscale), "s"(krot));
   const int64_t m0 = (int64_t)blockIdx.x * R;
   const int64_t half = I / 2;
   for (int64_t e = threadIdx.x; e < R * half; e += kFullThreads) {

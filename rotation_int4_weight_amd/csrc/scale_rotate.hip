@@ -165,27 +165,40 @@ rot_build_kernel(int64_t I, const int16_t *__restrict__ pairs, const float *__re
 }
 
 // One workgroup: group g = blockIdx.x, token rows [R*blockIdx.y, +R) with
-// R = 16 * wg_tiles (kApplyRows unless overridden); each
-// wave takes batches of 4 row tiles (64 rows) and prefetches the next batch's
-// x fragments as the current ones retire.  LDS holds H_T and L_T of the group
-// (row stride 136 halves: the 16-byte fragment reads of 16 lanes spread over
-// the banks).
+// R = 16 * wg_tiles (apply_rows below); each wave takes batches of 4 row
+// tiles (64 rows) and fetches the next batch's x while it computes the
+// current one.  LDS holds H_T and L_T of the group (row stride 136 halves:
+// the 16-byte fragment reads of 16 lanes spread over the banks).
 constexpr int kHS = kG + 8;
-// default token rows per workgroup (a multiple of 256); on 2048 x 14336 bf16
-// 1024 measured 32.7 us against 34.6 us at 512 (the group's H / L pair is
-// loaded into LDS once per workgroup) and 48.9 us at 2048 (too few workgroups)
-constexpr int kApplyRows = 1024;
-// with the MXFP4 epilogue (VALU-heavy) two workgroups per CU overlap it with
-// the other's products: 42.1 us at 512 rows against 56.9 us at 1024
+// default token rows per workgroup of the MXFP4 variant: with its epilogue
+// (VALU-heavy) two workgroups per CU overlap it with the other's products:
+// 42.1 us at 512 rows against 56.9 us at 1024
 constexpr int kApplyRowsMx = 512;
+constexpr int kApplyCUs = 256;  // compute units of an MI355X (one plain-apply workgroup each)
 constexpr int kApplyTiles = 4;  // row tiles per wave and batch
+
+// X staging of the plain apply (MX = false): a wave's next batch of 64 token
+// rows x 128 channels moves global -> LDS in 16 DMA loads of 4 whole
+// 256-byte row pieces each (lane l: row l%4, 16-byte chunk l/4), instead
+// of 16 register loads of 16 rows x 64 bytes: wider pieces stream faster
+// (about 12 % on 2048 x 14336).  Load q lands in block q of the wave's
+// region (1 KB + 64 bytes of padding), so that a fragment read (16 rows of
+// one 16-byte chunk) touches 16 distinct 16-byte bank groups.
+constexpr int kXBlk = (1024 + 64) / 2;  // halves per staged load block
+// One 1 KB global -> LDS load: lane l's 16 bytes at voff + soff land at
+// lds + 16 l.  (A plain device function: inside a kernel template the
+// builtin would keep the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void apply_dma_1k(__amdgpu_buffer_rsrc_t r, uint16_t *lds, uint32_t voff, uint32_t soff) {
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
+}
 
 // MX = true: instead of the tiled X_r, each row's 32-channel blocks are
 // quantized to MXFP4 in the epilogue (codes [tokens][I/2], E8M0 scales
 // [tokens][I/32]): a lane holds 8 consecutive channels of a block, and the
 // block's other 24 are in lanes l ^ 16, l ^ 32, l ^ 48 (same token).
 template <int XDT, bool MX>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, MX ? 2 : 1)  // the plain apply's x staging fills the LDS of one
 rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int64_t tokens, int64_t I,
                  const uint16_t *__restrict__ hl, uint8_t *__restrict__ mx_codes, uint8_t *__restrict__ mx_scales,
                  int wg_tiles) {
@@ -213,7 +226,33 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
 
   int64_t mt0 = mt_first + wave * kApplyTiles;
   u32x4 xf[kApplyTiles][4];
-  if (mt0 < mt_end) load_x(mt0, xf);
+  // plain apply: the staged batch's region of this wave, the DMA lane offset
+  // and the lane's fragment offset in the region (row 16t + fr lies in block
+  // 4t + fr/4 at row position fr%4; chunk 4ks + l/16)
+  __shared__ __attribute__((aligned(16))) uint16_t xlds[MX ? 1 : 4][MX ? 8 : 16 * kXBlk];
+  uint16_t *xw = xlds[MX ? 0 : wave];
+  const uint32_t dma_voff = (uint32_t)(((lane & 3) * I + 8 * (lane >> 2)) * 2);
+  const int xf_off = (fr >> 2) * kXBlk + 32 * (lane >> 4) + 8 * (fr & 3);
+  auto dma_x = [&](int64_t mt) {
+    const int64_t row0 = mt * 16;
+    const int64_t rows = tokens - row0 < 64 ? tokens - row0 : 64;
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + row0 * I + g * kG, rows > 0 ? (uint32_t)(rows * I * 2) : 0u);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) apply_dma_1k(xr, xw + q * kXBlk, dma_voff, (uint32_t)(4 * q * I * 2));
+  };
+  auto read_x = [&]() {
+#pragma unroll
+    for (int t = 0; t < kApplyTiles; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        xf[t][ks] = *reinterpret_cast<const u32x4 *>(xw + xf_off + 4 * t * kXBlk + 128 * ks);
+  };
+  if (mt0 < mt_end && mt0 < mt_first + wg_tiles) {
+    if constexpr (MX)
+      load_x(mt0, xf);
+    else
+      dma_x(mt0);
+  }
 
   // H_T, L_T of the group into LDS: 256 rows x 16 chunks of 16 bytes (16 per
   // thread, in two halves so that the x fragments in flight stay in registers)
@@ -229,11 +268,21 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
+  if constexpr (!MX) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first batch has landed in LDS
+    read_x();
+  }
 
   constexpr int kStride = 4 * kApplyTiles;  // row tiles per batch of the workgroup
   for (; mt0 < mt_end && mt0 < mt_first + wg_tiles; mt0 += kStride) {
     const int64_t next = mt0 + kStride;
     const bool more = next < mt_end && next < mt_first + wg_tiles;
+    if constexpr (!MX) {
+      // the fragment reads of this batch are done before its region is
+      // rewritten with the next batch
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (more) dma_x(next);
+    }
     f32x4 acc[kApplyTiles][8];
 #pragma unroll
     for (int t = 0; t < kApplyTiles; ++t)
@@ -258,7 +307,7 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
       if (step + 2 < 64) ar[(step + 2) % 3] = read_a(step + 2);
 #pragma unroll
       for (int t = 0; t < kApplyTiles; ++t) mfma_acc<XDT>(ar[step % 3], xf[t][ks], acc[t][ct]);
-      if ((step & 15) == 15 && more) {  // k-step ks consumed: fetch the next batch's fragments
+      if (MX && (step & 15) == 15 && more) {  // k-step ks consumed: fetch the next batch's fragments
         const int64_t row0 = next * 16;
         const int64_t rows = tokens - row0 < 64 ? tokens - row0 : 64;
         const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + row0 * I + g * kG, (uint32_t)(rows * I * 2));
@@ -273,6 +322,12 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
     for (int t = 0; t < kApplyTiles; ++t)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc_fence(acc[t][ct]);
+    if constexpr (!MX) {
+      if (more) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next batch has landed
+        read_x();
+      }
+    }
     // lane l, tile t, 32-channel block b: token l%16, channels 32b + 8(l/16) .. +7.
     if constexpr (MX) {
 #pragma unroll
@@ -330,24 +385,35 @@ hipError_t launch_rot_build(int x_dt, int64_t I, const int16_t *pairs, const flo
 }
 
 // token rows per apply workgroup; tuning override PARO_APPLY_ROWS (256, 512,
-// 1024, 2048 or 4096), read once per process.  Without it the default is
-// halved (down to 256) while the launch would have fewer than 192
-// workgroups, so narrow layers still spread over the chip.
-static int apply_rows(int dflt, int64_t tokens, int64_t I) {
+// 1024, 2048 or 4096), read once per process.  Without it: the MXFP4
+// variant (two workgroups per CU) starts from its default and halves it
+// (down to 256) while the launch would have fewer than 192 workgroups, so
+// narrow layers still spread over the chip; the plain apply (one workgroup
+// per CU, its LDS holds the x staging) takes the fewest rows, from 256 up,
+// whose grid fits the 256 CUs in one round (2048 x 14336: 1024 rows, 224
+// workgroups; 4096 x 14336: 2048 rows, 224 workgroups, against 448 in two
+// rounds at 1024).
+static int apply_rows(int dflt, int64_t tokens, int64_t I, bool one_per_cu) {
   static const int r = [] {
     const char *v = getenv("PARO_APPLY_ROWS");
     const int n = (v && *v) ? atoi(v) : 0;
     return (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) ? n : 0;
   }();
   if (r) return r;
+  auto grid = [&](int rows) { return (I / kG) * ((tiled_rows(tokens) + rows - 1) / rows); };
+  if (one_per_cu) {
+    int rows = 256;
+    while (rows < 4096 && grid(rows) > kApplyCUs) rows *= 2;
+    return rows;
+  }
   int rows = dflt;
-  while (rows > 256 && (I / kG) * ((tiled_rows(tokens) + rows - 1) / rows) < 192) rows /= 2;
+  while (rows > 256 && grid(rows) < 192) rows /= 2;
   return rows;
 }
 
 hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t tokens, int64_t I,
                             const uint16_t *hl, hipStream_t st) {
-  const int rows = apply_rows(kApplyRows, tokens, I);
+  const int rows = apply_rows(0, tokens, I, true);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, false>), grid, dim3(256), 0, st, x, xt, tokens, I, hl, nullptr,
@@ -361,7 +427,7 @@ hipError_t launch_rot_apply(const uint16_t *x, int x_dt, uint16_t *xt, int64_t t
 hipError_t launch_rot_apply_mx(const uint16_t *x, int x_dt, int64_t tokens, int64_t I, const uint16_t *hl,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
   if (tokens == 0) return hipSuccess;
-  const int rows = apply_rows(kApplyRowsMx, tokens, I);
+  const int rows = apply_rows(kApplyRowsMx, tokens, I, false);
   const dim3 grid((unsigned)(I / kG), (unsigned)((tiled_rows(tokens) + rows - 1) / rows));
   if (x_dt == kF16)
     hipLaunchKernelGGL((rot_apply_kernel<kF16, true>), grid, dim3(256), 0, st, x, nullptr, tokens, I, hl, codes,

@@ -33,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# layer pairs that read the same input in the model (one grouped call each)
+SHARED_INPUT = (("k_proj", "v_proj"), ("gate_proj", "up_proj"))
 METRIC = "ParoQuant linear: decode weight GB/s, prefill TFLOP/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, published
@@ -570,6 +572,10 @@ def main():
     ap.add_argument("--rebuild-rotation", action="store_true",
                     help="prefill: rebuild each layer's dense rotation in every call (paro_w4a16_linear) "
                          "instead of building it once per layer (paro_w4a16_linear_prepared)")
+    ap.add_argument("--no-group", action="store_true",
+                    help="prefill: run every layer with its own calls instead of running the layers that read "
+                         "the same input (k_proj + v_proj, gate_proj + up_proj) through "
+                         "paro_w4a16_linear_prepared_multi, one GEMM launch per pair")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured ceiling (device copy for decode, library dense GEMM for prefill)")
     ap.add_argument("--op", choices=("linear", "quantize", "rotate", "rotate_backward", "moe", "mxfp4"),
@@ -672,9 +678,35 @@ def main():
                 hl_row.append(hl)
             hls.append(hl_row)
 
+    # Layers that read the same input (the key and value projections, the
+    # gate and up projections) run together, one rotation each and one GEMM
+    # launch per pair, on the pair's first input.
+    names = [n for n, _, _, _, _ in layers]
+    groups, li = [], 0
+    while li < len(layers):
+        grp = [li]
+        if prepared and not args.no_group and li + 1 < len(layers):
+            for a, b in SHARED_INPUT:
+                if names[li] == a and names[li + 1] == b and layers[li][1:3] == layers[li + 1][1:3]:
+                    grp = [li, li + 1]
+        groups.append(grp)
+        li += len(grp)
+    for grp in groups:
+        if len(grp) > 1:
+            Dg = [sets[0][l][0] for l in grp]
+            ws_bytes = max(ws_bytes, paro.paro_w4a16_linear_prepared_multi_workspace_bytes(Dg, M))
+    if ws_bytes > ws.numel() * ws.element_size():
+        ws = paro.make_workspace(ws_bytes, device=dev)
+
     def step(i):
         row = sets[i % nsets]
-        for l, (D, xd) in enumerate(row):
+        for grp in groups:
+            if len(grp) > 1:
+                paro.paro_w4a16_linear_prepared_multi([row[l][0] for l in grp], [hls[i % nsets][l] for l in grp],
+                                                      row[grp[0]][1], [ys[l] for l in grp], ws, stream=stream)
+                continue
+            l = grp[0]
+            D, xd = row[l]
             if prepared:
                 paro.paro_w4a16_linear_prepared(D, hls[i % nsets][l], xd, ys[l], ws, stream=stream)
             else:
@@ -750,10 +782,16 @@ def main():
 
             def launch(i):
                 row = sets[i % nsets]
-                for l, (D, _) in enumerate(row):
-                    paro.paro_w4a16_linear_tiled(D, xts[i % nsets][l], act, M, ys[l], stream=stream)
+                for grp in groups:
+                    if len(grp) > 1:
+                        paro.paro_w4a16_linear_tiled_multi([row[l][0] for l in grp],
+                                                           [xts[i % nsets][l] for l in grp], act, M,
+                                                           [ys[l] for l in grp], stream=stream)
+                    else:
+                        l = grp[0]
+                        paro.paro_w4a16_linear_tiled(row[l][0], xts[i % nsets][l], act, M, ys[l], stream=stream)
             per_launch_bytes, per_launch_flops = alg_bytes, flops
-            launches_per_call = len(layers)
+            launches_per_call = len(groups)
         for i in range(min(args.warmup, 20)):
             launch(i)
         torch.cuda.synchronize()
@@ -823,6 +861,7 @@ def main():
                    "group_size": args.group, "krot": 8, "path": PATH_NAMES[path], "buffer_sets": nsets,
                    "rotation_matrix": ("built once per layer (paro_rotation_matrix), applied every step"
                                        if prepared else "built in every call" if path == 3 else None),
+                   "grouped": [[names[l] for l in g] for g in groups if len(g) > 1] or None,
                    "parallelism": "single-gpu"},
         "roofline": roofline, "cpu_baseline": cpu, "kernel_sources": khash,
     }

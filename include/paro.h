@@ -200,6 +200,40 @@ int paro_w4a16_linear_prepared(const paro_w4_layer *layer, const void *hl, const
 size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /*
+ * Several layers of one shape that read the same input, each with its own
+ * rotation, packed weight, bias and output: the key and value projections
+ * of an attention block, the gate and up projections of an MLP.  For
+ * i < n_layers:
+ *   y[i] = paro_w4a16_linear_prepared(&layers[i], hl[i], x, ...)
+ * (page "ParoQuant", Concepts / Activation and weight transforms: every
+ * layer is its own rotated linear; nothing is shared but the input x).
+ *   layers   : n_layers (1..PARO_MULTI_MAX_LAYERS) host descriptors; their
+ *              in_features, out_features, group_size (32, 64 or 128) and
+ *              krot must be equal (PARO_ERR_SHAPE otherwise).
+ *   hl       : n_layers rotation matrices from paro_rotation_matrix (as
+ *              for paro_w4a16_linear_prepared), caller-owned, not written.
+ *   y        : n_layers outputs [tokens][out_features] in y_dt, 16-byte
+ *              aligned, not overlapping x, each other or the workspace.
+ * Many tokens (the PREFILL path): each layer's input rotation runs into its
+ * own tiled X_r, then ONE GEMM launch covers the output tiles of all the
+ * layers, so layers too narrow to fill the chip alone (1024 outputs at 4096
+ * tokens) fill it together.  Up to 16 tokens the layers run one after
+ * another through the decode kernels.  Results equal those of n_layers
+ * paro_w4a16_linear_prepared calls bit for bit.  workspace: zero-filled
+ * before first use, of
+ * paro_w4a16_linear_prepared_multi_workspace_bytes(layers, n_layers, tokens)
+ * bytes (one tiled X_r per layer on the PREFILL path).  Errors as
+ * paro_w4a16_linear_prepared, plus PARO_ERR_SHAPE for n_layers or
+ * mismatched shapes.
+ */
+#define PARO_MULTI_MAX_LAYERS 4
+int paro_w4a16_linear_prepared_multi(const paro_w4_layer *layers, int n_layers, const void *const *hl,
+                                     const void *x, paro_dtype x_dt, int64_t tokens, void *const *y,
+                                     paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream);
+size_t paro_w4a16_linear_prepared_multi_workspace_bytes(const paro_w4_layer *layers, int n_layers,
+                                                        int64_t tokens);
+
+/*
  * paro_w4a16_linear for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same computation with no workspace argument.  The
@@ -289,6 +323,18 @@ int paro_scale_rotate_tiled(const paro_w4_layer *layer, const void *hl, const vo
  */
 int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dtype x_dt,
                             int64_t tokens, void *y, paro_dtype y_dt, void *stream);
+
+/*
+ * paro_w4a16_linear_tiled for several layers of one shape (in_features,
+ * out_features and group size equal; PARO_ERR_SHAPE otherwise) in ONE GEMM
+ * launch over the union of their output tiles: layer i reads x_t[i] and
+ * writes y[i] (1 <= n_layers <= PARO_MULTI_MAX_LAYERS; outputs must overlap
+ * no x_t and no other output).  Each y[i] equals that layer's
+ * paro_w4a16_linear_tiled result bit for bit.  The GEMM of
+ * paro_w4a16_linear_prepared_multi's PREFILL path.
+ */
+int paro_w4a16_linear_tiled_multi(const paro_w4_layer *layers, int n_layers, const void *const *x_t,
+                                  paro_dtype x_dt, int64_t tokens, void *const *y, paro_dtype y_dt, void *stream);
 
 /*
  * Mixture-of-experts projection with one rotation shared by all experts

@@ -23,6 +23,8 @@ STATUS = {0: "PARO_OK", 1: "PARO_ERR_NULL", 2: "PARO_ERR_SHAPE", 3: "PARO_ERR_DT
 EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated",
            "paro_w4a16_linear_prepared", "paro_w4a16_linear_prepared_workspace_bytes",
+           "paro_w4a16_linear_prepared_multi", "paro_w4a16_linear_prepared_multi_workspace_bytes",
+           "paro_w4a16_linear_tiled_multi",
            "paro_w4a16_linear_noalloc",
            "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
@@ -72,6 +74,10 @@ def load(path: str | None = None):
     lib.paro_w4a16_linear_prepared.argtypes = [P, P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_w4a16_linear_prepared_workspace_bytes.argtypes = [P, I64]
     lib.paro_w4a16_linear_prepared_workspace_bytes.restype = SZ
+    lib.paro_w4a16_linear_prepared_multi.argtypes = [P, ctypes.c_int, P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_w4a16_linear_prepared_multi_workspace_bytes.argtypes = [P, ctypes.c_int, I64]
+    lib.paro_w4a16_linear_prepared_multi_workspace_bytes.restype = SZ
+    lib.paro_w4a16_linear_tiled_multi.argtypes = [P, ctypes.c_int, P, I32, I64, P, I32, P]
     lib.paro_w4a16_linear_noalloc.argtypes = [P, P, I32, I64, P, I32, P]
     lib.paro_tiled_bytes.argtypes = [P, I64]
     lib.paro_tiled_bytes.restype = SZ
@@ -104,7 +110,7 @@ def load(path: str | None = None):
     lib.paro_abi_version.argtypes = []
     for name in ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
                  "paro_w4a16_linear_path", "paro_w4a16_linear_prerotated", "paro_w4a16_linear_prepared",
-                 "paro_w4a16_linear_noalloc",
+                 "paro_w4a16_linear_prepared_multi", "paro_w4a16_linear_tiled_multi", "paro_w4a16_linear_noalloc",
                  "paro_w4_quantize_pack", "paro_scale_rotate_backward", "paro_w4a16_moe_linear",
                  "paro_mxfp4_quantize_weight", "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm",
                  "paro_mxfp4_linear",
@@ -243,6 +249,39 @@ def paro_w4a16_linear_prepared(layer: DeviceLayer, hl, x, y, workspace=None, str
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().paro_w4a16_linear_prepared(layer.ref, _ptr(hl), _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
                                              ws_ptr, ws_bytes, _stream_handle(stream)), "paro_w4a16_linear_prepared")
+
+
+def _layer_array(layers):
+    """A contiguous C array of the layers' descriptors (copies of their structs)."""
+    arr = (ParoLayerC * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = L.c
+    return arr
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def paro_w4a16_linear_prepared_multi_workspace_bytes(layers, tokens: int) -> int:
+    return int(load().paro_w4a16_linear_prepared_multi_workspace_bytes(_layer_array(layers), len(layers), tokens))
+
+
+def paro_w4a16_linear_prepared_multi(layers, hls, x, ys, workspace=None, stream=None) -> None:
+    """Layers of one shape over the same input x, each with its rotation matrix hls[i] and output ys[i]."""
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_w4a16_linear_prepared_multi(_layer_array(layers), len(layers), _ptr_array(hls), _ptr(x),
+                                                   _dt(x), x.shape[0], _ptr_array(ys), _dt(ys[0]), ws_ptr,
+                                                   ws_bytes, _stream_handle(stream)),
+           "paro_w4a16_linear_prepared_multi")
+
+
+def paro_w4a16_linear_tiled_multi(layers, x_ts, x_dt: int, tokens: int, ys, stream=None) -> None:
+    """The prefill GEMM alone for layers of one shape, each over its tiled X_r, in one launch."""
+    _check(load().paro_w4a16_linear_tiled_multi(_layer_array(layers), len(layers), _ptr_array(x_ts), x_dt, tokens,
+                                                _ptr_array(ys), _dt(ys[0]), _stream_handle(stream)),
+           "paro_w4a16_linear_tiled_multi")
 
 
 def paro_w4a16_linear_noalloc(layer: DeviceLayer, x, y, stream=None) -> None:

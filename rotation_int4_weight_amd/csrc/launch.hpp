@@ -104,6 +104,21 @@ hipError_t launch_retile(const uint16_t *xr, uint16_t *xt, int64_t tokens, int64
 
 // Prefill: MFMA GEMM over rotated activations in the tiled layout.
 hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *xt, hipStream_t st);
+// Several dense layers of one shape (a's I, O, tokens, group, dtypes) in one
+// launch: layer i takes its weights, bias and output from the table and its
+// rotated activations from xt[i]; the launch covers the union of the
+// layers' output tiles.  a's own pointers are not read.
+constexpr int kMaxMultiLayers = 4;
+struct LayerTable {
+  int n;  // layers, 1..kMaxMultiLayers
+  const int32_t *qweight[kMaxMultiLayers];
+  const int32_t *qzeros[kMaxMultiLayers];
+  const uint16_t *scales[kMaxMultiLayers];
+  const uint16_t *bias[kMaxMultiLayers];  // entries may be null
+  const uint16_t *xt[kMaxMultiLayers];
+  void *y[kMaxMultiLayers];
+};
+hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt, hipStream_t st);
 // Upper bound on the (expert, 256-row tile) work items of a MoE call.
 int64_t moe_work_tiles(int64_t tokens, int experts);
 

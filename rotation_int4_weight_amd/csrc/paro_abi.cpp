@@ -313,6 +313,51 @@ int paro_w4a16_linear_tiled(const paro_w4_layer *L, const void *x_t, paro_dtype 
   return ok();
 }
 
+int paro_w4a16_linear_tiled_multi(const paro_w4_layer *layers, int n_layers, const void *const *x_t,
+                                  paro_dtype x_dt, int64_t tokens, void *const *y, paro_dtype y_dt, void *stream) {
+  if (!layers || !x_t || !y) return fail(PARO_ERR_NULL, "layers, x_t and y are required");
+  if (n_layers < 1 || n_layers > paro::kMaxMultiLayers)
+    return fail(PARO_ERR_SHAPE, "n_layers=%d must be in 1..%d", n_layers, paro::kMaxMultiLayers);
+  const paro_w4_layer *L0 = &layers[0];
+  int rc = PARO_OK;
+  for (int i = 0; i < n_layers; ++i) {
+    const paro_w4_layer *L = &layers[i];
+    if ((rc = check_gpu_shape(L, true))) return rc;
+    if (L->in_features != L0->in_features || L->out_features != L0->out_features || group_of(L) != group_of(L0))
+      return fail(PARO_ERR_SHAPE, "layer %d: in/out features and group size must equal layer 0's", i);
+  }
+  if ((rc = check_tokens(tokens))) return rc;
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
+  if (tokens == 0) return ok();
+  const size_t tb = paro_tiled_bytes(L0, tokens), yb = (size_t)tokens * L0->out_features * (y_dt == PARO_F32 ? 4 : 2);
+  for (int i = 0; i < n_layers; ++i) {
+    if (!x_t[i] || !y[i]) return fail(PARO_ERR_NULL, "layer %d: x_t and y are required", i);
+    if ((rc = check_weight_tensors(&layers[i]))) return rc;
+    if (!aligned(x_t[i], 16) || !aligned(y[i], 16))
+      return fail(PARO_ERR_ALIGN, "layer %d: x_t and y must be 16-byte aligned", i);
+  }
+  for (int i = 0; i < n_layers; ++i)
+    for (int j = 0; j < n_layers; ++j) {
+      if (overlap(y[i], yb, x_t[j], tb)) return fail(PARO_ERR_SHAPE, "the output of layer %d overlaps x_t of %d", i, j);
+      if (j < i && overlap(y[i], yb, y[j], yb)) return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
+    }
+  paro::LinearArgs a = linear_args(L0, tokens, x_t[0], x_dt, y[0], y_dt);
+  paro::LayerTable lt{};
+  lt.n = n_layers;
+  for (int i = 0; i < n_layers; ++i) {
+    lt.qweight[i] = layers[i].qweight;
+    lt.qzeros[i] = layers[i].qzeros;
+    lt.scales[i] = layers[i].scales;
+    lt.bias[i] = layers[i].bias;
+    lt.xt[i] = (const uint16_t *)x_t[i];
+    lt.y[i] = y[i];
+  }
+  const hipError_t e = paro::launch_prefill_gemm_multi(a, lt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
+  return ok();
+}
+
 int paro_w4_unpack_dequant(const paro_w4_layer *L, uint8_t *q_out, uint8_t *z_out, void *w_out, paro_dtype w_dt,
                            void *stream) {
   int rc = check_gpu_shape(L, true);
@@ -758,6 +803,83 @@ size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *L, int64_
   if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
   const paro_path path = auto_path(tokens);
   return path == PARO_PATH_PREFILL ? kCounterBytes + xr_region(L, tokens, path) : workspace_for(L, tokens, path);
+}
+
+size_t paro_w4a16_linear_prepared_multi_workspace_bytes(const paro_w4_layer *layers, int n_layers,
+                                                        int64_t tokens) {
+  if (!layers || n_layers < 1 || n_layers > paro::kMaxMultiLayers || tokens <= 0) return 0;
+  const paro_w4_layer *L = &layers[0];
+  if (check_gpu_shape(L)) return 0;
+  const paro_path path = auto_path(tokens);
+  const size_t one = path == PARO_PATH_PREFILL ? kCounterBytes + xr_region(L, tokens, path) : workspace_for(L, tokens, path);
+  // prefill: one tiled X_r per layer (the layers run in one GEMM launch);
+  // decode: the layers run one after another on one workspace
+  return path == PARO_PATH_PREFILL ? kCounterBytes + (size_t)n_layers * xr_region(L, tokens, path) : one;
+}
+
+static_assert(PARO_MULTI_MAX_LAYERS == paro::kMaxMultiLayers, "the header and the kernels agree on the layer count");
+
+int paro_w4a16_linear_prepared_multi(const paro_w4_layer *layers, int n_layers, const void *const *hl,
+                                     const void *x, paro_dtype x_dt, int64_t tokens, void *const *y,
+                                     paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!layers || !hl || !y) return fail(PARO_ERR_NULL, "layers, hl and y are required");
+  if (n_layers < 1 || n_layers > paro::kMaxMultiLayers)
+    return fail(PARO_ERR_SHAPE, "n_layers=%d must be in 1..%d", n_layers, paro::kMaxMultiLayers);
+  const paro_w4_layer *L0 = &layers[0];
+  int rc = check_gpu_shape(L0);
+  if (!rc) rc = check_tokens(tokens);
+  if (rc) return rc;
+  for (int i = 0; i < n_layers; ++i) {
+    const paro_w4_layer *L = &layers[i];
+    if ((rc = check_gpu_shape(L))) return rc;
+    if (L->in_features != L0->in_features || L->out_features != L0->out_features ||
+        group_of(L) != group_of(L0) || L->krot != L0->krot)
+      return fail(PARO_ERR_SHAPE, "layer %d: in/out features, group size and krot must equal layer 0's", i);
+    if (!hl[i] || !y[i]) return fail(PARO_ERR_NULL, "layer %d: hl and y are required", i);
+  }
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
+  if (tokens == 0) return ok();
+  const paro_path path = auto_path(tokens);
+  if (path != PARO_PATH_PREFILL || n_layers == 1) {
+    // decode (or one layer): the single-layer call per layer, in order, on
+    // one workspace (stream order keeps the calls apart)
+    for (int i = 0; i < n_layers; ++i)
+      if ((rc = paro_w4a16_linear_prepared(&layers[i], hl[i], x, x_dt, tokens, y[i], y_dt, workspace,
+                                           workspace_bytes, stream)))
+        return rc;
+    return ok();
+  }
+  if (!x) return fail(PARO_ERR_NULL, "x is required");
+  const int64_t I = L0->in_features, O = L0->out_features;
+  const size_t xb = (size_t)tokens * I * 2, yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+  const size_t hb = paro::rot_mat_bytes(I), xrb = xr_region(L0, tokens, path);
+  const size_t need = kCounterBytes + (size_t)n_layers * xrb;
+  if (!aligned(x, 16)) return fail(PARO_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!workspace) return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (workspace_bytes < need) return fail(PARO_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (overlap(workspace, need, x, xb)) return fail(PARO_ERR_SHAPE, "the workspace overlaps x");
+  for (int i = 0; i < n_layers; ++i) {
+    const paro_w4_layer *L = &layers[i];
+    if ((rc = check_rotation_tensors(L)) || (rc = check_weight_tensors(L))) return rc;
+    if (!aligned(y[i], 16) || !aligned(hl[i], 16))
+      return fail(PARO_ERR_ALIGN, "layer %d: y and hl must be 16-byte aligned", i);
+    if (overlap(y[i], yb, x, xb)) return fail(PARO_ERR_SHAPE, "layer %d: y overlaps x", i);
+    if (overlap(workspace, need, y[i], yb) || overlap(workspace, need, hl[i], hb))
+      return fail(PARO_ERR_SHAPE, "layer %d: the workspace overlaps y or hl", i);
+    for (int j = 0; j < i; ++j)
+      if (overlap(y[i], yb, y[j], yb)) return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const void *xts[paro::kMaxMultiLayers];
+  for (int i = 0; i < n_layers; ++i) {
+    uint16_t *xt = (uint16_t *)((char *)workspace + kCounterBytes + (size_t)i * xrb);
+    const hipError_t e = paro::launch_rot_apply((const uint16_t *)x, (int)x_dt, xt, tokens, I, (const uint16_t *)hl[i], st);
+    if (e != hipSuccess) return hip_fail(e, "scale_rotate launch");
+    xts[i] = xt;
+  }
+  return paro_w4a16_linear_tiled_multi(layers, n_layers, xts, x_dt, tokens, y, y_dt, stream);
 }
 
 int paro_w4a16_moe_linear(const paro_w4_layer *L, int num_experts, const int64_t *expert_offsets, const void *x,

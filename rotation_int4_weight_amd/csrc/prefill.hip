@@ -209,7 +209,7 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
 // flight, instead of every tile starting from an empty pipeline.
 template <int DT, int GK, bool MOE, int RT>
 __global__ void __launch_bounds__(kThreads)
-prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
+prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   static_assert(RT == 4 || (RT == 2 && !MOE), "256-row tiles, or 128-row tiles for dense layers");
   constexpr int BM = 64 * RT;
   __shared__ __attribute__((aligned(16))) uint16_t bl[kTiles][kBN * kBStride];
@@ -217,14 +217,18 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
   // that their scalar loads go out together instead of in two dependent
   // round trips.
   asm volatile("" ::"s"(a.I), "s"(a.O), "s"(a.tokens), "s"(a.group), "s"(a.experts), "s"(a.expert_offsets),
-               "s"(a.qweight), "s"(a.qzeros), "s"(a.scales), "s"(a.bias), "s"(a.y), "s"(a.y_dt), "s"(xt),
-               "s"(gridDim.x));
+               "s"(a.qweight), "s"(a.qzeros), "s"(a.scales), "s"(a.bias), "s"(a.y), "s"(a.y_dt), "s"(lt.n),
+               "s"(lt.xt[0]), "s"(lt.y[0]), "s"(gridDim.x));
   const int lane = lane_id(), wave = wave_id();
+  // the layer table is read where a tile is entered, from the argument
+  // segment (a scalar load at the entry's offset), not held in registers
+  const LayerTable *ltp = &lt;
   PREFILL_MARK(0);
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
   const int n_tiles = (int)((O + kBN - 1) / kBN);
   const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + BM - 1) / BM);
-  const int total = n_tiles * m_tiles;
+  // dense: the layers of the table one after another in the tile order
+  const int per_layer = n_tiles * m_tiles, total = MOE ? per_layer : per_layer * lt.n;
   // tiles of this workgroup (the grid never exceeds the tile count)
   const int my_tiles = MOE ? 1 : (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
@@ -239,18 +243,36 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     int64_t n0, mb, row_lo, row_hi;
     const int32_t *qweight, *qzeros;
     const uint16_t *scales, *bias;
+    int layer;  // entry of the layer table (MoE: 0)
   };
   auto tile_of = [&](int it, Tile &t) -> bool {
-    t.qweight = a.qweight;
-    t.qzeros = a.qzeros;
-    t.scales = a.scales;
-    t.bias = a.bias;
     t.row_lo = 0;
     t.row_hi = M;
     // XCD-local order: consecutive logical tiles (the N tiles of one M block)
     // share an XCD and its L2.  Workgroup b's iteration it stands for launch
     // id b + it G, which lies on b's XCD when G is a multiple of 8.
-    const int lwg = xcd_local_order((int)blockIdx.x + it * (int)gridDim.x, total);
+    int lwg = xcd_local_order((int)blockIdx.x + it * (int)gridDim.x, total);
+    if constexpr (MOE) {
+      t.layer = 0;
+      t.qweight = a.qweight;
+      t.qzeros = a.qzeros;
+      t.scales = a.scales;
+      t.bias = a.bias;
+    } else {
+      t.layer = __builtin_amdgcn_readfirstlane(lwg / per_layer);
+      lwg -= t.layer * per_layer;
+      if (t.layer == 0) {  // entry 0 is also in a (the single-layer launch)
+        t.qweight = a.qweight;
+        t.qzeros = a.qzeros;
+        t.scales = a.scales;
+        t.bias = a.bias;
+      } else {
+        t.qweight = ltp->qweight[t.layer];
+        t.qzeros = ltp->qzeros[t.layer];
+        t.scales = ltp->scales[t.layer];
+        t.bias = ltp->bias[t.layer];
+      }
+    }
     // Dense layers: logical tiles go in groups of kGroupM M blocks, the M
     // block fastest, so an XCD's share of consecutive tiles spans kGroupM
     // blocks of rows and 1/kGroupM as many weight columns as a row-major
@@ -463,6 +485,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     const int64_t rtiles = (t.row_hi + 15) / 16 - t.mb / 16;
     const int tiles = (int)(rtiles < BM / 16 ? rtiles : BM / 16);
     const uint32_t kb = (uint32_t)ls * 1024u;
+    const uint16_t *xt = t.layer == 0 ? lt.xt[0] : ltp->xt[t.layer];
     const char *a_base = reinterpret_cast<const char *>(xt + (t.mb / 16) * (I / 32) * 512);
     const __amdgpu_buffer_rsrc_t r = raw_rsrc(a_base + kb, (uint32_t)tiles * tile_bytes - kb);
 #pragma unroll
@@ -605,7 +628,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
     auto epilogue = [&](auto ydt) {
       constexpr int YD = decltype(ydt)::value;
       typedef typename std::conditional<YD == kF32, float, uint16_t>::type YT;
-      YT *ybase = reinterpret_cast<YT *>(a.y) + (m0 + erow) * O + t.n0 + 8 * eg;
+      YT *ybase = reinterpret_cast<YT *>(t.layer == 0 ? a.y : ltp->y[t.layer]) + (m0 + erow) * O + t.n0 + 8 * eg;
       // Two fp32 sums -> one packed pair, RNE.  For fp16 the conversion is
       // written as asm: the compiler would otherwise fuse it with the bias
       // fma into one mixed fma with an fp16 result (a single rounding),
@@ -679,7 +702,7 @@ prefill_gemm_kernel(LinearArgs a, const uint16_t *__restrict__ xt) {
 }
 
 template <int GK, bool MOE, int RT>
-static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
+static void launch_prefill_gk(const LinearArgs &a, const LayerTable &x, dim3 grid, hipStream_t st) {
   if (a.x_dt == kF16)
     hipLaunchKernelGGL((prefill_gemm_kernel<kF16, GK, MOE, RT>), grid, dim3(kThreads), 0, st, a, x);
   else
@@ -687,7 +710,7 @@ static void launch_prefill_gk(const LinearArgs &a, const uint16_t *x, dim3 grid,
 }
 
 template <bool MOE, int RT>
-static void launch_prefill_moe(const LinearArgs &a, const uint16_t *x, dim3 grid, hipStream_t st) {
+static void launch_prefill_moe(const LinearArgs &a, const LayerTable &x, dim3 grid, hipStream_t st) {
   if constexpr (!MOE) {  // one group over the whole row (dense layers only)
     if (a.group == a.I && a.group > kG) {
       launch_prefill_gk<0, MOE, RT>(a, x, grid, st);
@@ -731,20 +754,32 @@ int64_t moe_work_tiles(int64_t tokens, int experts) {
   return (tokens + 15 * (int64_t)experts + kBM - 1) / kBM + experts;
 }
 
-hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
+hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt, hipStream_t st) {
   const int64_t n_tiles = (a.O + kBN - 1) / kBN;
   if (a.experts > 0) {
-    launch_prefill_moe<true, 4>(a, x, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
+    launch_prefill_moe<true, 4>(a, lt, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
   } else {
-    const int bm = dense_tile_rows(a.tokens, n_tiles);
-    const int64_t tiles = n_tiles * ((a.tokens + bm - 1) / bm);
+    const int bm = dense_tile_rows(a.tokens, n_tiles * lt.n);
+    const int64_t tiles = n_tiles * ((a.tokens + bm - 1) / bm) * lt.n;
     const dim3 grid((unsigned)persistent_grid(tiles));
     if (bm == 128)
-      launch_prefill_moe<false, 2>(a, x, grid, st);
+      launch_prefill_moe<false, 2>(a, lt, grid, st);
     else
-      launch_prefill_moe<false, 4>(a, x, grid, st);
+      launch_prefill_moe<false, 4>(a, lt, grid, st);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream_t st) {
+  LayerTable lt{};
+  lt.n = 1;
+  lt.qweight[0] = a.qweight;
+  lt.qzeros[0] = a.qzeros;
+  lt.scales[0] = a.scales;
+  lt.bias[0] = a.bias;
+  lt.xt[0] = x;
+  lt.y[0] = a.y;
+  return launch_prefill_gemm_multi(a, lt, st);
 }
 
 }  // namespace paro

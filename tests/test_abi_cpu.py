@@ -367,3 +367,83 @@ def test_whole_row_group_workspace_and_path():
     assert lib.paro_w4a16_linear_workspace_bytes(ctypes.byref(L), 32, 1, 3) == counters + 32 * 4096 * 2
     assert lib.paro_w4a16_linear_workspace_bytes(ctypes.byref(L128), 32, 1, 3) == counters + 32 * 4096 * 2 + 4096 * 512
     assert lib.paro_w4a16_linear_prepared_workspace_bytes(ctypes.byref(L), 32) == 0   # no prebuilt form
+
+
+def multi(layers, n=None, hl=(FAKE * 8, FAKE * 9), x=FAKE, xdt=0, tokens=32, y=(FAKE * 2, FAKE * 3), ydt=0,
+          ws=FAKE * 16, wsb=1 << 30):
+    """paro_w4a16_linear_prepared_multi on fake descriptors (validation only)."""
+    arr = (_lib.ParoLayerC * len(layers))(*layers) if layers is not None else None
+    hla = (ctypes.c_void_p * len(hl))(*hl) if hl is not None else None
+    ya = (ctypes.c_void_p * len(y))(*y) if y is not None else None
+    if n is None:
+        n = len(layers) if layers is not None else 2
+    return _lib.load().paro_w4a16_linear_prepared_multi(arr, n, hla, x, xdt, tokens, ya, ydt, ws, wsb, None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("case,code", [
+    (dict(n=0), 2),                                    # 1..4 layers
+    (dict(n=5), 2),
+    (dict(layers=None), 1),
+    (dict(hl=None), 1),
+    (dict(y=None), 1),
+    (dict(hl=(FAKE * 8, 0)), 1),                       # every layer needs its rotation matrix
+    (dict(y=(FAKE * 2, 0)), 1),
+    (dict(L1=dict(O=128)), 2),                         # the layers share one shape
+    (dict(L1=dict(G=64)), 2),
+    (dict(L1=dict(krot=4)), 2),
+    (dict(L1=dict(G=16)), 5),
+    (dict(xdt=2), 3),
+    (dict(ydt=1), 3),
+    (dict(x=FAKE + 2), 4),
+    (dict(hl=(FAKE * 8, FAKE * 9 + 4)), 4),
+    (dict(y=(FAKE * 2, FAKE * 2 + 64)), 2),            # the two outputs overlap
+    (dict(y=(FAKE * 2, FAKE + 32)), 2),                # an output overlaps x
+    (dict(wsb=64), 7),
+    (dict(ws=0), 7),
+    (dict(L1=dict(qweight=0)), 1),
+])
+def test_multi_linear_argument_checks(case, code):
+    L0 = fake_layer(I=256, O=64)
+    L1 = fake_layer(**{"I": 256, "O": 64, **case.get("L1", {})})
+    kw = {k: v for k, v in case.items() if k not in ("L1",)}
+    layers = kw.pop("layers", [L0, L1])
+    rc = multi(layers, **kw)
+    assert rc == code, _lib.paro_last_error()
+    assert _lib.paro_last_error()
+
+
+@needs_no_gpu
+def test_multi_linear_zero_tokens_is_a_noop():
+    assert multi([fake_layer(), fake_layer()], tokens=0, x=0, ws=0, wsb=0) == 0
+
+
+def test_multi_linear_workspace_sizes():
+    lib = _lib.load()
+    L = fake_layer(I=4096, O=1024)
+    arr = lambda n: (_lib.ParoLayerC * n)(*([L] * n))
+    mw = lambda n, m: lib.paro_w4a16_linear_prepared_multi_workspace_bytes(arr(n), n, m)
+    one = lambda m: lib.paro_w4a16_linear_prepared_workspace_bytes(ctypes.byref(L), m)
+    # prefill: one tiled X_r per layer after the counters; decode: one layer's workspace
+    assert mw(2, 4096) - mw(1, 4096) == 4096 * 4096 * 2
+    assert mw(1, 4096) == one(4096)
+    assert mw(3, 16) == one(16) and mw(2, 1) == one(1)
+    assert mw(0, 4096) == 0 and mw(5, 4096) == 0 and mw(2, 0) == 0
+
+
+@needs_no_gpu
+def test_tiled_multi_argument_checks():
+    lib = _lib.load()
+    arr = lambda ls: (_lib.ParoLayerC * len(ls))(*ls)
+    ptrs = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    L0, L1 = fake_layer(I=256, O=64), fake_layer(I=256, O=64)
+    call = lambda ls, n, xt, y, tokens=32: lib.paro_w4a16_linear_tiled_multi(arr(ls), n, xt, 0, tokens, y, 0, None)
+    ok_xt, ok_y = ptrs(FAKE * 4, FAKE * 5), ptrs(FAKE * 6, FAKE * 7)
+    assert call([L0, L1], 0, ok_xt, ok_y) == 2
+    assert call([L0, L1], 5, ok_xt, ok_y) == 2
+    assert call([L0, fake_layer(I=256, O=128)], 2, ok_xt, ok_y) == 2          # one shape
+    assert call([L0, L1], 2, ptrs(FAKE * 4, 0), ok_y) == 1
+    assert call([L0, L1], 2, ok_xt, ptrs(FAKE * 6, FAKE * 6 + 64)) == 2      # outputs overlap
+    assert call([L0, L1], 2, ok_xt, ptrs(FAKE * 6, FAKE * 5 + 32)) == 2      # an output overlaps an x_t
+    assert call([L0, L1], 2, ptrs(FAKE * 4 + 4, FAKE * 5), ok_y) == 4
+    assert call([L0, L1], 2, None, None, tokens=0) == 1                      # arrays are required

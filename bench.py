@@ -818,7 +818,10 @@ def main():
             ach = kern["flops_per_launch"] / (kern["avg_us"] * 1e-6) / 1e12
             roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
-        roofline["traffic"] = load_traffic(f"{args.workload}{gsuffix(args)}", khash)
+        # (the committed readings are per launch of the grouped step; an
+        # ungrouped run launches other kernels)
+        ungrouped = "-nogroup" if path == 3 and args.no_group else ""
+        roofline["traffic"] = load_traffic(f"{args.workload}{gsuffix(args)}{ungrouped}", khash)
         roofline["kernel"] = kern["name"]
         roofline["avg_launch_us"] = round(kern["avg_us"], 3)
         roofline["launches_per_step"] = kern["launches_per_step"]

@@ -191,7 +191,7 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
 // MOE: experts stacked in the weight tensors (qweight [E][I][O/8], qzeros
 // [E][I/G][O/8], scales [E][I/G][O], bias [E][O]) share one rotation; the
 // rows of expert e are [offsets[e], offsets[e+1]) of the rotated activations
-// (rotated once for all experts).  A workgroup takes one 256-row tile of one
+// (rotated once for all experts).  An output tile is a 256-row block of one
 // expert's rows, starting at the 16-row tile that holds the expert's first
 // row: rows of neighbouring experts in its tiles are computed and dropped.
 // Offsets are clamped into [0, tokens] and made nondecreasing, so no offsets
@@ -201,12 +201,13 @@ __device__ __forceinline__ void expand_pair_to_lds(uint32_t ra, uint32_t rb, con
 // 256-row grid would leave CUs idle (each weight tile then serves half as
 // many MFMAs, and twice as many workgroups fill the chip).
 //
-// Dense layers run persistent workgroups: workgroup b takes the output tiles
-// b, b + G, b + 2G, ... (G workgroups, at most one per CU) in turn.  Steps
-// are numbered across its tiles, so the weight ring simply continues: while
-// the consumers finish a tile (its epilogue), the producers already expand
-// the first steps of the next one, and the consumers' A loads for it are in
-// flight, instead of every tile starting from an empty pipeline.
+// Dense layers and the MoE run persistent workgroups: workgroup b takes the
+// output tiles b, b + G, b + 2G, ... (G workgroups, at most one per CU) in
+// turn.  Steps are numbered across its tiles, so the weight ring simply
+// continues: while the consumers finish a tile (its epilogue), the producers
+// already expand the first steps of the next one, and the consumers' A loads
+// for it are in flight, instead of every tile starting from an empty
+// pipeline.
 template <int DT, int GK, bool MOE, int RT>
 __global__ void __launch_bounds__(kThreads)
 prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
@@ -226,11 +227,28 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   PREFILL_MARK(0);
   const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
   const int n_tiles = (int)((O + kBN - 1) / kBN);
-  const int m_tiles = MOE ? (int)(gridDim.x / n_tiles) : (int)((M + BM - 1) / BM);
+  // MoE: the experts' 256-row work items, counted from the offsets (each
+  // expert's rows, clamped into [0, M] and made nondecreasing, start at the
+  // 16-row tile that holds its first row)
+  auto moe_items = [&]() -> int {
+    int64_t cum = 0, prev = a.expert_offsets[0];
+    prev = prev < 0 ? 0 : (prev > M ? M : prev);
+    for (int k = 0; k < a.experts; ++k) {
+      int64_t o1 = a.expert_offsets[k + 1];
+      o1 = o1 < prev ? prev : (o1 > M ? M : o1);
+      cum += o1 > prev ? (o1 - (prev & ~(int64_t)15) + kBM - 1) / kBM : 0;
+      prev = o1;
+    }
+    return (int)cum;
+  };
+  const int m_tiles = MOE ? moe_items() : (int)((M + BM - 1) / BM);
   // dense: the layers of the table one after another in the tile order
   const int per_layer = n_tiles * m_tiles, total = MOE ? per_layer : per_layer * lt.n;
-  // tiles of this workgroup (the grid never exceeds the tile count)
-  const int my_tiles = MOE ? 1 : (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // tiles of this workgroup: b, b + G, ... (MoE: the grid is sized on the
+  // host for the most work items the offsets can give, so a workgroup may
+  // have none)
+  const int my_tiles = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  if (my_tiles <= 0) return;  // the whole workgroup leaves before any barrier
   // GK k-steps per quantization group (G = 32 * GK); I is a multiple of 128
   // (GK = 0: one quantization group over the whole row)
   const int nsteps = (int)(I / kBK), ngroups = GK ? (int)(I / (kBK * GK)) : 1;
@@ -307,7 +325,10 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
         cum += c;
         prev = o1;
       }
-      if (e < 0) return false;
+      if (e < 0) {  // (not reached: every tile below total has its expert)
+        t.mb = t.row_lo = t.row_hi = 0;
+        return false;
+      }
       t.mb = (lo & ~(int64_t)15) + j * kBM;
       t.row_lo = lo > t.mb ? lo : t.mb;
       t.row_hi = hi < t.mb + kBM ? hi : t.mb + kBM;
@@ -324,10 +345,9 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   const uint32_t tile_bytes = (uint32_t)nsteps * 1024u;  // one row tile over all of k
 
   Tile t0;
-  if (!tile_of(0, t0)) return;  // MoE past the last tile: the whole workgroup leaves before any barrier
-  // (a MoE workgroup has one tile: its expert scan is not repeated)
+  tile_of(0, t0);  // (every tile below total exists)
   auto tile_at = [&](int it, Tile &t) {
-    if (MOE || it == 0)
+    if (it == 0)
       t = t0;
     else
       tile_of(it, t);
@@ -757,7 +777,9 @@ int64_t moe_work_tiles(int64_t tokens, int experts) {
 hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt, hipStream_t st) {
   const int64_t n_tiles = (a.O + kBN - 1) / kBN;
   if (a.experts > 0) {
-    launch_prefill_moe<true, 4>(a, lt, dim3((unsigned)(n_tiles * moe_work_tiles(a.tokens, a.experts))), st);
+    // persistent: the workgroups take the tiles the offsets give in turn
+    launch_prefill_moe<true, 4>(a, lt, dim3((unsigned)persistent_grid(n_tiles * moe_work_tiles(a.tokens, a.experts))),
+                                st);
   } else {
     const int bm = dense_tile_rows(a.tokens, n_tiles * lt.n);
     const int64_t tiles = n_tiles * ((a.tokens + bm - 1) / bm) * lt.n;

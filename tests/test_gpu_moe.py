@@ -5,7 +5,8 @@ per-expert linears, through the C-ABI.
 Each expert's rows must meet the linear gate (5e-3 of the largest |Y| of that
 expert's rows, plus one output rounding for a 16-bit y).  Cases: skewed
 routing with an empty expert, experts of one row, expert boundaries inside a
-16-row tile and inside a 256-row tile, all rows to one expert, G = 64, and the
+16-row tile and inside a 256-row tile, all rows to one expert, no rows routed
+at all, more tiles than the persistent workgroups, G = 64, and the
 Mixtral-8x7B-shaped expert projection at 2048 tokens x top-2 on sampled rows.
 Rows outside every expert's range must stay untouched, and offsets past the
 row count are clamped.
@@ -123,3 +124,28 @@ def test_moe_full_size_sampled():
     rows = np.unique(np.concatenate([sample_rows(int(offs[-1]), 40), offs[1:-1], offs[1:-1] - 1]))
     rows = rows[(rows >= 0) & (rows < offs[-1])]
     check_moe(Lm, E, offs, x, spec["act"], rows=rows, label="mixtral w1")
+
+
+def test_moe_all_experts_empty():
+    """Offsets that give no expert any row: the launch has no tile, every
+    workgroup leaves at once, and y keeps its contents."""
+    E, I, O, M = 4, 256, 128, 40
+    Lm = synth.make_moe_layer(614, E, I, O)
+    x = synth.make_x(614, 1, M, I, synth.BF16)
+    yh = run_moe(paro.DeviceLayer(Lm), E, [0, 0, 0, 0, 0], x, synth.BF16, synth.F32)
+    assert np.isnan(yh).all()
+
+
+def test_moe_more_tiles_than_workgroups():
+    """More (expert block, column tile) pairs than the 256 persistent
+    workgroups: each workgroup takes several tiles, across expert boundaries,
+    in turn."""
+    E, I, O = 5, 256, 4096
+    Lm = synth.make_moe_layer(615, E, I, O)
+    offs = synth.make_routing(615, E, 1300, 2)
+    x = synth.make_x(615, 1, int(offs[-1]), I, synth.BF16)
+    items = sum(-(-(int(offs[e + 1]) - (int(offs[e]) & ~15)) // 256) for e in range(E) if offs[e + 1] > offs[e])
+    assert items * (O // 128) > 256
+    rows = np.unique(np.concatenate([sample_rows(int(offs[-1]), 64, seed=615), offs[1:-1], offs[1:-1] - 1]))
+    rows = rows[(rows >= 0) & (rows < offs[-1])]
+    check_moe(Lm, E, offs, x, synth.BF16, rows=rows, label="persistent")

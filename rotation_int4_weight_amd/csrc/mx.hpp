@@ -12,14 +12,15 @@
 
 namespace paro {
 
-// E2M1 code of a (already divided by the block scale): the count of rounding
-// boundaries below |a|, ties to the even code (0, 1.0, 1.0, 2.0, 2.0, 4.0,
-// 4.0), saturating at 6; sign in bit 3 unless the magnitude is zero.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-  const float m = fabsf(a);
-  const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
-                     (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
-  return (a < 0.0f && c != 0) ? (c | 8u) : c;
+// E2M1 codes of two values already divided by the block scale, as one byte
+// (a in the low nibble).  The CDNA4 format conversion (divisor 1.0) rounds to
+// the nearest code with ties to the even one and saturates at 6, which is the
+// rule above; a negative value that rounds to zero keeps its sign bit there,
+// so that bit is cleared (zero is stored as +0).
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xffu;
+  const uint32_t nz = ((r & 0x77u) + 0x77u) & 0x88u;  // bit 3 of each nibble whose magnitude is nonzero
+  return r & (nz | 0x77u);
 }
 
 // Biased E8M0 exponent of a block whose largest magnitude is amax (fp32):

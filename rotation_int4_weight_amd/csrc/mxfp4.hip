@@ -77,7 +77,7 @@ mx_quant_kernel(const void *__restrict__ src, int64_t rows, int64_t I, const int
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // the 16 lanes of a block
     const int biased = mx_block_exponent(amax);
-    const uint32_t byte = e2m1_code(mx_scaled(v0, biased)) | (e2m1_code(mx_scaled(v1, biased)) << 4);
+    const uint32_t byte = e2m1_pair(mx_scaled(v0, biased), mx_scaled(v1, biased));
     codes[(r0 + m) * (I / 2) + g * kPairs + lane] = (uint8_t)byte;
     if ((lane & 15) == 0) scales[(r0 + m) * (I / 32) + g * 4 + (lane >> 4)] = (uint8_t)biased;
   }

@@ -345,7 +345,8 @@ rot_apply_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xt, int6
           const int biased = mx_block_exponent(am);
           uint32_t word = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) word |= e2m1_code(mx_scaled(v[e], biased)) << (4 * e);
+          for (int e = 0; e < 8; e += 2)
+            word |= e2m1_pair(mx_scaled(v[e], biased), mx_scaled(v[e + 1], biased)) << (4 * e);
           if (tok < tokens) {
             *reinterpret_cast<uint32_t *>(mx_codes + tok * (I / 2) + g * (kG / 2) + 16 * b + (fk >> 1)) = word;
             if (fk == 0) mx_scales[tok * (I / 32) + g * 4 + b] = (uint8_t)biased;

@@ -464,8 +464,18 @@ def bench_mxfp4(args, paro, synth, np, torch, dev):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e3 / n
 
-    us = timed(lambda i: paro.paro_mxfp4_linear(D, wcs[i % nsets], wss[i % nsets], xd, y, work, stream=stream),
-               args.steps)
+    # The layer's dense rotation R' is built once (paro_rotation_matrix), as
+    # for the W4A16 prefill bench; --rebuild-rotation builds it in every call.
+    if args.rebuild_rotation:
+        us = timed(lambda i: paro.paro_mxfp4_linear(D, wcs[i % nsets], wss[i % nsets], xd, y, work, stream=stream),
+                   args.steps)
+    else:
+        hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device=dev)
+        paro.paro_rotation_matrix(D, dt, hl, stream=stream)
+        pwork = torch.empty(max(paro.paro_mxfp4_linear_prepared_workspace_bytes(D, M), 16), dtype=torch.uint8,
+                            device=dev)
+        us = timed(lambda i: paro.paro_mxfp4_linear_prepared(D, hl, wcs[i % nsets], wss[i % nsets], xd, y, pwork,
+                                                             stream=stream), args.steps)
     g_us = None
     if not args.no_kernel_timing:
         g_us = timed(lambda i: paro.paro_mxfp4_gemm(ac, as_, wcs[i % nsets], wss[i % nsets], y, bias, stream=stream),
@@ -495,7 +505,10 @@ def bench_mxfp4(args, paro, synth, np, torch, dev):
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
         "config": {"workload": f"{spec['name']}-mxfp4{gsuffix(args)}", "tokens": M, "layer": [lname, I, O],
-                   "group_size": args.group, "krot": host.krot, "weight_sets": nsets, "parallelism": "single-gpu"},
+                   "group_size": args.group, "krot": host.krot, "weight_sets": nsets,
+                   "rotation_matrix": ("built in every call" if args.rebuild_rotation
+                                       else "built once (paro_rotation_matrix), applied every call"),
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / FP4_PEAK_TFLOPS, 4),
                      "traffic": load_traffic(f"mxfp4-{args.workload}{gsuffix(args)}", kernel_source_hash("mxfp4"))
@@ -570,7 +583,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel timing loop")
     ap.add_argument("--rebuild-rotation", action="store_true",
-                    help="prefill: rebuild each layer's dense rotation in every call (paro_w4a16_linear) "
+                    help="prefill and --op mxfp4: rebuild each layer's dense rotation in every call (paro_w4a16_linear, "
+                         "paro_mxfp4_linear) "
                          "instead of building it once per layer (paro_w4a16_linear_prepared)")
     ap.add_argument("--no-group", action="store_true",
                     help="prefill: run every layer with its own calls instead of running the layers that read "

@@ -476,6 +476,20 @@ int paro_mxfp4_linear(const paro_w4_layer *layer, const uint8_t *w_codes, const 
                       paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
                       size_t workspace_bytes, void *stream);
 size_t paro_mxfp4_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
+/* The W4A4 MXFP4 linear with the layer's dense rotation prebuilt: hl from
+ * paro_rotation_matrix for this layer and x_dt (I * 512 bytes, 16-byte
+ * aligned, caller-owned, not written), as a model builds it once at load
+ * time (it depends on the layer alone).  Results equal paro_mxfp4_linear's
+ * bit for bit.  workspace: paro_mxfp4_linear_prepared_workspace_bytes(layer,
+ * tokens) bytes (the activation codes and scales; no room for the rotation
+ * matrix), 16-byte aligned, not overlapping x, y or hl.  Errors as
+ * paro_mxfp4_linear, plus PARO_ERR_NULL for hl, PARO_ERR_ALIGN for its
+ * alignment and PARO_ERR_SHAPE for its overlaps.  ("ParoQuant" blog, Bits
+ * and formats: the MXFP4 variant of the W4A4 extension.) */
+int paro_mxfp4_linear_prepared(const paro_w4_layer *layer, const void *hl, const uint8_t *w_codes,
+                               const uint8_t *w_scales, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                               paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream);
+size_t paro_mxfp4_linear_prepared_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /* Bytes of workspace the linear needs for this shape and path (0 allowed). */
 size_t paro_w4a16_linear_workspace_bytes(const paro_w4_layer *layer, int64_t tokens,

@@ -30,6 +30,7 @@ EXPORTS = ("paro_scale_rotate", "paro_w4_unpack_dequant", "paro_w4a16_linear",
            "paro_w4a16_moe_linear_workspace_bytes", "paro_mxfp4_quantize_weight",
            "paro_mxfp4_quantize_activations", "paro_mxfp4_gemm", "paro_mxfp4_linear",
            "paro_mxfp4_linear_workspace_bytes", "paro_mxfp4_activation_workspace_bytes",
+           "paro_mxfp4_linear_prepared", "paro_mxfp4_linear_prepared_workspace_bytes",
            "paro_scale_rotate_backward_workspace_bytes",
            "paro_tiled_bytes", "paro_rotation_matrix_bytes", "paro_rotation_matrix",
            "paro_scale_rotate_tiled", "paro_w4a16_linear_tiled",
@@ -93,6 +94,9 @@ def load(path: str | None = None):
     lib.paro_mxfp4_linear.argtypes = [P, P, P, P, I32, I64, P, I32, P, SZ, P]
     lib.paro_mxfp4_linear_workspace_bytes.argtypes = [P, I64]
     lib.paro_mxfp4_linear_workspace_bytes.restype = SZ
+    lib.paro_mxfp4_linear_prepared.argtypes = [P, P, P, P, P, I32, I64, P, I32, P, SZ, P]
+    lib.paro_mxfp4_linear_prepared_workspace_bytes.argtypes = [P, I64]
+    lib.paro_mxfp4_linear_prepared_workspace_bytes.restype = SZ
     lib.paro_scale_rotate_backward.argtypes = [P, P, I32, P, I32, I64, P, I32, P, P, P, SZ, P]
     lib.paro_scale_rotate_backward_workspace_bytes.argtypes = [P, I64]
     lib.paro_scale_rotate_backward_workspace_bytes.restype = SZ
@@ -347,6 +351,18 @@ def paro_mxfp4_linear(layer: DeviceLayer, w_codes, w_scales, x, y, workspace, st
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().paro_mxfp4_linear(layer.ref, _ptr(w_codes), _ptr(w_scales), _ptr(x), _dt(x), x.shape[0], _ptr(y),
                                     _dt(y), _ptr(workspace), ws_bytes, _stream_handle(stream)), "paro_mxfp4_linear")
+
+
+def paro_mxfp4_linear_prepared_workspace_bytes(layer: DeviceLayer, tokens: int) -> int:
+    return int(load().paro_mxfp4_linear_prepared_workspace_bytes(layer.ref, tokens))
+
+
+def paro_mxfp4_linear_prepared(layer: DeviceLayer, hl, w_codes, w_scales, x, y, workspace, stream=None) -> None:
+    """The W4A4 MXFP4 linear with the layer's dense rotation hl prebuilt by paro_rotation_matrix."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paro_mxfp4_linear_prepared(layer.ref, _ptr(hl), _ptr(w_codes), _ptr(w_scales), _ptr(x), _dt(x),
+                                             x.shape[0], _ptr(y), _dt(y), _ptr(workspace), ws_bytes,
+                                             _stream_handle(stream)), "paro_mxfp4_linear_prepared")
 
 
 def paro_w4a16_moe_linear_workspace_bytes(layer: DeviceLayer, tokens: int, x_dt: int = F16) -> int:

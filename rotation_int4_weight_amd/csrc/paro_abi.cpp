@@ -531,9 +531,15 @@ size_t paro_mxfp4_activation_workspace_bytes(const paro_w4_layer *L) {
   return align_up(paro::rot_mat_bytes(L->in_features), 256);
 }
 
-int paro_mxfp4_quantize_activations(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens,
-                                    uint8_t *codes, uint8_t *scales, void *workspace, size_t workspace_bytes,
-                                    void *stream) {
+}  // extern "C"
+
+namespace {
+
+// hl_pre: a caller-built rotation matrix (paro_rotation_matrix), or NULL to
+// build it into the workspace.
+int mx_quantize_activations_impl(const paro_w4_layer *L, const void *hl_pre, const void *x, paro_dtype x_dt,
+                                 int64_t tokens, uint8_t *codes, uint8_t *scales, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
   int rc = check_gpu_shape(L);
   if (rc) return rc;
   const int64_t I = L->in_features;
@@ -542,26 +548,83 @@ int paro_mxfp4_quantize_activations(const paro_w4_layer *L, const void *x, paro_
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
   if (tokens == 0) return ok();
   if (!x || !codes || !scales) return fail(PARO_ERR_NULL, "x, codes and scales are required");
-  rc = check_rotation_tensors(L);
+  size_t need = 0;
+  if (!hl_pre) {
+    rc = check_rotation_tensors(L);
+    if (rc) return rc;
+    need = paro_mxfp4_activation_workspace_bytes(L);
+    if (!workspace || workspace_bytes < need)
+      return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                  need);
+  }
+  const void *mat = hl_pre ? hl_pre : workspace;  // where the rotation matrix is read
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(mat, 16))
+    return fail(PARO_ERR_ALIGN, "x, codes and workspace (or hl) 16-byte, scales 4-byte aligned");
+  const size_t xb = (size_t)tokens * I * 2, cb = (size_t)tokens * I / 2, sb = (size_t)tokens * I / 32;
+  const size_t mb = hl_pre ? paro::rot_mat_bytes(I) : need;
+  if (overlap(codes, cb, x, xb) || overlap(scales, sb, x, xb) || overlap(codes, cb, scales, sb) ||
+      overlap(mat, mb, codes, cb) || overlap(mat, mb, scales, sb) || (!hl_pre && overlap(mat, mb, x, xb)))
+    return fail(PARO_ERR_SHAPE, "x, codes, scales and the workspace (or hl) must not overlap");
+  hipStream_t st = (hipStream_t)stream;
+  if (!hl_pre) {
+    hipError_t e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot,
+                                          (int)group_of(L), (uint16_t *)workspace, st);
+    if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
+  }
+  hipError_t e = paro::launch_rot_apply_mx((const uint16_t *)x, (int)x_dt, tokens, I, (const uint16_t *)mat, codes,
+                                           scales, st);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 activation launch");
+  return ok();
+}
+
+size_t mx_linear_workspace(const paro_w4_layer *L, int64_t tokens, bool prepared) {
+  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
+  return mx_codes_region(tokens, L->in_features) + align_up((size_t)tokens * L->in_features / 32, 256) +
+         (prepared ? 0 : paro_mxfp4_activation_workspace_bytes(L));
+}
+
+int mx_linear_impl(const paro_w4_layer *L, const void *hl_pre, const uint8_t *w_codes, const uint8_t *w_scales,
+                   const void *x, paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  int rc = check_gpu_shape(L);
+  if (!rc) rc = check_tokens(tokens);
   if (rc) return rc;
-  const size_t need = paro_mxfp4_activation_workspace_bytes(L);
+  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
+  const int64_t I = L->in_features, O = L->out_features;
+  if (tokens == 0) return ok();
+  const size_t need = mx_linear_workspace(L, tokens, hl_pre != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 need);
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(workspace, 16))
-    return fail(PARO_ERR_ALIGN, "x, codes and workspace 16-byte, scales 4-byte aligned");
-  const size_t xb = (size_t)tokens * I * 2, cb = (size_t)tokens * I / 2, sb = (size_t)tokens * I / 32;
-  if (overlap(codes, cb, x, xb) || overlap(scales, sb, x, xb) || overlap(codes, cb, scales, sb) ||
-      overlap(workspace, need, x, xb) || overlap(workspace, need, codes, cb) || overlap(workspace, need, scales, sb))
-    return fail(PARO_ERR_SHAPE, "x, codes, scales and the workspace must not overlap");
-  hipStream_t st = (hipStream_t)stream;
-  uint16_t *hl = (uint16_t *)workspace;
-  hipError_t e = paro::launch_rot_build((int)x_dt, I, L->pairs, L->theta, L->channel_scales, L->krot,
-                                        (int)group_of(L), hl, st);
-  if (e != hipSuccess) return hip_fail(e, "rotation matrix launch");
-  e = paro::launch_rot_apply_mx((const uint16_t *)x, (int)x_dt, tokens, I, hl, codes, scales, st);
-  if (e != hipSuccess) return hip_fail(e, "mxfp4 activation launch");
+  if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
+  uint8_t *ac = (uint8_t *)workspace, *as = ac + mx_codes_region(tokens, I);
+  uint8_t *hl = as + align_up((size_t)tokens * I / 32, 256);
+  rc = mx_gemm_checks(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, y_dt);
+  if (rc) return rc;
+  const size_t yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2), xb = (size_t)tokens * I * 2;
+  if (overlap(y, yb, x, xb) || overlap(workspace, need, x, xb) || overlap(workspace, need, y, yb))
+    return fail(PARO_ERR_SHAPE, "x, y and the workspace must not overlap");
+  if (hl_pre && (overlap(hl_pre, paro::rot_mat_bytes(I), workspace, need) ||
+                 overlap(hl_pre, paro::rot_mat_bytes(I), y, yb)))
+    return fail(PARO_ERR_SHAPE, "hl must not overlap y or the workspace");
+  rc = mx_quantize_activations_impl(L, hl_pre, x, x_dt, tokens, ac, as, hl_pre ? nullptr : hl,
+                                    hl_pre ? 0 : paro_mxfp4_activation_workspace_bytes(L), stream);
+  if (rc) return rc;
+  hipError_t e = paro::launch_mx_gemm(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, (int)y_dt,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4 GEMM launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paro_mxfp4_quantize_activations(const paro_w4_layer *L, const void *x, paro_dtype x_dt, int64_t tokens,
+                                    uint8_t *codes, uint8_t *scales, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  return mx_quantize_activations_impl(L, nullptr, x, x_dt, tokens, codes, scales, workspace, workspace_bytes,
+                                      stream);
 }
 
 int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tokens, const uint8_t *w_codes,
@@ -577,40 +640,24 @@ int paro_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t tok
 }
 
 size_t paro_mxfp4_linear_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
-  if (!L || tokens <= 0 || check_gpu_shape(L)) return 0;
-  return mx_codes_region(tokens, L->in_features) + align_up((size_t)tokens * L->in_features / 32, 256) +
-         paro_mxfp4_activation_workspace_bytes(L);
+  return mx_linear_workspace(L, tokens, false);
 }
 
 int paro_mxfp4_linear(const paro_w4_layer *L, const uint8_t *w_codes, const uint8_t *w_scales, const void *x,
                       paro_dtype x_dt, int64_t tokens, void *y, paro_dtype y_dt, void *workspace,
                       size_t workspace_bytes, void *stream) {
-  int rc = check_gpu_shape(L);
-  if (!rc) rc = check_tokens(tokens);
-  if (rc) return rc;
-  if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
-  const int64_t I = L->in_features, O = L->out_features;
-  if (tokens == 0) return ok();
-  const size_t need = paro_mxfp4_linear_workspace_bytes(L, tokens);
-  if (!workspace || workspace_bytes < need)
-    return fail(PARO_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                need);
-  if (!aligned(workspace, 16)) return fail(PARO_ERR_ALIGN, "workspace must be 16-byte aligned");
-  uint8_t *ac = (uint8_t *)workspace, *as = ac + mx_codes_region(tokens, I);
-  uint8_t *hl = as + align_up((size_t)tokens * I / 32, 256);
-  rc = mx_gemm_checks(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, y_dt);
-  if (rc) return rc;
-  if (overlap(y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2), x, (size_t)tokens * I * 2) ||
-      overlap(workspace, need, x, (size_t)tokens * I * 2) ||
-      overlap(workspace, need, y, (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2)))
-    return fail(PARO_ERR_SHAPE, "x, y and the workspace must not overlap");
-  rc = paro_mxfp4_quantize_activations(L, x, x_dt, tokens, ac, as, hl, paro_mxfp4_activation_workspace_bytes(L),
-                                       stream);
-  if (rc) return rc;
-  hipError_t e = paro::launch_mx_gemm(ac, as, tokens, w_codes, w_scales, O, I, L->bias, y, (int)y_dt,
-                                      (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "mxfp4 GEMM launch");
-  return ok();
+  return mx_linear_impl(L, nullptr, w_codes, w_scales, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+size_t paro_mxfp4_linear_prepared_workspace_bytes(const paro_w4_layer *L, int64_t tokens) {
+  return mx_linear_workspace(L, tokens, true);
+}
+
+int paro_mxfp4_linear_prepared(const paro_w4_layer *L, const void *hl, const uint8_t *w_codes,
+                               const uint8_t *w_scales, const void *x, paro_dtype x_dt, int64_t tokens, void *y,
+                               paro_dtype y_dt, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!hl) return fail(PARO_ERR_NULL, "hl is required");
+  return mx_linear_impl(L, hl, w_codes, w_scales, x, x_dt, tokens, y, y_dt, workspace, workspace_bytes, stream);
 }
 
 paro_path paro_w4a16_linear_choose_path(const paro_w4_layer *L, int64_t tokens) {

@@ -351,6 +351,15 @@ def test_mxfp4_argument_checks():
     assert ln(wsb=need - 1) == 7
     assert ln(ws=0) == 7
     assert ln(xdt=2) == 3
+    pneed = lib.paro_mxfp4_linear_prepared_workspace_bytes(ctypes.byref(L), 4)
+    assert pneed == 512 + 256                       # no room for R': the caller built it
+    lp = lambda hl=FAKE * 7, wsb=pneed, ws=FAKE * 6: lib.paro_mxfp4_linear_prepared(
+        ctypes.byref(L), hl, FAKE * 3, FAKE * 4, FAKE, 0, 4, FAKE * 5, 0, ws, wsb, None)
+    assert lp(hl=0) == 1
+    assert lp(wsb=pneed - 1) == 7
+    assert lp(hl=FAKE * 7 + 8) == 4                 # hl 16-byte aligned
+    assert lp(hl=FAKE * 6 + 256) == 2               # hl overlaps the workspace
+    assert lp(hl=FAKE * 5) == 2                     # hl overlaps y
 
 
 @needs_no_gpu

@@ -182,6 +182,31 @@ def test_linear_is_quantize_then_gemm(I, O, M, dt):
     check_gemm(ac.cpu().numpy(), as_.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), L.bias, synth.F32)
 
 
+@pytest.mark.parametrize("I,O,M,dt", [(512, 264, 70, synth.BF16), (256, 64, 3, synth.F16)])
+def test_prepared_linear_equals_linear(I, O, M, dt):
+    """The linear over a caller-built rotation matrix gives the same bits as
+    the one that builds it in its workspace, on a workspace that holds no
+    rotation matrix."""
+    L = synth.make_layer(704, 0, I, O)
+    x = synth.make_x(704, 1, M, I, dt)
+    w = synth.make_w(704, 0, O, I, synth.F32)
+    D = paro.DeviceLayer(L)
+    wc, ws = gpu_quant_weight(D, w, synth.F32, O, I)
+    xd = x_to_device(x, dt)
+    y = torch.empty((M, O), dtype=torch_dtype(dt), device="cuda")
+    work = torch.empty(paro.paro_mxfp4_linear_workspace_bytes(D, M), dtype=torch.uint8, device="cuda")
+    paro.paro_mxfp4_linear(D, wc, ws, xd, y, work)
+    hl = torch.empty((paro.paro_rotation_matrix_bytes(D) // 2,), dtype=torch.int16, device="cuda")
+    paro.paro_rotation_matrix(D, dt, hl)
+    need = paro.paro_mxfp4_linear_prepared_workspace_bytes(D, M)
+    assert need < paro.paro_mxfp4_linear_workspace_bytes(D, M)
+    y2 = torch.empty_like(y)
+    work2 = torch.empty(need, dtype=torch.uint8, device="cuda")
+    paro.paro_mxfp4_linear_prepared(D, hl, wc, ws, xd, y2, work2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 def test_full_size_gemm_sampled_rows():
     """The down_proj shape at 2048 tokens: every output of 24 sampled rows."""
     M, K, O = 2048, 14336, 4096

@@ -33,8 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# layer pairs that read the same input in the model (one grouped call each)
-SHARED_INPUT = (("k_proj", "v_proj"), ("gate_proj", "up_proj"))
+# layer groups that read the same input in the model (one grouped call each)
+SHARED_INPUT = (("q_proj", "k_proj", "v_proj"), ("gate_proj", "up_proj"))
 METRIC = "ParoQuant linear: decode weight GB/s, prefill TFLOP/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, published
@@ -588,8 +588,8 @@ def main():
                          "instead of building it once per layer (paro_w4a16_linear_prepared)")
     ap.add_argument("--no-group", action="store_true",
                     help="prefill: run every layer with its own calls instead of running the layers that read "
-                         "the same input (k_proj + v_proj, gate_proj + up_proj) through "
-                         "paro_w4a16_linear_prepared_multi, one GEMM launch per pair")
+                         "the same input (q_proj + k_proj + v_proj, gate_proj + up_proj) through "
+                         "paro_w4a16_linear_prepared_multi, one GEMM launch per group")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured ceiling (device copy for decode, library dense GEMM for prefill)")
     ap.add_argument("--op", choices=("linear", "quantize", "rotate", "rotate_backward", "moe", "mxfp4"),
@@ -692,17 +692,19 @@ def main():
                 hl_row.append(hl)
             hls.append(hl_row)
 
-    # Layers that read the same input (the key and value projections, the
-    # gate and up projections) run together, one rotation each and one GEMM
-    # launch per pair, on the pair's first input.
+    # Layers that read the same input (the query, key and value projections,
+    # the gate and up projections) run together, one rotation each and one
+    # GEMM launch per group, on the group's first input.
     names = [n for n, _, _, _, _ in layers]
     groups, li = [], 0
     while li < len(layers):
         grp = [li]
-        if prepared and not args.no_group and li + 1 < len(layers):
-            for a, b in SHARED_INPUT:
-                if names[li] == a and names[li + 1] == b and layers[li][1:3] == layers[li + 1][1:3]:
-                    grp = [li, li + 1]
+        if prepared and not args.no_group:
+            for names_g in SHARED_INPUT:
+                k = len(names_g)
+                if (tuple(names[li:li + k]) == names_g and
+                        all(layers[li + j][1] == layers[li][1] for j in range(k))):  # same in_features
+                    grp = list(range(li, li + k))
         groups.append(grp)
         li += len(grp)
     for grp in groups:

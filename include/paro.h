@@ -200,19 +200,19 @@ int paro_w4a16_linear_prepared(const paro_w4_layer *layer, const void *hl, const
 size_t paro_w4a16_linear_prepared_workspace_bytes(const paro_w4_layer *layer, int64_t tokens);
 
 /*
- * Several layers of one shape that read the same input, each with its own
- * rotation, packed weight, bias and output: the key and value projections
- * of an attention block, the gate and up projections of an MLP.  For
+ * Several layers that read the same input, each with its own rotation,
+ * packed weight, bias and output: the query, key and value projections of
+ * an attention block, the gate and up projections of an MLP.  For
  * i < n_layers:
  *   y[i] = paro_w4a16_linear_prepared(&layers[i], hl[i], x, ...)
  * (page "ParoQuant", Concepts / Activation and weight transforms: every
  * layer is its own rotated linear; nothing is shared but the input x).
  *   layers   : n_layers (1..PARO_MULTI_MAX_LAYERS) host descriptors; their
- *              in_features, out_features, group_size (32, 64 or 128) and
- *              krot must be equal (PARO_ERR_SHAPE otherwise).
+ *              in_features, group_size (32, 64 or 128) and krot must be
+ *              equal (PARO_ERR_SHAPE otherwise); out_features may differ.
  *   hl       : n_layers rotation matrices from paro_rotation_matrix (as
  *              for paro_w4a16_linear_prepared), caller-owned, not written.
- *   y        : n_layers outputs [tokens][out_features] in y_dt, 16-byte
+ *   y        : n_layers outputs [tokens][their out_features] in y_dt, 16-byte
  *              aligned, not overlapping x, each other or the workspace.
  * Many tokens (the PREFILL path): each layer's input rotation runs into its
  * own tiled X_r, then ONE GEMM launch covers the output tiles of all the
@@ -325,10 +325,11 @@ int paro_w4a16_linear_tiled(const paro_w4_layer *layer, const void *x_t, paro_dt
                             int64_t tokens, void *y, paro_dtype y_dt, void *stream);
 
 /*
- * paro_w4a16_linear_tiled for several layers of one shape (in_features,
- * out_features and group size equal; PARO_ERR_SHAPE otherwise) in ONE GEMM
+ * paro_w4a16_linear_tiled for several layers (in_features and group size
+ * equal, PARO_ERR_SHAPE otherwise; out_features may differ) in ONE GEMM
  * launch over the union of their output tiles: layer i reads x_t[i] and
- * writes y[i] (1 <= n_layers <= PARO_MULTI_MAX_LAYERS; outputs must overlap
+ * writes y[i] [tokens][its out_features] (1 <= n_layers <=
+ * PARO_MULTI_MAX_LAYERS; outputs must overlap
  * no x_t and no other output).  Each y[i] equals that layer's
  * paro_w4a16_linear_tiled result bit for bit.  The GEMM of
  * paro_w4a16_linear_prepared_multi's PREFILL path.

@@ -117,6 +117,8 @@ struct LayerTable {
   const uint16_t *bias[kMaxMultiLayers];  // entries may be null
   const uint16_t *xt[kMaxMultiLayers];
   void *y[kMaxMultiLayers];
+  int64_t o[kMaxMultiLayers];         // out_features of each layer (dense launches)
+  int32_t tile0[kMaxMultiLayers + 1];  // first output tile of each layer; tile0[n]: all tiles (set by the launcher)
 };
 hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt, hipStream_t st);
 // Upper bound on the (expert, 256-row tile) work items of a MoE call.

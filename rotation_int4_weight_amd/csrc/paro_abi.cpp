@@ -323,14 +323,15 @@ int paro_w4a16_linear_tiled_multi(const paro_w4_layer *layers, int n_layers, con
   for (int i = 0; i < n_layers; ++i) {
     const paro_w4_layer *L = &layers[i];
     if ((rc = check_gpu_shape(L, true))) return rc;
-    if (L->in_features != L0->in_features || L->out_features != L0->out_features || group_of(L) != group_of(L0))
-      return fail(PARO_ERR_SHAPE, "layer %d: in/out features and group size must equal layer 0's", i);
+    if (L->in_features != L0->in_features || group_of(L) != group_of(L0))
+      return fail(PARO_ERR_SHAPE, "layer %d: in_features and group size must equal layer 0's", i);
   }
   if ((rc = check_tokens(tokens))) return rc;
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
   if (y_dt != x_dt && y_dt != PARO_F32) return fail(PARO_ERR_DTYPE, "y dtype %d must equal x dtype or F32", (int)y_dt);
   if (tokens == 0) return ok();
-  const size_t tb = paro_tiled_bytes(L0, tokens), yb = (size_t)tokens * L0->out_features * (y_dt == PARO_F32 ? 4 : 2);
+  const size_t tb = paro_tiled_bytes(L0, tokens);
+  auto yb = [&](int i) { return (size_t)tokens * layers[i].out_features * (y_dt == PARO_F32 ? 4 : 2); };
   for (int i = 0; i < n_layers; ++i) {
     if (!x_t[i] || !y[i]) return fail(PARO_ERR_NULL, "layer %d: x_t and y are required", i);
     if ((rc = check_weight_tensors(&layers[i]))) return rc;
@@ -339,8 +340,9 @@ int paro_w4a16_linear_tiled_multi(const paro_w4_layer *layers, int n_layers, con
   }
   for (int i = 0; i < n_layers; ++i)
     for (int j = 0; j < n_layers; ++j) {
-      if (overlap(y[i], yb, x_t[j], tb)) return fail(PARO_ERR_SHAPE, "the output of layer %d overlaps x_t of %d", i, j);
-      if (j < i && overlap(y[i], yb, y[j], yb)) return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
+      if (overlap(y[i], yb(i), x_t[j], tb)) return fail(PARO_ERR_SHAPE, "the output of layer %d overlaps x_t of %d", i, j);
+      if (j < i && overlap(y[i], yb(i), y[j], yb(j)))
+        return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
     }
   paro::LinearArgs a = linear_args(L0, tokens, x_t[0], x_dt, y[0], y_dt);
   paro::LayerTable lt{};
@@ -352,6 +354,7 @@ int paro_w4a16_linear_tiled_multi(const paro_w4_layer *layers, int n_layers, con
     lt.bias[i] = layers[i].bias;
     lt.xt[i] = (const uint16_t *)x_t[i];
     lt.y[i] = y[i];
+    lt.o[i] = layers[i].out_features;
   }
   const hipError_t e = paro::launch_prefill_gemm_multi(a, lt, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
@@ -856,12 +859,16 @@ size_t paro_w4a16_linear_prepared_multi_workspace_bytes(const paro_w4_layer *lay
                                                         int64_t tokens) {
   if (!layers || n_layers < 1 || n_layers > paro::kMaxMultiLayers || tokens <= 0) return 0;
   const paro_w4_layer *L = &layers[0];
-  if (check_gpu_shape(L)) return 0;
+  for (int i = 0; i < n_layers; ++i)
+    if (check_gpu_shape(&layers[i])) return 0;
   const paro_path path = auto_path(tokens);
-  const size_t one = path == PARO_PATH_PREFILL ? kCounterBytes + xr_region(L, tokens, path) : workspace_for(L, tokens, path);
-  // prefill: one tiled X_r per layer (the layers run in one GEMM launch);
-  // decode: the layers run one after another on one workspace
-  return path == PARO_PATH_PREFILL ? kCounterBytes + (size_t)n_layers * xr_region(L, tokens, path) : one;
+  // prefill: one tiled X_r per layer (the layers run in one GEMM launch; its
+  // size depends on in_features alone); decode: the layers run one after
+  // another on one workspace, the largest any of them needs
+  if (path == PARO_PATH_PREFILL) return kCounterBytes + (size_t)n_layers * xr_region(L, tokens, path);
+  size_t most = 0;
+  for (int i = 0; i < n_layers; ++i) most = std::max(most, workspace_for(&layers[i], tokens, path));
+  return most;
 }
 
 static_assert(PARO_MULTI_MAX_LAYERS == paro::kMaxMultiLayers, "the header and the kernels agree on the layer count");
@@ -879,9 +886,8 @@ int paro_w4a16_linear_prepared_multi(const paro_w4_layer *layers, int n_layers, 
   for (int i = 0; i < n_layers; ++i) {
     const paro_w4_layer *L = &layers[i];
     if ((rc = check_gpu_shape(L))) return rc;
-    if (L->in_features != L0->in_features || L->out_features != L0->out_features ||
-        group_of(L) != group_of(L0) || L->krot != L0->krot)
-      return fail(PARO_ERR_SHAPE, "layer %d: in/out features, group size and krot must equal layer 0's", i);
+    if (L->in_features != L0->in_features || group_of(L) != group_of(L0) || L->krot != L0->krot)
+      return fail(PARO_ERR_SHAPE, "layer %d: in_features, group size and krot must equal layer 0's", i);
     if (!hl[i] || !y[i]) return fail(PARO_ERR_NULL, "layer %d: hl and y are required", i);
   }
   if (!act_dtype(x_dt)) return fail(PARO_ERR_DTYPE, "x dtype %d must be F16 or BF16", (int)x_dt);
@@ -898,8 +904,9 @@ int paro_w4a16_linear_prepared_multi(const paro_w4_layer *layers, int n_layers, 
     return ok();
   }
   if (!x) return fail(PARO_ERR_NULL, "x is required");
-  const int64_t I = L0->in_features, O = L0->out_features;
-  const size_t xb = (size_t)tokens * I * 2, yb = (size_t)tokens * O * (y_dt == PARO_F32 ? 4 : 2);
+  const int64_t I = L0->in_features;
+  const size_t xb = (size_t)tokens * I * 2;
+  auto yb = [&](int i) { return (size_t)tokens * layers[i].out_features * (y_dt == PARO_F32 ? 4 : 2); };
   const size_t hb = paro::rot_mat_bytes(I), xrb = xr_region(L0, tokens, path);
   const size_t need = kCounterBytes + (size_t)n_layers * xrb;
   if (!aligned(x, 16)) return fail(PARO_ERR_ALIGN, "x must be 16-byte aligned");
@@ -912,11 +919,11 @@ int paro_w4a16_linear_prepared_multi(const paro_w4_layer *layers, int n_layers, 
     if ((rc = check_rotation_tensors(L)) || (rc = check_weight_tensors(L))) return rc;
     if (!aligned(y[i], 16) || !aligned(hl[i], 16))
       return fail(PARO_ERR_ALIGN, "layer %d: y and hl must be 16-byte aligned", i);
-    if (overlap(y[i], yb, x, xb)) return fail(PARO_ERR_SHAPE, "layer %d: y overlaps x", i);
-    if (overlap(workspace, need, y[i], yb) || overlap(workspace, need, hl[i], hb))
+    if (overlap(y[i], yb(i), x, xb)) return fail(PARO_ERR_SHAPE, "layer %d: y overlaps x", i);
+    if (overlap(workspace, need, y[i], yb(i)) || overlap(workspace, need, hl[i], hb))
       return fail(PARO_ERR_SHAPE, "layer %d: the workspace overlaps y or hl", i);
     for (int j = 0; j < i; ++j)
-      if (overlap(y[i], yb, y[j], yb)) return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
+      if (overlap(y[i], yb(i), y[j], yb(j))) return fail(PARO_ERR_SHAPE, "the outputs of layers %d and %d overlap", j, i);
   }
   hipStream_t st = (hipStream_t)stream;
   const void *xts[paro::kMaxMultiLayers];

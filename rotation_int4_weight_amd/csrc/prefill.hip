@@ -225,8 +225,10 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   // segment (a scalar load at the entry's offset), not held in registers
   const LayerTable *ltp = &lt;
   PREFILL_MARK(0);
-  const int64_t I = a.I, O = a.O, W = O / 8, M = a.tokens;
-  const int n_tiles = (int)((O + kBN - 1) / kBN);
+  // dense layers of a table may differ in out_features (each tile carries
+  // its layer's); a MoE launch has one
+  const int64_t I = a.I, M = a.tokens;
+  const int moe_n_tiles = (int)((a.O + kBN - 1) / kBN);
   // MoE: the experts' 256-row work items, counted from the offsets (each
   // expert's rows, clamped into [0, M] and made nondecreasing, start at the
   // 16-row tile that holds its first row)
@@ -243,7 +245,9 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   };
   const int m_tiles = MOE ? moe_items() : (int)((M + BM - 1) / BM);
   // dense: the layers of the table one after another in the tile order
-  const int per_layer = n_tiles * m_tiles, total = MOE ? per_layer : per_layer * lt.n;
+  // (layer l's tiles start at tile0[l] = m_tiles times the column tiles of
+  // the layers before it)
+  const int total = MOE ? moe_n_tiles * m_tiles : ltp->tile0[lt.n];
   // tiles of this workgroup: b, b + G, ... (MoE: the grid is sized on the
   // host for the most work items the offsets can give, so a workgroup may
   // have none)
@@ -259,6 +263,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   // them stays in scalar registers).
   struct Tile {
     int64_t n0, mb, row_lo, row_hi;
+    int64_t O, W;  // the layer's out_features and packed words per row
     const int32_t *qweight, *qzeros;
     const uint16_t *scales, *bias;
     int layer;  // entry of the layer table (MoE: 0)
@@ -270,15 +275,22 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     // share an XCD and its L2.  Workgroup b's iteration it stands for launch
     // id b + it G, which lies on b's XCD when G is a multiple of 8.
     int lwg = xcd_local_order((int)blockIdx.x + it * (int)gridDim.x, total);
+    int n_tiles = moe_n_tiles;
     if constexpr (MOE) {
       t.layer = 0;
+      t.O = a.O;
       t.qweight = a.qweight;
       t.qzeros = a.qzeros;
       t.scales = a.scales;
       t.bias = a.bias;
     } else {
-      t.layer = __builtin_amdgcn_readfirstlane(lwg / per_layer);
-      lwg -= t.layer * per_layer;
+      int l = 0;
+      for (int k = 1; k < lt.n; ++k)
+        if (lwg >= ltp->tile0[k]) l = k;
+      t.layer = __builtin_amdgcn_readfirstlane(l);
+      lwg -= ltp->tile0[t.layer];
+      t.O = ltp->o[t.layer];
+      n_tiles = (int)((t.O + kBN - 1) / kBN);
       if (t.layer == 0) {  // entry 0 is also in a (the single-layer launch)
         t.qweight = a.qweight;
         t.qzeros = a.qzeros;
@@ -291,6 +303,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
         t.bias = ltp->bias[t.layer];
       }
     }
+    t.W = t.O / 8;
     // Dense layers: logical tiles go in groups of kGroupM M blocks, the M
     // block fastest, so an XCD's share of consecutive tiles spans kGroupM
     // blocks of rows and 1/kGroupM as many weight columns as a row-major
@@ -332,7 +345,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
       t.mb = (lo & ~(int64_t)15) + j * kBM;
       t.row_lo = lo > t.mb ? lo : t.mb;
       t.row_hi = hi < t.mb + kBM ? hi : t.mb + kBM;
-      const int64_t G = (int64_t)kBK * GK;
+      const int64_t G = (int64_t)kBK * GK, O = a.O, W = O / 8;
       t.qweight += (int64_t)e * I * W;
       t.qzeros += (int64_t)e * (I / G) * W;
       t.scales += (int64_t)e * (I / G) * O;
@@ -375,12 +388,11 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     // ------------------------------ producer ------------------------------
     const int tp = threadIdx.x - 256;
     const int dw = tp & 15, drp = tp >> 4;  // word dw of the tile's 16, rows 2drp, 2drp+1 of a step
-    const uint32_t w_step_bytes = (uint32_t)(kBK * W * 4);
     // this thread's packed word of a tile's column block (tail tile: any
     // in-bounds word)
-    auto word_of = [&](int64_t n0) -> uint32_t {
-      const int64_t dword = n0 / 8 + dw;
-      return (uint32_t)(dword < W ? dword : W - 1);
+    auto word_of = [&](const Tile &t) -> uint32_t {
+      const int64_t dword = t.n0 / 8 + dw;
+      return (uint32_t)(dword < t.W ? dword : t.W - 1);
     };
 
     struct Words {
@@ -389,8 +401,9 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     // packed words of the next step of the sequence (steps in order)
     Cursor cw{0, 0, t0};
     auto load_words = [&](Words &wd) {
-      const uint32_t w_off = (uint32_t)((2 * drp) * W + word_of(cw.t.n0)) * 4u;
-      const __amdgpu_buffer_rsrc_t r = raw_rsrc(cw.t.qweight + (int64_t)cw.pos * kBK * W, w_step_bytes);
+      const int64_t W = cw.t.W;
+      const uint32_t w_off = (uint32_t)((2 * drp) * W + word_of(cw.t)) * 4u;
+      const __amdgpu_buffer_rsrc_t r = raw_rsrc(cw.t.qweight + (int64_t)cw.pos * kBK * W, (uint32_t)(kBK * W * 4));
       wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
       wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
       advance(cw, nsteps);
@@ -402,7 +415,8 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     // scales and zeros of the next group of the sequence (groups in order)
     Cursor cg{0, 0, t0};
     auto load_group = [&](GroupRaw &gr) {
-      const uint32_t dwc = word_of(cg.t.n0);
+      const uint32_t dwc = word_of(cg.t);
+      const int64_t O = cg.t.O, W = cg.t.W;
       const __amdgpu_buffer_rsrc_t rs = raw_rsrc(cg.t.scales + (int64_t)cg.pos * O, (uint32_t)(O * 2));
       gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
       const __amdgpu_buffer_rsrc_t rz = raw_rsrc(cg.t.qzeros + (int64_t)cg.pos * W, (uint32_t)(W * 4));
@@ -614,7 +628,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     int el;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
     uint32_t bw = 0u;
-    if (t.bias && t.n0 + 2 * el < O) bw = *reinterpret_cast<const uint32_t *>(t.bias + t.n0 + 2 * el);
+    if (t.bias && t.n0 + 2 * el < t.O) bw = *reinterpret_cast<const uint32_t *>(t.bias + t.n0 + 2 * el);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kASlots; ++k) cstep(step + k, ab[k], k == 3, tn, k, k < 2);
@@ -648,6 +662,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     auto epilogue = [&](auto ydt) {
       constexpr int YD = decltype(ydt)::value;
       typedef typename std::conditional<YD == kF32, float, uint16_t>::type YT;
+      const int64_t O = t.O;
       YT *ybase = reinterpret_cast<YT *>(t.layer == 0 ? a.y : ltp->y[t.layer]) + (m0 + erow) * O + t.n0 + 8 * eg;
       // Two fp32 sums -> one packed pair, RNE.  For fp16 the conversion is
       // written as asm: the compiler would otherwise fuse it with the bias
@@ -774,16 +789,22 @@ int64_t moe_work_tiles(int64_t tokens, int experts) {
   return (tokens + 15 * (int64_t)experts + kBM - 1) / kBM + experts;
 }
 
-hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt, hipStream_t st) {
-  const int64_t n_tiles = (a.O + kBN - 1) / kBN;
+hipError_t launch_prefill_gemm_multi(const LinearArgs &a, const LayerTable &lt_in, hipStream_t st) {
+  LayerTable lt = lt_in;
   if (a.experts > 0) {
+    const int64_t n_tiles = (a.O + kBN - 1) / kBN;
     // persistent: the workgroups take the tiles the offsets give in turn
     launch_prefill_moe<true, 4>(a, lt, dim3((unsigned)persistent_grid(n_tiles * moe_work_tiles(a.tokens, a.experts))),
                                 st);
   } else {
-    const int bm = dense_tile_rows(a.tokens, n_tiles * lt.n);
-    const int64_t tiles = n_tiles * ((a.tokens + bm - 1) / bm) * lt.n;
-    const dim3 grid((unsigned)persistent_grid(tiles));
+    // the layers' column tiles one after another, each over all M blocks
+    int64_t col_tiles = 0;
+    for (int l = 0; l < lt.n; ++l) col_tiles += (lt.o[l] + kBN - 1) / kBN;
+    const int bm = dense_tile_rows(a.tokens, col_tiles);
+    const int64_t m_tiles = (a.tokens + bm - 1) / bm;
+    lt.tile0[0] = 0;
+    for (int l = 0; l < lt.n; ++l) lt.tile0[l + 1] = lt.tile0[l] + (int32_t)((lt.o[l] + kBN - 1) / kBN * m_tiles);
+    const dim3 grid((unsigned)persistent_grid(lt.tile0[lt.n]));
     if (bm == 128)
       launch_prefill_moe<false, 2>(a, lt, grid, st);
     else
@@ -801,6 +822,7 @@ hipError_t launch_prefill_gemm(const LinearArgs &a, const uint16_t *x, hipStream
   lt.bias[0] = a.bias;
   lt.xt[0] = x;
   lt.y[0] = a.y;
+  lt.o[0] = a.O;
   return launch_prefill_gemm_multi(a, lt, st);
 }
 

@@ -398,7 +398,7 @@ def multi(layers, n=None, hl=(FAKE * 8, FAKE * 9), x=FAKE, xdt=0, tokens=32, y=(
     (dict(y=None), 1),
     (dict(hl=(FAKE * 8, 0)), 1),                       # every layer needs its rotation matrix
     (dict(y=(FAKE * 2, 0)), 1),
-    (dict(L1=dict(O=128)), 2),                         # the layers share one shape
+    (dict(L1=dict(I=384)), 2),                         # the layers share in_features, group size, krot
     (dict(L1=dict(G=64)), 2),
     (dict(L1=dict(krot=4)), 2),
     (dict(L1=dict(G=16)), 5),
@@ -438,6 +438,14 @@ def test_multi_linear_workspace_sizes():
     assert mw(1, 4096) == one(4096)
     assert mw(3, 16) == one(16) and mw(2, 1) == one(1)
     assert mw(0, 4096) == 0 and mw(5, 4096) == 0 and mw(2, 0) == 0
+    # out_features may differ: prefill still one tiled X_r per layer (it
+    # depends on in_features alone); decode the largest single-layer need
+    Lw = fake_layer(I=4096, O=14336)
+    mixed = (_lib.ParoLayerC * 2)(L, Lw)
+    mwx = lambda m: lib.paro_w4a16_linear_prepared_multi_workspace_bytes(mixed, 2, m)
+    assert mwx(4096) == mw(2, 4096)
+    assert mwx(16) == max(one(16), lib.paro_w4a16_linear_prepared_workspace_bytes(ctypes.byref(Lw), 16))
+    assert mwx(16) > one(16)
 
 
 @needs_no_gpu
@@ -450,7 +458,11 @@ def test_tiled_multi_argument_checks():
     ok_xt, ok_y = ptrs(FAKE * 4, FAKE * 5), ptrs(FAKE * 6, FAKE * 7)
     assert call([L0, L1], 0, ok_xt, ok_y) == 2
     assert call([L0, L1], 5, ok_xt, ok_y) == 2
-    assert call([L0, fake_layer(I=256, O=128)], 2, ok_xt, ok_y) == 2          # one shape
+    assert call([L0, fake_layer(I=384, O=64)], 2, ok_xt, ok_y) == 2          # one in_features
+    assert call([L0, fake_layer(I=256, O=64, G=64)], 2, ok_xt, ok_y) == 2    # one group size
+    # outputs sized by each layer's out_features: a 128-wide layer's output
+    # at 32 tokens (8 KB as fp16) reaches the next one 4 KB on
+    assert call([fake_layer(I=256, O=128), L1], 2, ok_xt, ptrs(FAKE * 6, FAKE * 6 + 4096)) == 2
     assert call([L0, L1], 2, ptrs(FAKE * 4, 0), ok_y) == 1
     assert call([L0, L1], 2, ok_xt, ptrs(FAKE * 6, FAKE * 6 + 64)) == 2      # outputs overlap
     assert call([L0, L1], 2, ok_xt, ptrs(FAKE * 6, FAKE * 5 + 32)) == 2      # an output overlaps an x_t

@@ -398,15 +398,21 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     struct Words {
       uint32_t ra, rb;
     };
-    // packed words of the next step of the sequence (steps in order)
+    // packed words of the next step of the sequence (steps in order).  The
+    // thread's byte offset within a step's rows depends on the tile alone
+    // (its column block and its layer's width), so it is formed where the
+    // cursor enters a tile rather than at every step.
     Cursor cw{0, 0, t0};
+    auto w_lane_of = [&](const Tile &t) { return (uint32_t)((2 * drp) * t.W + word_of(t)) * 4u; };
+    uint32_t w_lane = w_lane_of(t0);
     auto load_words = [&](Words &wd) {
       const int64_t W = cw.t.W;
-      const uint32_t w_off = (uint32_t)((2 * drp) * W + word_of(cw.t)) * 4u;
       const __amdgpu_buffer_rsrc_t r = raw_rsrc(cw.t.qweight + (int64_t)cw.pos * kBK * W, (uint32_t)(kBK * W * 4));
-      wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_off, 0, 0);
-      wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_off + (uint32_t)(W * 4), 0, 0);
+      wd.ra = __builtin_amdgcn_raw_buffer_load_b32(r, w_lane, 0, 0);
+      wd.rb = __builtin_amdgcn_raw_buffer_load_b32(r, w_lane + (uint32_t)(W * 4), 0, 0);
+      const int it0 = cw.it;
       advance(cw, nsteps);
+      if (cw.it != it0) w_lane = w_lane_of(cw.t);
     };
     struct GroupRaw {
       u32x4 sw;
@@ -414,14 +420,16 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     };
     // scales and zeros of the next group of the sequence (groups in order)
     Cursor cg{0, 0, t0};
+    uint32_t g_word = word_of(t0);
     auto load_group = [&](GroupRaw &gr) {
-      const uint32_t dwc = word_of(cg.t);
       const int64_t O = cg.t.O, W = cg.t.W;
       const __amdgpu_buffer_rsrc_t rs = raw_rsrc(cg.t.scales + (int64_t)cg.pos * O, (uint32_t)(O * 2));
-      gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, dwc * 16u, 0, 0);
+      gr.sw = __builtin_amdgcn_raw_buffer_load_b128(rs, g_word * 16u, 0, 0);
       const __amdgpu_buffer_rsrc_t rz = raw_rsrc(cg.t.qzeros + (int64_t)cg.pos * W, (uint32_t)(W * 4));
-      gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, dwc * 4u, 0, 0);
+      gr.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, g_word * 4u, 0, 0);
+      const int it0 = cg.it;
       advance(cg, ngroups);
+      if (cg.it != it0) g_word = word_of(cg.t);
     };
 
     // Scales and zeros: a ring of NSLOT groups.  Group q sits in slot

@@ -264,6 +264,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
   struct Tile {
     int64_t n0, mb, row_lo, row_hi;
     int64_t O, W;  // the layer's out_features and packed words per row
+    const uint16_t *xt;  // the layer's tiled activations (read at every k step)
     const int32_t *qweight, *qzeros;
     const uint16_t *scales, *bias;
     int layer;  // entry of the layer table (MoE: 0)
@@ -279,6 +280,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     if constexpr (MOE) {
       t.layer = 0;
       t.O = a.O;
+      t.xt = lt.xt[0];
       t.qweight = a.qweight;
       t.qzeros = a.qzeros;
       t.scales = a.scales;
@@ -290,6 +292,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
       t.layer = __builtin_amdgcn_readfirstlane(l);
       lwg -= ltp->tile0[t.layer];
       t.O = ltp->o[t.layer];
+      t.xt = t.layer == 0 ? lt.xt[0] : ltp->xt[t.layer];
       n_tiles = (int)((t.O + kBN - 1) / kBN);
       if (t.layer == 0) {  // entry 0 is also in a (the single-layer launch)
         t.qweight = a.qweight;
@@ -527,7 +530,7 @@ prefill_gemm_kernel(LinearArgs a, LayerTable lt) {
     const int64_t rtiles = (t.row_hi + 15) / 16 - t.mb / 16;
     const int tiles = (int)(rtiles < BM / 16 ? rtiles : BM / 16);
     const uint32_t kb = (uint32_t)ls * 1024u;
-    const uint16_t *xt = t.layer == 0 ? lt.xt[0] : ltp->xt[t.layer];
+    const uint16_t *xt = t.xt;
     const char *a_base = reinterpret_cast<const char *>(xt + (t.mb / 16) * (I / 32) * 512);
     const __amdgpu_buffer_rsrc_t r = raw_rsrc(a_base + kb, (uint32_t)tiles * tile_bytes - kb);
 #pragma unroll
